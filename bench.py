@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Throughput of the GPT-2 training step on one MI355X.
+
+Workload: GPT-2 124M (L=12, NH=12, C=768, V=50257 padded to 50304), bf16
+activations and matrix products with fp32 master weights, gradients and AdamW
+state; micro-batch B=8, T=1024; one step = 2 micro-steps (forward + backward,
+gradients accumulated with dloss = 1/(2*B*T)) + one AdamW update (lr 6e-4,
+betas 0.9/0.999, eps 1e-8, weight decay 0.1).  Random GPT-2 initialisation and
+a Zipf(1.1) token stream (seeded, synthetic), all resident in HBM before the
+timed region.
+
+Prints one JSON line: train tokens/s over the timed steps, MFU against the
+2.5 PFLOP/s dense bf16 peak, the roofline position of the dominant kernel
+(timed with HIP events on its stream), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def flops_per_token(L, C, V, T):
+    """Algorithmic training FLOPs per token: 3x the forward's
+    24 L C^2 (layer products) + 2 C V (classifier over the real vocabulary)
+    + 2 L (T+1) C (causal attention scores and weighted sum)."""
+    return 3.0 * (24.0 * L * C * C + 2.0 * C * V + 2.0 * L * (T + 1) * C)
+
+
+def cpu_baseline(cfg, budget_s=30.0):
+    """The CPU oracle (single-threaded C, fp64) on a bounded sample of the same
+    workload: one micro-step (forward + backward) of GPT-2 124M on B=1 x T
+    tokens with T chosen to stay within ~budget_s."""
+    import oracle
+    import synthetic as S
+    params = S.init_params(cfg)
+    flat = oracle.pack_params(cfg, {k: S.round_to_bf16(v) for k, v in params.items()})
+    T = 48
+    stream = S.token_stream(T + 1, cfg.vocab_size, dist="zipf")
+    x, y = S.batch(stream, 0, 1, T)
+    t0 = time.perf_counter()
+    oracle.gpt2_step(cfg, flat, x, y)
+    dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one forward+backward micro-step of GPT-2 124M, B=1 T={T} (fp64, single thread), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--seq", type=int, default=1024)
+    ap.add_argument("--accum", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the data-parallel multi-GPU path is not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic as S
+    from transformer_lm_step_amd import binding as Bnd
+    from transformer_lm_step_amd.model import GPT2
+
+    cfg = S.GPT2_124M
+    B, T, accum = args.batch, args.seq, args.accum
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: GPT-2 124M bf16 B={B} T={T} accum={accum} steps={args.steps} warmup={args.warmup}")
+
+    model = GPT2(cfg, Bnd.GPT2_BF16, B, T)
+    params = S.init_params(cfg)
+    model.init(model.pack(params))
+    n_micro = (args.warmup + args.steps) * accum
+    stream = S.token_stream(n_micro * B * T + 1, cfg.vocab_size, dist="zipf")
+    toks = torch.from_numpy(stream).to(dev)
+    BT = B * T
+    xs = [toks[i * BT:(i + 1) * BT] for i in range(n_micro)]
+    ys = [toks[i * BT + 1:(i + 1) * BT + 1].clone() for i in range(n_micro)]
+    mean_loss = torch.zeros(n_micro, dtype=torch.float32, device=dev)
+    dloss = 1.0 / (accum * BT)
+
+    def step(s):
+        model.zero_grad()
+        for a in range(accum):
+            i = s * accum + a
+            model.forward(xs[i], ys[i], None, mean_loss[i:i + 1])
+            model.backward(dloss)
+        model.update(6e-4, 0.9, 0.999, 1e-8, 0.1, s + 1)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    if model.check() != 0:
+        raise RuntimeError("device-side error during warmup")
+    log("bench: warmup done")
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(cur)
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    losses = mean_loss.cpu().numpy()
+    if not np.all(np.isfinite(losses)):
+        raise RuntimeError("non-finite loss")
+    tok_s = accum * BT / (ms / 1e3)
+    fpt = flops_per_token(cfg.num_layers, cfg.channels, cfg.vocab_size, T)
+    mfu = tok_s * fpt / (PEAK_BF16_TFLOPS * 1e12)
+    log(f"bench: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, MFU {mfu:.3f}, wall {wall:.2f}s, "
+        f"loss first {losses[0]:.4f} last {losses[-1]:.4f}")
+
+    # ---- dominant kernel: the classifier product logits[BT,Vp] = lnf[BT,C] wte[Vp,C]^T,
+    # launched standalone with the same kernel and launch configuration as in the step.
+    M, N, K = BT, cfg.padded_vocab_size, cfg.channels
+    x = torch.randn(M, K, device=dev).to(torch.bfloat16)
+    w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
+    y = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    sh = cur.cuda_stream
+    for _ in range(3):
+        Bnd.gpt2_linear_forward(Bnd.GPT2_BF16, x.data_ptr(), w.data_ptr(), 0, y.data_ptr(), M, N, K, sh)
+    reps = 20
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(cur)
+    for _ in range(reps):
+        Bnd.gpt2_linear_forward(Bnd.GPT2_BF16, x.data_ptr(), w.data_ptr(), 0, y.data_ptr(), M, N, K, sh)
+    k1.record(cur)
+    torch.cuda.synchronize()
+    kms = k0.elapsed_time(k1) / reps
+    kflop = 2.0 * M * N * K
+    achieved = kflop / (kms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_kernel (classifier forward, 8192x50304x768 bf16)", "avg_ms": round(kms, 4)}
+    log(f"bench: classifier GEMM {kms:.3f} ms, {achieved:.1f} TFLOP/s")
+    del x, w, y
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle sample ...")
+        cpu = cpu_baseline(cfg)
+        log(f"bench: oracle {cpu['value']:.3f} tok/s ({cpu['sample']})")
+
+    out = {
+        "metric": "train tokens/sec + MFU, GPT-2 124M bf16 B=8 T=1024 on 1x MI355X",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (Zipf(1.1) token stream, random GPT-2 init)",
+        "config": {"workload": "GPT-2 124M training step: 2 micro-steps of B=8 T=1024 + AdamW",
+                   "global_batch": accum * B, "seq_len": T, "grad_accum": accum, "parallelism": "single GPU"},
+        "mfu": round(mfu, 4),
+        "flops_per_token": fpt,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * gpt2.h - C ABI of the MI355X (gfx950) GPT-2 training-step library.
+ *
+ * One GPT-2 training micro-step -- forward, backward, AdamW -- over a
+ * decoder-only transformer, every step in hand-written HIP kernels.  The model
+ * and its step follow the "train_gpt2.cu" page (llm.c, mixed precision):
+ * GPT2Config, ParameterTensors, gpt2_forward, gpt2_zero_grad, gpt2_backward and
+ * gpt2_update.  Differences from that page are listed per function.
+ *
+ * Conventions for every entry point:
+ *  - All pointers named d_* (and every pointer inside gpt2_buffers) are DEVICE
+ *    pointers, allocated and owned by the caller, 256-byte aligned, valid on the
+ *    device that is current when the call is made.  The library never allocates
+ *    or frees device memory.
+ *  - hip_stream is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; results are ready when the stream is.
+ *  - Return value: GPT2_OK (0) or a negative GPT2_E_* code; no entry point
+ *    exits the process.  gpt2_strerror names the code.
+ *  - A context is not thread-safe: calls on one context must be serialised by
+ *    the caller.
+ *  - Layout: every matrix is row-major.  Weights are (out_features,
+ *    in_features), as on the page.  Activations are [B*T, channels].
+ */
+#ifndef GPT2_MI355X_H
+#define GPT2_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* train_gpt2.cu, GPT2Config.  padded_vocab_size >= vocab_size; the classifier
+ * runs over padded_vocab_size columns, the loss over vocab_size of them. */
+typedef struct {
+    int max_seq_len;
+    int vocab_size;
+    int padded_vocab_size;
+    int num_layers;
+    int num_heads;
+    int channels;
+} gpt2_config;
+
+/* Arithmetic mode (train_gpt2.cu, PrecisionMode; fp16 is not offered because
+ * the page leaves it unsupported).
+ *  GPT2_FP32: fp32 parameters, activations and products (full-precision fp32
+ *             products, no reduced-precision inputs).
+ *  GPT2_BF16: bf16 parameters, activations and matrix-core products with fp32
+ *             accumulation; fp32 master weights, fp32 gradients, fp32 AdamW
+ *             state, fp32 LayerNorm statistics, losses and residual gradient. */
+enum { GPT2_FP32 = 0, GPT2_BF16 = 1 };
+
+enum {
+    GPT2_OK = 0,
+    GPT2_E_ARG = -1,    /* NULL / out-of-range argument */
+    GPT2_E_SHAPE = -2,  /* unsupported shape (see gpt2_init) */
+    GPT2_E_STATE = -3,  /* call order violated (e.g. backward without a forward with targets) */
+    GPT2_E_TOKEN = -4,  /* a token or target id outside [0, vocab_size) was seen on the device */
+    GPT2_E_ALIGN = -5,  /* a pointer is not 256-byte aligned */
+    GPT2_E_HIP = -6     /* a HIP runtime call or kernel launch failed */
+};
+
+typedef struct gpt2_ctx gpt2_ctx;
+
+/* Byte sizes of the caller-owned device buffers for one (config, precision,
+ * B, T).  master is 0 in GPT2_FP32 mode. */
+typedef struct {
+    size_t params, master, grads, adam_m, adam_v, acts, scratch;
+} gpt2_sizes;
+
+/* The device buffers, each at least the size gpt2_query_sizes reports.
+ *  params : the 16 parameter tensors, flat, in gpt2_param_layout order;
+ *           fp32 (GPT2_FP32) or bf16 (GPT2_BF16).
+ *  master : GPT2_BF16 only: fp32 copy of params (the AdamW master weights);
+ *           NULL in GPT2_FP32 mode.
+ *  grads, adam_m, adam_v : fp32, flat, same layout.
+ *  acts   : forward activations and backward scratch (opaque except for the
+ *           tensors gpt2_act_tensor exposes).
+ *  scratch: split-K and reduction workspace (opaque). */
+typedef struct {
+    void *params, *master, *grads, *adam_m, *adam_v, *acts, *scratch;
+} gpt2_buffers;
+
+/* Fills *out with the buffer sizes.  Errors: GPT2_E_ARG, GPT2_E_SHAPE. */
+int gpt2_query_sizes(const gpt2_config* cfg, int precision, int B, int T, gpt2_sizes* out);
+
+/* Element offsets and counts of the 16 parameter tensors in the page's order
+ * (train_gpt2.cu, ParameterTensors / fill_in_parameter_sizes): wte (Vp,C),
+ * wpe (maxT,C), ln1w (L,C), ln1b (L,C), qkvw (L,3C,C), qkvb (L,3C),
+ * attprojw (L,C,C), attprojb (L,C), ln2w (L,C), ln2b (L,C), fcw (L,4C,C),
+ * fcb (L,4C), fcprojw (L,C,4C), fcprojb (L,C), lnfw (C), lnfb (C).
+ * *total receives the parameter count.  Errors: GPT2_E_ARG. */
+int gpt2_param_layout(const gpt2_config* cfg, size_t offset[16], size_t count[16], size_t* total);
+
+/* Creates a context bound to the caller's buffers for fixed B and T (the page
+ * fixes them at the first forward).  Enqueues on hip_stream: zeroing of
+ * adam_m and adam_v (as gpt2_update does at its first call) and, in GPT2_BF16
+ * mode, the round-to-nearest-even cast master -> params (the caller writes the
+ * fp32 initial values into master).  In GPT2_FP32 mode the caller writes
+ * params directly.
+ * Shape limits: channels % num_heads == 0; head size C/NH a multiple of 16 and
+ * at most 128; channels and padded_vocab_size multiples of 8;
+ * 1 <= T <= max_seq_len; B >= 1; padded_vocab_size <= 53248.
+ * Errors: GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_ALIGN, GPT2_E_HIP. */
+int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, int precision, int B, int T,
+              const gpt2_buffers* bufs, void* hip_stream);
+
+/* train_gpt2.cu, gpt2_forward.  d_inputs [B*T] int32 token ids.  d_targets
+ * [B*T] int32 or NULL.  With targets: per-position losses are written to
+ * d_losses [B*T] fp32 (if not NULL), their mean to d_mean_loss [1] fp32 (if not
+ * NULL), and the logits are overwritten in place by softmax - onehot (over the
+ * first vocab_size columns; the padded columns are set to 0), which backward
+ * consumes -- so logits are not readable after a forward with targets.
+ * Without targets the logits stay readable (gpt2_act_tensor).  Ids outside
+ * [0, vocab_size) are clamped for memory safety and raise a device flag that
+ * gpt2_check_device_error reports (the page asserts on the host).
+ * Errors: GPT2_E_ARG, GPT2_E_ALIGN, GPT2_E_HIP. */
+int gpt2_forward(gpt2_ctx* ctx, const int32_t* d_inputs, const int32_t* d_targets,
+                 float* d_losses, float* d_mean_loss, void* hip_stream);
+
+/* train_gpt2.cu, gpt2_zero_grad, restricted to the parameter gradients (the
+ * activation gradients are internal and overwritten by every backward).
+ * Errors: GPT2_E_ARG, GPT2_E_HIP. */
+int gpt2_zero_grad(gpt2_ctx* ctx, void* hip_stream);
+
+/* train_gpt2.cu, gpt2_backward.  Parameter gradients are ADDED into grads, so
+ * consecutive backwards accumulate (gradient accumulation).  dloss scales the
+ * loss gradient: dloss <= 0 means 1/(B*T), the page's fixed choice; with
+ * accumulation over n micro-steps pass 1/(n*B*T).  The residual-stream
+ * gradient is kept in fp32 and re-initialised by every backward.
+ * Errors: GPT2_E_ARG, GPT2_E_STATE (the last forward had no targets),
+ * GPT2_E_HIP. */
+int gpt2_backward(gpt2_ctx* ctx, float dloss, void* hip_stream);
+
+/* train_gpt2.cu, gpt2_update / adamw_kernel3: for every parameter
+ * m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2, p -= lr (m/(1-b1^t)) /
+ * (sqrt(v/(1-b2^t)) + eps) + lr wd p, with one weight decay for all
+ * parameters.  t is the 1-based step.  GPT2_BF16: the fp32 master weights are
+ * updated and params receives their round-to-nearest-even bf16 value.
+ * Errors: GPT2_E_ARG (t < 1), GPT2_E_HIP. */
+int gpt2_adamw_update(gpt2_ctx* ctx, float lr, float beta1, float beta2, float eps,
+                      float weight_decay, int t, void* hip_stream);
+
+/* Synchronises hip_stream and reports device-side conditions raised since the
+ * last call (GPT2_E_TOKEN for an out-of-range id), then clears them. */
+int gpt2_check_device_error(gpt2_ctx* ctx, void* hip_stream);
+
+/* Device pointer and element count of an internal activation tensor, for
+ * inspection.  Tensor ids: GPT2_T_LOGITS [B*T, Vp] (logits after a forward
+ * without targets; softmax - onehot after one with targets), GPT2_T_LNF
+ * [B*T, C], GPT2_T_RESIDUAL [B*T, C] (final residual stream),
+ * GPT2_T_DRESIDUAL [B*T, C] fp32 (residual gradient after a backward, i.e.
+ * the gradient of the loss w.r.t. the encoder output), GPT2_T_ENCODED
+ * [B*T, C] (token + position encoding).  Element type is the activation
+ * type (fp32 or bf16) except where stated.
+ * Errors: GPT2_E_ARG. */
+enum { GPT2_T_LOGITS = 0, GPT2_T_LNF = 1, GPT2_T_RESIDUAL = 2, GPT2_T_DRESIDUAL = 3, GPT2_T_ENCODED = 4 };
+int gpt2_act_tensor(gpt2_ctx* ctx, int which, void** d_ptr, size_t* count);
+
+/* Frees the host-side context (no device memory is owned). */
+int gpt2_free(gpt2_ctx* ctx);
+
+const char* gpt2_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

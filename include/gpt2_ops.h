@@ -1,0 +1,30 @@
+/*
+ * gpt2_ops.h - single operations of the GPT-2 step as standalone entry points.
+ *
+ * Each entry point launches exactly the kernels, in exactly the launch
+ * configuration, that gpt2_forward / gpt2_backward use for that operation, on
+ * caller-owned device memory (256-byte aligned, row-major), asynchronously on
+ * hip_stream.  They exist so that one operation can be checked and timed on
+ * its own at full size.  Return: GPT2_OK or a GPT2_E_* code (see gpt2.h).
+ */
+#ifndef GPT2_MI355X_OPS_H
+#define GPT2_MI355X_OPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* train_gpt2.cu, matmul_forward_cublaslt: y[M,N] = x[M,K] w[N,K]^T (+ bias[N]
+ * when d_bias is not NULL).  precision GPT2_FP32 (fp32 tensors) or GPT2_BF16
+ * (bf16 tensors, fp32 accumulation).  K and N multiples of 8.
+ * Errors: GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_ALIGN, GPT2_E_HIP. */
+int gpt2_linear_forward(int precision, const void* d_x, const void* d_w, const void* d_bias, void* d_y,
+                        int M, int N, int K, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,114 @@
+"""CPU-only checks of the HIP library: it loads, exports every symbol that
+include/gpt2.h declares, and its host logic (layout, buffer plan, argument and
+shape checks) behaves as documented.  No kernel is launched here: every call
+below returns before any device work."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    from transformer_lm_step_amd import binding as B
+    decl = declared_symbols()
+    assert "gpt2_init" in decl and "gpt2_adamw_update" in decl
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = decl - exported
+    assert not missing, missing
+    for name in decl:
+        getattr(B.lib(), name)
+
+
+def test_param_layout_matches_oracle_layout():
+    from transformer_lm_step_amd import binding as B
+    for cfg in (S.TINY, S.GPT2_124M, S.GPT2_1558M):
+        assert B.gpt2_param_layout(cfg) == oracle.param_layout(cfg)
+
+
+def test_query_sizes_plan():
+    from transformer_lm_step_amd import binding as B
+    P = 124475904
+    s = B.gpt2_query_sizes(S.GPT2_124M, B.GPT2_BF16, 8, 1024)
+    assert s["params"] >= 2 * P and s["master"] >= 4 * P
+    assert s["grads"] >= 4 * P and s["adam_m"] >= 4 * P and s["adam_v"] >= 4 * P
+    assert all(v % 256 == 0 for v in s.values())
+    # activations: at least the logits (bf16) and 12 layers of the 8 per-layer tensors
+    BT, C = 8 * 1024, 768
+    assert s["acts"] >= BT * 50304 * 2 + 12 * BT * C * 2 * 16
+    s32 = B.gpt2_query_sizes(S.TINY, B.GPT2_FP32, 4, 64)
+    assert s32["master"] == 0 and s32["params"] >= 136960 * 4
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(channels=100), -2),                 # head size not a multiple of 16
+    (dict(num_heads=3), -2),                  # C % NH != 0
+    (dict(padded_vocab_size=500), -1),        # Vp < V
+    (dict(padded_vocab_size=60000, vocab_size=59000), -2),
+    (dict(channels=4096, num_heads=32), -2),  # C > 2048
+])
+def test_config_errors(mut, code):
+    from transformer_lm_step_amd import binding as B
+    import dataclasses
+    cfg = dataclasses.replace(S.TINY, **mut)
+    with pytest.raises(B.GPT2Error) as e:
+        B.gpt2_query_sizes(cfg, B.GPT2_FP32, 4, 64)
+    assert e.value.code == code
+
+
+def test_shape_and_argument_errors():
+    from transformer_lm_step_amd import binding as B
+    with pytest.raises(B.GPT2Error) as e:
+        B.gpt2_query_sizes(S.TINY, B.GPT2_FP32, 4, 65)  # T > max_seq_len
+    assert e.value.code == B.GPT2_E_SHAPE
+    with pytest.raises(B.GPT2Error) as e:
+        B.gpt2_query_sizes(S.TINY, 7, 4, 64)  # unknown precision
+    assert e.value.code == B.GPT2_E_ARG
+    with pytest.raises(B.GPT2Error) as e:
+        B.gpt2_query_sizes(S.TINY, B.GPT2_FP32, 0, 64)
+    assert e.value.code == B.GPT2_E_SHAPE
+
+
+def test_init_rejects_missing_and_misaligned_buffers_without_device_work():
+    from transformer_lm_step_amd import binding as B
+    good = {k: 0x100000 * (i + 1) for i, k in enumerate(("params", "master", "grads", "adam_m", "adam_v", "acts", "scratch"))}
+    missing = dict(good, grads=0)
+    with pytest.raises(B.GPT2Error) as e:
+        B.gpt2_init(S.TINY, B.GPT2_FP32, 4, 64, missing, 0)
+    assert e.value.code == B.GPT2_E_ARG
+    bad = dict(good, acts=good["acts"] + 8)
+    with pytest.raises(B.GPT2Error) as e:
+        B.gpt2_init(S.TINY, B.GPT2_FP32, 4, 64, bad, 0)
+    assert e.value.code == B.GPT2_E_ALIGN
+    with pytest.raises(B.GPT2Error) as e:  # bf16 needs master weights
+        B.gpt2_init(S.TINY, B.GPT2_BF16, 4, 64, dict(good, master=0), 0)
+    assert e.value.code == B.GPT2_E_ARG
+
+
+def test_null_context_calls_fail_cleanly():
+    from transformer_lm_step_amd import binding as B
+    L = B.lib()
+    assert L.gpt2_forward(None, None, None, None, None, None) == B.GPT2_E_ARG
+    assert L.gpt2_backward(None, ctypes.c_float(0.0), None) == B.GPT2_E_ARG
+    assert L.gpt2_zero_grad(None, None) == B.GPT2_E_ARG
+    assert L.gpt2_adamw_update(None, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == B.GPT2_E_ARG
+    assert B.strerror(B.GPT2_E_TOKEN).startswith("token")

@@ -1,0 +1,154 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars (fp32): loss rel <= 1e-5; every gradient tensor rel-L2 <= 1e-4; every
+updated parameter tensor and AdamW moment rel-L2 <= 1e-4.
+Bars (bf16): loss abs <= 2e-2; gradient cosine >= 0.995 per tensor.
+Token gather / causal mask / padded vocabulary: bit-exact (see test_gpu_exact).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from helpers import PARAM_NAMES, cosine, gpu_step, make_inputs, oracle_step, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+# several tiles and ragged tails: BT = 300 (128-row tiles), T = 150 (64-row
+# attention blocks), Vp = 1000 (128-column tiles), head size 64 and 32
+RAGGED64 = S.Config(max_seq_len=160, vocab_size=997, padded_vocab_size=1000, num_layers=2, num_heads=3, channels=192)
+RAGGED32 = S.Config(max_seq_len=160, vocab_size=997, padded_vocab_size=1000, num_layers=1, num_heads=6, channels=192)
+
+FP32_CASES = [
+    ("tiny", S.TINY, 4, 64, False),
+    ("tiny-perturbed", S.TINY, 4, 64, True),
+    ("ragged-hs64", RAGGED64, 2, 150, True),
+    ("ragged-hs32", RAGGED32, 3, 100, True),
+]
+
+
+def key_bias_mask(cfg):
+    """Elements of qkvb that are key biases.  Their gradient is exactly zero in
+    exact arithmetic: adding the same q.b_k to every score of a softmax row
+    changes nothing.  Adam divides by the gradient's magnitude, so the update
+    of those elements is set by round-off on both sides and is compared only
+    for being bounded by the learning rate."""
+    L, C = cfg.num_layers, cfg.channels
+    m = np.zeros((L, 3 * C), bool)
+    m[:, C:2 * C] = True
+    return m.ravel()
+
+
+def _check_key_bias(cfg, o, g, lr):
+    kb = key_bias_mask(cfg)
+    go, gg = o["grads"]["qkvb"].ravel(), g["grads"]["qkvb"].ravel()
+    scale = np.abs(go[~kb]).max()
+    assert np.abs(go[kb]).max() <= 1e-12 * max(scale, 1.0)
+    assert np.abs(gg[kb]).max() <= 1e-5 * scale
+    return kb
+
+
+def _compare_fp32(name, o, g, n_micro=1, cfg=None, lr=1e-4, p0=None):
+    kb = _check_key_bias(cfg, o, g, lr)
+    d = g["params"]["qkvb"].ravel()[kb] - p0["qkvb"].astype(np.float64).ravel()[kb]
+    assert np.all(np.abs(d) <= lr * 1.001 + 1e-12)
+    for i in range(n_micro):
+        lo, lg = np.asarray(o["losses"][i]), g["losses"][i]
+        assert np.max(np.abs(lg - lo) / np.abs(lo)) < 1e-5, (name, "per-position loss")
+        assert abs(g["means"][i] - o["means"][i]) / abs(o["means"][i]) < 1e-5, (name, "mean loss")
+    worst = {}
+    for key in ("grads", "params", "m", "v"):
+        for p in PARAM_NAMES:
+            a, b = np.ravel(g[key][p]), np.ravel(o[key][p])
+            if p == "qkvb" and key != "grads":
+                a, b = a[~kb], b[~kb]
+            e = rel_l2(a, b)
+            worst[f"{key}.{p}"] = e
+            assert e < 1e-4, (name, key, p, e)
+    say(name, "worst rel-L2", max(worst.items(), key=lambda kv: kv[1]))
+
+
+@pytest.mark.parametrize("name,cfg,B,T,perturb", FP32_CASES, ids=[c[0] for c in FP32_CASES])
+def test_fp32_step_matches_oracle(name, cfg, B, T, perturb):
+    say("case", name, "fp32", B, T)
+    params, batches = make_inputs(cfg, B, T, perturb=perturb)
+    o = oracle_step(cfg, params, batches, lr=1e-4)
+    g = gpu_step(cfg, 0, params, batches, lr=1e-4)
+    assert g["code"] == 0
+    _compare_fp32(name, o, g, cfg=cfg, lr=1e-4, p0=params)
+    # padded vocabulary rows: zero gradient, unchanged (zero) parameters
+    V = cfg.vocab_size
+    assert np.all(g["grads"]["wte"].reshape(cfg.padded_vocab_size, -1)[V:] == 0.0)
+    assert np.all(g["params"]["wte"].reshape(cfg.padded_vocab_size, -1)[V:] == 0.0)
+
+
+def test_fp32_grad_accumulation_and_weight_decay():
+    cfg = RAGGED64
+    say("case fp32 accumulation", cfg)
+    params, batches = make_inputs(cfg, 2, 96, n_micro=2, perturb=True)
+    dloss = 1.0 / (2 * 2 * 96)
+    o = oracle_step(cfg, params, batches, dloss=dloss, lr=6e-4, wd=0.1)
+    g = gpu_step(cfg, 0, params, batches, dloss=dloss, lr=6e-4, wd=0.1)
+    _compare_fp32("accum", o, g, n_micro=2, cfg=cfg, lr=6e-4, p0=params)
+
+
+@pytest.mark.parametrize("name,cfg,B,T,perturb", FP32_CASES[1:3], ids=[c[0] for c in FP32_CASES[1:3]])
+def test_bf16_step_matches_oracle(name, cfg, B, T, perturb):
+    say("case", name, "bf16", B, T)
+    params, batches = make_inputs(cfg, B, T, perturb=perturb, bf16=True)
+    o = oracle_step(cfg, params, batches, lr=1e-4)
+    g = gpu_step(cfg, 1, params, batches, lr=1e-4)
+    assert g["code"] == 0
+    assert abs(g["means"][0] - o["means"][0]) <= 2e-2
+    assert np.max(np.abs(g["losses"][0] - o["losses"][0])) <= 2e-2 * 4
+    cos = {p: cosine(g["grads"][p], o["grads"][p]) for p in PARAM_NAMES}
+    say(name, "min grad cosine", min(cos.items(), key=lambda kv: kv[1]))
+    for p, c in cos.items():
+        assert c >= 0.995, (p, c)
+    # the AdamW update direction: cosine of (p1 - p0) per tensor
+    p0 = params
+    kb = key_bias_mask(cfg)
+    for p in PARAM_NAMES:
+        dg = np.ravel(g["params"][p]) - p0[p].astype(np.float64).ravel()
+        do = np.ravel(o["params"][p]) - p0[p].astype(np.float64).ravel()
+        if p == "qkvb":
+            dg, do = dg[~kb], do[~kb]
+        c = cosine(dg, do)
+        assert c >= 0.9, (p, c)
+
+
+def test_bf16_accumulation_matches_oracle():
+    cfg = RAGGED64
+    say("case bf16 accumulation")
+    params, batches = make_inputs(cfg, 2, 128, n_micro=2, perturb=True, bf16=True)
+    dloss = 1.0 / (2 * 2 * 128)
+    o = oracle_step(cfg, params, batches, dloss=dloss, lr=6e-4, wd=0.1)
+    g = gpu_step(cfg, 1, params, batches, dloss=dloss, lr=6e-4, wd=0.1)
+    for i in range(2):
+        assert abs(g["means"][i] - o["means"][i]) <= 2e-2
+    for p in PARAM_NAMES:
+        c = cosine(g["grads"][p], o["grads"][p])
+        assert c >= 0.995, (p, c)
+
+
+def test_deterministic_bitwise():
+    cfg = RAGGED64
+    say("case determinism bf16")
+    params, batches = make_inputs(cfg, 2, 150, perturb=True, bf16=True)
+    a = gpu_step(cfg, 1, params, batches)
+    b = gpu_step(cfg, 1, params, batches)
+    for p in PARAM_NAMES:
+        assert np.array_equal(a["grads"][p], b["grads"][p]), p
+        assert np.array_equal(a["params"][p], b["params"][p]), p
+    assert np.array_equal(a["losses"][0], b["losses"][0])
+
+
+def test_loss_at_init_near_log_v():
+    cfg = S.TINY
+    params, batches = make_inputs(cfg, 4, 64)
+    g = gpu_step(cfg, 0, params, batches)
+    expect = math.log(cfg.vocab_size) + cfg.channels * 0.02 ** 2 / 2
+    assert abs(g["means"][0] - expect) < 0.02

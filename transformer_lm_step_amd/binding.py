@@ -1,0 +1,170 @@
+"""ctypes binding of include/gpt2.h -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls and takes
+integer device pointers (``tensor.data_ptr()``) and an integer HIP stream
+handle (``torch.cuda.current_stream().cuda_stream``).  Errors come back as
+:class:`GPT2Error`.  All compute runs in the HIP library; if the library has
+not been built this module raises at import time -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgpt2_hip.so")
+
+GPT2_FP32 = 0
+GPT2_BF16 = 1
+GPT2_OK, GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_STATE, GPT2_E_TOKEN, GPT2_E_ALIGN, GPT2_E_HIP = 0, -1, -2, -3, -4, -5, -6
+GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0, 1, 2, 3, 4
+
+EXPORTED = (
+    "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
+    "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
+    "gpt2_free", "gpt2_strerror", "gpt2_linear_forward",
+)
+
+
+class GPT2Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+
+
+class gpt2_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "max_seq_len", "vocab_size", "padded_vocab_size", "num_layers", "num_heads", "channels")]
+
+
+_BUF_FIELDS = ("params", "master", "grads", "adam_m", "adam_v", "acts", "scratch")
+
+
+class gpt2_sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in _BUF_FIELDS]
+
+
+class gpt2_buffers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _BUF_FIELDS]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m transformer_lm_step_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    cfgp = ctypes.POINTER(gpt2_config)
+    sig = {
+        "gpt2_query_sizes": (i, [cfgp, i, i, i, ctypes.POINTER(gpt2_sizes)]),
+        "gpt2_param_layout": (i, [cfgp, ctypes.POINTER(z), ctypes.POINTER(z), ctypes.POINTER(z)]),
+        "gpt2_init": (i, [ctypes.POINTER(vp), cfgp, i, i, i, ctypes.POINTER(gpt2_buffers), vp]),
+        "gpt2_forward": (i, [vp, vp, vp, vp, vp, vp]),
+        "gpt2_zero_grad": (i, [vp, vp]),
+        "gpt2_backward": (i, [vp, f, vp]),
+        "gpt2_adamw_update": (i, [vp, f, f, f, f, f, i, vp]),
+        "gpt2_check_device_error": (i, [vp, vp]),
+        "gpt2_act_tensor": (i, [vp, i, ctypes.POINTER(vp), ctypes.POINTER(z)]),
+        "gpt2_free": (i, [vp]),
+        "gpt2_strerror": (ctypes.c_char_p, [i]),
+        "gpt2_linear_forward": (i, [i, vp, vp, vp, vp, i, i, i, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _cfg(cfg) -> gpt2_config:
+    return gpt2_config(cfg.max_seq_len, cfg.vocab_size, cfg.padded_vocab_size,
+                       cfg.num_layers, cfg.num_heads, cfg.channels)
+
+
+def _check(rc: int, where: str):
+    if rc != GPT2_OK:
+        raise GPT2Error(rc, where)
+
+
+def strerror(code: int) -> str:
+    return _lib.gpt2_strerror(int(code)).decode()
+
+
+gpt2_strerror = strerror
+
+
+def gpt2_query_sizes(cfg, precision: int, B: int, T: int) -> dict:
+    s = gpt2_sizes()
+    c = _cfg(cfg)
+    _check(_lib.gpt2_query_sizes(ctypes.byref(c), precision, B, T, ctypes.byref(s)), "gpt2_query_sizes")
+    return {n: int(getattr(s, n)) for n in _BUF_FIELDS}
+
+
+def gpt2_param_layout(cfg):
+    off = (ctypes.c_size_t * 16)()
+    cnt = (ctypes.c_size_t * 16)()
+    tot = ctypes.c_size_t()
+    c = _cfg(cfg)
+    _check(_lib.gpt2_param_layout(ctypes.byref(c), off, cnt, ctypes.byref(tot)), "gpt2_param_layout")
+    return list(off), list(cnt), int(tot.value)
+
+
+def gpt2_init(cfg, precision: int, B: int, T: int, buffers: dict, stream: int) -> int:
+    ctx = ctypes.c_void_p()
+    c = _cfg(cfg)
+    b = gpt2_buffers(*[buffers.get(n) or None for n in _BUF_FIELDS])
+    _check(_lib.gpt2_init(ctypes.byref(ctx), ctypes.byref(c), precision, B, T, ctypes.byref(b), stream or None),
+           "gpt2_init")
+    return ctx.value
+
+
+def gpt2_forward(ctx: int, d_inputs: int, d_targets: int, d_losses: int, d_mean_loss: int, stream: int):
+    _check(_lib.gpt2_forward(ctx, d_inputs or None, d_targets or None, d_losses or None, d_mean_loss or None,
+                             stream or None), "gpt2_forward")
+
+
+def gpt2_zero_grad(ctx: int, stream: int):
+    _check(_lib.gpt2_zero_grad(ctx, stream or None), "gpt2_zero_grad")
+
+
+def gpt2_backward(ctx: int, dloss: float, stream: int):
+    _check(_lib.gpt2_backward(ctx, float(dloss), stream or None), "gpt2_backward")
+
+
+def gpt2_adamw_update(ctx: int, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, t: int,
+                      stream: int):
+    _check(_lib.gpt2_adamw_update(ctx, lr, beta1, beta2, eps, weight_decay, int(t), stream or None),
+           "gpt2_adamw_update")
+
+
+def gpt2_check_device_error(ctx: int, stream: int) -> int:
+    """Returns the status code (GPT2_OK or GPT2_E_TOKEN) instead of raising for
+    device-side conditions; raises for failures of the call itself."""
+    rc = _lib.gpt2_check_device_error(ctx, stream or None)
+    if rc not in (GPT2_OK, GPT2_E_TOKEN):
+        raise GPT2Error(rc, "gpt2_check_device_error")
+    return rc
+
+
+def gpt2_act_tensor(ctx: int, which: int):
+    p = ctypes.c_void_p()
+    n = ctypes.c_size_t()
+    _check(_lib.gpt2_act_tensor(ctx, which, ctypes.byref(p), ctypes.byref(n)), "gpt2_act_tensor")
+    return p.value, int(n.value)
+
+
+def gpt2_free(ctx: int):
+    _check(_lib.gpt2_free(ctx), "gpt2_free")
+
+
+def gpt2_linear_forward(precision: int, d_x: int, d_w: int, d_bias: int, d_y: int, M: int, N: int, K: int,
+                        stream: int):
+    _check(_lib.gpt2_linear_forward(precision, d_x, d_w, d_bias or None, d_y, M, N, K, stream or None),
+           "gpt2_linear_forward")

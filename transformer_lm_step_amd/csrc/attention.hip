@@ -1,0 +1,467 @@
+// attention.hip - causal multi-head attention, forward and backward (gfx950).
+//
+// What is computed is train_gpt2.cu's attention_forward / attention_backward
+// (permute_kernel, the two batched products, softmax_forward_kernel5,
+// softmax_autoregressive_backward_kernel, unpermute_kernel): per (b, h),
+//   S = Q K^T / sqrt(HS), P = softmax over the causal prefix s <= t, O = P V,
+//   dP = dO V^T, dV = P^T dO, dS = P * (dP - rowsum(P * dP)) / sqrt(HS),
+//   dQ = dS K, dK = dS^T Q.
+// Q, K, V are read in place from the qkv activation (B, T, 3, NH, HS) and O is
+// written as (B, T, NH, HS), so the page's permute / unpermute copies vanish.
+//
+// The T x T matrices are never stored.  The forward keeps, per query row, the
+// running maximum and sum of an online softmax (base 2: scores are scaled by
+// log2(e)/sqrt(HS)) and stores lse2 = max + log2(sum); the backward rebuilds
+// P = exp2(S * log2(e)/sqrt(HS) - lse2) tile by tile.  rowsum(P * dP) equals
+// rowsum(dO * O), computed up front (delta).  The backward runs as two kernels
+// so that every output element is produced by exactly one workgroup with a
+// fixed summation order (no atomics): one per 64-key block accumulating dK and
+// dV over the query blocks at or after it, one per 64-query block accumulating
+// dQ over the key blocks at or before it.
+//
+// Tiling: a workgroup is 4 wave64s and owns a 64-row block (queries in the
+// forward and dQ kernels, keys in the dK/dV kernel); each wave owns 16 of those
+// rows, held as MFMA fragments in registers for the whole kernel.  The other
+// side (64 keys or 64 queries per step) is staged in LDS, as row x d (for the
+// S / dP products) and as d x row (for the P V, dS K, P^T dO, dS^T Q
+// products).  Score tiles are computed transposed where needed so that the
+// lane owning a row's statistics also owns that row in the next product, and
+// a 16x16 score tile pair is fed straight back as the next MFMA's operand
+// (slot j of lane group g <-> row 32c + 16*(j/4) + 4g + j%4, the same map on
+// both operands).  Workgroups are issued longest-first along the causal
+// triangle.
+#include <math.h>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+template <typename T, int HS>
+struct ACfg {
+    static constexpr int KD = HS < 32 ? 32 : HS;         // d extent padded to one MFMA step
+    static constexpr int DSTEPS = KD / 32;               // MFMA steps over d
+    static constexpr int DT = HS / 16;                   // 16-wide d tiles of an output
+    static constexpr int RP = KD + 16 / (int)sizeof(T);  // pitch of row x d tiles
+    static constexpr int TP = 64 + 16 / (int)sizeof(T);  // pitch of d x row tiles
+    static constexpr int VEC = VecT<T>::N;
+};
+
+// 64 rows x KD of one head slice: dst[row*RP + d] = src(row0+row, d); zero past T or HS.
+template <typename T, int HS>
+DEV void stage_rows(T* dst, const T* src, long rs, int row0, int T_, int tid) {
+    using A = ACfg<T, HS>;
+    constexpr int VPR = A::KD / A::VEC;
+    for (int idx = tid; idx < 64 * VPR; idx += 256) {
+        const int row = idx / VPR, d0 = (idx % VPR) * A::VEC;
+        const int gr = row0 + row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (gr < T_ && d0 < HS) v = ld16(src + (long)gr * rs + d0);
+        st16(dst + row * A::RP + d0, v);
+    }
+}
+// The same 64 rows transposed: dst[d*TP + row] (rows past T are zero).
+template <typename T, int HS>
+DEV void stage_rows_t(T* dst, const T* src, long rs, int row0, int T_, int tid) {
+    using A = ACfg<T, HS>;
+    constexpr int DG = HS / A::VEC;
+    for (int idx = tid; idx < 16 * DG; idx += 256) {
+        const int kq = idx % 16, dg = idx / 16;
+        uint4 r[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int gr = row0 + 4 * kq + i;
+            r[i] = gr < T_ ? ld16(src + (long)gr * rs + dg * A::VEC) : make_uint4(0, 0, 0, 0);
+        }
+        store_t4<T>(dst + dg * A::VEC * A::TP + 4 * kq, A::TP, r);
+    }
+}
+
+// This lane's row (global index `row`) of a head slice as DSTEPS fragments over d.
+template <typename T, int HS>
+DEV void row_frags(Frag<T>* f, const T* src, long rs, int row, int T_, int g4) {
+#pragma unroll
+    for (int ks = 0; ks < ACfg<T, HS>::DSTEPS; ks++) {
+        const int d0 = 32 * ks + 8 * g4;
+        if (row < T_ && d0 < HS) frag_gld(f[ks], src + (long)row * rs + d0);
+        else frag_zero(f[ks]);
+    }
+}
+
+// ------------------------------------------------------------------ forward -
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(T* __restrict__ out, float* __restrict__ lse,
+                                                       const T* __restrict__ qkv, int T_, int C, int NH,
+                                                       float sl2) {
+    using A = ACfg<T, HS>;
+    __shared__ __attribute__((aligned(16))) T sK[64 * A::RP];
+    __shared__ __attribute__((aligned(16))) T sVt[HS * A::TP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int qb = gridDim.x - 1 - blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const long rs = 3L * C;
+    const T* Qh = qkv + (long)b * T_ * rs + h * HS;
+    const T* Kh = Qh + C;
+    const T* Vh = Qh + 2 * C;
+    const int q = qb * 64 + wave * 16 + l16;
+
+    Frag<T> fq[A::DSTEPS];
+    row_frags<T, HS>(fq, Qh, rs, q, T_, g4);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t o[A::DT];
+#pragma unroll
+    for (int dt = 0; dt < A::DT; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = 0; kb <= qb; kb++) {
+        __syncthreads();
+        stage_rows<T, HS>(sK, Kh, rs, kb * 64, T_, tid);
+        stage_rows_t<T, HS>(sVt, Vh, rs, kb * 64, T_, tid);
+        __syncthreads();
+        // S^T tiles: lane holds S^T[key = 16kt + 4g4 + r][query = l16]
+        f32x4_t s[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++) {
+            s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < A::DSTEPS; ks++) {
+                Frag<T> fk;
+                frag_ld(fk, sK + (16 * kt + l16) * A::RP + 32 * ks + 8 * g4);
+                mma(s[kt], fk, fq[ks]);
+            }
+        }
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int key = kb * 64 + 16 * kt + 4 * g4 + r;
+                const float v = key <= q ? s[kt][r] * sl2 : -INFINITY;
+                s[kt][r] = v;
+                mloc = fmaxf(mloc, v);
+            }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = exp2f(m_run - m_new);
+        float lsum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float p = exp2f(s[kt][r] - m_new);
+                s[kt][r] = p;
+                lsum += p;
+            }
+        lsum += __shfl_xor(lsum, 16, 64);
+        lsum += __shfl_xor(lsum, 32, 64);
+        l_run = l_run * alpha + lsum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < A::DT; dt++) o[dt] *= alpha;
+        // O^T[d][q] += V^T[d][key] P^T[key][q], 32 keys per step
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            float pv[8] = {s[2 * c][0], s[2 * c][1], s[2 * c][2], s[2 * c][3],
+                           s[2 * c + 1][0], s[2 * c + 1][1], s[2 * c + 1][2], s[2 * c + 1][3]};
+            Frag<T> fp;
+            frag_from(fp, pv);
+#pragma unroll
+            for (int dt = 0; dt < A::DT; dt++) {
+                const T* vr = sVt + (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
+                Frag<T> fv;
+                frag_ld2(fv, vr, vr + 16);
+                mma(o[dt], fv, fp);
+            }
+        }
+    }
+    if (q < T_) {
+        const float inv = 1.0f / l_run;
+        T* orow = out + ((long)b * T_ + q) * C + h * HS;
+#pragma unroll
+        for (int dt = 0; dt < A::DT; dt++) {
+            float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+            store4<T>(orow + 16 * dt + 4 * g4, v);
+        }
+        if (g4 == 0) lse[((long)b * NH + h) * T_ + q] = m_run + log2f(l_run);
+    }
+}
+
+// ---------------------------------------------------------------- backward --
+// delta[b,h,t] = sum_d dO[b,t,h,d] * O[b,t,h,d]
+template <typename T, int HS>
+__global__ void attn_delta_kernel(float* __restrict__ delta, const T* __restrict__ dout, const T* __restrict__ out,
+                                  int B, int T_, int C, int NH) {
+    constexpr int VEC = VecT<T>::N;
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // over B*T*NH, head fastest
+    if (i >= (long)B * T_ * NH) return;
+    const int h = (int)(i % NH);
+    const long bt = i / NH;
+    const T* a = dout + bt * C + h * HS;
+    const T* o = out + bt * C + h * HS;
+    float s = 0.f;
+#pragma unroll 2
+    for (int d = 0; d < HS; d += VEC) {
+        float x[VEC], y[VEC];
+        unpack16<T>(ld16(a + d), x);
+        unpack16<T>(ld16(o + d), y);
+#pragma unroll
+        for (int e = 0; e < VEC; e++) s += x[e] * y[e];
+    }
+    const long b = bt / T_, t = bt % T_;
+    delta[(b * NH + h) * T_ + t] = s;
+}
+
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
+                                                            const T* __restrict__ qkv, const float* __restrict__ lse,
+                                                            const float* __restrict__ delta, int T_, int C, int NH,
+                                                            float sl2, float scale) {
+    using A = ACfg<T, HS>;
+    __shared__ __attribute__((aligned(16))) T sQ[64 * A::RP];
+    __shared__ __attribute__((aligned(16))) T sdO[64 * A::RP];
+    __shared__ __attribute__((aligned(16))) T sQt[HS * A::TP];
+    __shared__ __attribute__((aligned(16))) T sdOt[HS * A::TP];
+    __shared__ __attribute__((aligned(16))) float sL[64];
+    __shared__ __attribute__((aligned(16))) float sD[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int kb = blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const long rs = 3L * C;
+    const T* Qh = qkv + (long)b * T_ * rs + h * HS;
+    const T* Kh = Qh + C;
+    const T* Vh = Qh + 2 * C;
+    const T* dOh = dout + (long)b * T_ * C + h * HS;
+    const float* lse_h = lse + ((long)b * NH + h) * T_;
+    const float* del_h = delta + ((long)b * NH + h) * T_;
+    const int key = kb * 64 + wave * 16 + l16;
+
+    Frag<T> fk[A::DSTEPS], fv[A::DSTEPS];
+    row_frags<T, HS>(fk, Kh, rs, key, T_, g4);
+    row_frags<T, HS>(fv, Vh, rs, key, T_, g4);
+    f32x4_t dk[A::DT], dv[A::DT];
+#pragma unroll
+    for (int dt = 0; dt < A::DT; dt++) {
+        dk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dv[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int nqb = (T_ + 63) / 64;
+    for (int qb = kb; qb < nqb; qb++) {
+        __syncthreads();
+        stage_rows<T, HS>(sQ, Qh, rs, qb * 64, T_, tid);
+        stage_rows<T, HS>(sdO, dOh, C, qb * 64, T_, tid);
+        stage_rows_t<T, HS>(sQt, Qh, rs, qb * 64, T_, tid);
+        stage_rows_t<T, HS>(sdOt, dOh, C, qb * 64, T_, tid);
+        if (tid < 64) {
+            const int qq = qb * 64 + tid;
+            sL[tid] = qq < T_ ? lse_h[qq] : INFINITY;
+            sD[tid] = qq < T_ ? del_h[qq] : 0.f;
+        }
+        __syncthreads();
+        // S[q][key] and dP[q][key]: lane holds q = 16qt + 4g4 + r, key = l16 (+ block offsets)
+        f32x4_t p[4], ds[4];
+#pragma unroll
+        for (int qt = 0; qt < 4; qt++) {
+            p[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ds[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < A::DSTEPS; ks++) {
+                Frag<T> fa;
+                frag_ld(fa, sQ + (16 * qt + l16) * A::RP + 32 * ks + 8 * g4);
+                mma(p[qt], fa, fk[ks]);
+                frag_ld(fa, sdO + (16 * qt + l16) * A::RP + 32 * ks + 8 * g4);
+                mma(ds[qt], fa, fv[ks]);
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < 4; qt++) {
+            const float4 L4 = *reinterpret_cast<const float4*>(sL + 16 * qt + 4 * g4);
+            const float4 D4 = *reinterpret_cast<const float4*>(sD + 16 * qt + 4 * g4);
+            const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+            const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int qq = qb * 64 + 16 * qt + 4 * g4 + r;
+                const float pr = (key <= qq && qq < T_) ? exp2f(p[qt][r] * sl2 - Lr[r]) : 0.f;
+                p[qt][r] = pr;
+                ds[qt][r] = pr * (ds[qt][r] - Dr[r]) * scale;
+            }
+        }
+        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            float pv[8] = {p[2 * c][0], p[2 * c][1], p[2 * c][2], p[2 * c][3],
+                           p[2 * c + 1][0], p[2 * c + 1][1], p[2 * c + 1][2], p[2 * c + 1][3]};
+            float sv[8] = {ds[2 * c][0], ds[2 * c][1], ds[2 * c][2], ds[2 * c][3],
+                           ds[2 * c + 1][0], ds[2 * c + 1][1], ds[2 * c + 1][2], ds[2 * c + 1][3]};
+            Frag<T> fp, fs;
+            frag_from(fp, pv);
+            frag_from(fs, sv);
+#pragma unroll
+            for (int dt = 0; dt < A::DT; dt++) {
+                const int ofs = (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
+                Frag<T> fa;
+                frag_ld2(fa, sdOt + ofs, sdOt + ofs + 16);
+                mma(dv[dt], fa, fp);
+                frag_ld2(fa, sQt + ofs, sQt + ofs + 16);
+                mma(dk[dt], fa, fs);
+            }
+        }
+    }
+    if (key < T_) {
+        T* row = dqkv + ((long)b * T_ + key) * rs + h * HS;
+#pragma unroll
+        for (int dt = 0; dt < A::DT; dt++) {
+            float kv[4] = {dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]};
+            float vv[4] = {dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
+            store4<T>(row + C + 16 * dt + 4 * g4, kv);
+            store4<T>(row + 2 * C + 16 * dt + 4 * g4, vv);
+        }
+    }
+}
+
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
+                                                          const T* __restrict__ qkv, const float* __restrict__ lse,
+                                                          const float* __restrict__ delta, int T_, int C, int NH,
+                                                          float sl2, float scale) {
+    using A = ACfg<T, HS>;
+    __shared__ __attribute__((aligned(16))) T sK[64 * A::RP];
+    __shared__ __attribute__((aligned(16))) T sV[64 * A::RP];
+    __shared__ __attribute__((aligned(16))) T sKt[HS * A::TP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int qb = gridDim.x - 1 - blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const long rs = 3L * C;
+    const T* Qh = qkv + (long)b * T_ * rs + h * HS;
+    const T* Kh = Qh + C;
+    const T* Vh = Qh + 2 * C;
+    const T* dOh = dout + (long)b * T_ * C + h * HS;
+    const int q = qb * 64 + wave * 16 + l16;
+    const float Lq = q < T_ ? lse[((long)b * NH + h) * T_ + q] : INFINITY;
+    const float Dq = q < T_ ? delta[((long)b * NH + h) * T_ + q] : 0.f;
+
+    Frag<T> fq[A::DSTEPS], fo[A::DSTEPS];
+    row_frags<T, HS>(fq, Qh, rs, q, T_, g4);
+    row_frags<T, HS>(fo, dOh, C, q, T_, g4);
+    f32x4_t dq[A::DT];
+#pragma unroll
+    for (int dt = 0; dt < A::DT; dt++) dq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = 0; kb <= qb; kb++) {
+        __syncthreads();
+        stage_rows<T, HS>(sK, Kh, rs, kb * 64, T_, tid);
+        stage_rows<T, HS>(sV, Vh, rs, kb * 64, T_, tid);
+        stage_rows_t<T, HS>(sKt, Kh, rs, kb * 64, T_, tid);
+        __syncthreads();
+        // S^T[key][q], dP^T[key][q]: lane holds key = 16kt + 4g4 + r, q = l16
+        f32x4_t s[4], dp[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++) {
+            s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dp[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < A::DSTEPS; ks++) {
+                Frag<T> fa;
+                frag_ld(fa, sK + (16 * kt + l16) * A::RP + 32 * ks + 8 * g4);
+                mma(s[kt], fa, fq[ks]);
+                frag_ld(fa, sV + (16 * kt + l16) * A::RP + 32 * ks + 8 * g4);
+                mma(dp[kt], fa, fo[ks]);
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int key = kb * 64 + 16 * kt + 4 * g4 + r;
+                const float pr = (key <= q && q < T_) ? exp2f(s[kt][r] * sl2 - Lq) : 0.f;
+                s[kt][r] = pr * (dp[kt][r] - Dq) * scale;  // dS^T
+            }
+        // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            float sv[8] = {s[2 * c][0], s[2 * c][1], s[2 * c][2], s[2 * c][3],
+                           s[2 * c + 1][0], s[2 * c + 1][1], s[2 * c + 1][2], s[2 * c + 1][3]};
+            Frag<T> fs;
+            frag_from(fs, sv);
+#pragma unroll
+            for (int dt = 0; dt < A::DT; dt++) {
+                const T* kr = sKt + (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
+                Frag<T> fa;
+                frag_ld2(fa, kr, kr + 16);
+                mma(dq[dt], fa, fs);
+            }
+        }
+    }
+    if (q < T_) {
+        T* row = dqkv + ((long)b * T_ + q) * rs + h * HS;
+#pragma unroll
+        for (int dt = 0; dt < A::DT; dt++) {
+            float v[4] = {dq[dt][0], dq[dt][1], dq[dt][2], dq[dt][3]};
+            store4<T>(row + 16 * dt + 4 * g4, v);
+        }
+    }
+}
+
+template <typename T, int HS>
+int fwd_hs(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
+    const int nb = (T_ + 63) / 64;
+    const float sl2 = LOG2E / sqrtf((float)HS);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, HS>), dim3(nb, NH, B), dim3(256), 0, s, out, lse, qkv, T_, C, NH, sl2);
+    return (int)hipGetLastError();
+}
+
+template <typename T, int HS>
+int bwd_hs(T* dqkv, float* delta, const T* dout, const T* out, const T* qkv, const float* lse,
+           int B, int T_, int C, int NH, hipStream_t s) {
+    const int nb = (T_ + 63) / 64;
+    const float scale = 1.0f / sqrtf((float)HS);
+    const float sl2 = LOG2E * scale;
+    const long rows = (long)B * T_ * NH;
+    hipLaunchKernelGGL((attn_delta_kernel<T, HS>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                       delta, dout, out, B, T_, C, NH);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HS>), dim3(nb, NH, B), dim3(256), 0, s, dqkv, dout, qkv, lse,
+                       delta, T_, C, NH, sl2, scale);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HS>), dim3(nb, NH, B), dim3(256), 0, s, dqkv, dout, qkv, lse,
+                       delta, T_, C, NH, sl2, scale);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T>
+int attention_fwd_launch(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
+    if (B <= 0 || T_ <= 0) return 0;
+    switch (C / NH) {
+        case 16: return fwd_hs<T, 16>(out, lse, qkv, B, T_, C, NH, s);
+        case 32: return fwd_hs<T, 32>(out, lse, qkv, B, T_, C, NH, s);
+        case 64: return fwd_hs<T, 64>(out, lse, qkv, B, T_, C, NH, s);
+        case 128: return fwd_hs<T, 128>(out, lse, qkv, B, T_, C, NH, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+int attention_bwd_launch(T* dqkv, float* delta, const T* dout, const T* out, const T* qkv,
+                         const float* lse, int B, int T_, int C, int NH, hipStream_t s) {
+    if (B <= 0 || T_ <= 0) return 0;
+    switch (C / NH) {
+        case 16: return bwd_hs<T, 16>(dqkv, delta, dout, out, qkv, lse, B, T_, C, NH, s);
+        case 32: return bwd_hs<T, 32>(dqkv, delta, dout, out, qkv, lse, B, T_, C, NH, s);
+        case 64: return bwd_hs<T, 64>(dqkv, delta, dout, out, qkv, lse, B, T_, C, NH, s);
+        case 128: return bwd_hs<T, 128>(dqkv, delta, dout, out, qkv, lse, B, T_, C, NH, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template int attention_fwd_launch<float>(float*, float*, const float*, int, int, int, int, hipStream_t);
+template int attention_fwd_launch<bf16_t>(bf16_t*, float*, const bf16_t*, int, int, int, int, hipStream_t);
+template int attention_bwd_launch<float>(float*, float*, const float*, const float*, const float*, const float*,
+                                         int, int, int, int, hipStream_t);
+template int attention_bwd_launch<bf16_t>(bf16_t*, float*, const bf16_t*, const bf16_t*, const bf16_t*, const float*,
+                                          int, int, int, int, hipStream_t);

@@ -1,0 +1,208 @@
+// device.h - device-side building blocks shared by the gfx950 kernels.
+//
+// Element types: activations and parameters are either fp32 (`float`) or bf16
+// stored as `uint16_t` (`bf16_t`).  All arithmetic is fp32.  Global memory is
+// moved in 16-byte vectors (`uint4`): 4 fp32 or 8 bf16 elements.
+//
+// Matrix-core fragments: every product runs on 16x16 output tiles of the
+// gfx950 MFMA unit with a 32-deep contraction per step.  A fragment is what
+// one lane feeds into one such step: 8 contraction-consecutive elements of one
+// row (A operand) or one column (B operand).  Lane l covers row/column l%16
+// and contraction slots 8*(l/16) .. 8*(l/16)+7; the 16x16 fp32 result tile
+// leaves lane l holding rows 4*(l/16)+r (r = 0..3) of column l%16.
+//  - bf16: one v_mfma_f32_16x16x32_bf16 per step.
+//  - fp32: eight v_mfma_f32_16x16x4f32 per step, the j-th consuming slot j of
+//    every lane, so the 32 slots are contracted exactly once, in fp32.
+// Because only the pairing of A and B slots matters, a fragment may map its
+// 8 slots to any 8 distinct contraction indices as long as both operands use
+// the same map (the attention kernels use this to feed a result tile straight
+// back in as an operand).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+#define DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------- scalars ---
+
+DEV float bf2f(uint32_t u16) { return __uint_as_float(u16 << 16); }
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+DEV uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t f = {lo, hi};
+    bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+DEV bf16_t f2bf(float f) { return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xffffu); }
+
+template <typename T> DEV float to_f(T v);
+template <> DEV float to_f<float>(float v) { return v; }
+template <> DEV float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <typename T> DEV T from_f(float v);
+template <> DEV float from_f<float>(float v) { return v; }
+template <> DEV bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// ---------------------------------------------------------------- vectors ---
+
+template <typename T> struct VecT;
+template <> struct VecT<float> { static constexpr int N = 4; };
+template <> struct VecT<bf16_t> { static constexpr int N = 8; };
+
+// unpack a 16-byte vector to VecT<T>::N floats
+template <typename T> DEV void unpack16(const uint4& v, float* f);
+template <> DEV void unpack16<float>(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+template <> DEV void unpack16<bf16_t>(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+    f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+    f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+template <typename T> DEV uint4 pack16(const float* f);
+template <> DEV uint4 pack16<float>(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+template <> DEV uint4 pack16<bf16_t>(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
+DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+DEV void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+DEV uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+DEV void st8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
+
+// store 4 consecutive values (8 bytes for bf16, 16 bytes for fp32)
+template <typename T> DEV void store4(T* p, const float* f);
+template <> DEV void store4<float>(float* p, const float* f) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+}
+template <> DEV void store4<bf16_t>(bf16_t* p, const float* f) {
+    st8(p, make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])));
+}
+template <typename T> DEV void load4(const T* p, float* f);
+template <> DEV void load4<float>(const float* p, float* f) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
+template <> DEV void load4<bf16_t>(const bf16_t* p, float* f) {
+    uint2 v = ld8(p);
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+// ------------------------------------------------------------- reductions ---
+
+DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// -------------------------------------------------------------- fragments ---
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { bf16x8_t v; };
+template <> struct Frag<float> { float v[8]; };
+
+DEV void mma(f32x4_t& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+DEV void mma(f32x4_t& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+// 8 consecutive elements from LDS (16-byte aligned)
+DEV void frag_ld(Frag<bf16_t>& f, const bf16_t* p) {
+    f.v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+DEV void frag_ld(Frag<float>& f, const float* p) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+// slots 0..3 from p0, slots 4..7 from p1 (each 4 consecutive elements)
+DEV void frag_ld2(Frag<bf16_t>& f, const bf16_t* p0, const bf16_t* p1) {
+    uint2 a = *reinterpret_cast<const uint2*>(p0);
+    uint2 b = *reinterpret_cast<const uint2*>(p1);
+    f.v = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+DEV void frag_ld2(Frag<float>& f, const float* p0, const float* p1) {
+    float4 a = *reinterpret_cast<const float4*>(p0);
+    float4 b = *reinterpret_cast<const float4*>(p1);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+// from 8 fp32 values held in registers
+DEV void frag_from(Frag<bf16_t>& f, const float* x) {
+    f.v = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
+}
+DEV void frag_from(Frag<float>& f, const float* x) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) f.v[j] = x[j];
+}
+DEV void frag_zero(Frag<bf16_t>& f) { f.v = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+DEV void frag_zero(Frag<float>& f) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) f.v[j] = 0.0f;
+}
+// 8 consecutive elements straight from global memory (16 B per bf16 fragment)
+DEV void frag_gld(Frag<bf16_t>& f, const bf16_t* p) { frag_ld(f, p); }
+DEV void frag_gld(Frag<float>& f, const float* p) { frag_ld(f, p); }
+
+// ---------------------------------------------------------------- GELU ------
+// train_gpt2.cu, gelu_forward_kernel2 / gelu_backward_kernel (tanh form).
+#define GELU_K0 0.7978845608028654f  // sqrt(2/pi)
+#define GELU_K1 0.044715f
+
+DEV float gelu_f(float x) {
+    float u = GELU_K0 * (x + GELU_K1 * x * x * x);
+    return 0.5f * x * (1.0f + tanhf(u));
+}
+DEV float gelu_grad_f(float x) {
+    float u = GELU_K0 * (x + GELU_K1 * x * x * x);
+    float th = tanhf(u);
+    float sech2 = 1.0f - th * th;  // 1/cosh^2(u)
+    return 0.5f * (1.0f + th) + 0.5f * x * sech2 * GELU_K0 * (1.0f + 3.0f * GELU_K1 * x * x);
+}
+
+// ------------------------------------------------------------- transpose ----
+// r[i] holds one 16-byte vector of row i (4 rows).  Writes, for every element
+// e of the vector, the 4 values (r[0][e], r[1][e], r[2][e], r[3][e]) to
+// dst + e*pitch (8 bytes for bf16, 16 bytes for fp32).
+DEV uint32_t vec_h16(const uint4& v, int e) {
+    uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+DEV uint32_t vec_w32(const uint4& v, int e) {
+    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+template <typename T>
+DEV void store_t4(T* dst, int pitch, const uint4 (&r)[4]) {
+#pragma unroll
+    for (int e = 0; e < VecT<T>::N; e++) {
+        if constexpr (sizeof(T) == 2) {
+            st8(dst + e * pitch, make_uint2(vec_h16(r[0], e) | (vec_h16(r[1], e) << 16),
+                                            vec_h16(r[2], e) | (vec_h16(r[3], e) << 16)));
+        } else {
+            st16(dst + e * pitch, make_uint4(vec_w32(r[0], e), vec_w32(r[1], e), vec_w32(r[2], e), vec_w32(r[3], e)));
+        }
+    }
+}

@@ -1,0 +1,367 @@
+// elementwise.hip - token/position encoder, fused softmax cross-entropy,
+// AdamW and small utilities (gfx950).
+#include <math.h>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace {
+
+// ------------------------------------------------------------ encoder fwd ---
+// train_gpt2.cu, encoder_forward_kernel2: out[b,t,:] = wte[tok[b,t],:] + wpe[t,:].
+// One thread per 16-byte vector.  Token ids outside [0, V) raise *flag and are
+// replaced by 0 so that no read leaves the table; the (clamped) ids are copied
+// for the backward pass.
+template <typename T>
+__global__ void encoder_fwd_kernel(T* __restrict__ out, int* __restrict__ tok_copy, const int* __restrict__ tok,
+                                   const T* __restrict__ wte, const T* __restrict__ wpe, int BT, int T_, int C,
+                                   int V, int* __restrict__ flag) {
+    constexpr int VEC = VecT<T>::N;
+    const int vpr = C / VEC;
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)BT * vpr) return;
+    const int bt = (int)(i / vpr), c0 = (int)(i % vpr) * VEC;
+    int ix = tok[bt];
+    if (ix < 0 || ix >= V) {
+        if (c0 == 0) flag[0] = 1;
+        ix = 0;
+    }
+    if (c0 == 0) tok_copy[bt] = ix;
+    const int t = bt % T_;
+    float a[VEC], p[VEC];
+    unpack16<T>(ld16(wte + (long)ix * C + c0), a);
+    unpack16<T>(ld16(wpe + (long)t * C + c0), p);
+#pragma unroll
+    for (int e = 0; e < VEC; e++) a[e] += p[e];
+    st16(out + (long)bt * C + c0, pack16<T>(a));
+}
+
+// ------------------------------------------------------------ encoder bwd ---
+// train_gpt2.cu, encoder_backward_kernel, without atomics.  dwte: one wave per
+// position i; the wave scans the ids before i and stops if its id occurs
+// there.  The wave of the first occurrence of id v then sums, in increasing
+// position order, the residual-gradient rows of every position holding v and
+// adds the sum into dwte[v].  Each row of dwte is thus written by one wave
+// with a fixed order of summation.
+__global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict__ dwte, const float* __restrict__ dres,
+                                                              const int* __restrict__ tok, int BT, int C) {
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= BT) return;
+    const int v = tok[i];
+    for (int j0 = 0; j0 < i; j0 += 64) {
+        const int j = j0 + lane;
+        const bool hit = (j < i) && tok[j] == v;
+        if (__any(hit)) return;
+    }
+    constexpr int NV = 8;  // C <= 2048 as float4 vectors over 64 lanes
+    const int nvec = C / 4;
+    float acc[NV][4];
+#pragma unroll
+    for (int k = 0; k < NV; k++) acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
+    for (int j0 = i; j0 < BT; j0 += 64) {
+        const int j = j0 + lane;
+        unsigned long long mask = __ballot(j < BT && tok[j] == v);
+        while (mask) {
+            const int jj = j0 + __ffsll((long long)mask) - 1;
+            mask &= mask - 1;
+            const float* r = dres + (long)jj * C;
+#pragma unroll
+            for (int k = 0; k < NV; k++) {
+                const int vv = lane + 64 * k;
+                if (vv < nvec) {
+                    float x[4];
+                    load4<float>(r + vv * 4, x);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) acc[k][e] += x[e];
+                }
+            }
+        }
+    }
+    float* w = dwte + (long)v * C;
+#pragma unroll
+    for (int k = 0; k < NV; k++) {
+        const int vv = lane + 64 * k;
+        if (vv < nvec) {
+            float o[4];
+            load4<float>(w + vv * 4, o);
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] += acc[k][e];
+            store4<float>(w + vv * 4, o);
+        }
+    }
+}
+
+// dwpe[t, :] += sum over b of dres[b*T + t, :]  (b in increasing order)
+__global__ void encoder_bwd_wpe_kernel(float* __restrict__ dwpe, const float* __restrict__ dres, int B, int T_, int C) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index over T*C
+    if (i >= (long)T_ * C / 4) return;
+    const long t = i / (C / 4), c = (i % (C / 4)) * 4;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < B; b++) {
+        float x[4];
+        load4<float>(dres + ((long)b * T_ + t) * C + c, x);
+#pragma unroll
+        for (int e = 0; e < 4; e++) s[e] += x[e];
+    }
+    float o[4];
+    load4<float>(dwpe + t * C + c, o);
+#pragma unroll
+    for (int e = 0; e < 4; e++) o[e] += s[e];
+    store4<float>(dwpe + t * C + c, o);
+}
+
+// ---------------------------------------------------- softmax + cross-ent. --
+// train_gpt2.cu, fused_classifier_kernel3 and prepare_softmax_blockwide:
+// one workgroup per row.  The row (Vp logits) is read once into registers;
+// block-wide max and sum of exp over the first V columns give
+// lse = max + log(sum); loss = lse - z[target]; the row is overwritten in
+// place with softmax - onehot for columns < V and with 0 for the padded
+// columns.  The loss-gradient scale is applied later, by the classifier's
+// backward products.
+template <typename T, int NT, int NV>
+__global__ __launch_bounds__(NT) void classifier_ce_kernel(T* __restrict__ logits, float* __restrict__ losses,
+                                                           const int* __restrict__ targets, int V, int Vp,
+                                                           int* __restrict__ flag) {
+    constexpr int VEC = VecT<T>::N;
+    constexpr int NW = NT / 64;
+    __shared__ float red[NW];
+    __shared__ float zt_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const long row = blockIdx.x;
+    T* z = logits + row * Vp;
+    int tgt = targets[row];
+    if (tgt < 0 || tgt >= V) {
+        if (tid == 0) flag[0] = 1;
+        tgt = 0;
+    }
+    if (tid == 0) zt_s = to_f<T>(z[tgt]);
+    const int nvec = Vp / VEC;
+    uint4 reg[NV];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV; k++) {
+        const int v = tid + NT * k;
+        if (v < nvec) {
+            reg[k] = ld16(z + (long)v * VEC);
+            float f[VEC];
+            unpack16<T>(reg[k], f);
+#pragma unroll
+            for (int e = 0; e < VEC; e++)
+                if (v * VEC + e < V) mx = fmaxf(mx, f[e]);
+        }
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; w++) mx = fmaxf(mx, red[w]);
+    float sm = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; k++) {
+        const int v = tid + NT * k;
+        if (v < nvec) {
+            float f[VEC];
+            unpack16<T>(reg[k], f);
+#pragma unroll
+            for (int e = 0; e < VEC; e++)
+                if (v * VEC + e < V) sm += __expf(f[e] - mx);
+        }
+    }
+    sm = wave_sum(sm);
+    __syncthreads();  // everyone has read red[] (max)
+    if (lane == 0) red[wave] = sm;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) tot += red[w];
+    const float lse = mx + __logf(tot);
+    if (tid == 0) losses[row] = lse - zt_s;
+#pragma unroll
+    for (int k = 0; k < NV; k++) {
+        const int v = tid + NT * k;
+        if (v < nvec) {
+            float f[VEC];
+            unpack16<T>(reg[k], f);
+#pragma unroll
+            for (int e = 0; e < VEC; e++) {
+                const int col = v * VEC + e;
+                f[e] = col < V ? __expf(f[e] - lse) - (col == tgt ? 1.0f : 0.0f) : 0.0f;
+            }
+            st16(z + (long)v * VEC, pack16<T>(f));
+        }
+    }
+}
+
+// out[0] = mean of x[0..n): fixed-order reduction in one workgroup
+__global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out, const float* __restrict__ x, int n) {
+    __shared__ float red[16];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < n; i += 1024) s += x[i];
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.f;
+        for (int w = 0; w < 16; w++) t += red[w];
+        out[0] = t / (float)n;
+    }
+}
+
+// ------------------------------------------------------------------ AdamW ---
+// train_gpt2.cu, adamw_kernel3 (master-weight path) and gpt2_update's bias
+// corrections c1 = 1 - beta1^t, c2 = 1 - beta2^t.  Four parameters per thread.
+template <typename PT>
+DEV void adamw_one(float g, float& m, float& v, float& p, float lr, float b1, float b2, float c1, float c2,
+                   float eps, float wd) {
+    m = fmaf(b1, m, fmaf(-b1, g, g));          // b1*m + (1-b1)*g
+    v = fmaf(b2, v, fmaf(-b2, g * g, g * g));  // b2*v + (1-b2)*g^2
+    const float mh = m / c1, vh = v / c2;
+    p = p - lr * (mh / (sqrtf(vh) + eps) + wd * p);
+}
+
+template <typename PT>
+__global__ void adamw_kernel(PT* __restrict__ params, float* __restrict__ master, const float* __restrict__ grads,
+                             float* __restrict__ mom, float* __restrict__ var, size_t n, float lr, float b1, float b2,
+                             float c1, float c2, float eps, float wd) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+    for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+        if (i + 4 <= n) {
+            float g[4], m[4], v[4], p[4];
+            load4<float>(grads + i, g);
+            load4<float>(mom + i, m);
+            load4<float>(var + i, v);
+            if constexpr (sizeof(PT) == 2) load4<float>(master + i, p);
+            else load4<float>((const float*)params + i, p);
+#pragma unroll
+            for (int e = 0; e < 4; e++) adamw_one<PT>(g[e], m[e], v[e], p[e], lr, b1, b2, c1, c2, eps, wd);
+            store4<float>(mom + i, m);
+            store4<float>(var + i, v);
+            if constexpr (sizeof(PT) == 2) {
+                store4<float>(master + i, p);
+                store4<bf16_t>((bf16_t*)params + i, p);
+            } else {
+                store4<float>((float*)params + i, p);
+            }
+        } else {
+            for (size_t k = i; k < n; k++) {
+                float g = grads[k], m = mom[k], v = var[k];
+                float p = (sizeof(PT) == 2) ? master[k] : (float)((const float*)params)[k];
+                adamw_one<PT>(g, m, v, p, lr, b1, b2, c1, c2, eps, wd);
+                mom[k] = m;
+                var[k] = v;
+                if constexpr (sizeof(PT) == 2) {
+                    master[k] = p;
+                    ((bf16_t*)params)[k] = f2bf(p);
+                } else {
+                    ((float*)params)[k] = p;
+                }
+            }
+        }
+    }
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, float value, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+    for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+        if (i + 4 <= n) *reinterpret_cast<float4*>(p + i) = make_float4(value, value, value, value);
+        else for (size_t k = i; k < n; k++) p[k] = value;
+    }
+}
+
+__global__ void fill_i32_kernel(int* __restrict__ p, int value, size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = value;
+}
+
+__global__ void cast_bf16_kernel(bf16_t* __restrict__ dst, const float* __restrict__ src, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+    for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+        if (i + 4 <= n) {
+            float f[4];
+            load4<float>(src + i, f);
+            store4<bf16_t>(dst + i, f);
+        } else {
+            for (size_t k = i; k < n; k++) dst[k] = f2bf(src[k]);
+        }
+    }
+}
+
+unsigned grid_for(size_t n4) {  // grid-stride launches: at most 8 blocks of 256 per CU slot
+    size_t b = (n4 + 255) / 256;
+    if (b > 65536) b = 65536;
+    return (unsigned)(b ? b : 1);
+}
+
+}  // namespace
+
+template <typename T>
+int encoder_fwd_launch(T* out, int* tok_copy, const int* tok, const T* wte, const T* wpe, int B, int T_, int C,
+                       int V, int* flag, hipStream_t s) {
+    const long n = (long)B * T_ * (C / VecT<T>::N);
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(encoder_fwd_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, tok_copy, tok,
+                       wte, wpe, B * T_, T_, C, V, flag);
+    return (int)hipGetLastError();
+}
+
+int encoder_bwd_launch(float* dwte, float* dwpe, const float* dres, const int* tok, int B, int T_, int C,
+                       hipStream_t s) {
+    const int BT = B * T_;
+    if (BT == 0) return 0;
+    hipLaunchKernelGGL(encoder_bwd_wte_kernel, dim3((BT + 3) / 4), dim3(256), 0, s, dwte, dres, tok, BT, C);
+    const long n4 = (long)T_ * C / 4;
+    hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dwpe, dres, B, T_, C);
+    return (int)hipGetLastError();
+}
+
+template <typename T>
+int classifier_ce_launch(T* logits, float* losses, const int* targets, int N, int V, int Vp, int* flag, hipStream_t s) {
+    if (N == 0) return 0;
+    if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((classifier_ce_kernel<T, 256, 26>), dim3(N), dim3(256), 0, s, logits, losses, targets, V, Vp, flag);
+    } else {
+        hipLaunchKernelGGL((classifier_ce_kernel<T, 1024, 13>), dim3(N), dim3(1024), 0, s, logits, losses, targets, V, Vp, flag);
+    }
+    return (int)hipGetLastError();
+}
+
+int mean_launch(float* out, const float* x, int n, hipStream_t s) {
+    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, out, x, n);
+    return (int)hipGetLastError();
+}
+
+template <typename PT>
+int adamw_launch(PT* params, float* master, const float* grads, float* m, float* v, size_t n, float lr, float b1,
+                 float b2, float c1, float c2, float eps, float wd, hipStream_t s) {
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(adamw_kernel<PT>, dim3(grid_for((n + 3) / 4)), dim3(256), 0, s, params, master, grads, m, v, n,
+                       lr, b1, b2, c1, c2, eps, wd);
+    return (int)hipGetLastError();
+}
+
+int fill_f32_launch(float* p, float value, size_t n, hipStream_t s) {
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for((n + 3) / 4)), dim3(256), 0, s, p, value, n);
+    return (int)hipGetLastError();
+}
+
+int fill_i32_launch(int* p, int value, size_t n, hipStream_t s) {
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, value, n);
+    return (int)hipGetLastError();
+}
+
+int cast_f32_to_bf16_launch(bf16_t* dst, const float* src, size_t n, hipStream_t s) {
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for((n + 3) / 4)), dim3(256), 0, s, dst, src, n);
+    return (int)hipGetLastError();
+}
+
+template int encoder_fwd_launch<float>(float*, int*, const int*, const float*, const float*, int, int, int, int, int*, hipStream_t);
+template int encoder_fwd_launch<bf16_t>(bf16_t*, int*, const int*, const bf16_t*, const bf16_t*, int, int, int, int, int*, hipStream_t);
+template int classifier_ce_launch<float>(float*, float*, const int*, int, int, int, int*, hipStream_t);
+template int classifier_ce_launch<bf16_t>(bf16_t*, float*, const int*, int, int, int, int*, hipStream_t);
+template int adamw_launch<float>(float*, float*, const float*, float*, float*, size_t, float, float, float, float, float, float, float, hipStream_t);
+template int adamw_launch<bf16_t>(bf16_t*, float*, const float*, float*, float*, size_t, float, float, float, float, float, float, float, hipStream_t);

@@ -1,0 +1,468 @@
+// gpt2_api.hip - the C ABI of include/gpt2.h: buffer planning, argument and
+// state checks, and the kernel schedule of one GPT-2 micro-step.
+//
+// The schedule is train_gpt2.cu's gpt2_forward / gpt2_backward / gpt2_update
+// with these MI355X-side changes:
+//  - bias, GELU and residual additions are epilogues of the matrix products
+//    (no attproj / fcproj / residual / gelu round trips through HBM);
+//  - attention never materialises the (B, NH, T, T) matrices; it keeps one
+//    fp32 log-sum-exp per query row for the backward;
+//  - the residual-stream gradient is fp32 (plus a bf16 copy as the next
+//    products' operand in bf16 mode) and parameter gradients are fp32;
+//  - every reduction is deterministic (no atomics), so two identical calls
+//    give bit-identical results;
+//  - the mean loss is reduced on the device (no device-to-host copy inside
+//    the step).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "gpt2.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kPlanCUs = 256;  // split-K planning constant (MI355X: 256 CUs)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
+
+struct Plan {
+    // element counts
+    size_t BT, C, L, Vp, NH, T, B;
+    int esz;
+    // byte offsets into acts
+    size_t enc, ln1, ln1m, ln1r, qkv, atty, lse, res2, ln2, ln2m, ln2r, fch, fchg, res3;
+    size_t lnf, lnfm, lnfr, logits, losses, tok;
+    size_t dres32, dres_lp, dbtc, dbt4c, dqkv, delta;
+    size_t acts_bytes;
+    // per-layer strides (bytes)
+    size_t s_btc, s_bt3c, s_bt4c, s_bt, s_lse;
+    // scratch
+    size_t flag, work, work_bytes, scratch_bytes;
+};
+
+void param_layout(const gpt2_config& c, size_t off[16], size_t cnt[16], size_t* total) {
+    const size_t Vp = c.padded_vocab_size, C = c.channels, maxT = c.max_seq_len, L = c.num_layers;
+    const size_t n[16] = {Vp * C, maxT * C, L * C, L * C, L * 3 * C * C, L * 3 * C, L * C * C, L * C,
+                          L * C, L * C, L * 4 * C * C, L * 4 * C, L * C * 4 * C, L * C, C, C};
+    size_t t = 0;
+    for (int i = 0; i < 16; i++) {
+        off[i] = t;
+        cnt[i] = n[i];
+        t += n[i];
+    }
+    *total = t;
+}
+
+int check_config(const gpt2_config* cfg, int precision, int B, int T) {
+    if (!cfg) return GPT2_E_ARG;
+    if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_E_ARG;
+    if (cfg->num_layers < 1 || cfg->num_heads < 1 || cfg->channels < 1 || cfg->vocab_size < 1 ||
+        cfg->max_seq_len < 1 || cfg->padded_vocab_size < cfg->vocab_size)
+        return GPT2_E_ARG;
+    if (B < 1 || T < 1 || T > cfg->max_seq_len) return GPT2_E_SHAPE;
+    if (cfg->channels % cfg->num_heads) return GPT2_E_SHAPE;
+    const int hs = cfg->channels / cfg->num_heads;
+    if (hs != 16 && hs != 32 && hs != 64 && hs != 128) return GPT2_E_SHAPE;
+    if (cfg->channels % 8 || cfg->channels > 2048 || cfg->padded_vocab_size % 8) return GPT2_E_SHAPE;
+    if (cfg->padded_vocab_size > 53248) return GPT2_E_SHAPE;
+    if ((long)B * T > (1L << 30) / 4) return GPT2_E_SHAPE;
+    return GPT2_OK;
+}
+
+size_t dw_workspace(size_t M, size_t N, size_t K, int esz) {
+    GemmDesc d = {};
+    d.M = (int)M; d.N = (int)N; d.K = (int)K; d.epi = GEMM_ACCUM;
+    return gemm_workspace_bytes(d, esz, kPlanCUs);
+}
+
+Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
+    Plan p;
+    p.esz = precision == GPT2_BF16 ? 2 : 4;
+    p.B = B; p.T = T; p.BT = (size_t)B * T; p.C = c.channels; p.L = c.num_layers;
+    p.Vp = c.padded_vocab_size; p.NH = c.num_heads;
+    const size_t e = p.esz, BT = p.BT, C = p.C, L = p.L;
+    p.s_btc = align_up(BT * C * e);
+    p.s_bt3c = align_up(BT * 3 * C * e);
+    p.s_bt4c = align_up(BT * 4 * C * e);
+    p.s_bt = align_up(BT * 4);
+    p.s_lse = align_up((size_t)B * p.NH * T * 4);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o += align_up(bytes); return r; };
+    p.enc = take(p.s_btc);
+    p.ln1 = take(L * p.s_btc);
+    p.ln1m = take(L * p.s_bt);
+    p.ln1r = take(L * p.s_bt);
+    p.qkv = take(L * p.s_bt3c);
+    p.atty = take(L * p.s_btc);
+    p.lse = take(L * p.s_lse);
+    p.res2 = take(L * p.s_btc);
+    p.ln2 = take(L * p.s_btc);
+    p.ln2m = take(L * p.s_bt);
+    p.ln2r = take(L * p.s_bt);
+    p.fch = take(L * p.s_bt4c);
+    p.fchg = take(L * p.s_bt4c);
+    p.res3 = take(L * p.s_btc);
+    p.lnf = take(p.s_btc);
+    p.lnfm = take(p.s_bt);
+    p.lnfr = take(p.s_bt);
+    p.logits = take(BT * p.Vp * e);
+    p.losses = take(BT * 4);
+    p.tok = take(BT * 4);
+    p.dres32 = take(BT * C * 4);
+    p.dres_lp = precision == GPT2_BF16 ? take(BT * C * e) : p.dres32;
+    p.dbtc = take(p.s_btc);
+    p.dbt4c = take(p.s_bt4c);
+    p.dqkv = take(p.s_bt3c);
+    p.delta = take(p.s_lse);
+    p.acts_bytes = o;
+    // scratch: device flag + one workspace shared (in stream order) by split-K,
+    // LayerNorm-backward partials and bias-gradient partials
+    size_t w = 0;
+    w = std::max(w, dw_workspace(p.Vp, C, BT, p.esz));
+    w = std::max(w, dw_workspace(3 * C, C, BT, p.esz));
+    w = std::max(w, dw_workspace(C, C, BT, p.esz));
+    w = std::max(w, dw_workspace(4 * C, C, BT, p.esz));
+    w = std::max(w, dw_workspace(C, 4 * C, BT, p.esz));
+    w = std::max(w, layernorm_bwd_workspace_bytes((int)BT, (int)C));
+    w = std::max(w, bias_grad_workspace_bytes((int)BT, (int)(4 * C)));
+    p.flag = 0;
+    p.work = kAlign;
+    p.work_bytes = align_up(w);
+    p.scratch_bytes = kAlign + p.work_bytes;
+    return p;
+}
+
+}  // namespace
+
+struct gpt2_ctx {
+    gpt2_config cfg;
+    int prec;
+    int B, T;
+    size_t P;
+    size_t off[16], cnt[16];
+    gpt2_buffers buf;
+    Plan plan;
+    int last_fwd_targets;  // -1: no forward yet, 0: without targets, 1: with
+    char* acts() const { return (char*)buf.acts; }
+    template <typename X> X* act(size_t ofs) const { return (X*)(acts() + ofs); }
+    template <typename X> X* act_l(size_t ofs, size_t stride, int l) const { return (X*)(acts() + ofs + stride * l); }
+    int* flag() const { return (int*)((char*)buf.scratch + plan.flag); }
+    float* work() const { return (float*)((char*)buf.scratch + plan.work); }
+};
+
+namespace {
+
+int hip_rc(int e) { return e == 0 ? GPT2_OK : GPT2_E_HIP; }
+#define TRY(x) do { int _e = (x); if (_e != 0) return GPT2_E_HIP; } while (0)
+
+template <typename T>
+T* prm(gpt2_ctx* c, int i, size_t l = 0, size_t per = 0) { return (T*)c->buf.params + c->off[i] + l * per; }
+float* grd(gpt2_ctx* c, int i, size_t l = 0, size_t per = 0) { return (float*)c->buf.grads + c->off[i] + l * per; }
+
+GemmDesc fwd_desc(int M, int N, int K, const void* X, const void* W, void* Y, int epi, const void* bias,
+                  const void* aux_in, void* aux_out) {
+    GemmDesc d = {};
+    d.M = M; d.N = N; d.K = K;
+    d.A = X; d.lda = K; d.a_kmajor = 1;
+    d.B = W; d.ldb = K; d.b_kmajor = 1;
+    d.C = Y; d.ldc = N; d.epi = epi; d.alpha = 1.0f;
+    d.bias = bias; d.aux_in = aux_in; d.aux_out = aux_out; d.ldaux = N;
+    return d;
+}
+// dX[BT, IC] = alpha * dY[BT, OC] W[OC, IC]
+GemmDesc dx_desc(int BT, int IC, int OC, const void* dY, const void* W, void* dX, int epi, const void* aux_in,
+                 float alpha) {
+    GemmDesc d = {};
+    d.M = BT; d.N = IC; d.K = OC;
+    d.A = dY; d.lda = OC; d.a_kmajor = 1;
+    d.B = W; d.ldb = IC; d.b_kmajor = 0;
+    d.C = dX; d.ldc = IC; d.epi = epi; d.alpha = alpha;
+    d.aux_in = aux_in; d.ldaux = IC;
+    return d;
+}
+// dW[OC, IC] += alpha * dY[BT, OC]^T X[BT, IC]
+GemmDesc dw_desc(int BT, int IC, int OC, const void* dY, const void* X, float* dW, float alpha) {
+    GemmDesc d = {};
+    d.M = OC; d.N = IC; d.K = BT;
+    d.A = dY; d.lda = OC; d.a_kmajor = 0;
+    d.B = X; d.ldb = IC; d.b_kmajor = 0;
+    d.C = dW; d.ldc = IC; d.epi = GEMM_ACCUM; d.alpha = alpha;
+    return d;
+}
+
+int gemm(gpt2_ctx* c, const GemmDesc& d, hipStream_t s) {
+    return gemm_launch(d, c->plan.esz, c->work(), c->plan.work_bytes, kPlanCUs, s);
+}
+
+template <typename T>
+int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, float* d_losses, float* d_mean,
+                 hipStream_t s) {
+    const Plan& p = c->plan;
+    const int B = c->B, Tn = c->T, BT = (int)p.BT, C = (int)p.C, L = (int)p.L, NH = (int)p.NH;
+    const int V = c->cfg.vocab_size, Vp = (int)p.Vp;
+    const size_t CC = (size_t)C * C;
+    T* enc = c->act<T>(p.enc);
+    TRY(encoder_fwd_launch<T>(enc, c->act<int>(p.tok), inputs, prm<T>(c, 0), prm<T>(c, 1), B, Tn, C, V, c->flag(), s));
+    for (int l = 0; l < L; l++) {
+        const T* res = l == 0 ? enc : c->act_l<T>(p.res3, p.s_btc, l - 1);
+        T* ln1 = c->act_l<T>(p.ln1, p.s_btc, l);
+        T* qkv = c->act_l<T>(p.qkv, p.s_bt3c, l);
+        T* atty = c->act_l<T>(p.atty, p.s_btc, l);
+        T* res2 = c->act_l<T>(p.res2, p.s_btc, l);
+        T* ln2 = c->act_l<T>(p.ln2, p.s_btc, l);
+        T* fch = c->act_l<T>(p.fch, p.s_bt4c, l);
+        T* fchg = c->act_l<T>(p.fchg, p.s_bt4c, l);
+        T* res3 = c->act_l<T>(p.res3, p.s_btc, l);
+        TRY(layernorm_fwd_launch<T>(ln1, c->act_l<float>(p.ln1m, p.s_bt, l), c->act_l<float>(p.ln1r, p.s_bt, l), res,
+                                    prm<T>(c, 2, l, C), prm<T>(c, 3, l, C), BT, C, s));
+        TRY(gemm(c, fwd_desc(BT, 3 * C, C, ln1, prm<T>(c, 4, l, 3 * CC), qkv, GEMM_BIAS, prm<T>(c, 5, l, 3 * C),
+                             nullptr, nullptr), s));
+        TRY(attention_fwd_launch<T>(atty, c->act_l<float>(p.lse, p.s_lse, l), qkv, B, Tn, C, NH, s));
+        TRY(gemm(c, fwd_desc(BT, C, C, atty, prm<T>(c, 6, l, CC), res2, GEMM_BIAS_RESID, prm<T>(c, 7, l, C), res,
+                             nullptr), s));
+        TRY(layernorm_fwd_launch<T>(ln2, c->act_l<float>(p.ln2m, p.s_bt, l), c->act_l<float>(p.ln2r, p.s_bt, l), res2,
+                                    prm<T>(c, 8, l, C), prm<T>(c, 9, l, C), BT, C, s));
+        TRY(gemm(c, fwd_desc(BT, 4 * C, C, ln2, prm<T>(c, 10, l, 4 * CC), fchg, GEMM_BIAS_GELU,
+                             prm<T>(c, 11, l, 4 * C), nullptr, fch), s));
+        TRY(gemm(c, fwd_desc(BT, C, 4 * C, fchg, prm<T>(c, 12, l, 4 * CC), res3, GEMM_BIAS_RESID,
+                             prm<T>(c, 13, l, C), res2, nullptr), s));
+    }
+    const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
+    T* lnf = c->act<T>(p.lnf);
+    TRY(layernorm_fwd_launch<T>(lnf, c->act<float>(p.lnfm), c->act<float>(p.lnfr), resL, prm<T>(c, 14), prm<T>(c, 15),
+                                BT, C, s));
+    T* logits = c->act<T>(p.logits);
+    TRY(gemm(c, fwd_desc(BT, Vp, C, lnf, prm<T>(c, 0), logits, GEMM_STORE, nullptr, nullptr, nullptr), s));
+    if (targets) {
+        float* losses = c->act<float>(p.losses);
+        TRY(classifier_ce_launch<T>(logits, losses, targets, BT, V, Vp, c->flag(), s));
+        if (d_losses) TRY((int)hipMemcpyAsync(d_losses, losses, (size_t)BT * 4, hipMemcpyDeviceToDevice, s));
+        if (d_mean) TRY(mean_launch(d_mean, losses, BT, s));
+    }
+    return GPT2_OK;
+}
+
+template <typename T>
+int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
+    const Plan& p = c->plan;
+    const int B = c->B, Tn = c->T, BT = (int)p.BT, C = (int)p.C, L = (int)p.L, NH = (int)p.NH, Vp = (int)p.Vp;
+    const size_t CC = (size_t)C * C;
+    const bool lowp = c->prec == GPT2_BF16;
+    const float alpha = dloss > 0.f ? dloss : 1.0f / (float)BT;
+    T* logits = c->act<T>(p.logits);  // holds softmax - onehot
+    T* lnf = c->act<T>(p.lnf);
+    T* dbtc = c->act<T>(p.dbtc);
+    T* dbt4c = c->act<T>(p.dbt4c);
+    T* dqkv = c->act<T>(p.dqkv);
+    float* dres = c->act<float>(p.dres32);
+    T* dres_lp = lowp ? c->act<T>(p.dres_lp) : (T*)dres;
+    T* dres_lp_out = lowp ? dres_lp : nullptr;
+    float* work = c->work();
+    // classifier (tied weights): dlnf = alpha * dlogits wte; dwte += alpha * dlogits^T lnf
+    TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s));
+    TRY(gemm(c, dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha), s));
+    const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
+    TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
+                                c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s));
+    for (int l = L - 1; l >= 0; l--) {
+        const T* res = l == 0 ? c->act<T>(p.enc) : c->act_l<T>(p.res3, p.s_btc, l - 1);
+        const T* ln1 = c->act_l<T>(p.ln1, p.s_btc, l);
+        const T* qkv = c->act_l<T>(p.qkv, p.s_bt3c, l);
+        const T* atty = c->act_l<T>(p.atty, p.s_btc, l);
+        const T* res2 = c->act_l<T>(p.res2, p.s_btc, l);
+        const T* ln2 = c->act_l<T>(p.ln2, p.s_btc, l);
+        const T* fch = c->act_l<T>(p.fch, p.s_bt4c, l);
+        const T* fchg = c->act_l<T>(p.fchg, p.s_bt4c, l);
+        // fcproj (+ GELU backward fused into its input-gradient product)
+        TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_lp, prm<T>(c, 12, l, 4 * CC), dbt4c, GEMM_GELU_BWD, fch, 1.0f), s));
+        TRY(gemm(c, dw_desc(BT, 4 * C, C, dres_lp, fchg, grd(c, 12, l, 4 * CC), 1.0f), s));
+        TRY(bias_grad_launch<T>(grd(c, 13, l, C), dres_lp, BT, C, C, work, s));
+        // fc
+        TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c, prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(gemm(c, dw_desc(BT, C, 4 * C, dbt4c, ln2, grd(c, 10, l, 4 * CC), 1.0f), s));
+        TRY(bias_grad_launch<T>(grd(c, 11, l, 4 * C), dbt4c, BT, 4 * C, 4 * C, work, s));
+        TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
+                                    prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
+                                    c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s));
+        // attproj
+        TRY(gemm(c, dx_desc(BT, C, C, dres_lp, prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(gemm(c, dw_desc(BT, C, C, dres_lp, atty, grd(c, 6, l, CC), 1.0f), s));
+        TRY(bias_grad_launch<T>(grd(c, 7, l, C), dres_lp, BT, C, C, work, s));
+        // attention
+        TRY(attention_bwd_launch<T>(dqkv, c->act<float>(p.delta), dbtc, atty, qkv, c->act_l<float>(p.lse, p.s_lse, l),
+                                    B, Tn, C, NH, s));
+        // qkv
+        TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv, prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(gemm(c, dw_desc(BT, C, 3 * C, dqkv, ln1, grd(c, 4, l, 3 * CC), 1.0f), s));
+        TRY(bias_grad_launch<T>(grd(c, 5, l, 3 * C), dqkv, BT, 3 * C, 3 * C, work, s));
+        TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 2, l, C), grd(c, 3, l, C), dbtc, res,
+                                    prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
+                                    c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, work, s));
+    }
+    TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, s));
+    return GPT2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpt2_query_sizes(const gpt2_config* cfg, int precision, int B, int T, gpt2_sizes* out) {
+    int rc = check_config(cfg, precision, B, T);
+    if (rc) return rc;
+    if (!out) return GPT2_E_ARG;
+    size_t off[16], cnt[16], P;
+    param_layout(*cfg, off, cnt, &P);
+    Plan p = make_plan(*cfg, precision, B, T);
+    out->params = align_up(P * p.esz);
+    out->master = precision == GPT2_BF16 ? align_up(P * 4) : 0;
+    out->grads = out->adam_m = out->adam_v = align_up(P * 4);
+    out->acts = p.acts_bytes;
+    out->scratch = p.scratch_bytes;
+    return GPT2_OK;
+}
+
+int gpt2_param_layout(const gpt2_config* cfg, size_t offset[16], size_t count[16], size_t* total) {
+    if (!cfg || !offset || !count || !total) return GPT2_E_ARG;
+    if (cfg->num_layers < 1 || cfg->channels < 1 || cfg->padded_vocab_size < 1 || cfg->max_seq_len < 1)
+        return GPT2_E_ARG;
+    param_layout(*cfg, offset, count, total);
+    return GPT2_OK;
+}
+
+int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, int precision, int B, int T, const gpt2_buffers* bufs,
+              void* hip_stream) {
+    if (!out) return GPT2_E_ARG;
+    *out = nullptr;
+    int rc = check_config(cfg, precision, B, T);
+    if (rc) return rc;
+    if (!bufs || !bufs->params || !bufs->grads || !bufs->adam_m || !bufs->adam_v || !bufs->acts || !bufs->scratch)
+        return GPT2_E_ARG;
+    if (precision == GPT2_BF16 && !bufs->master) return GPT2_E_ARG;
+    const void* ptrs[7] = {bufs->params, bufs->master, bufs->grads, bufs->adam_m, bufs->adam_v, bufs->acts, bufs->scratch};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return GPT2_E_ALIGN;
+    gpt2_ctx* c = new (std::nothrow) gpt2_ctx();
+    if (!c) return GPT2_E_ARG;
+    c->cfg = *cfg;
+    c->prec = precision;
+    c->B = B;
+    c->T = T;
+    param_layout(*cfg, c->off, c->cnt, &c->P);
+    c->buf = *bufs;
+    if (precision == GPT2_FP32) c->buf.master = nullptr;
+    c->plan = make_plan(*cfg, precision, B, T);
+    c->last_fwd_targets = -1;
+    hipStream_t s = (hipStream_t)hip_stream;
+    int e = 0;
+    e |= fill_f32_launch((float*)c->buf.adam_m, 0.f, c->P, s);
+    e |= fill_f32_launch((float*)c->buf.adam_v, 0.f, c->P, s);
+    e |= fill_i32_launch(c->flag(), 0, 64, s);
+    if (precision == GPT2_BF16) e |= cast_f32_to_bf16_launch((bf16_t*)c->buf.params, (const float*)c->buf.master, c->P, s);
+    if (e) {
+        delete c;
+        return GPT2_E_HIP;
+    }
+    *out = c;
+    return GPT2_OK;
+}
+
+int gpt2_forward(gpt2_ctx* c, const int32_t* d_inputs, const int32_t* d_targets, float* d_losses,
+                 float* d_mean_loss, void* hip_stream) {
+    if (!c || !d_inputs) return GPT2_E_ARG;
+    if (!aligned(d_inputs) || (d_targets && !aligned(d_targets)) || (d_losses && !aligned(d_losses)) ||
+        (d_mean_loss && ((uintptr_t)d_mean_loss % 4)))
+        return GPT2_E_ALIGN;
+    hipStream_t s = (hipStream_t)hip_stream;
+    int rc = c->prec == GPT2_BF16 ? forward_impl<bf16_t>(c, d_inputs, d_targets, d_losses, d_mean_loss, s)
+                                  : forward_impl<float>(c, d_inputs, d_targets, d_losses, d_mean_loss, s);
+    c->last_fwd_targets = rc == GPT2_OK ? (d_targets ? 1 : 0) : -1;
+    return rc;
+}
+
+int gpt2_zero_grad(gpt2_ctx* c, void* hip_stream) {
+    if (!c) return GPT2_E_ARG;
+    return hip_rc(fill_f32_launch((float*)c->buf.grads, 0.f, c->P, (hipStream_t)hip_stream));
+}
+
+int gpt2_backward(gpt2_ctx* c, float dloss, void* hip_stream) {
+    if (!c) return GPT2_E_ARG;
+    if (c->last_fwd_targets != 1) return GPT2_E_STATE;
+    if (!(dloss == dloss)) return GPT2_E_ARG;  // NaN
+    hipStream_t s = (hipStream_t)hip_stream;
+    int rc = c->prec == GPT2_BF16 ? backward_impl<bf16_t>(c, dloss, s) : backward_impl<float>(c, dloss, s);
+    // the in-place softmax - onehot has been consumed; a new forward is needed
+    c->last_fwd_targets = -1;
+    return rc;
+}
+
+int gpt2_adamw_update(gpt2_ctx* c, float lr, float beta1, float beta2, float eps, float weight_decay, int t,
+                      void* hip_stream) {
+    if (!c || t < 1) return GPT2_E_ARG;
+    if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f)) return GPT2_E_ARG;
+    const float c1 = (float)(1.0 - pow((double)beta1, t));
+    const float c2 = (float)(1.0 - pow((double)beta2, t));
+    hipStream_t s = (hipStream_t)hip_stream;
+    int e;
+    if (c->prec == GPT2_BF16)
+        e = adamw_launch<bf16_t>((bf16_t*)c->buf.params, (float*)c->buf.master, (const float*)c->buf.grads,
+                                 (float*)c->buf.adam_m, (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps,
+                                 weight_decay, s);
+    else
+        e = adamw_launch<float>((float*)c->buf.params, nullptr, (const float*)c->buf.grads, (float*)c->buf.adam_m,
+                                (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps, weight_decay, s);
+    return hip_rc(e);
+}
+
+int gpt2_check_device_error(gpt2_ctx* c, void* hip_stream) {
+    if (!c) return GPT2_E_ARG;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (hipStreamSynchronize(s) != hipSuccess) return GPT2_E_HIP;
+    int flag = 0;
+    if (hipMemcpy(&flag, c->flag(), sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return GPT2_E_HIP;
+    if (flag) {
+        if (fill_i32_launch(c->flag(), 0, 64, s) != 0) return GPT2_E_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return GPT2_E_HIP;
+        return GPT2_E_TOKEN;
+    }
+    return GPT2_OK;
+}
+
+int gpt2_act_tensor(gpt2_ctx* c, int which, void** d_ptr, size_t* count) {
+    if (!c || !d_ptr || !count) return GPT2_E_ARG;
+    const Plan& p = c->plan;
+    switch (which) {
+        case GPT2_T_LOGITS: *d_ptr = c->act<char>(p.logits); *count = p.BT * p.Vp; return GPT2_OK;
+        case GPT2_T_LNF: *d_ptr = c->act<char>(p.lnf); *count = p.BT * p.C; return GPT2_OK;
+        case GPT2_T_RESIDUAL: *d_ptr = c->act<char>(p.res3 + p.s_btc * (p.L - 1)); *count = p.BT * p.C; return GPT2_OK;
+        case GPT2_T_DRESIDUAL: *d_ptr = c->act<char>(p.dres32); *count = p.BT * p.C; return GPT2_OK;
+        case GPT2_T_ENCODED: *d_ptr = c->act<char>(p.enc); *count = p.BT * p.C; return GPT2_OK;
+        default: return GPT2_E_ARG;
+    }
+}
+
+int gpt2_free(gpt2_ctx* c) {
+    delete c;
+    return GPT2_OK;
+}
+
+const char* gpt2_strerror(int code) {
+    switch (code) {
+        case GPT2_OK: return "ok";
+        case GPT2_E_ARG: return "invalid argument";
+        case GPT2_E_SHAPE: return "unsupported shape";
+        case GPT2_E_STATE: return "call order violated (backward needs a forward with targets)";
+        case GPT2_E_TOKEN: return "token or target id outside [0, vocab_size)";
+        case GPT2_E_ALIGN: return "pointer not 256-byte aligned";
+        case GPT2_E_HIP: return "HIP runtime or kernel launch failure";
+        default: return "unknown error";
+    }
+}
+
+}  // extern "C"

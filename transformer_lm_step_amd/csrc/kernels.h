@@ -1,0 +1,84 @@
+// kernels.h - host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+
+// ---------------------------------------------------------------- GEMM ------
+// C[m,n] (op)= alpha * sum_k A(m,k) B(k,n), every matrix row-major.
+//  A(m,k) = a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//  B(k,n) = b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+// Epilogues (per output element v = alpha * acc):
+enum GemmEpi {
+    GEMM_STORE = 0,      // C = v
+    GEMM_BIAS = 1,       // C = v + bias[n]
+    GEMM_BIAS_GELU = 2,  // aux_out = v + bias[n]; C = gelu(aux_out)
+    GEMM_BIAS_RESID = 3, // C = aux_in + v + bias[n]
+    GEMM_GELU_BWD = 4,   // C = v * gelu'(aux_in)
+    GEMM_ACCUM = 5,      // C (fp32) += v
+};
+struct GemmDesc {
+    int M, N, K;
+    const void* A; long lda; int a_kmajor;
+    const void* B; long ldb; int b_kmajor;
+    void* C; long ldc;        // C element type: the activation type, or fp32 for GEMM_ACCUM
+    int epi;
+    float alpha;
+    const void* bias;         // activation/param type, [N]
+    const void* aux_in;       // activation type, ld = ldaux
+    void* aux_out;            // activation type, ld = ldaux
+    long ldaux;
+};
+// Workspace (fp32) needed by gemm_launch for split-K (0 if it will not split).
+size_t gemm_workspace_bytes(const GemmDesc& d, int elem_bytes, int num_cus);
+// Returns 0 or a hipError_t.  ws may be NULL if gemm_workspace_bytes(d) == 0.
+int gemm_launch(const GemmDesc& d, int elem_bytes, float* ws, size_t ws_bytes, int num_cus, hipStream_t s);
+
+// db[n] += sum_m dY[m*ldy + n]; partial: ceil(M/256) * N floats of workspace.
+template <typename T>
+int bias_grad_launch(float* db, const T* dY, int M, int N, long ldy, float* partial, hipStream_t s);
+size_t bias_grad_workspace_bytes(int M, int N);
+
+// ---------------------------------------------------------- LayerNorm -------
+template <typename T>
+int layernorm_fwd_launch(T* out, float* mean, float* rstd, const T* x, const T* w, const T* b,
+                         int N, int C, hipStream_t s);
+// dres (fp32) = (accumulate ? dres : 0) + dx; dres_lp (may be NULL) = T(dres);
+// dw, db (fp32) += column sums.  partial: layernorm_bwd_workspace_bytes.
+template <typename T>
+int layernorm_bwd_launch(float* dres, T* dres_lp, float* dw, float* db, const T* dy, const T* x,
+                         const T* w, const float* mean, const float* rstd, int N, int C,
+                         int accumulate, float* partial, hipStream_t s);
+size_t layernorm_bwd_workspace_bytes(int N, int C);
+
+// ---------------------------------------------------------- attention -------
+// qkv [B,T,3C] -> out [B,T,C], lse [B,NH,T] (base-2 log-sum-exp of the scaled scores)
+template <typename T>
+int attention_fwd_launch(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s);
+// dqkv [B,T,3C] (=) from dout [B,T,C]; delta [B,NH,T] fp32 scratch.
+template <typename T>
+int attention_bwd_launch(T* dqkv, float* delta, const T* dout, const T* out, const T* qkv,
+                         const float* lse, int B, int T_, int C, int NH, hipStream_t s);
+
+// ------------------------------------------------------- elementwise etc. ---
+template <typename T>
+int encoder_fwd_launch(T* out, int* tok_copy, const int* tok, const T* wte, const T* wpe,
+                       int B, int T_, int C, int V, int* flag, hipStream_t s);
+// dwte[tok] += dres rows, dwpe[t] += sum_b dres; fp32.  tok already clamped.
+int encoder_bwd_launch(float* dwte, float* dwpe, const float* dres, const int* tok,
+                       int B, int T_, int C, hipStream_t s);
+// in place: logits -> softmax - onehot (padded columns 0); losses [N] fp32
+template <typename T>
+int classifier_ce_launch(T* logits, float* losses, const int* targets, int N, int V, int Vp,
+                         int* flag, hipStream_t s);
+int mean_launch(float* out, const float* x, int n, hipStream_t s);
+template <typename PT>
+int adamw_launch(PT* params, float* master, const float* grads, float* m, float* v, size_t n,
+                 float lr, float beta1, float beta2, float c1, float c2, float eps, float wd,
+                 hipStream_t s);
+int fill_f32_launch(float* p, float value, size_t n, hipStream_t s);
+int fill_i32_launch(int* p, int value, size_t n, hipStream_t s);
+int cast_f32_to_bf16_launch(bf16_t* dst, const float* src, size_t n, hipStream_t s);
