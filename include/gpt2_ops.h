@@ -24,6 +24,19 @@ extern "C" {
 int gpt2_linear_forward(int precision, const void* d_x, const void* d_w, const void* d_bias, void* d_y,
                         int M, int N, int K, void* hip_stream);
 
+/* train_gpt2.cu, matmul_backward (with matmul_backward_bias_kernel4), for
+ * y = x w^T + b with x [M,K], w [N,K]:
+ *   dx[M,K]  = alpha * dy[M,N] w[N,K]            (overwrite; skipped if d_dx NULL)
+ *   dw[N,K] += alpha * dy[M,N]^T x[M,K]          (fp32, accumulate; skipped if d_dw NULL)
+ *   db[N]   += alpha * sum over rows of dy       (fp32, accumulate; needs d_dw)
+ * dy, x, w, dx in the precision's type.  K and N multiples of 8.  d_work:
+ * device workspace of gpt2_linear_backward_workspace() bytes (may be NULL
+ * when that is 0).  Errors: GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_ALIGN, GPT2_E_HIP. */
+int gpt2_linear_backward(int precision, const void* d_dy, const void* d_x, const void* d_w, void* d_dx,
+                         float* d_dw, float* d_db, int M, int N, int K, float alpha, void* d_work,
+                         size_t work_bytes, void* hip_stream);
+size_t gpt2_linear_backward_workspace(int precision, int M, int N, int K);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,12 +21,15 @@ pytestmark = pytest.mark.gpu
 # attention blocks), Vp = 1000 (128-column tiles), head size 64 and 32
 RAGGED64 = S.Config(max_seq_len=160, vocab_size=997, padded_vocab_size=1000, num_layers=2, num_heads=3, channels=192)
 RAGGED32 = S.Config(max_seq_len=160, vocab_size=997, padded_vocab_size=1000, num_layers=1, num_heads=6, channels=192)
+# T a multiple of 64 with several full key blocks before the diagonal one
+BLOCKS64 = S.Config(max_seq_len=256, vocab_size=500, padded_vocab_size=512, num_layers=1, num_heads=2, channels=128)
 
 FP32_CASES = [
     ("tiny", S.TINY, 4, 64, False),
     ("tiny-perturbed", S.TINY, 4, 64, True),
     ("ragged-hs64", RAGGED64, 2, 150, True),
     ("ragged-hs32", RAGGED32, 3, 100, True),
+    ("blocks-hs64", BLOCKS64, 2, 256, True),
 ]
 
 

@@ -23,7 +23,8 @@ GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0
 EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
-    "gpt2_free", "gpt2_strerror", "gpt2_linear_forward",
+    "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
+    "gpt2_linear_backward_workspace",
 )
 
 
@@ -68,6 +69,8 @@ def _load():
         "gpt2_free": (i, [vp]),
         "gpt2_strerror": (ctypes.c_char_p, [i]),
         "gpt2_linear_forward": (i, [i, vp, vp, vp, vp, i, i, i, vp]),
+        "gpt2_linear_backward": (i, [i, vp, vp, vp, vp, vp, vp, i, i, i, f, vp, z, vp]),
+        "gpt2_linear_backward_workspace": (z, [i, i, i, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -168,3 +171,14 @@ def gpt2_linear_forward(precision: int, d_x: int, d_w: int, d_bias: int, d_y: in
                         stream: int):
     _check(_lib.gpt2_linear_forward(precision, d_x, d_w, d_bias or None, d_y, M, N, K, stream or None),
            "gpt2_linear_forward")
+
+
+def gpt2_linear_backward_workspace(precision: int, M: int, N: int, K: int) -> int:
+    return int(_lib.gpt2_linear_backward_workspace(precision, M, N, K))
+
+
+def gpt2_linear_backward(precision: int, d_dy: int, d_x: int, d_w: int, d_dx: int, d_dw: int, d_db: int,
+                         M: int, N: int, K: int, alpha: float, d_work: int, work_bytes: int, stream: int):
+    _check(_lib.gpt2_linear_backward(precision, d_dy, d_x or None, d_w or None, d_dx or None, d_dw or None,
+                                     d_db or None, M, N, K, float(alpha), d_work or None, int(work_bytes),
+                                     stream or None), "gpt2_linear_backward")

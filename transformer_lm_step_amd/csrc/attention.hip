@@ -32,6 +32,8 @@
 // triangle.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -50,30 +52,33 @@ struct ACfg {
 };
 
 // 64 rows x KD of one head slice: dst[row*RP + d] = src(row0+row, d); zero past T or HS.
-template <typename T, int HS>
+// FULL: the caller guarantees row0 + 63 < T_ (no row check).
+template <typename T, int HS, bool FULL = false>
 DEV void stage_rows(T* dst, const T* src, long rs, int row0, int T_, int tid) {
     using A = ACfg<T, HS>;
     constexpr int VPR = A::KD / A::VEC;
+#pragma unroll
     for (int idx = tid; idx < 64 * VPR; idx += 256) {
         const int row = idx / VPR, d0 = (idx % VPR) * A::VEC;
         const int gr = row0 + row;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (gr < T_ && d0 < HS) v = ld16(src + (long)gr * rs + d0);
+        if ((FULL || gr < T_) && d0 < HS) v = ld16(src + (long)gr * rs + d0);
         st16(dst + row * A::RP + d0, v);
     }
 }
 // The same 64 rows transposed: dst[d*TP + row] (rows past T are zero).
-template <typename T, int HS>
+template <typename T, int HS, bool FULL = false>
 DEV void stage_rows_t(T* dst, const T* src, long rs, int row0, int T_, int tid) {
     using A = ACfg<T, HS>;
     constexpr int DG = HS / A::VEC;
+#pragma unroll
     for (int idx = tid; idx < 16 * DG; idx += 256) {
         const int kq = idx % 16, dg = idx / 16;
         uint4 r[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int gr = row0 + 4 * kq + i;
-            r[i] = gr < T_ ? ld16(src + (long)gr * rs + dg * A::VEC) : make_uint4(0, 0, 0, 0);
+            r[i] = (FULL || gr < T_) ? ld16(src + (long)gr * rs + dg * A::VEC) : make_uint4(0, 0, 0, 0);
         }
         store_t4<T>(dst + dg * A::VEC * A::TP + 4 * kq, A::TP, r);
     }
@@ -91,13 +96,22 @@ DEV void row_frags(Frag<T>* f, const T* src, long rs, int row, int T_, int g4) {
 }
 
 // ------------------------------------------------------------------ forward -
+// Per 64-key block and wave (16 query rows): S^T = K Q^T (HS/32 MFMA steps per
+// 16-key tile), online softmax in fp32 on the lane-owned scores, O^T += V^T P^T.
+// The scores' scale is folded into the exponent (one FMA per score), exp2 is
+// the hardware instruction (results below 2^-126 flush to zero, far below
+// anything that reaches bf16 or the loss), the causal mask is only evaluated
+// on the diagonal block, and the row sums come out of the P V product itself:
+// V^T is extended by 16 rows of ones, so that extra output tile holds
+// sum_key P for every query.  O is rescaled only when some row's maximum grew.
 template <typename T, int HS>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(T* __restrict__ out, float* __restrict__ lse,
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, float* __restrict__ lse,
                                                        const T* __restrict__ qkv, int T_, int C, int NH,
                                                        float sl2) {
     using A = ACfg<T, HS>;
+    constexpr int DT1 = A::DT + 1;  // output tiles incl. the row-sum tile
     __shared__ __attribute__((aligned(16))) T sK[64 * A::RP];
-    __shared__ __attribute__((aligned(16))) T sVt[HS * A::TP];
+    __shared__ __attribute__((aligned(16))) T sVt[(HS + 16) * A::TP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int qb = gridDim.x - 1 - blockIdx.x;
@@ -108,18 +122,22 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(T* __restrict__ out, floa
     const T* Vh = Qh + 2 * C;
     const int q = qb * 64 + wave * 16 + l16;
 
+    // the ones rows of the extended V^T (written once)
+    for (int i = tid; i < 16 * 64; i += 256) sVt[(HS + i / 64) * A::TP + (i % 64)] = from_f<T>(1.0f);
+
     Frag<T> fq[A::DSTEPS];
     row_frags<T, HS>(fq, Qh, rs, q, T_, g4);
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4_t o[A::DT];
+    float m_run = -INFINITY;  // running max of the raw scores of this lane's query
+    f32x4_t o[DT1];
 #pragma unroll
-    for (int dt = 0; dt < A::DT; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT1; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = 0; kb <= qb; kb++) {
+    auto block = [&](int kb, auto diag) {
         __syncthreads();
-        stage_rows<T, HS>(sK, Kh, rs, kb * 64, T_, tid);
-        stage_rows_t<T, HS>(sVt, Vh, rs, kb * 64, T_, tid);
+        constexpr bool full = !decltype(diag)::value;
+        stage_rows<T, HS, full>(sK, Kh, rs, kb * 64, T_, tid);
+        stage_rows_t<T, HS, full>(sVt, Vh, rs, kb * 64, T_, tid);
         __syncthreads();
         // S^T tiles: lane holds S^T[key = 16kt + 4g4 + r][query = l16]
         f32x4_t s[4];
@@ -133,36 +151,32 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(T* __restrict__ out, floa
                 mma(s[kt], fk, fq[ks]);
             }
         }
+        if constexpr (decltype(diag)::value) {
+#pragma unroll
+            for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (kb * 64 + 16 * kt + 4 * g4 + r > q) s[kt][r] = -INFINITY;
+        }
         float mloc = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; kt++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int key = kb * 64 + 16 * kt + 4 * g4 + r;
-                const float v = key <= q ? s[kt][r] * sl2 : -INFINITY;
-                s[kt][r] = v;
-                mloc = fmaxf(mloc, v);
-            }
+            mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
         const float m_new = fmaxf(m_run, mloc);
-        const float alpha = exp2f(m_run - m_new);
-        float lsum = 0.f;
+        if (__any(m_new > m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
+#pragma unroll
+            for (int dt = 0; dt < DT1; dt++) o[dt] *= alpha;
+        }
+        m_run = m_new;
+        const float mc = -m_new * sl2;
 #pragma unroll
         for (int kt = 0; kt < 4; kt++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float p = exp2f(s[kt][r] - m_new);
-                s[kt][r] = p;
-                lsum += p;
-            }
-        lsum += __shfl_xor(lsum, 16, 64);
-        lsum += __shfl_xor(lsum, 32, 64);
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < A::DT; dt++) o[dt] *= alpha;
-        // O^T[d][q] += V^T[d][key] P^T[key][q], 32 keys per step
+            for (int r = 0; r < 4; r++) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], sl2, mc));
+        // O^T[d][q] += V^T[d][key] P^T[key][q], 32 keys per step; d-tile DT is the row sum
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             float pv[8] = {s[2 * c][0], s[2 * c][1], s[2 * c][2], s[2 * c][3],
@@ -170,15 +184,19 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(T* __restrict__ out, floa
             Frag<T> fp;
             frag_from(fp, pv);
 #pragma unroll
-            for (int dt = 0; dt < A::DT; dt++) {
+            for (int dt = 0; dt < DT1; dt++) {
                 const T* vr = sVt + (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
                 Frag<T> fv;
                 frag_ld2(fv, vr, vr + 16);
                 mma(o[dt], fv, fp);
             }
         }
-    }
+    };
+    for (int kb = 0; kb < qb; kb++) block(kb, std::false_type{});
+    block(qb, std::true_type{});
+
     if (q < T_) {
+        const float l_run = o[A::DT][0];
         const float inv = 1.0f / l_run;
         T* orow = out + ((long)b * T_ + q) * C + h * HS;
 #pragma unroll
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(T* __restrict__ out, floa
             float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
             store4<T>(orow + 16 * dt + 4 * g4, v);
         }
-        if (g4 == 0) lse[((long)b * NH + h) * T_ + q] = m_run + log2f(l_run);
+        if (g4 == 0) lse[((long)b * NH + h) * T_ + q] = m_run * sl2 + log2f(l_run);
     }
 }
 
@@ -215,11 +233,15 @@ __global__ void attn_delta_kernel(float* __restrict__ delta, const T* __restrict
     delta[(b * NH + h) * T_ + t] = s;
 }
 
+// dK/dV: one workgroup per 64-key block, looping over the query blocks at or
+// after it.  Query rows past T carry lse = +inf, so their P is exactly zero and
+// only the diagonal block needs the causal test; the 1/sqrt(HS) factor of dS is
+// applied once to dK at the end.
 template <typename T, int HS>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
-                                                            const T* __restrict__ qkv, const float* __restrict__ lse,
-                                                            const float* __restrict__ delta, int T_, int C, int NH,
-                                                            float sl2, float scale) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
+                                                               const T* __restrict__ qkv, const float* __restrict__ lse,
+                                                               const float* __restrict__ delta, int T_, int C, int NH,
+                                                               float sl2, float scale) {
     using A = ACfg<T, HS>;
     __shared__ __attribute__((aligned(16))) T sQ[64 * A::RP];
     __shared__ __attribute__((aligned(16))) T sdO[64 * A::RP];
@@ -250,12 +272,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv
         dv[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const int nqb = (T_ + 63) / 64;
-    for (int qb = kb; qb < nqb; qb++) {
+    auto block = [&](int qb, auto diag, auto full) {
         __syncthreads();
-        stage_rows<T, HS>(sQ, Qh, rs, qb * 64, T_, tid);
-        stage_rows<T, HS>(sdO, dOh, C, qb * 64, T_, tid);
-        stage_rows_t<T, HS>(sQt, Qh, rs, qb * 64, T_, tid);
-        stage_rows_t<T, HS>(sdOt, dOh, C, qb * 64, T_, tid);
+        stage_rows<T, HS, decltype(full)::value>(sQ, Qh, rs, qb * 64, T_, tid);
+        stage_rows<T, HS, decltype(full)::value>(sdO, dOh, C, qb * 64, T_, tid);
+        stage_rows_t<T, HS, decltype(full)::value>(sQt, Qh, rs, qb * 64, T_, tid);
+        stage_rows_t<T, HS, decltype(full)::value>(sdOt, dOh, C, qb * 64, T_, tid);
         if (tid < 64) {
             const int qq = qb * 64 + tid;
             sL[tid] = qq < T_ ? lse_h[qq] : INFINITY;
@@ -285,10 +307,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv
             const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int qq = qb * 64 + 16 * qt + 4 * g4 + r;
-                const float pr = (key <= qq && qq < T_) ? exp2f(p[qt][r] * sl2 - Lr[r]) : 0.f;
+                float pr = __builtin_amdgcn_exp2f(fmaf(p[qt][r], sl2, -Lr[r]));
+                if constexpr (decltype(diag)::value)
+                    if (key > qb * 64 + 16 * qt + 4 * g4 + r) pr = 0.f;
                 p[qt][r] = pr;
-                ds[qt][r] = pr * (ds[qt][r] - Dr[r]) * scale;
+                ds[qt][r] = pr * (ds[qt][r] - Dr[r]);
             }
         }
         // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
@@ -311,12 +334,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv
                 mma(dk[dt], fa, fs);
             }
         }
+    };
+    const bool tail_full = (T_ % 64) == 0;
+    if (kb + 1 < nqb || tail_full) block(kb, std::true_type{}, std::true_type{});
+    else block(kb, std::true_type{}, std::false_type{});
+    for (int qb = kb + 1; qb + 1 < nqb; qb++) block(qb, std::false_type{}, std::true_type{});
+    if (kb + 1 < nqb) {
+        if (tail_full) block(nqb - 1, std::false_type{}, std::true_type{});
+        else block(nqb - 1, std::false_type{}, std::false_type{});
     }
     if (key < T_) {
         T* row = dqkv + ((long)b * T_ + key) * rs + h * HS;
 #pragma unroll
         for (int dt = 0; dt < A::DT; dt++) {
-            float kv[4] = {dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]};
+            float kv[4] = {dk[dt][0] * scale, dk[dt][1] * scale, dk[dt][2] * scale, dk[dt][3] * scale};
             float vv[4] = {dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
             store4<T>(row + C + 16 * dt + 4 * g4, kv);
             store4<T>(row + 2 * C + 16 * dt + 4 * g4, vv);
@@ -324,11 +355,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv
     }
 }
 
+// dQ: one workgroup per 64-query block, looping over the key blocks at or
+// before it (all full but the diagonal one); 1/sqrt(HS) applied at the end.
 template <typename T, int HS>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
-                                                          const T* __restrict__ qkv, const float* __restrict__ lse,
-                                                          const float* __restrict__ delta, int T_, int C, int NH,
-                                                          float sl2, float scale) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
+                                                             const T* __restrict__ qkv, const float* __restrict__ lse,
+                                                             const float* __restrict__ delta, int T_, int C, int NH,
+                                                             float sl2, float scale) {
     using A = ACfg<T, HS>;
     __shared__ __attribute__((aligned(16))) T sK[64 * A::RP];
     __shared__ __attribute__((aligned(16))) T sV[64 * A::RP];
@@ -353,11 +386,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(T* __restrict__ dqkv, 
 #pragma unroll
     for (int dt = 0; dt < A::DT; dt++) dq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = 0; kb <= qb; kb++) {
+    auto block = [&](int kb, auto diag) {
+        constexpr bool full = !decltype(diag)::value;
         __syncthreads();
-        stage_rows<T, HS>(sK, Kh, rs, kb * 64, T_, tid);
-        stage_rows<T, HS>(sV, Vh, rs, kb * 64, T_, tid);
-        stage_rows_t<T, HS>(sKt, Kh, rs, kb * 64, T_, tid);
+        stage_rows<T, HS, full>(sK, Kh, rs, kb * 64, T_, tid);
+        stage_rows<T, HS, full>(sV, Vh, rs, kb * 64, T_, tid);
+        stage_rows_t<T, HS, full>(sKt, Kh, rs, kb * 64, T_, tid);
         __syncthreads();
         // S^T[key][q], dP^T[key][q]: lane holds key = 16kt + 4g4 + r, q = l16
         f32x4_t s[4], dp[4];
@@ -378,9 +412,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(T* __restrict__ dqkv, 
         for (int kt = 0; kt < 4; kt++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int key = kb * 64 + 16 * kt + 4 * g4 + r;
-                const float pr = (key <= q && q < T_) ? exp2f(s[kt][r] * sl2 - Lq) : 0.f;
-                s[kt][r] = pr * (dp[kt][r] - Dq) * scale;  // dS^T
+                float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], sl2, -Lq));
+                if constexpr (decltype(diag)::value)
+                    if (kb * 64 + 16 * kt + 4 * g4 + r > q) pr = 0.f;
+                s[kt][r] = pr * (dp[kt][r] - Dq);  // dS^T / scale
             }
         // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
 #pragma unroll
@@ -397,12 +432,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(T* __restrict__ dqkv, 
                 mma(dq[dt], fa, fs);
             }
         }
-    }
+    };
+    for (int kb = 0; kb < qb; kb++) block(kb, std::false_type{});
+    block(qb, std::true_type{});
     if (q < T_) {
         T* row = dqkv + ((long)b * T_ + q) * rs + h * HS;
 #pragma unroll
         for (int dt = 0; dt < A::DT; dt++) {
-            float v[4] = {dq[dt][0], dq[dt][1], dq[dt][2], dq[dt][3]};
+            float v[4] = {dq[dt][0] * scale, dq[dt][1] * scale, dq[dt][2] * scale, dq[dt][3] * scale};
             store4<T>(row + 16 * dt + 4 * g4, v);
         }
     }

@@ -77,6 +77,22 @@ template <> DEV uint4 pack16<bf16_t>(const float* f) {
 }
 
 DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Raw buffer access (gfx9 buffer resource: base, byte range, dword data
+// format).  A load whose byte offset falls outside [0, bytes) returns zeros.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+DEV uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+constexpr uint32_t kBufOOB = 0x80000000u;  // an offset past any range used here
+
+// v if ok, else zeros (component-wise select, no branch and no memory)
+DEV uint4 keep16(bool ok, const uint4& v) {
+    const uint32_t m = ok ? 0xffffffffu : 0u;
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
 DEV void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 DEV uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 DEV void st8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }

@@ -92,6 +92,155 @@ __global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict_
     }
 }
 
+// Sort-based variant (B*T <= 16384), all deterministic:
+//  1. one workgroup sorts the keys (id << shift | position) in LDS (bitonic);
+//     equal ids end up adjacent, in increasing position order;
+//  2. one wave per chunk of 16 sorted entries sums each run of equal ids in
+//     order.  A run that neither continues from the previous chunk nor into the
+//     next one is complete and is added into dwte by that wave; otherwise the
+//     piece goes to workspace (a run continuing from the previous chunk is a
+//     "head" piece, one that starts here and continues is a "tail" piece);
+//  3. for every tail piece, one wave adds the head pieces of the following
+//     chunks, in chunk order, and adds the total into dwte.
+constexpr int ENC_CHUNK = 16;
+constexpr int ENC_SORT_MAX = 16384;
+
+__global__ __launch_bounds__(1024) void enc_sort_kernel(unsigned* __restrict__ sorted, const int* __restrict__ tok,
+                                                        int BT, int shift) {
+    __shared__ unsigned keys[ENC_SORT_MAX];
+    int n = 1;
+    while (n < BT) n <<= 1;
+    for (int i = threadIdx.x; i < n; i += 1024)
+        keys[i] = i < BT ? (((unsigned)tok[i] << shift) | (unsigned)i) : 0xffffffffu;
+    __syncthreads();
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += 1024) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const unsigned a = keys[i], b = keys[ixj];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) {
+                        keys[i] = b;
+                        keys[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = threadIdx.x; i < BT; i += 1024) sorted[i] = keys[i];
+}
+
+__global__ __launch_bounds__(256) void enc_chunk_kernel(float* __restrict__ dwte, float* __restrict__ headws,
+                                                        float* __restrict__ tailws, int* __restrict__ meta,
+                                                        const float* __restrict__ dres,
+                                                        const unsigned* __restrict__ sorted, int BT, int C,
+                                                        int shift, int nch) {
+    constexpr int NV = 8;
+    const int lane = threadIdx.x & 63;
+    const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (c >= nch) return;
+    const int e0 = c * ENC_CHUNK, e1 = min(e0 + ENC_CHUNK, BT);
+    const unsigned pmask = (1u << shift) - 1u;
+    const int prev = e0 > 0 ? (int)(sorted[e0 - 1] >> shift) : -1;
+    const int next = e1 < BT ? (int)(sorted[e1] >> shift) : -1;
+    const int nvec = C / 4;
+    float acc[NV][4];
+#pragma unroll
+    for (int k = 0; k < NV; k++) acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
+    int head_tok = -1, head_cont = 0, tail_tok = -1, run_start = e0;
+    for (int e = e0; e < e1; e++) {
+        const unsigned key = sorted[e];
+        const int v = (int)(key >> shift);
+        const float* r = dres + (long)(key & pmask) * C;
+#pragma unroll
+        for (int k = 0; k < NV; k++) {
+            const int vv = lane + 64 * k;
+            if (vv < nvec) {
+                float x[4];
+                load4<float>(r + vv * 4, x);
+#pragma unroll
+                for (int q = 0; q < 4; q++) acc[k][q] += x[q];
+            }
+        }
+        const bool end = (e == e1 - 1) || (int)(sorted[e + 1] >> shift) != v;
+        if (end) {
+            const bool head = run_start == e0 && prev == v;
+            const bool tail = e == e1 - 1 && next == v;
+            float* dst = (!head && !tail) ? dwte + (long)v * C : (head ? headws : tailws) + (long)c * C;
+#pragma unroll
+            for (int k = 0; k < NV; k++) {
+                const int vv = lane + 64 * k;
+                if (vv < nvec) {
+                    float o[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (!head && !tail) load4<float>(dst + vv * 4, o);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) o[q] += acc[k][q];
+                    store4<float>(dst + vv * 4, o);
+                }
+                acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
+            }
+            if (head) {
+                head_tok = v;
+                head_cont = tail ? 1 : 0;
+            } else if (tail) {
+                tail_tok = v;
+            }
+            run_start = e + 1;
+        }
+    }
+    if (lane == 0) {
+        meta[3 * c + 0] = head_tok;
+        meta[3 * c + 1] = head_cont;
+        meta[3 * c + 2] = tail_tok;
+    }
+}
+
+__global__ __launch_bounds__(256) void enc_fix_kernel(float* __restrict__ dwte, const float* __restrict__ headws,
+                                                      const float* __restrict__ tailws, const int* __restrict__ meta,
+                                                      int C, int nch) {
+    constexpr int NV = 8;
+    const int lane = threadIdx.x & 63;
+    const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (c >= nch) return;
+    const int v = meta[3 * c + 2];
+    if (v < 0) return;
+    const int nvec = C / 4;
+    float acc[NV][4];
+#pragma unroll
+    for (int k = 0; k < NV; k++) {
+        const int vv = lane + 64 * k;
+        acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
+        if (vv < nvec) load4<float>(tailws + (long)c * C + vv * 4, acc[k]);
+    }
+    for (int c2 = c + 1; c2 < nch; c2++) {
+#pragma unroll
+        for (int k = 0; k < NV; k++) {
+            const int vv = lane + 64 * k;
+            if (vv < nvec) {
+                float x[4];
+                load4<float>(headws + (long)c2 * C + vv * 4, x);
+#pragma unroll
+                for (int q = 0; q < 4; q++) acc[k][q] += x[q];
+            }
+        }
+        if (!meta[3 * c2 + 1]) break;
+    }
+    float* w = dwte + (long)v * C;
+#pragma unroll
+    for (int k = 0; k < NV; k++) {
+        const int vv = lane + 64 * k;
+        if (vv < nvec) {
+            float o[4];
+            load4<float>(w + vv * 4, o);
+#pragma unroll
+            for (int q = 0; q < 4; q++) o[q] += acc[k][q];
+            store4<float>(w + vv * 4, o);
+        }
+    }
+}
+
 // dwpe[t, :] += sum over b of dres[b*T + t, :]  (b in increasing order)
 __global__ void encoder_bwd_wpe_kernel(float* __restrict__ dwpe, const float* __restrict__ dres, int B, int T_, int C) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index over T*C
@@ -306,11 +455,34 @@ int encoder_fwd_launch(T* out, int* tok_copy, const int* tok, const T* wte, cons
     return (int)hipGetLastError();
 }
 
+size_t encoder_bwd_workspace_bytes(int BT, int C) {
+    if (BT > ENC_SORT_MAX) return 0;
+    const size_t nch = (BT + ENC_CHUNK - 1) / ENC_CHUNK;
+    return (size_t)BT * 4 + nch * 3 * 4 + 2 * nch * C * 4 + 1024;
+}
+
 int encoder_bwd_launch(float* dwte, float* dwpe, const float* dres, const int* tok, int B, int T_, int C,
-                       hipStream_t s) {
+                       void* work, hipStream_t s) {
     const int BT = B * T_;
     if (BT == 0) return 0;
-    hipLaunchKernelGGL(encoder_bwd_wte_kernel, dim3((BT + 3) / 4), dim3(256), 0, s, dwte, dres, tok, BT, C);
+    if (BT <= ENC_SORT_MAX && work != nullptr) {
+        int shift = 0;
+        while ((1 << shift) < BT) shift++;
+        const int nch = (BT + ENC_CHUNK - 1) / ENC_CHUNK;
+        char* w = (char*)work;
+        unsigned* sorted = (unsigned*)w;
+        w += ((size_t)BT * 4 + 255) / 256 * 256;
+        int* meta = (int*)w;
+        w += ((size_t)nch * 12 + 255) / 256 * 256;
+        float* headws = (float*)w;
+        float* tailws = headws + (size_t)nch * C;
+        hipLaunchKernelGGL(enc_sort_kernel, dim3(1), dim3(1024), 0, s, sorted, tok, BT, shift);
+        hipLaunchKernelGGL(enc_chunk_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, dres,
+                           sorted, BT, C, shift, nch);
+        hipLaunchKernelGGL(enc_fix_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, C, nch);
+    } else {
+        hipLaunchKernelGGL(encoder_bwd_wte_kernel, dim3((BT + 3) / 4), dim3(256), 0, s, dwte, dres, tok, BT, C);
+    }
     const long n4 = (long)T_ * C / 4;
     hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dwpe, dres, B, T_, C);
     return (int)hipGetLastError();

@@ -1,21 +1,24 @@
 // gemm.hip - MFMA matrix products with fused epilogues (gfx950).
 //
 // Every Linear layer of the step runs through this kernel (train_gpt2.cu,
-// matmul_forward_cublaslt and matmul_backward; the classifier of gpt2_forward
-// and gpt2_backward):
+// matmul_forward_cublaslt and matmul_backward with matmul_backward_bias_kernel4;
+// the tied classifier of gpt2_forward and gpt2_backward):
 //   forward  Y[BT,OC]  = X[BT,IC] W[OC,IC]^T (+ bias, + GELU or + residual)
 //   backward dX[BT,IC] = dY[BT,OC] W[OC,IC]          (overwrite; GELU' fused)
-//            dW[OC,IC] += dY[BT,OC]^T X[BT,IC]       (accumulate, fp32)
+//            dW[OC,IC] += dY[BT,OC]^T X[BT,IC]       (accumulate, fp32;
+//                                                     bias gradient fused)
 // i.e. C[m,n] = sum_k A(m,k) B(k,n) with A and B either contraction-major
 // (k contiguous) or contraction-strided.
 //
-// Design (one workgroup = 256 threads = 4 wave64s):
-//  - 128x128 output tile per workgroup, 2x2 waves of 64x64, each wave a 4x4
-//    grid of 16x16 MFMA tiles (64 fp32 accumulators per lane).
-//  - Per stage the workgroup stages a 128 x BK slab of A and of B in LDS, both
-//    stored "row x contraction" with k contiguous (BK = 64 bf16 / 32 fp32,
-//    i.e. 128 bytes per row, rows padded by 16 bytes so that the 16-byte
-//    fragment reads of 8 consecutive lanes hit distinct banks).
+// Design (one workgroup = 256 threads = 4 wave64s in a 2x2 grid):
+//  - BM x BN output tile per workgroup (256x256, 256x128, 128x256, 256x96 or
+//    128x128, chosen per shape), each wave a (BM/2)x(BN/2) grid of 16x16
+//    MFMA tiles.  The big tiles keep up to 256 fp32 accumulators per lane
+//    and run one workgroup per CU; 128x128 runs two.
+//  - Per stage the workgroup stages a BM x BK slab of A and a BN x BK slab of
+//    B in LDS, both stored "row x contraction" with k contiguous (BK = 64 bf16
+//    / 32 fp32, i.e. 128 bytes per row, rows padded by 16 bytes so that the
+//    16-byte fragment reads of 8 consecutive lanes hit distinct banks).
 //  - Global loads are 16-byte vectors.  A k-contiguous operand is copied as
 //    is; a k-strided operand is read as 4 k-rows x one 16-byte vector and
 //    transposed in registers into 4-element k-runs before the LDS store, so
@@ -31,25 +34,44 @@
 //    remapped so that each XCD walks a contiguous run of tiles, and tiles run
 //    in groups of 8 row-tiles so neighbours share operand slabs in that XCD's
 //    L2.
-//  - Weight-gradient products (K = B*T, few output tiles) split K across
-//    workgroups; each split writes fp32 partials to workspace and a second
-//    kernel adds them into dW in split order, so results are deterministic.
+//  - Products with few output tiles and a long K (weight gradients, K = B*T;
+//    the classifier's input gradient, K = Vp) split K across workgroups; each
+//    split writes fp32 partials to workspace and a second kernel combines them
+//    in split order, so results are deterministic.
+#include <algorithm>
+#include <cmath>
+
 #include "device.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
 constexpr int NTHREADS = 256;
+#ifndef GEMM_SCHED_GROUPS
+#define GEMM_SCHED_GROUPS 1
+#endif
 
-template <typename T>
-struct Cfg {
+template <typename T, int BM_, int BN_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_;
     static constexpr int BK = 128 / (int)sizeof(T);  // contraction depth per stage
     static constexpr int PAD = 16 / (int)sizeof(T);
     static constexpr int LDSK = BK + PAD;            // LDS row pitch (elements)
     static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
     static constexpr int KSTEPS = BK / 32;           // MFMA steps per stage
+    static constexpr int WM = BM / 64, WN = BN / 64; // waves, each owning a 64x64 output tile
+    static constexpr int NT = 64 * WM * WN;          // threads per workgroup
+    static constexpr int TM = 4, TN = 4;             // 16x16 MFMA tiles per wave
+    static constexpr int OCC = NT == 256 ? 2 : 1;    // workgroups per CU
+    static constexpr int DEPTH = NT <= 512 ? 2 : 1;  // slab prefetch distance
+    static constexpr int FBUF = NT <= 512 ? 2 : 1;   // fragment buffers
+};
+
+// Per-thread register count for staging an R x BK slab (both layouts).
+template <int R, int NT> struct StageRegs {
+    static constexpr int KM = (R * 8 + NT - 1) / NT;            // k-major: R*8 vectors
+    static constexpr int KS_BLOCKS = (2 * R + NT - 1) / NT;     // k-strided: 2R blocks of 4
+    static constexpr int N = (KM > 4 * KS_BLOCKS) ? KM : 4 * KS_BLOCKS;
 };
 
 enum { EPI_SPLIT = 100 };
@@ -61,60 +83,102 @@ struct Args {
     const void* bias;
     const void* aux_in; void* aux_out; long ldaux;
     float* ws;
+    float* dbias;   // GEMM_ACCUM only: dbias[m] += alpha * sum_k A(m,k) (or split partials in wsb)
+    float* wsb;
     int M, N, K;
     int kps;  // k-tiles per split
     float alpha;
 };
 
-// Load this thread's share of a 128-row x BK slab of X(r, k) into registers.
-template <typename T, bool KMAJ>
-DEV void slab_load(uint4 (&r)[4], const T* __restrict__ p, long ld, int r0, int R, int k0, int K, int tid) {
-    using C = Cfg<T>;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    if constexpr (KMAJ) {
-        // 8 vectors per row; thread covers rows tid/8 + 32i, vector tid%8
-        const int kk = k0 + (tid & 7) * C::VEC;
+// Staging of an R-row x BK slab of X(r, k) with buffer loads.  Each operand
+// tile gets a buffer resource whose base is the slab's first element and
+// whose byte range ends at the end of the operand's valid data, so rows past
+// the matrix (and, for a k-strided operand, contraction rows past K) read as
+// zeros in hardware.  Per-lane byte offsets are loop invariant; moving to the
+// next slab only changes the (scalar) resource.  The one case the range cannot
+// cover -- contraction indices past K inside a row of a k-contiguous operand,
+// when K is not a multiple of BK -- is sent to an out-of-range offset.
+template <typename T, int R, bool KMAJ, int NT>
+struct SlabAddr {
+    uint32_t off[StageRegs<R, NT>::N];   // per-lane byte offsets within a slab
+    int krel[KMAJ ? StageRegs<R, NT>::N : 1];
+    DEV void init(long ld, int tid) {
+        constexpr int VEC = 16 / (int)sizeof(T), BK = 128 / (int)sizeof(T);
+        if constexpr (KMAJ) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int gr = r0 + (tid >> 3) + 32 * i;
-            r[i] = (gr < R && kk < K) ? ld16(p + (long)gr * ld + kk) : z;
+            for (int i = 0; i < StageRegs<R, NT>::KM; i++) {
+                const int idx = tid + NT * i;
+                krel[i] = (idx & 7) * VEC;
+                off[i] = (uint32_t)(((long)(idx >> 3) * ld + krel[i]) * (long)sizeof(T));
+            }
+        } else {
+            constexpr int KQ = BK / 4;
+#pragma unroll
+            for (int bl = 0; bl < StageRegs<R, NT>::KS_BLOCKS; bl++) {
+                const int idx = tid + NT * bl;
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    off[4 * bl + i] = (uint32_t)(((long)(4 * (idx % KQ) + i) * ld + (idx / KQ) * VEC) * (long)sizeof(T));
+            }
+        }
+    }
+};
+
+// p: operand base; (r0, k0): slab origin; Rmax rows, K contraction length.
+template <typename T, int R, bool KMAJ, int NT>
+DEV void slab_load(uint4* r, const SlabAddr<T, R, KMAJ, NT>& ad, const T* __restrict__ p, long ld, int r0, int Rmax,
+                   int k0, int K) {
+    if constexpr (KMAJ) {
+        const T* base = p + (long)r0 * ld + k0;
+        const long end = (long)Rmax * ld;  // elements
+        const uint32_t bytes = (uint32_t)max(0L, (end - ((long)r0 * ld + k0)) * (long)sizeof(T));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+        const int klim = K - k0;
+#pragma unroll
+        for (int i = 0; i < StageRegs<R, NT>::KM; i++) r[i] = buf_ld16(rs, ad.krel[i] < klim ? ad.off[i] : kBufOOB);
+    } else {
+        const T* base = p + (long)k0 * ld + r0;
+        const long end = (long)K * ld;
+        const uint32_t bytes = (uint32_t)max(0L, (end - ((long)k0 * ld + r0)) * (long)sizeof(T));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+        for (int i = 0; i < 4 * StageRegs<R, NT>::KS_BLOCKS; i++) r[i] = buf_ld16(rs, ad.off[i]);
+    }
+}
+
+template <typename T, int R, bool KMAJ, int NT>
+DEV void slab_store(const uint4* r, T* __restrict__ s, int tid) {
+    constexpr int VEC = 16 / (int)sizeof(T), BK = 128 / (int)sizeof(T), LDSK = BK + 16 / (int)sizeof(T);
+    if constexpr (KMAJ) {
+#pragma unroll
+        for (int i = 0; i < StageRegs<R, NT>::KM; i++) {
+            const int idx = tid + NT * i;
+            if ((R * 8) % NT == 0 || idx < R * 8) st16(s + (idx >> 3) * LDSK + (idx & 7) * VEC, r[i]);
         }
     } else {
-        // 4 consecutive k-rows x one vector of VEC r-values
-        constexpr int KQ = C::BK / 4;
-        const int kq = tid % KQ, rg = tid / KQ;
-        const int gr = r0 + rg * C::VEC;
+        constexpr int KQ = BK / 4;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int kk = k0 + 4 * kq + i;
-            r[i] = (kk < K && gr < R) ? ld16(p + (long)kk * ld + gr) : z;
+        for (int bl = 0; bl < StageRegs<R, NT>::KS_BLOCKS; bl++) {
+            const int idx = tid + NT * bl;
+            if ((2 * R) % NT == 0 || idx < 2 * R) {
+                const int kq = idx % KQ, rg = idx / KQ;
+                const uint4 t[4] = {r[4 * bl], r[4 * bl + 1], r[4 * bl + 2], r[4 * bl + 3]};
+                store_t4<T>(s + rg * VEC * LDSK + 4 * kq, LDSK, t);
+            }
         }
     }
 }
 
-template <typename T, bool KMAJ>
-DEV void slab_store(const uint4 (&r)[4], T* __restrict__ s, int tid) {
-    using C = Cfg<T>;
-    if constexpr (KMAJ) {
-        const int col = (tid & 7) * C::VEC;
-#pragma unroll
-        for (int i = 0; i < 4; i++) st16(s + ((tid >> 3) + 32 * i) * C::LDSK + col, r[i]);
-    } else {
-        constexpr int KQ = C::BK / 4;
-        const int kq = tid % KQ, rg = tid / KQ;
-        store_t4<T>(s + rg * C::VEC * C::LDSK + 4 * kq, C::LDSK, r);
-    }
-}
-
-template <typename T, bool AK, bool BKM, int EPI, typename OutT>
-__global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const Args g) {
-    using C = Cfg<T>;
-    __shared__ __attribute__((aligned(16))) T sA[2][BM * C::LDSK];
-    __shared__ __attribute__((aligned(16))) T sB[2][BN * C::LDSK];
+template <typename T, int BM, int BN, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
+__global__ __launch_bounds__((Tile<T, BM, BN>::NT), (Tile<T, BM, BN>::OCC)) void gemm_kernel(const Args g) {
+    using TL = Tile<T, BM, BN>;
+    constexpr int LDSK = TL::LDSK, BK = TL::BK, TM = TL::TM, TN = TL::TN, NT = TL::NT;
+    __shared__ __attribute__((aligned(16))) T sA[2][BM * LDSK];
+    __shared__ __attribute__((aligned(16))) T sB[2][BN * LDSK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % TL::WM, wn = wave / TL::WM;
     const int l16 = lane & 15, g4 = lane >> 4;
 
     // ---- tile order: XCD-contiguous runs, then groups of 8 row-tiles
@@ -132,64 +196,156 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const Args g) {
     const int tn = (b % in_group) / gsz;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const int ktiles = (g.K + C::BK - 1) / C::BK;
+    const int ktiles = (g.K + BK - 1) / BK;
     const int kt0 = blockIdx.y * g.kps;
     const int kt1 = min(kt0 + g.kps, ktiles);
 
     const T* __restrict__ A = (const T*)g.A;
     const T* __restrict__ B = (const T*)g.B;
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[4], rb[4];
+    // fused bias gradient (weight-gradient products): the A slab holds dY^T, so
+    // its row sums over k are the column sums of dY.  Only the first column
+    // tile of each row tile does it.
+    const bool do_bias = BIAS && tn == 0;
+    constexpr int TPR = NT / BM;        // threads per slab row (2 or 4)
+    constexpr int EPT = BK / TPR;       // elements each sums per stage
+    float bsum = 0.f;
+
+    // Operand slabs are prefetched into registers DEPTH stages ahead of their
+    // use: with DEPTH = 2 (two workgroups per CU) the slab for stage kt+2 is
+    // requested at the start of stage kt and written to LDS at the end of
+    // stage kt+1, so a global load has two stages of MFMA work to arrive; the
+    // big tiles (one workgroup per CU, accumulators filling the register file)
+    // prefetch one stage ahead.
+    constexpr int DEPTH = TL::DEPTH;
+    constexpr int NRA = StageRegs<BM, NT>::N, NRB = StageRegs<BN, NT>::N;
+    uint4 ra0[NRA], rb0[NRB], ra1[DEPTH == 2 ? NRA : 1], rb1[DEPTH == 2 ? NRB : 1];
+    SlabAddr<T, BM, AK, NT> adA;
+    SlabAddr<T, BN, BKM, NT> adB;
+    adA.init(g.lda, tid);
+    adB.init(g.ldb, tid);
     if (kt0 < kt1) {
-        slab_load<T, AK>(ra, A, g.lda, m0, g.M, kt0 * C::BK, g.K, tid);
-        slab_load<T, BKM>(rb, B, g.ldb, n0, g.N, kt0 * C::BK, g.K, tid);
-        slab_store<T, AK>(ra, sA[0], tid);
-        slab_store<T, BKM>(rb, sB[0], tid);
+        slab_load<T, BM, AK, NT>(ra0, adA, A, g.lda, m0, g.M, kt0 * BK, g.K);
+        slab_load<T, BN, BKM, NT>(rb0, adB, B, g.ldb, n0, g.N, kt0 * BK, g.K);
+        slab_store<T, BM, AK, NT>(ra0, sA[0], tid);
+        slab_store<T, BN, BKM, NT>(rb0, sB[0], tid);
+        if constexpr (DEPTH == 2) {
+            const int k1 = min(kt0 + 1, kt1 - 1);
+            slab_load<T, BM, AK, NT>(ra1, adA, A, g.lda, m0, g.M, k1 * BK, g.K);
+            slab_load<T, BN, BKM, NT>(rb1, adB, B, g.ldb, n0, g.N, k1 * BK, g.K);
+        }
     }
     __syncthreads();
 
-    for (int kt = kt0; kt < kt1; kt++) {
+    // One stage: the loop body has no branches, fragments of step ks+1 are
+    // read while step ks runs, and the instruction groups are interleaved
+    // explicitly: global loads first, then MFMAs alternating with the next
+    // step's LDS reads, then MFMAs alternating with the LDS writes of the
+    // prefetched slab.
+    constexpr int NF = TM + TN;                                // fragment reads per step
+    constexpr int NMMA = TM * TN * (sizeof(T) == 2 ? 1 : 8);  // MFMAs per step
+    auto stage = [&](int kt, uint4* lda_, uint4* ldb_, const uint4* sta_, const uint4* stb_) {
         const int cur = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;
-        if (more) {
-            slab_load<T, AK>(ra, A, g.lda, m0, g.M, (kt + 1) * C::BK, g.K, tid);
-            slab_load<T, BKM>(rb, B, g.ldb, n0, g.N, (kt + 1) * C::BK, g.K, tid);
-        }
+        const int nk = min(kt + DEPTH, kt1 - 1);
+        slab_load<T, BM, AK, NT>(lda_, adA, A, g.lda, m0, g.M, nk * BK, g.K);
+        slab_load<T, BN, BKM, NT>(ldb_, adB, B, g.ldb, n0, g.N, nk * BK, g.K);
         const T* a_s = sA[cur];
         const T* b_s = sB[cur];
+        Frag<T> fa[TL::FBUF][TM], fb[TL::FBUF][TN];
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ks++) {
-            Frag<T> fa[4], fb[4];
-            const int kofs = ks * 32 + 8 * g4;
+        for (int t = 0; t < TN; t++) frag_ld(fb[0][t], b_s + (wn * 64 + 16 * t + l16) * LDSK + 8 * g4);
 #pragma unroll
-            for (int t = 0; t < 4; t++) frag_ld(fb[t], b_s + (wn * 64 + 16 * t + l16) * C::LDSK + kofs);
+        for (int t = 0; t < TM; t++) frag_ld(fa[0][t], a_s + (wm * 64 + 16 * t + l16) * LDSK + 8 * g4);
 #pragma unroll
-            for (int t = 0; t < 4; t++) frag_ld(fa[t], a_s + (wm * 64 + 16 * t + l16) * C::LDSK + kofs);
+        for (int ks = 0; ks < TL::KSTEPS; ks++) {
+            const int c = TL::FBUF == 2 ? (ks & 1) : 0;
+            if (TL::FBUF == 2 && ks + 1 < TL::KSTEPS) {
+                const int kofs = (ks + 1) * 32 + 8 * g4;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+                for (int t = 0; t < TN; t++) frag_ld(fb[c ^ 1][t], b_s + (wn * 64 + 16 * t + l16) * LDSK + kofs);
 #pragma unroll
-                for (int j = 0; j < 4; j++) mma(acc[i][j], fb[j], fa[i]);
+                for (int t = 0; t < TM; t++) frag_ld(fa[c ^ 1][t], a_s + (wm * 64 + 16 * t + l16) * LDSK + kofs);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) mma(acc[i][j], fb[c][j], fa[c][i]);
+            if (TL::FBUF == 1 && ks + 1 < TL::KSTEPS) {
+                const int kofs = (ks + 1) * 32 + 8 * g4;
+#pragma unroll
+                for (int t = 0; t < TN; t++) frag_ld(fb[0][t], b_s + (wn * 64 + 16 * t + l16) * LDSK + kofs);
+#pragma unroll
+                for (int t = 0; t < TM; t++) frag_ld(fa[0][t], a_s + (wm * 64 + 16 * t + l16) * LDSK + kofs);
+            }
         }
-        if (more) {
-            slab_store<T, AK>(ra, sA[cur ^ 1], tid);
-            slab_store<T, BKM>(rb, sB[cur ^ 1], tid);
+        if constexpr (BIAS) {
+            // (every workgroup sums, only the first column tile keeps the result:
+            // a uniform branch here would split the scheduling region)
+            const T* rowp = a_s + (tid / TPR) * LDSK + (tid % TPR) * EPT;
+#pragma unroll
+            for (int q = 0; q < EPT / TL::VEC; q++) {
+                float f[TL::VEC];
+                unpack16<T>(ld16(rowp + q * TL::VEC), f);
+#pragma unroll
+                for (int e = 0; e < TL::VEC; e++) bsum += f[e];
+            }
         }
+        slab_store<T, BM, AK, NT>(sta_, sA[cur ^ 1], tid);
+        slab_store<T, BN, BKM, NT>(stb_, sB[cur ^ 1], tid);
+#if GEMM_SCHED_GROUPS
+        __builtin_amdgcn_sched_group_barrier(0x020, NRA + NRB, 0);  // global loads
+        __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);         // step-0 fragments
+#pragma unroll
+        for (int ks = 0; ks < TL::KSTEPS; ks++) {
+            if (ks + 1 < TL::KSTEPS) {
+#pragma unroll
+                for (int q = 0; q < NF; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, NMMA / NF > 0 ? NMMA / NF : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, NMMA / 16 > 0 ? NMMA / 16 : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+                }
+            }
+        }
+#endif
         __syncthreads();
+    };
+    if constexpr (DEPTH == 2) {
+        for (int kt = kt0; kt < kt1; kt += 2) {
+            stage(kt, ra0, rb0, ra1, rb1);
+            if (kt + 1 < kt1) stage(kt + 1, ra1, rb1, ra0, rb0);
+        }
+    } else {
+        for (int kt = kt0; kt < kt1; kt++) stage(kt, ra0, rb0, ra0, rb0);
+    }
+
+    if (do_bias) {
+        if constexpr (TPR >= 2) bsum += __shfl_xor(bsum, 1, 64);
+        if constexpr (TPR >= 4) bsum += __shfl_xor(bsum, 2, 64);
+        const int m = m0 + tid / TPR;
+        if ((tid % TPR) == 0 && m < g.M) {
+            if constexpr (EPI == EPI_SPLIT) g.wsb[(size_t)blockIdx.y * g.M + m] = g.alpha * bsum;
+            else g.dbias[m] += g.alpha * bsum;
+        }
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3]
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < TM; i++) {
         const int m = m0 + wm * 64 + 16 * i + l16;
         if (m >= g.M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < TN; j++) {
             const int n = n0 + wn * 64 + 16 * j + 4 * g4;
             if (n >= g.N) continue;
             float v[4];
@@ -238,106 +394,192 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const Args g) {
     }
 }
 
-// C[i] += sum_z ws[z*MN + i], z in increasing order (n4 float4 groups)
-__global__ void splitk_reduce_kernel(float* __restrict__ C, const float* __restrict__ ws, size_t MN, int splits) {
+// C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0)
+template <typename OutT, bool ACCUM>
+__global__ void splitk_reduce_kernel(OutT* __restrict__ C, const float* __restrict__ ws, size_t MN, int splits) {
     size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (i >= MN) return;
-    float4 s = *reinterpret_cast<const float4*>(ws + i);
+    float s[4];
+    load4<float>(ws + i, s);
     for (int z = 1; z < splits; z++) {
-        float4 w = *reinterpret_cast<const float4*>(ws + (size_t)z * MN + i);
-        s.x += w.x; s.y += w.y; s.z += w.z; s.w += w.w;
+        float w[4];
+        load4<float>(ws + (size_t)z * MN + i, w);
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[r] += w[r];
     }
-    float4 c = *reinterpret_cast<float4*>(C + i);
-    c.x += s.x; c.y += s.y; c.z += s.z; c.w += s.w;
-    *reinterpret_cast<float4*>(C + i) = c;
+    if constexpr (ACCUM) {
+        float c[4];
+        load4<float>((const float*)C + i, c);
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[r] += c[r];
+    }
+    store4<OutT>(C + i, s);
+}
+
+// db[m] += sum_z wsb[z*M + m], z in increasing order
+__global__ void splitk_bias_reduce_kernel(float* __restrict__ db, const float* __restrict__ wsb, int M, int splits) {
+    const int m = blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M) return;
+    float s = 0.f;
+    for (int z = 0; z < splits; z++) s += wsb[(size_t)z * M + m];
+    db[m] += s;
+}
+
+// ---------------------------------------------------------------- dispatch --
+struct Choice {
+    int bm, bn, splits;
+};
+
+// Tile configurations per element type, with their measured relative per-CU
+// throughput (MI355X, bf16, K = 768 products): 256x256 ~754 TFLOP/s,
+// 256x128 / 128x256 ~700, 128x128 (two per CU) ~665.
+struct TileCfg {
+    int bm, bn, occ;
+    double speed;
+};
+const TileCfg kCfgBf16[] = {{256, 256, 1, 1.00}, {256, 128, 1, 0.93}, {128, 256, 1, 0.93},
+                            {128, 128, 2, 0.88}};
+const TileCfg kCfgF32[] = {{128, 128, 2, 1.0}};
+
+// Pick the tile and the K split minimising a simple cost: waves of
+// workgroups over the CUs times the work per workgroup, plus the split
+// partials' extra HBM traffic.  Split-K only for plain-store and accumulate
+// epilogues (their epilogue moves into the reduction).
+Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
+    const bool bf16 = elem_bytes == 2;
+    const TileCfg* cfgs = bf16 ? kCfgBf16 : kCfgF32;
+    const int ncfg = bf16 ? 4 : 1;
+    const int bk = 128 / elem_bytes;
+    const int ktiles = (d.K + bk - 1) / bk;
+    const bool can_split = d.split_ok && (d.epi == GEMM_ACCUM || d.epi == GEMM_STORE) && (d.N % 4 == 0) &&
+                           d.ldc == d.N;
+    const double flop_rate = 2.5e15 / 256.0;  // per CU, dense bf16
+    const double hbm = 5.0e12;                // bytes/s usable
+    Choice best = {cfgs[0].bm, cfgs[0].bn, 1};
+    double best_cost = 1e300;
+    for (int c = 0; c < ncfg; c++) {
+        const TileCfg& t = cfgs[c];
+#ifdef GEMM_ONLY_TILE_BM
+        if (bf16 && (t.bm != GEMM_ONLY_TILE_BM || t.bn != GEMM_ONLY_TILE_BN)) continue;
+#endif
+        const long tiles = (long)((d.M + t.bm - 1) / t.bm) * ((d.N + t.bn - 1) / t.bn);
+        const int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
+        for (int s = 1; s <= max_split; s++) {
+            const int kps = (ktiles + s - 1) / s;
+            const int sp = (ktiles + kps - 1) / kps;
+            if (sp != s) continue;
+            const long units = tiles * sp;
+            const long slots = (long)num_cus * t.occ;
+            // waves of workgroups; with two per CU the last partial wave
+            // overlaps the previous one, so it is counted in half steps
+            double rounds = t.occ == 1 ? (double)((units + slots - 1) / slots)
+                                       : std::max(1.0, std::ceil(2.0 * units / slots) / 2.0);
+            double cost = rounds * (2.0 * t.bm * t.bn * (double)kps * bk) / (flop_rate * t.speed / t.occ);
+            if (sp > 1) cost += (double)(sp + 1) * d.M * d.N * 4.0 / hbm;
+            if (cost < best_cost * 0.999) {
+                best_cost = cost;
+                best = {t.bm, t.bn, sp};
+            }
+        }
+    }
+    return best;
+}
+
+template <typename T, int BM, int BN, bool AK, bool BKM, int EPI, typename OutT, bool BIAS = false>
+void launch_t(const Args& a, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, AK, BKM, EPI, OutT, BIAS>), grid, dim3(Tile<T, BM, BN>::NT), 0, s, a);
+}
+
+// Instantiated (layout, epilogue) pairs: forward products (A and B
+// k-contiguous), input-gradient products (A k-contiguous, B k-strided) and
+// weight-gradient products (both k-strided).
+template <typename T, int BM, int BN>
+int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int epi, hipStream_t s) {
+    const int lay = (d.a_kmajor ? 2 : 0) | (d.b_kmajor ? 1 : 0);
+    if (lay == 3) {
+        switch (epi) {
+            case GEMM_STORE: launch_t<T, BM, BN, true, true, GEMM_STORE, T>(a, grid, s); return 0;
+            case GEMM_BIAS: launch_t<T, BM, BN, true, true, GEMM_BIAS, T>(a, grid, s); return 0;
+            case GEMM_BIAS_GELU: launch_t<T, BM, BN, true, true, GEMM_BIAS_GELU, T>(a, grid, s); return 0;
+            case GEMM_BIAS_RESID: launch_t<T, BM, BN, true, true, GEMM_BIAS_RESID, T>(a, grid, s); return 0;
+        }
+    } else if (lay == 2) {
+        switch (epi) {
+            case GEMM_STORE: launch_t<T, BM, BN, true, false, GEMM_STORE, T>(a, grid, s); return 0;
+            case GEMM_GELU_BWD: launch_t<T, BM, BN, true, false, GEMM_GELU_BWD, T>(a, grid, s); return 0;
+            case EPI_SPLIT: launch_t<T, BM, BN, true, false, EPI_SPLIT, float>(a, grid, s); return 0;
+        }
+    } else if (lay == 0) {
+        const bool bias = a.dbias != nullptr;
+        switch (epi) {
+            case GEMM_ACCUM:
+                if (bias) launch_t<T, BM, BN, false, false, GEMM_ACCUM, float, true>(a, grid, s);
+                else launch_t<T, BM, BN, false, false, GEMM_ACCUM, float, false>(a, grid, s);
+                return 0;
+            case EPI_SPLIT:
+                if (bias) launch_t<T, BM, BN, false, false, EPI_SPLIT, float, true>(a, grid, s);
+                else launch_t<T, BM, BN, false, false, EPI_SPLIT, float, false>(a, grid, s);
+                return 0;
+        }
+    }
+    return (int)hipErrorInvalidValue;
 }
 
 template <typename T>
-__global__ void bias_partial_kernel(float* __restrict__ partial, const T* __restrict__ dY, int M, int N, long ldy) {
-    const int n = blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= N) return;
-    const int r0 = blockIdx.y * 256, r1 = min(r0 + 256, M);
-    float s = 0.f;
-    for (int m = r0; m < r1; m++) s += to_f<T>(dY[(long)m * ldy + n]);
-    partial[(size_t)blockIdx.y * N + n] = s;
-}
-
-__global__ void bias_finish_kernel(float* __restrict__ db, const float* __restrict__ partial, int N, int chunks) {
-    const int n = blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= N) return;
-    float s = 0.f;
-    for (int c = 0; c < chunks; c++) s += partial[(size_t)c * N + n];
-    db[n] += s;
-}
-
-int split_count(const GemmDesc& d, int elem_bytes, int num_cus) {
-    if (d.epi != GEMM_ACCUM) return 1;
-    const int bk = 128 / elem_bytes;
-    const long tiles = (long)((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
-    const int ktiles = (d.K + bk - 1) / bk;
-    const long want = 2L * num_cus;
-    if (tiles >= want) return 1;
-    int s = (int)((want + tiles - 1) / tiles);
-    s = min(s, max(1, ktiles / 4));
-    s = min(s, 32);
-    if (s <= 1) return 1;
-    const int kps = (ktiles + s - 1) / s;
-    return (ktiles + kps - 1) / kps;
-}
-
-template <typename T, bool AK, bool BKM, int EPI, typename OutT>
-void launch_t(const Args& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<T, AK, BKM, EPI, OutT>), grid, dim3(NTHREADS), 0, s, a);
-}
-
-template <typename T, int EPI, typename OutT>
-void launch_layout(const GemmDesc& d, const Args& a, dim3 grid, hipStream_t s) {
-    if (d.a_kmajor && d.b_kmajor) launch_t<T, true, true, EPI, OutT>(a, grid, s);
-    else if (d.a_kmajor && !d.b_kmajor) launch_t<T, true, false, EPI, OutT>(a, grid, s);
-    else if (!d.a_kmajor && !d.b_kmajor) launch_t<T, false, false, EPI, OutT>(a, grid, s);
-    else launch_t<T, false, true, EPI, OutT>(a, grid, s);
+int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, int epi, hipStream_t s) {
+    if constexpr (sizeof(T) == 2) {
+        if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256>(d, a, grid, epi, s);
+        if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128>(d, a, grid, epi, s);
+        if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256>(d, a, grid, epi, s);
+    }
+    if (ch.bm == 128 && ch.bn == 128) return launch_epi<T, 128, 128>(d, a, grid, epi, s);
+    return (int)hipErrorInvalidValue;
 }
 
 template <typename T>
 int gemm_launch_t(const GemmDesc& d, float* ws, size_t ws_bytes, int num_cus, hipStream_t s) {
-    constexpr int BK = Cfg<T>::BK;
-    const int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
+    constexpr int BK = 128 / (int)sizeof(T);
+    const Choice ch = choose(d, (int)sizeof(T), num_cus);
+    const int tiles = ((d.M + ch.bm - 1) / ch.bm) * ((d.N + ch.bn - 1) / ch.bn);
     const int ktiles = (d.K + BK - 1) / BK;
-    const int splits = split_count(d, (int)sizeof(T), num_cus);
     Args a;
     a.A = d.A; a.lda = d.lda; a.B = d.B; a.ldb = d.ldb; a.C = d.C; a.ldc = d.ldc;
     a.bias = d.bias; a.aux_in = d.aux_in; a.aux_out = d.aux_out; a.ldaux = d.ldaux;
     a.ws = ws; a.M = d.M; a.N = d.N; a.K = d.K; a.alpha = d.alpha;
+    a.dbias = d.epi == GEMM_ACCUM ? d.dbias : nullptr;
+    a.wsb = nullptr;
     if (tiles == 0) return 0;
-    if (splits > 1) {
-        const size_t need = (size_t)splits * d.M * d.N * sizeof(float);
-        if (ws == nullptr || ws_bytes < need || d.ldc != d.N) return (int)hipErrorInvalidValue;
-        a.kps = (ktiles + splits - 1) / splits;
-        launch_layout<T, EPI_SPLIT, float>(d, a, dim3(tiles, splits), s);
+    if (ch.splits > 1) {
         const size_t MN = (size_t)d.M * d.N;
+        const size_t need = (size_t)ch.splits * (MN + d.M) * sizeof(float);
+        if (ws == nullptr || ws_bytes < need || d.ldc != d.N) return (int)hipErrorInvalidValue;
+        a.kps = (ktiles + ch.splits - 1) / ch.splits;
+        if (a.dbias) a.wsb = ws + (size_t)ch.splits * MN;
+        int e = launch_tile<T>(d, a, ch, dim3(tiles, ch.splits), EPI_SPLIT, s);
+        if (e) return e;
         const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, (float*)d.C, ws, MN, splits);
+        if (d.epi == GEMM_ACCUM)
+            hipLaunchKernelGGL((splitk_reduce_kernel<float, true>), dim3(blocks), dim3(256), 0, s, (float*)d.C, ws, MN,
+                               ch.splits);
+        else
+            hipLaunchKernelGGL((splitk_reduce_kernel<T, false>), dim3(blocks), dim3(256), 0, s, (T*)d.C, ws, MN,
+                               ch.splits);
+        if (a.dbias)
+            hipLaunchKernelGGL(splitk_bias_reduce_kernel, dim3((d.M + 255) / 256), dim3(256), 0, s, d.dbias, a.wsb,
+                               d.M, ch.splits);
         return (int)hipGetLastError();
     }
     a.kps = ktiles;
-    const dim3 grid(tiles, 1);
-    switch (d.epi) {
-        case GEMM_STORE: launch_layout<T, GEMM_STORE, T>(d, a, grid, s); break;
-        case GEMM_BIAS: launch_layout<T, GEMM_BIAS, T>(d, a, grid, s); break;
-        case GEMM_BIAS_GELU: launch_layout<T, GEMM_BIAS_GELU, T>(d, a, grid, s); break;
-        case GEMM_BIAS_RESID: launch_layout<T, GEMM_BIAS_RESID, T>(d, a, grid, s); break;
-        case GEMM_GELU_BWD: launch_layout<T, GEMM_GELU_BWD, T>(d, a, grid, s); break;
-        case GEMM_ACCUM: launch_layout<T, GEMM_ACCUM, float>(d, a, grid, s); break;
-        default: return (int)hipErrorInvalidValue;
-    }
+    int e = launch_tile<T>(d, a, ch, dim3(tiles, 1), d.epi, s);
+    if (e) return e;
     return (int)hipGetLastError();
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(const GemmDesc& d, int elem_bytes, int num_cus) {
-    const int s = split_count(d, elem_bytes, num_cus);
-    return s > 1 ? (size_t)s * d.M * d.N * sizeof(float) : 0;
+    const Choice ch = choose(d, elem_bytes, num_cus);
+    return ch.splits > 1 ? (size_t)ch.splits * ((size_t)d.M * d.N + d.M) * sizeof(float) : 0;
 }
 
 int gemm_launch(const GemmDesc& d, int elem_bytes, float* ws, size_t ws_bytes, int num_cus, hipStream_t s) {
@@ -345,18 +587,3 @@ int gemm_launch(const GemmDesc& d, int elem_bytes, float* ws, size_t ws_bytes, i
     if (elem_bytes == 4) return gemm_launch_t<float>(d, ws, ws_bytes, num_cus, s);
     return (int)hipErrorInvalidValue;
 }
-
-size_t bias_grad_workspace_bytes(int M, int N) {
-    return (size_t)((M + 255) / 256) * N * sizeof(float);
-}
-
-template <typename T>
-int bias_grad_launch(float* db, const T* dY, int M, int N, long ldy, float* partial, hipStream_t s) {
-    const int chunks = (M + 255) / 256;
-    if (chunks == 0 || N == 0) return 0;
-    hipLaunchKernelGGL(bias_partial_kernel<T>, dim3((N + 255) / 256, chunks), dim3(256), 0, s, partial, dY, M, N, ldy);
-    hipLaunchKernelGGL(bias_finish_kernel, dim3((N + 255) / 256), dim3(256), 0, s, db, partial, N, chunks);
-    return (int)hipGetLastError();
-}
-template int bias_grad_launch<float>(float*, const float*, int, int, long, float*, hipStream_t);
-template int bias_grad_launch<bf16_t>(float*, const bf16_t*, int, int, long, float*, hipStream_t);

@@ -75,9 +75,16 @@ int check_config(const gpt2_config* cfg, int precision, int B, int T) {
     return GPT2_OK;
 }
 
-size_t dw_workspace(size_t M, size_t N, size_t K, int esz) {
+// split-K workspace of dW[OC,IC] += dY^T X (M=OC, N=IC, K=BT) and of
+// dX[BT,IC] = dY W (M=BT, N=IC, K=OC)
+size_t dw_workspace(size_t OC, size_t IC, size_t BT, int esz) {
     GemmDesc d = {};
-    d.M = (int)M; d.N = (int)N; d.K = (int)K; d.epi = GEMM_ACCUM;
+    d.M = (int)OC; d.N = (int)IC; d.K = (int)BT; d.ldc = (long)IC; d.epi = GEMM_ACCUM; d.split_ok = 1;
+    return gemm_workspace_bytes(d, esz, kPlanCUs);
+}
+size_t dx_workspace(size_t BT, size_t IC, size_t OC, int esz, int epi) {
+    GemmDesc d = {};
+    d.M = (int)BT; d.N = (int)IC; d.K = (int)OC; d.ldc = (long)IC; d.epi = epi; d.split_ok = 1;
     return gemm_workspace_bytes(d, esz, kPlanCUs);
 }
 
@@ -129,8 +136,13 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     w = std::max(w, dw_workspace(C, C, BT, p.esz));
     w = std::max(w, dw_workspace(4 * C, C, BT, p.esz));
     w = std::max(w, dw_workspace(C, 4 * C, BT, p.esz));
+    w = std::max(w, dx_workspace(BT, C, p.Vp, p.esz, GEMM_STORE));
+    w = std::max(w, dx_workspace(BT, 4 * C, C, p.esz, GEMM_GELU_BWD));
+    w = std::max(w, dx_workspace(BT, C, 4 * C, p.esz, GEMM_STORE));
+    w = std::max(w, dx_workspace(BT, C, C, p.esz, GEMM_STORE));
+    w = std::max(w, dx_workspace(BT, C, 3 * C, p.esz, GEMM_STORE));
     w = std::max(w, layernorm_bwd_workspace_bytes((int)BT, (int)C));
-    w = std::max(w, bias_grad_workspace_bytes((int)BT, (int)(4 * C)));
+    w = std::max(w, encoder_bwd_workspace_bytes((int)BT, (int)C));
     p.flag = 0;
     p.work = kAlign;
     p.work_bytes = align_up(w);
@@ -184,15 +196,18 @@ GemmDesc dx_desc(int BT, int IC, int OC, const void* dY, const void* W, void* dX
     d.B = W; d.ldb = IC; d.b_kmajor = 0;
     d.C = dX; d.ldc = IC; d.epi = epi; d.alpha = alpha;
     d.aux_in = aux_in; d.ldaux = IC;
+    d.split_ok = 1;
     return d;
 }
-// dW[OC, IC] += alpha * dY[BT, OC]^T X[BT, IC]
-GemmDesc dw_desc(int BT, int IC, int OC, const void* dY, const void* X, float* dW, float alpha) {
+// dW[OC, IC] += alpha * dY[BT, OC]^T X[BT, IC]; db[OC] += alpha * column sums of dY (db may be NULL)
+GemmDesc dw_desc(int BT, int IC, int OC, const void* dY, const void* X, float* dW, float alpha, float* db) {
     GemmDesc d = {};
     d.M = OC; d.N = IC; d.K = BT;
     d.A = dY; d.lda = OC; d.a_kmajor = 0;
     d.B = X; d.ldb = IC; d.b_kmajor = 0;
     d.C = dW; d.ldc = IC; d.epi = GEMM_ACCUM; d.alpha = alpha;
+    d.dbias = db;
+    d.split_ok = 1;
     return d;
 }
 
@@ -266,7 +281,7 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     float* work = c->work();
     // classifier (tied weights): dlnf = alpha * dlogits wte; dwte += alpha * dlogits^T lnf
     TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s));
-    TRY(gemm(c, dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha), s));
+    TRY(gemm(c, dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr), s));
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
     TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
                                 c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s));
@@ -281,31 +296,27 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
         const T* fchg = c->act_l<T>(p.fchg, p.s_bt4c, l);
         // fcproj (+ GELU backward fused into its input-gradient product)
         TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_lp, prm<T>(c, 12, l, 4 * CC), dbt4c, GEMM_GELU_BWD, fch, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, 4 * C, C, dres_lp, fchg, grd(c, 12, l, 4 * CC), 1.0f), s));
-        TRY(bias_grad_launch<T>(grd(c, 13, l, C), dres_lp, BT, C, C, work, s));
+        TRY(gemm(c, dw_desc(BT, 4 * C, C, dres_lp, fchg, grd(c, 12, l, 4 * CC), 1.0f, grd(c, 13, l, C)), s));
         // fc
         TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c, prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, C, 4 * C, dbt4c, ln2, grd(c, 10, l, 4 * CC), 1.0f), s));
-        TRY(bias_grad_launch<T>(grd(c, 11, l, 4 * C), dbt4c, BT, 4 * C, 4 * C, work, s));
+        TRY(gemm(c, dw_desc(BT, C, 4 * C, dbt4c, ln2, grd(c, 10, l, 4 * CC), 1.0f, grd(c, 11, l, 4 * C)), s));
         TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
                                     prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
                                     c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s));
         // attproj
         TRY(gemm(c, dx_desc(BT, C, C, dres_lp, prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, C, C, dres_lp, atty, grd(c, 6, l, CC), 1.0f), s));
-        TRY(bias_grad_launch<T>(grd(c, 7, l, C), dres_lp, BT, C, C, work, s));
+        TRY(gemm(c, dw_desc(BT, C, C, dres_lp, atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C)), s));
         // attention
         TRY(attention_bwd_launch<T>(dqkv, c->act<float>(p.delta), dbtc, atty, qkv, c->act_l<float>(p.lse, p.s_lse, l),
                                     B, Tn, C, NH, s));
         // qkv
         TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv, prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, C, 3 * C, dqkv, ln1, grd(c, 4, l, 3 * CC), 1.0f), s));
-        TRY(bias_grad_launch<T>(grd(c, 5, l, 3 * C), dqkv, BT, 3 * C, 3 * C, work, s));
+        TRY(gemm(c, dw_desc(BT, C, 3 * C, dqkv, ln1, grd(c, 4, l, 3 * CC), 1.0f, grd(c, 5, l, 3 * C)), s));
         TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 2, l, C), grd(c, 3, l, C), dbtc, res,
                                     prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
                                     c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, work, s));
     }
-    TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, s));
+    TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, work, s));
     return GPT2_OK;
 }
 

@@ -31,16 +31,14 @@ struct GemmDesc {
     const void* aux_in;       // activation type, ld = ldaux
     void* aux_out;            // activation type, ld = ldaux
     long ldaux;
+    float* dbias;             // GEMM_ACCUM only (may be NULL): dbias[m] += alpha * sum_k A(m,k)
+    int split_ok;             // GEMM_STORE / GEMM_ACCUM may split K (needs workspace)
 };
 // Workspace (fp32) needed by gemm_launch for split-K (0 if it will not split).
 size_t gemm_workspace_bytes(const GemmDesc& d, int elem_bytes, int num_cus);
 // Returns 0 or a hipError_t.  ws may be NULL if gemm_workspace_bytes(d) == 0.
 int gemm_launch(const GemmDesc& d, int elem_bytes, float* ws, size_t ws_bytes, int num_cus, hipStream_t s);
 
-// db[n] += sum_m dY[m*ldy + n]; partial: ceil(M/256) * N floats of workspace.
-template <typename T>
-int bias_grad_launch(float* db, const T* dY, int M, int N, long ldy, float* partial, hipStream_t s);
-size_t bias_grad_workspace_bytes(int M, int N);
 
 // ---------------------------------------------------------- LayerNorm -------
 template <typename T>
@@ -68,8 +66,10 @@ template <typename T>
 int encoder_fwd_launch(T* out, int* tok_copy, const int* tok, const T* wte, const T* wpe,
                        int B, int T_, int C, int V, int* flag, hipStream_t s);
 // dwte[tok] += dres rows, dwpe[t] += sum_b dres; fp32.  tok already clamped.
+// work: encoder_bwd_workspace_bytes(B*T, C) bytes (256-aligned).
 int encoder_bwd_launch(float* dwte, float* dwpe, const float* dres, const int* tok,
-                       int B, int T_, int C, hipStream_t s);
+                       int B, int T_, int C, void* work, hipStream_t s);
+size_t encoder_bwd_workspace_bytes(int BT, int C);
 // in place: logits -> softmax - onehot (padded columns 0); losses [N] fp32
 template <typename T>
 int classifier_ce_launch(T* logits, float* losses, const int* targets, int N, int V, int Vp,

@@ -180,15 +180,26 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T
     }
 }
 
-// dw[c] += sum_blocks partial[blk][c]; db[c] += sum_blocks partial[blk][C + c]
-__global__ void ln_bwd_finish_kernel(float* __restrict__ dw, float* __restrict__ db,
-                                     const float* __restrict__ partial, int C, int blocks) {
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= 2 * C) return;
+// dw[c] += sum_blocks partial[blk][c]; db[c] += sum_blocks partial[blk][C + c].
+// 64 columns per workgroup, 4 phases of blocks per column (block k goes to
+// phase k % 4), phases combined in order 0..3 through LDS.
+__global__ __launch_bounds__(256) void ln_bwd_finish_kernel(float* __restrict__ dw, float* __restrict__ db,
+                                                            const float* __restrict__ partial, int C, int blocks) {
+    __shared__ float red[4][64];
+    const int col = threadIdx.x & 63, ph = threadIdx.x >> 6;
+    const int j = blockIdx.x * 64 + col;
     float s = 0.f;
-    for (int k = 0; k < blocks; k++) s += partial[(size_t)k * 2 * C + j];
-    if (j < C) dw[j] += s;
-    else db[j - C] += s;
+    if (j < 2 * C) {
+#pragma unroll 4
+        for (int k = ph; k < blocks; k += 4) s += partial[(size_t)k * 2 * C + j];
+    }
+    red[ph][col] = s;
+    __syncthreads();
+    if (ph == 0 && j < 2 * C) {
+        const float t = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+        if (j < C) dw[j] += t;
+        else db[j - C] += t;
+    }
 }
 
 }  // namespace
@@ -213,7 +224,7 @@ int layernorm_bwd_launch(float* dres, T* dres_lp, float* dw, float* db, const T*
     const int blocks = (N + ROWS_PER_BLOCK_BWD - 1) / ROWS_PER_BLOCK_BWD;
     hipLaunchKernelGGL(ln_bwd_kernel<T>, dim3(blocks), dim3(256), 0, s, dres, dres_lp, partial, dy, x, w,
                        mean, rstd, N, C, accumulate);
-    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + 255) / 256), dim3(256), 0, s, dw, db, partial, C, blocks);
+    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + 63) / 64), dim3(256), 0, s, dw, db, partial, C, blocks);
     return (int)hipGetLastError();
 }
 

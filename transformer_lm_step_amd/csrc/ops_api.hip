@@ -25,3 +25,57 @@ extern "C" int gpt2_linear_forward(int precision, const void* x, const void* w, 
     const int e = gemm_launch(d, precision == GPT2_BF16 ? 2 : 4, nullptr, 0, 256, (hipStream_t)hip_stream);
     return e == 0 ? GPT2_OK : GPT2_E_HIP;
 }
+
+namespace {
+GemmDesc bwd_dx_desc(const void* dy, const void* w, void* dx, int M, int N, int K, float alpha) {
+    GemmDesc d = {};
+    d.M = M; d.N = K; d.K = N;
+    d.A = dy; d.lda = N; d.a_kmajor = 1;
+    d.B = w; d.ldb = K; d.b_kmajor = 0;
+    d.C = dx; d.ldc = K; d.epi = GEMM_STORE; d.alpha = alpha; d.ldaux = K;
+    d.split_ok = 1;
+    return d;
+}
+GemmDesc bwd_dw_desc(const void* dy, const void* x, float* dw, float* db, int M, int N, int K, float alpha) {
+    GemmDesc d = {};
+    d.M = N; d.N = K; d.K = M;
+    d.A = dy; d.lda = N; d.a_kmajor = 0;
+    d.B = x; d.ldb = K; d.b_kmajor = 0;
+    d.C = dw; d.ldc = K; d.epi = GEMM_ACCUM; d.alpha = alpha; d.dbias = db;
+    d.split_ok = 1;
+    return d;
+}
+}  // namespace
+
+extern "C" size_t gpt2_linear_backward_workspace(int precision, int M, int N, int K) {
+    const int esz = precision == GPT2_BF16 ? 2 : 4;
+    const size_t a = gemm_workspace_bytes(bwd_dx_desc(nullptr, nullptr, nullptr, M, N, K, 1.f), esz, 256);
+    const size_t b = gemm_workspace_bytes(bwd_dw_desc(nullptr, nullptr, nullptr, nullptr, M, N, K, 1.f), esz, 256);
+    return a > b ? a : b;
+}
+
+extern "C" int gpt2_linear_backward(int precision, const void* dy, const void* x, const void* w, void* dx, float* dw,
+                                    float* db, int M, int N, int K, float alpha, void* work, size_t work_bytes,
+                                    void* hip_stream) {
+    if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_E_ARG;
+    if (!dy || M < 0 || N < 0 || K < 0 || (dx && !w) || (dw && !x) || (db && !dw)) return GPT2_E_ARG;
+    if (K % 8 || N % 8) return GPT2_E_SHAPE;
+    if (!al(dy) || (x && !al(x)) || (w && !al(w)) || (dx && !al(dx)) || (dw && !al(dw)) || (db && !al(db)) ||
+        (work && !al(work)))
+        return GPT2_E_ALIGN;
+    const int esz = precision == GPT2_BF16 ? 2 : 4;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (dx) {
+        const GemmDesc d = bwd_dx_desc(dy, w, dx, M, N, K, alpha);
+        const size_t need = gemm_workspace_bytes(d, esz, 256);
+        if (need > 0 && (work == nullptr || work_bytes < need)) return GPT2_E_ARG;
+        if (gemm_launch(d, esz, (float*)work, work_bytes, 256, s) != 0) return GPT2_E_HIP;
+    }
+    if (dw) {
+        const GemmDesc d = bwd_dw_desc(dy, x, dw, db, M, N, K, alpha);
+        const size_t need = gemm_workspace_bytes(d, esz, 256);
+        if (need > 0 && (work == nullptr || work_bytes < need)) return GPT2_E_ARG;
+        if (gemm_launch(d, esz, (float*)work, work_bytes, 256, s) != 0) return GPT2_E_HIP;
+    }
+    return GPT2_OK;
+}
