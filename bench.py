@@ -61,6 +61,72 @@ def cpu_baseline(cfg, budget_s=30.0):
                       f"{dt:.1f} s"}
 
 
+PEAK_FP32_TFLOPS = 157.3
+
+
+def bench_fused(args):
+    """The standalone fp32 op Y = softmax_row(GELU_tanh(X W^T + b)), X [1024,8192],
+    W [8192,8192]: median time per call of `steps` calls after `warmup`."""
+    import torch
+    import synthetic as S
+    from transformer_lm_step_amd import binding as Bnd
+
+    M, K, N = 1024, 8192, 8192
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    X, W, b = S.fused_op_inputs(M, K, N)
+    x, w, bb = (torch.from_numpy(a).to(dev) for a in (X, W, b))
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    wsz = Bnd.fused_linear_gelu_softmax_f32_workspace(M, N)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    cur = torch.cuda.current_stream()
+    sh = cur.cuda_stream
+
+    def call():
+        Bnd.fused_linear_gelu_softmax_f32(x.data_ptr(), w.data_ptr(), bb.data_ptr(), y.data_ptr(), M, K, N,
+                                          ws.data_ptr(), wsz, sh)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        call()
+        e1.record(cur)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(c) for a, c in times]))
+    flop = 2.0 * M * N * K
+    tf = flop / (ms / 1e3) / 1e12
+    rows_sum = y.sum(1)
+    if not bool(torch.all((rows_sum - 1).abs() < 1e-4)):
+        raise RuntimeError("fused op: rows do not sum to 1")
+    log(f"bench: fused op {ms:.3f} ms/call, {tf:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = np.arange(16, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.fused_linear_gelu_softmax(X, W, b, rows=rows)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(dt * M / rows.size * 1e3, 1), "unit": "ms/call", "cores": 1, "kind": "oracle",
+               "sample": f"16 of the 1024 rows (fp64, single thread) in {dt:.1f} s, scaled to 1024 rows"}
+    out = {
+        "metric": "ms per call, fused Linear+GELU_tanh+row softmax fp32",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "strong", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (X ~ N(0,1), W ~ N(0,1/8192), b ~ N(0,0.02))",
+        "config": {"workload": "fused Linear+GELU+softmax, X[1024,8192] W[8192,8192] b[8192]"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel + softmax_finish_kernel (whole call)", "avg_ms": round(ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -70,11 +136,17 @@ def main():
     ap.add_argument("--seq", type=int, default=1024)
     ap.add_argument("--accum", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("gpt2", "fused"), default="gpt2",
+                    help="gpt2: the GPT-2 124M training step (default); fused: the standalone "
+                         "Linear+GELU+softmax op")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the data-parallel multi-GPU path is not part of it.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the data-parallel multi-GPU path is not implemented.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "fused":
+        bench_fused(args)
+        return
 
     import torch
     import synthetic as S

@@ -37,6 +37,21 @@ int gpt2_linear_backward(int precision, const void* d_dy, const void* d_x, const
                          size_t work_bytes, void* hip_stream);
 size_t gpt2_linear_backward_workspace(int precision, int M, int N, int K);
 
+/* POPCORNBENCH l12_default_gpt trajectory page, the problem statement (a
+ * Linear layer followed by tanh-form GELU and a softmax over dim 1), in fp32:
+ *   Y[m, :] = softmax_n( GELU_tanh( sum_k X[m,k] W[n,k] + b[n] ) )
+ * X [M,K], W [N,K] (out, in), b [N], Y [M,N], all fp32 row-major device
+ * memory owned by the caller; products use fp32 MFMA with fp32 accumulation
+ * (no reduced-precision inputs).  d_work: device workspace of at least
+ * fused_linear_gelu_softmax_f32_workspace(M, N) bytes (per-row, per-64-column
+ * softmax partials; contents on return are unspecified).  K and N multiples of
+ * 8; M == 0 is a no-op.  Asynchronous on hip_stream.
+ * Errors: GPT2_E_ARG (NULL pointer, non-positive K or N, negative M, workspace
+ * too small), GPT2_E_SHAPE, GPT2_E_ALIGN, GPT2_E_HIP. */
+int fused_linear_gelu_softmax_f32(const float* d_X, const float* d_W, const float* d_b, float* d_Y, int M, int K,
+                                  int N, void* d_work, size_t work_bytes, void* hip_stream);
+size_t fused_linear_gelu_softmax_f32_workspace(int M, int N);
+
 #ifdef __cplusplus
 }
 #endif

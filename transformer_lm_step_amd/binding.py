@@ -24,7 +24,8 @@ EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
     "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
-    "gpt2_linear_backward_workspace",
+    "gpt2_linear_backward_workspace", "fused_linear_gelu_softmax_f32",
+    "fused_linear_gelu_softmax_f32_workspace",
 )
 
 
@@ -71,6 +72,8 @@ def _load():
         "gpt2_linear_forward": (i, [i, vp, vp, vp, vp, i, i, i, vp]),
         "gpt2_linear_backward": (i, [i, vp, vp, vp, vp, vp, vp, i, i, i, f, vp, z, vp]),
         "gpt2_linear_backward_workspace": (z, [i, i, i, i]),
+        "fused_linear_gelu_softmax_f32": (i, [vp, vp, vp, vp, i, i, i, vp, z, vp]),
+        "fused_linear_gelu_softmax_f32_workspace": (z, [i, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -182,3 +185,13 @@ def gpt2_linear_backward(precision: int, d_dy: int, d_x: int, d_w: int, d_dx: in
     _check(_lib.gpt2_linear_backward(precision, d_dy, d_x or None, d_w or None, d_dx or None, d_dw or None,
                                      d_db or None, M, N, K, float(alpha), d_work or None, int(work_bytes),
                                      stream or None), "gpt2_linear_backward")
+
+
+def fused_linear_gelu_softmax_f32_workspace(M: int, N: int) -> int:
+    return int(_lib.fused_linear_gelu_softmax_f32_workspace(M, N))
+
+
+def fused_linear_gelu_softmax_f32(d_X: int, d_W: int, d_b: int, d_Y: int, M: int, K: int, N: int, d_work: int,
+                                  work_bytes: int, stream: int):
+    _check(_lib.fused_linear_gelu_softmax_f32(d_X, d_W, d_b, d_Y, M, K, N, d_work or None, int(work_bytes),
+                                              stream or None), "fused_linear_gelu_softmax_f32")

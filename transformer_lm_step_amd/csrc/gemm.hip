@@ -340,6 +340,44 @@ __global__ __launch_bounds__((Tile<T, BM, BN>::NT), (Tile<T, BM, BN>::OCC)) void
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3]
+    if constexpr (EPI == GEMM_BIAS_GELU_SMX) {
+        // G = gelu(v + bias) stored, plus (max, sum exp(G - max)) of each row
+        // over this wave's 64 columns; a row's 64 values sit in the 4 lanes
+        // l16 + 16 g (4 tiles x 4 values each), combined with two shuffles.
+        const int nw = n0 + wn * 64;
+        float2* part = (float2*)g.aux_out;
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+            const int m = m0 + wm * 64 + 16 * i + l16;
+            float v[TN][4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int n = nw + 16 * j + 4 * g4;
+                const bool ok = n < g.N;
+                float bb[4] = {0.f, 0.f, 0.f, 0.f};
+                if (ok) load4<T>((const T*)g.bias + n, bb);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    v[j][r] = gelu_f(g.alpha * acc[i][j][r] + bb[r]);
+                    if (ok) mx = fmaxf(mx, v[j][r]);
+                }
+                if (ok && m < g.M) store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v[j]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            float sm = 0.f;
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                if (nw + 16 * j + 4 * g4 < g.N)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) sm += expf(v[j][r] - mx);
+            sm += __shfl_xor(sm, 16, 64);
+            sm += __shfl_xor(sm, 32, 64);
+            if (g4 == 0 && m < g.M && nw < g.N) part[(size_t)m * g.ldaux + nw / 64] = make_float2(mx, sm);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int m = m0 + wm * 64 + 16 * i + l16;
@@ -502,6 +540,12 @@ int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int epi, hipStream_t
             case GEMM_BIAS: launch_t<T, BM, BN, true, true, GEMM_BIAS, T>(a, grid, s); return 0;
             case GEMM_BIAS_GELU: launch_t<T, BM, BN, true, true, GEMM_BIAS_GELU, T>(a, grid, s); return 0;
             case GEMM_BIAS_RESID: launch_t<T, BM, BN, true, true, GEMM_BIAS_RESID, T>(a, grid, s); return 0;
+            case GEMM_BIAS_GELU_SMX:
+                if constexpr (sizeof(T) == 4) {
+                    launch_t<T, BM, BN, true, true, GEMM_BIAS_GELU_SMX, T>(a, grid, s);
+                    return 0;
+                }
+                break;
         }
     } else if (lay == 2) {
         switch (epi) {

@@ -19,6 +19,8 @@ enum GemmEpi {
     GEMM_BIAS_RESID = 3, // C = aux_in + v + bias[n]
     GEMM_GELU_BWD = 4,   // C = v * gelu'(aux_in)
     GEMM_ACCUM = 5,      // C (fp32) += v
+    GEMM_BIAS_GELU_SMX = 6,  // C = gelu(v + bias[n]); aux_out (float2, ldaux per row) gets, per row
+                             // and 64-column block j, (max, sum exp(C - max)) over that block
 };
 struct GemmDesc {
     int M, N, K;
@@ -35,6 +37,10 @@ struct GemmDesc {
     int split_ok;             // GEMM_STORE / GEMM_ACCUM may split K (needs workspace)
 };
 // Workspace (fp32) needed by gemm_launch for split-K (0 if it will not split).
+// Row softmax from the per-64-column partials of GEMM_BIAS_GELU_SMX:
+// Y[m, :] = exp(Y[m, :] - M_m) / S_m, in place (fp32, N % 4 == 0).
+int softmax_finish_launch(float* Y, const float2* part, int M, int N, int np, hipStream_t s);
+
 size_t gemm_workspace_bytes(const GemmDesc& d, int elem_bytes, int num_cus);
 // Returns 0 or a hipError_t.  ws may be NULL if gemm_workspace_bytes(d) == 0.
 int gemm_launch(const GemmDesc& d, int elem_bytes, float* ws, size_t ws_bytes, int num_cus, hipStream_t s);
