@@ -45,12 +45,12 @@ def flops_per_token(L, C, V, T):
 def cpu_baseline(cfg, budget_s=30.0):
     """The CPU oracle (single-threaded C, fp64) on a bounded sample of the same
     workload: one micro-step (forward + backward) of GPT-2 124M on B=1 x T
-    tokens with T chosen to stay within ~budget_s."""
+    tokens (T = 128: about 15 s on the host cores)."""
     import oracle
     import synthetic as S
     params = S.init_params(cfg)
     flat = oracle.pack_params(cfg, {k: S.round_to_bf16(v) for k, v in params.items()})
-    T = 48
+    T = 128
     stream = S.token_stream(T + 1, cfg.vocab_size, dist="zipf")
     x, y = S.batch(stream, 0, 1, T)
     t0 = time.perf_counter()

@@ -1,0 +1,211 @@
+"""GPU checks at the full GPT-2 sizes, through the C ABI, against stored oracle
+results (tests/golden/*.npz, written by tests/golden/make_golden.py, which
+calls only the oracle), plus size-independent properties.
+
+* GPT-2 124M fp32, B=4 T=64, 10 AdamW steps overfitting one batch (lr 1e-4,
+  wd 0): per-step mean loss rel <= 1e-5; per-step gradient norms rel <= 1e-4;
+  per-step sampled gradients and final sampled parameters rel-L2 <= 1e-4 per
+  tensor; the loss falls.
+* GPT-2 124M bf16, B=8 T=1024, step 1 of the benchmark workload (2
+  micro-steps, AdamW lr 6e-4 wd 0.1): micro-step mean losses abs <= 2e-2;
+  sampled gradient cosine >= 0.995 per tensor; sampled update direction
+  cosine >= 0.9.
+* GPT-2 1558M bf16, B=1 T=64 micro-step: loss abs <= 2e-2, sampled gradient
+  cosine >= 0.995 per tensor; at B=8 T=1024 the loss at init is near
+  ln V + C * 0.02^2 / 2 and falls over three small steps on one batch.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from helpers import cosine, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    p = os.path.join(GOLDEN, name)
+    if not os.path.exists(p):
+        pytest.skip(f"{name} not generated (tests/golden/make_golden.py)")
+    return np.load(p, allow_pickle=False)
+
+
+def _samples(model, flat, g):
+    out = {}
+    for i, name in enumerate(S.PARAM_NAMES):
+        t = flat[model.offsets[i]: model.offsets[i] + model.counts[i]]
+        out[name] = t[g[f"idx_{name}"]]
+    return out
+
+
+def _split(cfg, g, arr):
+    out, pos = {}, 0
+    for name in S.PARAM_NAMES:
+        n = g[f"idx_{name}"].size
+        out[name] = arr[pos: pos + n]
+        pos += n
+    return out
+
+
+def _norms(model, flat):
+    return np.array([np.linalg.norm(flat[model.offsets[i]: model.offsets[i] + model.counts[i]].astype(np.float64))
+                     for i in range(16)])
+
+
+def _tokens(cfg, n, dev):
+    import torch
+    return torch.from_numpy(S.token_stream(n, cfg.vocab_size, dist="zipf")).to(dev)
+
+
+def test_gpt2_124m_fp32_ten_steps_one_batch():
+    import torch
+    from transformer_lm_step_amd.model import GPT2
+
+    g = _golden("gpt2_124m_fp32_overfit10.npz")
+    cfg, B, T = S.GPT2_124M, 4, 64
+    model = GPT2(cfg, 0, B, T)
+    model.init(model.pack(S.init_params(cfg)))
+    dev = model.device
+    toks = _tokens(cfg, B * T + 1, dev)
+    x, y = toks[:B * T].clone(), toks[1:].clone()
+    mean = torch.zeros(1, dtype=torch.float32, device=dev)
+    for s in range(10):
+        model.zero_grad()
+        model.forward(x, y, None, mean)
+        model.backward(1.0 / (B * T))
+        grads = model.grads().cpu().numpy()
+        model.update(1e-4, 0.9, 0.999, 1e-8, 0.0, s + 1)
+        torch.cuda.synchronize()
+        lo = float(mean.cpu())
+        ref = float(g["mean_loss"][s])
+        say(f"124M fp32 step {s + 1}: loss {lo:.6f} oracle {ref:.6f}")
+        assert abs(lo - ref) / abs(ref) < 1e-5, (s, lo, ref)
+        gn = _norms(model, grads)
+        assert np.all(np.abs(gn - g["grad_norms"][s]) <= 1e-4 * g["grad_norms"][s] + 1e-30), s
+        gs = _samples(model, grads, g)
+        ref_s = _split(cfg, g, g["grad_samples"][s])
+        for name in S.PARAM_NAMES:
+            if np.linalg.norm(ref_s[name]) == 0:
+                assert np.all(gs[name] == 0), (s, name)
+            else:
+                assert rel_l2(gs[name], ref_s[name]) < 1e-4, (s, name)
+    assert model.check() == 0
+    ps = _samples(model, model.params().cpu().numpy(), g)
+    ref_p = _split(cfg, g, g["param_samples"][-1])
+    worst = max(rel_l2(ps[n], ref_p[n]) for n in S.PARAM_NAMES)
+    say(f"124M fp32 final sampled params worst rel-L2 {worst:.2e}")
+    assert worst < 1e-4
+    assert g["mean_loss"][-1] < g["mean_loss"][0] - 0.5
+    model.close()
+
+
+def test_gpt2_124m_bf16_benchmark_step1():
+    import torch
+    from transformer_lm_step_amd.model import GPT2
+
+    g = _golden("gpt2_124m_bf16_step1.npz")
+    cfg, B, T, accum = S.GPT2_124M, 8, 1024, 2
+    model = GPT2(cfg, 1, B, T)
+    model.init(model.pack(S.init_params(cfg)))
+    dev = model.device
+    toks = _tokens(cfg, accum * B * T + 1, dev)
+    BT = B * T
+    mean = torch.zeros(accum, dtype=torch.float32, device=dev)
+    model.zero_grad()
+    for a in range(accum):
+        model.forward(toks[a * BT:(a + 1) * BT].clone(), toks[a * BT + 1:(a + 1) * BT + 1].clone(),
+                      None, mean[a:a + 1])
+        model.backward(1.0 / (accum * BT))
+    grads = model.grads().cpu().numpy()
+    p0 = model.master().cpu().numpy().copy()
+    model.update(6e-4, 0.9, 0.999, 1e-8, 0.1, 1)
+    torch.cuda.synchronize()
+    assert model.check() == 0
+    lo = mean.cpu().numpy()
+    say(f"124M bf16 step 1: micro-step losses {lo} oracle {g['mean_loss']}")
+    assert np.all(np.abs(lo - g["mean_loss"]) <= 2e-2)
+    gs = _samples(model, grads, g)
+    ref = _split(cfg, g, g["grad_samples"])
+    cos = {n: cosine(gs[n], ref[n]) for n in S.PARAM_NAMES}
+    say("124M bf16 sampled gradient cosines", {k: round(v, 5) for k, v in cos.items()})
+    assert min(cos.values()) >= 0.995
+    gn = _norms(model, grads)
+    assert np.all(np.abs(gn / g["grad_norms"] - 1) < 0.05)
+    p1 = model.master().cpu().numpy()
+    d_gpu = _samples(model, p1, g)
+    d_p0 = _samples(model, p0, g)
+    ref_p = _split(cfg, g, g["param_samples"])
+    ref_p0 = _split(cfg, g, g["init_samples"])
+    for n in S.PARAM_NAMES:
+        assert np.array_equal(d_p0[n].astype(np.float64), ref_p0[n]), n  # same bf16-exact start
+        c = cosine(d_gpu[n] - d_p0[n], ref_p[n] - ref_p0[n])
+        assert c >= 0.9, (n, c)
+    model.close()
+
+
+def test_gpt2_1558m_bf16_micro_step_b1t64():
+    import torch
+    from transformer_lm_step_amd.model import GPT2
+
+    g = _golden("gpt2_1558m_bf16_b1t64.npz")
+    cfg, B, T = S.GPT2_1558M, 1, 64
+    model = GPT2(cfg, 1, B, T)
+    model.init(model.pack(S.init_params(cfg)))
+    dev = model.device
+    toks = _tokens(cfg, B * T + 1, dev)
+    mean = torch.zeros(1, dtype=torch.float32, device=dev)
+    losses = torch.zeros(B * T, dtype=torch.float32, device=dev)
+    model.zero_grad()
+    model.forward(toks[:B * T].clone(), toks[1:].clone(), losses, mean)
+    model.backward(1.0 / (B * T))
+    torch.cuda.synchronize()
+    assert model.check() == 0
+    lo = float(mean.cpu())
+    say(f"1558M bf16 B=1 T=64 loss {lo:.5f} oracle {float(g['mean_loss'][0]):.5f}")
+    assert abs(lo - float(g["mean_loss"][0])) <= 2e-2
+    assert np.max(np.abs(losses.cpu().numpy() - g["losses"].ravel())) < 0.1
+    grads = model.grads().cpu().numpy()
+    gs = _samples(model, grads, g)
+    ref = _split(cfg, g, g["grad_samples"])
+    cos = {n: cosine(gs[n], ref[n]) for n in S.PARAM_NAMES}
+    say("1558M bf16 sampled gradient cosines", {k: round(v, 5) for k, v in cos.items()})
+    assert min(cos.values()) >= 0.995
+    gn = _norms(model, grads)
+    assert np.all(np.abs(gn / g["grad_norms"] - 1) < 0.05)
+    model.close()
+
+
+def test_gpt2_1558m_bf16_full_size_steps():
+    """All activations resident at B=8 T=1024: loss at init, and its descent
+    over three small AdamW steps (lr 1e-5) on one batch."""
+    import torch
+    from transformer_lm_step_amd.model import GPT2
+
+    cfg, B, T = S.GPT2_1558M, 8, 1024
+    model = GPT2(cfg, 1, B, T)
+    model.init(model.pack(S.init_params(cfg)))
+    dev = model.device
+    toks = _tokens(cfg, B * T + 1, dev)
+    x, y = toks[:B * T].clone(), toks[1:].clone()
+    mean = torch.zeros(4, dtype=torch.float32, device=dev)
+    for s in range(3):
+        model.zero_grad()
+        model.forward(x, y, None, mean[s:s + 1])
+        model.backward(0.0)
+        model.update(1e-5, 0.9, 0.999, 1e-8, 0.0, s + 1)
+    model.forward(x, y, None, mean[3:4])
+    torch.cuda.synchronize()
+    assert model.check() == 0
+    lo = mean.cpu().numpy()
+    expect = math.log(cfg.vocab_size) + cfg.channels * 0.02 ** 2 / 2
+    say(f"1558M bf16 losses {lo} (init expectation {expect:.3f})")
+    assert np.all(np.isfinite(lo))
+    assert abs(lo[0] - expect) < 0.2
+    assert lo[3] < lo[0] - 0.01
+    model.close()

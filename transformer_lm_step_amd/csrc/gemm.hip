@@ -51,7 +51,7 @@ constexpr int NTHREADS = 256;
 #define GEMM_SCHED_GROUPS 1
 #endif
 
-template <typename T, int BM_, int BN_>
+template <typename T, int BM_, int BN_, int WTM_ = 64, int WTN_ = 64>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int BK = 128 / (int)sizeof(T);  // contraction depth per stage
@@ -59,12 +59,16 @@ struct Tile {
     static constexpr int LDSK = BK + PAD;            // LDS row pitch (elements)
     static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
     static constexpr int KSTEPS = BK / 32;           // MFMA steps per stage
-    static constexpr int WM = BM / 64, WN = BN / 64; // waves, each owning a 64x64 output tile
+    static constexpr int WTM = WTM_, WTN = WTN_;     // output tile of one wave
+    static constexpr int WM = BM / WTM, WN = BN / WTN;
     static constexpr int NT = 64 * WM * WN;          // threads per workgroup
-    static constexpr int TM = 4, TN = 4;             // 16x16 MFMA tiles per wave
-    static constexpr int OCC = NT == 256 ? 2 : 1;    // workgroups per CU
-    static constexpr int DEPTH = NT <= 512 ? 2 : 1;  // slab prefetch distance
-    static constexpr int FBUF = NT <= 512 ? 2 : 1;   // fragment buffers
+    static constexpr int TM = WTM / 16, TN = WTN / 16;  // 16x16 MFMA tiles per wave
+    static constexpr int OCC = NT == 256 && WTM == 64 ? 2 : 1;  // workgroups per CU
+    // slab prefetch distance and fragment buffers, within the register budget
+    // of NT/256 * OCC waves per SIMD
+    static constexpr int DEPTH = WTM * WTN == 64 * 64 ? (NT <= 512 ? 2 : 1)
+                                 : WTM * WTN == 128 * 64 ? (NT <= 256 ? 2 : 1) : 1;
+    static constexpr int FBUF = DEPTH;
 };
 
 // Per-thread register count for staging an R x BK slab (both layouts).
@@ -169,9 +173,9 @@ DEV void slab_store(const uint4* r, T* __restrict__ s, int tid) {
     }
 }
 
-template <typename T, int BM, int BN, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
-__global__ __launch_bounds__((Tile<T, BM, BN>::NT), (Tile<T, BM, BN>::OCC)) void gemm_kernel(const Args g) {
-    using TL = Tile<T, BM, BN>;
+template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
+__global__ __launch_bounds__((Tile<T, BM, BN, WT>::NT), (Tile<T, BM, BN, WT>::OCC)) void gemm_kernel(const Args g) {
+    using TL = Tile<T, BM, BN, WT>;
     constexpr int LDSK = TL::LDSK, BK = TL::BK, TM = TL::TM, TN = TL::TN, NT = TL::NT;
     __shared__ __attribute__((aligned(16))) T sA[2][BM * LDSK];
     __shared__ __attribute__((aligned(16))) T sB[2][BN * LDSK];
@@ -259,18 +263,18 @@ __global__ __launch_bounds__((Tile<T, BM, BN>::NT), (Tile<T, BM, BN>::OCC)) void
         const T* b_s = sB[cur];
         Frag<T> fa[TL::FBUF][TM], fb[TL::FBUF][TN];
 #pragma unroll
-        for (int t = 0; t < TN; t++) frag_ld(fb[0][t], b_s + (wn * 64 + 16 * t + l16) * LDSK + 8 * g4);
+        for (int t = 0; t < TN; t++) frag_ld(fb[0][t], b_s + (wn * TL::WTN + 16 * t + l16) * LDSK + 8 * g4);
 #pragma unroll
-        for (int t = 0; t < TM; t++) frag_ld(fa[0][t], a_s + (wm * 64 + 16 * t + l16) * LDSK + 8 * g4);
+        for (int t = 0; t < TM; t++) frag_ld(fa[0][t], a_s + (wm * TL::WTM + 16 * t + l16) * LDSK + 8 * g4);
 #pragma unroll
         for (int ks = 0; ks < TL::KSTEPS; ks++) {
             const int c = TL::FBUF == 2 ? (ks & 1) : 0;
             if (TL::FBUF == 2 && ks + 1 < TL::KSTEPS) {
                 const int kofs = (ks + 1) * 32 + 8 * g4;
 #pragma unroll
-                for (int t = 0; t < TN; t++) frag_ld(fb[c ^ 1][t], b_s + (wn * 64 + 16 * t + l16) * LDSK + kofs);
+                for (int t = 0; t < TN; t++) frag_ld(fb[c ^ 1][t], b_s + (wn * TL::WTN + 16 * t + l16) * LDSK + kofs);
 #pragma unroll
-                for (int t = 0; t < TM; t++) frag_ld(fa[c ^ 1][t], a_s + (wm * 64 + 16 * t + l16) * LDSK + kofs);
+                for (int t = 0; t < TM; t++) frag_ld(fa[c ^ 1][t], a_s + (wm * TL::WTM + 16 * t + l16) * LDSK + kofs);
             }
 #pragma unroll
             for (int i = 0; i < TM; i++)
@@ -279,9 +283,9 @@ __global__ __launch_bounds__((Tile<T, BM, BN>::NT), (Tile<T, BM, BN>::OCC)) void
             if (TL::FBUF == 1 && ks + 1 < TL::KSTEPS) {
                 const int kofs = (ks + 1) * 32 + 8 * g4;
 #pragma unroll
-                for (int t = 0; t < TN; t++) frag_ld(fb[0][t], b_s + (wn * 64 + 16 * t + l16) * LDSK + kofs);
+                for (int t = 0; t < TN; t++) frag_ld(fb[0][t], b_s + (wn * TL::WTN + 16 * t + l16) * LDSK + kofs);
 #pragma unroll
-                for (int t = 0; t < TM; t++) frag_ld(fa[0][t], a_s + (wm * 64 + 16 * t + l16) * LDSK + kofs);
+                for (int t = 0; t < TM; t++) frag_ld(fa[0][t], a_s + (wm * TL::WTM + 16 * t + l16) * LDSK + kofs);
             }
         }
         if constexpr (BIAS) {
@@ -344,11 +348,12 @@ __global__ __launch_bounds__((Tile<T, BM, BN>::NT), (Tile<T, BM, BN>::OCC)) void
         // G = gelu(v + bias) stored, plus (max, sum exp(G - max)) of each row
         // over this wave's 64 columns; a row's 64 values sit in the 4 lanes
         // l16 + 16 g (4 tiles x 4 values each), combined with two shuffles.
+        static_assert(TL::WTN == 64, "partials are per 64 columns");
         const int nw = n0 + wn * 64;
         float2* part = (float2*)g.aux_out;
 #pragma unroll
         for (int i = 0; i < TM; i++) {
-            const int m = m0 + wm * 64 + 16 * i + l16;
+            const int m = m0 + wm * TL::WTM + 16 * i + l16;
             float v[TN][4];
             float mx = -INFINITY;
 #pragma unroll
@@ -380,11 +385,11 @@ __global__ __launch_bounds__((Tile<T, BM, BN>::NT), (Tile<T, BM, BN>::OCC)) void
     }
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int m = m0 + wm * 64 + 16 * i + l16;
+        const int m = m0 + wm * TL::WTM + 16 * i + l16;
         if (m >= g.M) continue;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-            const int n = n0 + wn * 64 + 16 * j + 4 * g4;
+            const int n = n0 + wn * TL::WTN + 16 * j + 4 * g4;
             if (n >= g.N) continue;
             float v[4];
 #pragma unroll
@@ -465,19 +470,26 @@ __global__ void splitk_bias_reduce_kernel(float* __restrict__ db, const float* _
 
 // ---------------------------------------------------------------- dispatch --
 struct Choice {
-    int bm, bn, splits;
+    int bm, bn, wt, splits;
 };
 
 // Tile configurations per element type, with their measured relative per-CU
-// throughput (MI355X, bf16, K = 768 products): 256x256 ~754 TFLOP/s,
-// 256x128 / 128x256 ~700, 128x128 (two per CU) ~665.
+// throughput per operand layout (MI355X, bf16, 8192 x 50304 x 768 classifier
+// products; time per round of resident workgroups, so wave quantisation is
+// left to the cost model; 1.00 = the best tile of that layout).  The 128-row
+// waves (8 per 256x256 tile) read 25% fewer LDS bytes per MFMA, which matters
+// most when both operands are transposed on their way into LDS.
 struct TileCfg {
-    int bm, bn, occ;
-    double speed;
+    int bm, bn, wt, occ;
+    double speed[3];  // forward, input gradient, weight gradient
 };
-const TileCfg kCfgBf16[] = {{256, 256, 1, 1.00}, {256, 128, 1, 0.93}, {128, 256, 1, 0.93},
-                            {128, 128, 2, 0.88}};
-const TileCfg kCfgF32[] = {{128, 128, 2, 1.0}};
+const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {1.00, 0.79, 0.79}},
+                            {256, 128, 64, 1, {0.81, 0.70, 0.66}},
+                            {128, 256, 64, 1, {0.80, 0.90, 0.68}},
+                            {128, 128, 64, 2, {0.87, 0.70, 0.70}},
+                            {256, 256, 128, 1, {0.96, 1.00, 1.00}}};
+constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
+const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}}};
 
 // Pick the tile and the K split minimising a simple cost: waves of
 // workgroups over the CUs times the work per workgroup, plus the split
@@ -486,19 +498,20 @@ const TileCfg kCfgF32[] = {{128, 128, 2, 1.0}};
 Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     const bool bf16 = elem_bytes == 2;
     const TileCfg* cfgs = bf16 ? kCfgBf16 : kCfgF32;
-    const int ncfg = bf16 ? 4 : 1;
+    const int ncfg = bf16 ? kNumCfgBf16 : 1;
     const int bk = 128 / elem_bytes;
     const int ktiles = (d.K + bk - 1) / bk;
     const bool can_split = d.split_ok && (d.epi == GEMM_ACCUM || d.epi == GEMM_STORE) && (d.N % 4 == 0) &&
                            d.ldc == d.N;
+    const int lay = d.a_kmajor && d.b_kmajor ? 0 : (d.a_kmajor ? 1 : 2);
     const double flop_rate = 2.5e15 / 256.0;  // per CU, dense bf16
     const double hbm = 5.0e12;                // bytes/s usable
-    Choice best = {cfgs[0].bm, cfgs[0].bn, 1};
+    Choice best = {cfgs[0].bm, cfgs[0].bn, cfgs[0].wt, 1};
     double best_cost = 1e300;
     for (int c = 0; c < ncfg; c++) {
         const TileCfg& t = cfgs[c];
 #ifdef GEMM_ONLY_TILE_BM
-        if (bf16 && (t.bm != GEMM_ONLY_TILE_BM || t.bn != GEMM_ONLY_TILE_BN)) continue;
+        if (bf16 && (t.bm != GEMM_ONLY_TILE_BM || t.bn != GEMM_ONLY_TILE_BN || t.wt != GEMM_ONLY_TILE_WT)) continue;
 #endif
         const long tiles = (long)((d.M + t.bm - 1) / t.bm) * ((d.N + t.bn - 1) / t.bn);
         const int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
@@ -512,57 +525,59 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
             // overlaps the previous one, so it is counted in half steps
             double rounds = t.occ == 1 ? (double)((units + slots - 1) / slots)
                                        : std::max(1.0, std::ceil(2.0 * units / slots) / 2.0);
-            double cost = rounds * (2.0 * t.bm * t.bn * (double)kps * bk) / (flop_rate * t.speed / t.occ);
+            const double speed = t.speed[lay];
+            double cost = rounds * (2.0 * t.bm * t.bn * (double)kps * bk) / (flop_rate * speed / t.occ);
             if (sp > 1) cost += (double)(sp + 1) * d.M * d.N * 4.0 / hbm;
             if (cost < best_cost * 0.999) {
                 best_cost = cost;
-                best = {t.bm, t.bn, sp};
+                best = {t.bm, t.bn, t.wt, sp};
             }
         }
     }
     return best;
 }
 
-template <typename T, int BM, int BN, bool AK, bool BKM, int EPI, typename OutT, bool BIAS = false>
+template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS = false>
 void launch_t(const Args& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, AK, BKM, EPI, OutT, BIAS>), grid, dim3(Tile<T, BM, BN>::NT), 0, s, a);
+    using TL = Tile<T, BM, BN, WT>;
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
 }
 
 // Instantiated (layout, epilogue) pairs: forward products (A and B
 // k-contiguous), input-gradient products (A k-contiguous, B k-strided) and
 // weight-gradient products (both k-strided).
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int WT>
 int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int epi, hipStream_t s) {
     const int lay = (d.a_kmajor ? 2 : 0) | (d.b_kmajor ? 1 : 0);
     if (lay == 3) {
         switch (epi) {
-            case GEMM_STORE: launch_t<T, BM, BN, true, true, GEMM_STORE, T>(a, grid, s); return 0;
-            case GEMM_BIAS: launch_t<T, BM, BN, true, true, GEMM_BIAS, T>(a, grid, s); return 0;
-            case GEMM_BIAS_GELU: launch_t<T, BM, BN, true, true, GEMM_BIAS_GELU, T>(a, grid, s); return 0;
-            case GEMM_BIAS_RESID: launch_t<T, BM, BN, true, true, GEMM_BIAS_RESID, T>(a, grid, s); return 0;
+            case GEMM_STORE: launch_t<T, BM, BN, WT, true, true, GEMM_STORE, T>(a, grid, s); return 0;
+            case GEMM_BIAS: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS, T>(a, grid, s); return 0;
+            case GEMM_BIAS_GELU: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_GELU, T>(a, grid, s); return 0;
+            case GEMM_BIAS_RESID: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_RESID, T>(a, grid, s); return 0;
             case GEMM_BIAS_GELU_SMX:
                 if constexpr (sizeof(T) == 4) {
-                    launch_t<T, BM, BN, true, true, GEMM_BIAS_GELU_SMX, T>(a, grid, s);
+                    launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_GELU_SMX, T>(a, grid, s);
                     return 0;
                 }
                 break;
         }
     } else if (lay == 2) {
         switch (epi) {
-            case GEMM_STORE: launch_t<T, BM, BN, true, false, GEMM_STORE, T>(a, grid, s); return 0;
-            case GEMM_GELU_BWD: launch_t<T, BM, BN, true, false, GEMM_GELU_BWD, T>(a, grid, s); return 0;
-            case EPI_SPLIT: launch_t<T, BM, BN, true, false, EPI_SPLIT, float>(a, grid, s); return 0;
+            case GEMM_STORE: launch_t<T, BM, BN, WT, true, false, GEMM_STORE, T>(a, grid, s); return 0;
+            case GEMM_GELU_BWD: launch_t<T, BM, BN, WT, true, false, GEMM_GELU_BWD, T>(a, grid, s); return 0;
+            case EPI_SPLIT: launch_t<T, BM, BN, WT, true, false, EPI_SPLIT, float>(a, grid, s); return 0;
         }
     } else if (lay == 0) {
         const bool bias = a.dbias != nullptr;
         switch (epi) {
             case GEMM_ACCUM:
-                if (bias) launch_t<T, BM, BN, false, false, GEMM_ACCUM, float, true>(a, grid, s);
-                else launch_t<T, BM, BN, false, false, GEMM_ACCUM, float, false>(a, grid, s);
+                if (bias) launch_t<T, BM, BN, WT, false, false, GEMM_ACCUM, float, true>(a, grid, s);
+                else launch_t<T, BM, BN, WT, false, false, GEMM_ACCUM, float, false>(a, grid, s);
                 return 0;
             case EPI_SPLIT:
-                if (bias) launch_t<T, BM, BN, false, false, EPI_SPLIT, float, true>(a, grid, s);
-                else launch_t<T, BM, BN, false, false, EPI_SPLIT, float, false>(a, grid, s);
+                if (bias) launch_t<T, BM, BN, WT, false, false, EPI_SPLIT, float, true>(a, grid, s);
+                else launch_t<T, BM, BN, WT, false, false, EPI_SPLIT, float, false>(a, grid, s);
                 return 0;
         }
     }
@@ -572,11 +587,15 @@ int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int epi, hipStream_t
 template <typename T>
 int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, int epi, hipStream_t s) {
     if constexpr (sizeof(T) == 2) {
-        if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256>(d, a, grid, epi, s);
-        if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128>(d, a, grid, epi, s);
-        if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256>(d, a, grid, epi, s);
+        if (ch.wt == 128) {
+            if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 128>(d, a, grid, epi, s);
+            return (int)hipErrorInvalidValue;
+        }
+        if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, epi, s);
+        if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 64>(d, a, grid, epi, s);
+        if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 64>(d, a, grid, epi, s);
     }
-    if (ch.bm == 128 && ch.bn == 128) return launch_epi<T, 128, 128>(d, a, grid, epi, s);
+    if (ch.bm == 128 && ch.bn == 128) return launch_epi<T, 128, 128, 64>(d, a, grid, epi, s);
     return (int)hipErrorInvalidValue;
 }
 
