@@ -51,39 +51,6 @@ struct ACfg {
     static constexpr int VEC = VecT<T>::N;
 };
 
-// 64 rows x KD of one head slice: dst[row*RP + d] = src(row0+row, d); zero past T or HS.
-// FULL: the caller guarantees row0 + 63 < T_ (no row check).
-template <typename T, int HS, bool FULL = false>
-DEV void stage_rows(T* dst, const T* src, long rs, int row0, int T_, int tid) {
-    using A = ACfg<T, HS>;
-    constexpr int VPR = A::KD / A::VEC;
-#pragma unroll
-    for (int idx = tid; idx < 64 * VPR; idx += 256) {
-        const int row = idx / VPR, d0 = (idx % VPR) * A::VEC;
-        const int gr = row0 + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if ((FULL || gr < T_) && d0 < HS) v = ld16(src + (long)gr * rs + d0);
-        st16(dst + row * A::RP + d0, v);
-    }
-}
-// The same 64 rows transposed: dst[d*TP + row] (rows past T are zero).
-template <typename T, int HS, bool FULL = false>
-DEV void stage_rows_t(T* dst, const T* src, long rs, int row0, int T_, int tid) {
-    using A = ACfg<T, HS>;
-    constexpr int DG = HS / A::VEC;
-#pragma unroll
-    for (int idx = tid; idx < 16 * DG; idx += 256) {
-        const int kq = idx % 16, dg = idx / 16;
-        uint4 r[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int gr = row0 + 4 * kq + i;
-            r[i] = (FULL || gr < T_) ? ld16(src + (long)gr * rs + dg * A::VEC) : make_uint4(0, 0, 0, 0);
-        }
-        store_t4<T>(dst + dg * A::VEC * A::TP + 4 * kq, A::TP, r);
-    }
-}
-
 // This lane's row (global index `row`) of a head slice as DSTEPS fragments over d.
 template <typename T, int HS>
 DEV void row_frags(Frag<T>* f, const T* src, long rs, int row, int T_, int g4) {
@@ -94,6 +61,63 @@ DEV void row_frags(Frag<T>* f, const T* src, long rs, int row, int T_, int g4) {
         else frag_zero(f[ks]);
     }
 }
+
+// Register-staged copies of the same two layouts, split into a load (issued
+// one block ahead, so its latency hides behind the current block's MFMAs) and
+// an LDS store.  FULL: rows row0..row0+63 are all < T (no row check).
+template <typename T, int HS>
+struct RowsStage {
+    using A = ACfg<T, HS>;
+    static constexpr int VPR = A::KD / A::VEC;
+    static constexpr int N = 64 * VPR / 256;  // 64 * VPR is a multiple of 256 for every HS
+    uint4 r[N];
+    template <bool FULL>
+    DEV void load(const T* src, long rs, int row0, int T_, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const int idx = tid + 256 * i;
+            const int row = idx / VPR, d0 = (idx % VPR) * A::VEC;
+            const int gr = row0 + row;
+            r[i] = ((FULL || gr < T_) && d0 < HS) ? ld16(src + (long)gr * rs + d0) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    DEV void store(T* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const int idx = tid + 256 * i;
+            st16(dst + (idx / VPR) * A::RP + (idx % VPR) * A::VEC, r[i]);
+        }
+    }
+};
+template <typename T, int HS>
+struct RowsTStage {
+    using A = ACfg<T, HS>;
+    static constexpr int DG = HS / A::VEC;
+    static constexpr int ITEMS = 16 * DG;  // (4-row group, 16-byte column) pairs
+    static constexpr int N = (ITEMS + 255) / 256;
+    uint4 r[N][4];
+    template <bool FULL>
+    DEV void load(const T* src, long rs, int row0, int T_, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const int idx = tid + 256 * i;
+            const int kq = idx % 16, dg = idx / 16;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int gr = row0 + 4 * kq + j;
+                r[i][j] = (idx < ITEMS && (FULL || gr < T_)) ? ld16(src + (long)gr * rs + dg * A::VEC)
+                                                             : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+    DEV void store(T* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const int idx = tid + 256 * i;
+            if (ITEMS % 256 == 0 || idx < ITEMS) store_t4<T>(dst + (idx / 16) * A::VEC * A::TP + 4 * (idx % 16), A::TP, r[i]);
+        }
+    }
+};
 
 // ------------------------------------------------------------------ forward -
 // Per 64-key block and wave (16 query rows): S^T = K Q^T (HS/32 MFMA steps per
@@ -133,12 +157,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
 #pragma unroll
     for (int dt = 0; dt < DT1; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    RowsStage<T, HS> pk;
+    RowsTStage<T, HS> pv;
+    auto prefetch = [&](int kb) {
+        if (kb < qb) {
+            pk.template load<true>(Kh, rs, kb * 64, T_, tid);
+            pv.template load<true>(Vh, rs, kb * 64, T_, tid);
+        } else {
+            pk.template load<false>(Kh, rs, kb * 64, T_, tid);
+            pv.template load<false>(Vh, rs, kb * 64, T_, tid);
+        }
+    };
+    prefetch(0);
     auto block = [&](int kb, auto diag) {
         __syncthreads();
-        constexpr bool full = !decltype(diag)::value;
-        stage_rows<T, HS, full>(sK, Kh, rs, kb * 64, T_, tid);
-        stage_rows_t<T, HS, full>(sVt, Vh, rs, kb * 64, T_, tid);
+        pk.store(sK, tid);
+        pv.store(sVt, tid);
         __syncthreads();
+        if (kb < qb) prefetch(kb + 1);
         // S^T tiles: lane holds S^T[key = 16kt + 4g4 + r][query = l16]
         f32x4_t s[4];
 #pragma unroll
@@ -238,7 +274,7 @@ __global__ void attn_delta_kernel(float* __restrict__ delta, const T* __restrict
 // only the diagonal block needs the causal test; the 1/sqrt(HS) factor of dS is
 // applied once to dK at the end.
 template <typename T, int HS>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
+__global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void attn_bwd_dkdv_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
                                                                const T* __restrict__ qkv, const float* __restrict__ lse,
                                                                const float* __restrict__ delta, int T_, int C, int NH,
                                                                float sl2, float scale) {
@@ -272,18 +308,38 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(T* __restrict__ d
         dv[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const int nqb = (T_ + 63) / 64;
-    auto block = [&](int qb, auto diag, auto full) {
+    RowsStage<T, HS> pq, pdo;
+    RowsTStage<T, HS> pqt, pdot;
+    float pl = INFINITY, pd = 0.f;
+    auto prefetch = [&](int qb) {
+        if ((qb + 1) * 64 <= T_) {
+            pq.template load<true>(Qh, rs, qb * 64, T_, tid);
+            pdo.template load<true>(dOh, C, qb * 64, T_, tid);
+            pqt.template load<true>(Qh, rs, qb * 64, T_, tid);
+            pdot.template load<true>(dOh, C, qb * 64, T_, tid);
+        } else {
+            pq.template load<false>(Qh, rs, qb * 64, T_, tid);
+            pdo.template load<false>(dOh, C, qb * 64, T_, tid);
+            pqt.template load<false>(Qh, rs, qb * 64, T_, tid);
+            pdot.template load<false>(dOh, C, qb * 64, T_, tid);
+        }
+        const int qq = qb * 64 + (tid & 63);
+        pl = qq < T_ ? lse_h[qq] : INFINITY;
+        pd = qq < T_ ? del_h[qq] : 0.f;
+    };
+    prefetch(kb);
+    auto block = [&](int qb, auto diag) {
         __syncthreads();
-        stage_rows<T, HS, decltype(full)::value>(sQ, Qh, rs, qb * 64, T_, tid);
-        stage_rows<T, HS, decltype(full)::value>(sdO, dOh, C, qb * 64, T_, tid);
-        stage_rows_t<T, HS, decltype(full)::value>(sQt, Qh, rs, qb * 64, T_, tid);
-        stage_rows_t<T, HS, decltype(full)::value>(sdOt, dOh, C, qb * 64, T_, tid);
+        pq.store(sQ, tid);
+        pdo.store(sdO, tid);
+        pqt.store(sQt, tid);
+        pdot.store(sdOt, tid);
         if (tid < 64) {
-            const int qq = qb * 64 + tid;
-            sL[tid] = qq < T_ ? lse_h[qq] : INFINITY;
-            sD[tid] = qq < T_ ? del_h[qq] : 0.f;
+            sL[tid] = pl;
+            sD[tid] = pd;
         }
         __syncthreads();
+        if (qb + 1 < nqb) prefetch(qb + 1);
         // S[q][key] and dP[q][key]: lane holds q = 16qt + 4g4 + r, key = l16 (+ block offsets)
         f32x4_t p[4], ds[4];
 #pragma unroll
@@ -335,14 +391,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(T* __restrict__ d
             }
         }
     };
-    const bool tail_full = (T_ % 64) == 0;
-    if (kb + 1 < nqb || tail_full) block(kb, std::true_type{}, std::true_type{});
-    else block(kb, std::true_type{}, std::false_type{});
-    for (int qb = kb + 1; qb + 1 < nqb; qb++) block(qb, std::false_type{}, std::true_type{});
-    if (kb + 1 < nqb) {
-        if (tail_full) block(nqb - 1, std::false_type{}, std::true_type{});
-        else block(nqb - 1, std::false_type{}, std::false_type{});
-    }
+    block(kb, std::true_type{});
+    for (int qb = kb + 1; qb < nqb; qb++) block(qb, std::false_type{});
     if (key < T_) {
         T* row = dqkv + ((long)b * T_ + key) * rs + h * HS;
 #pragma unroll
@@ -358,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(T* __restrict__ d
 // dQ: one workgroup per 64-query block, looping over the key blocks at or
 // before it (all full but the diagonal one); 1/sqrt(HS) applied at the end.
 template <typename T, int HS>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
+__global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void attn_bwd_dq_kernel(T* __restrict__ dqkv, const T* __restrict__ dout,
                                                              const T* __restrict__ qkv, const float* __restrict__ lse,
                                                              const float* __restrict__ delta, int T_, int C, int NH,
                                                              float sl2, float scale) {
@@ -386,13 +436,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(T* __restrict__ dqk
 #pragma unroll
     for (int dt = 0; dt < A::DT; dt++) dq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    RowsStage<T, HS> pk, pv;
+    RowsTStage<T, HS> pkt;
+    auto prefetch = [&](int kb) {
+        if (kb < qb) {
+            pk.template load<true>(Kh, rs, kb * 64, T_, tid);
+            pv.template load<true>(Vh, rs, kb * 64, T_, tid);
+            pkt.template load<true>(Kh, rs, kb * 64, T_, tid);
+        } else {
+            pk.template load<false>(Kh, rs, kb * 64, T_, tid);
+            pv.template load<false>(Vh, rs, kb * 64, T_, tid);
+            pkt.template load<false>(Kh, rs, kb * 64, T_, tid);
+        }
+    };
+    prefetch(0);
     auto block = [&](int kb, auto diag) {
-        constexpr bool full = !decltype(diag)::value;
         __syncthreads();
-        stage_rows<T, HS, full>(sK, Kh, rs, kb * 64, T_, tid);
-        stage_rows<T, HS, full>(sV, Vh, rs, kb * 64, T_, tid);
-        stage_rows_t<T, HS, full>(sKt, Kh, rs, kb * 64, T_, tid);
+        pk.store(sK, tid);
+        pv.store(sV, tid);
+        pkt.store(sKt, tid);
         __syncthreads();
+        if (kb < qb) prefetch(kb + 1);
         // S^T[key][q], dP^T[key][q]: lane holds key = 16kt + 4g4 + r, q = l16
         f32x4_t s[4], dp[4];
 #pragma unroll
