@@ -160,7 +160,7 @@ def main():
     log(f"bench: GPT-2 124M bf16 B={B} T={T} accum={accum} steps={args.steps} warmup={args.warmup}")
 
     model = GPT2(cfg, Bnd.GPT2_BF16, B, T)
-    params = S.init_params(cfg)
+    params = {k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}  # bf16-exact start
     model.init(model.pack(params))
     n_micro = (args.warmup + args.steps) * accum
     stream = S.token_stream(n_micro * B * T + 1, cfg.vocab_size, dist="zipf")

@@ -3,9 +3,11 @@ results (tests/golden/*.npz, written by tests/golden/make_golden.py, which
 calls only the oracle), plus size-independent properties.
 
 * GPT-2 124M fp32, B=4 T=64, 10 AdamW steps overfitting one batch (lr 1e-4,
-  wd 0): per-step mean loss rel <= 1e-5; per-step gradient norms rel <= 1e-4;
-  per-step sampled gradients and final sampled parameters rel-L2 <= 1e-4 per
-  tensor; the loss falls.
+  wd 0): per-step mean loss rel <= 1e-5; step-1 gradients (norms and samples)
+  rel <= 1e-4; step-2 gradients rel-L2 <= 1e-4 per full tensor against the
+  oracle evaluated at the GPU's own parameters; trajectory gradients of steps
+  2..10 rel <= 1e-3 (AdamW's eps-region sensitivity, see the test); final
+  sampled parameters rel-L2 <= 1e-4; the loss falls.
 * GPT-2 124M bf16, B=8 T=1024, step 1 of the benchmark workload (2
   micro-steps, AdamW lr 6e-4 wd 0.1): micro-step mean losses abs <= 2e-2;
   sampled gradient cosine >= 0.995 per tensor; sampled update direction
@@ -65,6 +67,7 @@ def _tokens(cfg, n, dev):
 
 def test_gpt2_124m_fp32_ten_steps_one_batch():
     import torch
+    import oracle
     from transformer_lm_step_amd.model import GPT2
 
     g = _golden("gpt2_124m_fp32_overfit10.npz")
@@ -72,10 +75,13 @@ def test_gpt2_124m_fp32_ten_steps_one_batch():
     model = GPT2(cfg, 0, B, T)
     model.init(model.pack(S.init_params(cfg)))
     dev = model.device
-    toks = _tokens(cfg, B * T + 1, dev)
-    x, y = toks[:B * T].clone(), toks[1:].clone()
+    stream = S.token_stream(B * T + 1, cfg.vocab_size, dist="zipf")
+    xb, yb = S.batch(stream, 0, B, T)
+    x = torch.from_numpy(xb.reshape(-1)).to(dev)
+    y = torch.from_numpy(yb.reshape(-1)).to(dev)
     mean = torch.zeros(1, dtype=torch.float32, device=dev)
     for s in range(10):
+        p_before = model.params().cpu().numpy().astype(np.float64) if s == 1 else None
         model.zero_grad()
         model.forward(x, y, None, mean)
         model.backward(1.0 / (B * T))
@@ -86,15 +92,36 @@ def test_gpt2_124m_fp32_ten_steps_one_batch():
         ref = float(g["mean_loss"][s])
         say(f"124M fp32 step {s + 1}: loss {lo:.6f} oracle {ref:.6f}")
         assert abs(lo - ref) / abs(ref) < 1e-5, (s, lo, ref)
-        gn = _norms(model, grads)
-        assert np.all(np.abs(gn - g["grad_norms"][s]) <= 1e-4 * g["grad_norms"][s] + 1e-30), s
         gs = _samples(model, grads, g)
         ref_s = _split(cfg, g, g["grad_samples"][s])
+        # step 1 starts from identical parameters: the kernels' own accuracy.
+        # Later steps follow two trajectories (fp32 on the GPU, fp64 in the
+        # oracle) whose AdamW updates differ wherever |g| is near eps;
+        # tests/golden/adam_eps_sensitivity.py measures 2-3e-5 of step-2
+        # gradient change from fp32-sized gradient noise alone.
+        tol = 1e-4 if s == 0 else 1e-3
+        gn = _norms(model, grads)
+        assert np.all(np.abs(gn - g["grad_norms"][s]) <= tol * g["grad_norms"][s] + 1e-30), s
         for name in S.PARAM_NAMES:
             if np.linalg.norm(ref_s[name]) == 0:
                 assert np.all(gs[name] == 0), (s, name)
             else:
-                assert rel_l2(gs[name], ref_s[name]) < 1e-4, (s, name)
+                assert rel_l2(gs[name], ref_s[name]) < tol, (s, name)
+        if s == 1:
+            # step 2 against the oracle evaluated at the GPU's own parameters
+            r = oracle.gpt2_step(cfg, p_before, xb, yb, dloss=1.0 / (B * T))
+            worst = 0.0
+            for i, name in enumerate(S.PARAM_NAMES):
+                a = grads[model.offsets[i]: model.offsets[i] + model.counts[i]]
+                b = r["grads"][model.offsets[i]: model.offsets[i] + model.counts[i]]
+                if name == "qkvb":
+                    keep = (np.arange(a.size) % (3 * cfg.channels) < cfg.channels) | \
+                           (np.arange(a.size) % (3 * cfg.channels) >= 2 * cfg.channels)
+                    a, b = a[keep], b[keep]
+                e = rel_l2(a, b)
+                worst = max(worst, e)
+                assert e < 1e-4, (name, e)
+            say(f"124M fp32 step 2 at the GPU's parameters: worst full-tensor gradient rel-L2 {worst:.2e}")
     assert model.check() == 0
     ps = _samples(model, model.params().cpu().numpy(), g)
     ref_p = _split(cfg, g, g["param_samples"][-1])
@@ -112,7 +139,7 @@ def test_gpt2_124m_bf16_benchmark_step1():
     g = _golden("gpt2_124m_bf16_step1.npz")
     cfg, B, T, accum = S.GPT2_124M, 8, 1024, 2
     model = GPT2(cfg, 1, B, T)
-    model.init(model.pack(S.init_params(cfg)))
+    model.init(model.pack({k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}))
     dev = model.device
     toks = _tokens(cfg, accum * B * T + 1, dev)
     BT = B * T
@@ -156,7 +183,7 @@ def test_gpt2_1558m_bf16_micro_step_b1t64():
     g = _golden("gpt2_1558m_bf16_b1t64.npz")
     cfg, B, T = S.GPT2_1558M, 1, 64
     model = GPT2(cfg, 1, B, T)
-    model.init(model.pack(S.init_params(cfg)))
+    model.init(model.pack({k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}))
     dev = model.device
     toks = _tokens(cfg, B * T + 1, dev)
     mean = torch.zeros(1, dtype=torch.float32, device=dev)
@@ -189,7 +216,7 @@ def test_gpt2_1558m_bf16_full_size_steps():
 
     cfg, B, T = S.GPT2_1558M, 8, 1024
     model = GPT2(cfg, 1, B, T)
-    model.init(model.pack(S.init_params(cfg)))
+    model.init(model.pack({k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}))
     dev = model.device
     toks = _tokens(cfg, B * T + 1, dev)
     x, y = toks[:B * T].clone(), toks[1:].clone()

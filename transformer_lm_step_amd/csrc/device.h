@@ -188,13 +188,28 @@ DEV void frag_gld(Frag<float>& f, const float* p) { frag_ld(f, p); }
 #define GELU_K0 0.7978845608028654f  // sqrt(2/pi)
 #define GELU_K1 0.044715f
 
+// tanh for the GELU epilogues.  fp32 products use the library tanhf (1 ulp);
+// bf16 products use tanh(u) = 1 - 2 / (exp(2u) + 1) with the hardware exp2
+// and reciprocal, whose absolute error (a few ulp of 1) is far below bf16's
+// resolution, and which saturates to +-1 for large |u|.
+template <typename T>
+DEV float tanh_f(float u) {
+    if constexpr (sizeof(T) == 2) {
+        const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // exp(2u)
+        return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+    } else {
+        return tanhf(u);
+    }
+}
+template <typename T>
 DEV float gelu_f(float x) {
     float u = GELU_K0 * (x + GELU_K1 * x * x * x);
-    return 0.5f * x * (1.0f + tanhf(u));
+    return 0.5f * x * (1.0f + tanh_f<T>(u));
 }
+template <typename T>
 DEV float gelu_grad_f(float x) {
     float u = GELU_K0 * (x + GELU_K1 * x * x * x);
-    float th = tanhf(u);
+    float th = tanh_f<T>(u);
     float sech2 = 1.0f - th * th;  // 1/cosh^2(u)
     return 0.5f * (1.0f + th) + 0.5f * x * sech2 * GELU_K0 * (1.0f + 3.0f * GELU_K1 * x * x);
 }

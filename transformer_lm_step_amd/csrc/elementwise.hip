@@ -267,13 +267,17 @@ __global__ void encoder_bwd_wpe_kernel(float* __restrict__ dwpe, const float* __
 // lse = max + log(sum); loss = lse - z[target]; the row is overwritten in
 // place with softmax - onehot for columns < V and with 0 for the padded
 // columns.  The loss-gradient scale is applied later, by the classifier's
-// backward products.
+// backward products.  Columns >= V are set to -inf in registers right after
+// the load, so every pass treats all elements alike (exp2(-inf) = 0 both in
+// the sum and in the written gradient); exponentials are exp2(z log2(e) - c),
+// one FMA and the hardware exp2 per element.
 template <typename T, int NT, int NV>
-__global__ __launch_bounds__(NT) void classifier_ce_kernel(T* __restrict__ logits, float* __restrict__ losses,
+__global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T* __restrict__ logits, float* __restrict__ losses,
                                                            const int* __restrict__ targets, int V, int Vp,
                                                            int* __restrict__ flag) {
     constexpr int VEC = VecT<T>::N;
     constexpr int NW = NT / 64;
+    constexpr float L2E = 1.4426950408889634f;
     __shared__ float red[NW];
     __shared__ float zt_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -295,9 +299,14 @@ __global__ __launch_bounds__(NT) void classifier_ce_kernel(T* __restrict__ logit
             reg[k] = ld16(z + (long)v * VEC);
             float f[VEC];
             unpack16<T>(reg[k], f);
+            if ((v + 1) * VEC > V) {
 #pragma unroll
-            for (int e = 0; e < VEC; e++)
-                if (v * VEC + e < V) mx = fmaxf(mx, f[e]);
+                for (int e = 0; e < VEC; e++)
+                    if (v * VEC + e >= V) f[e] = -INFINITY;
+                reg[k] = pack16<T>(f);
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; e++) mx = fmaxf(mx, f[e]);
         }
     }
     mx = wave_max(mx);
@@ -306,6 +315,7 @@ __global__ __launch_bounds__(NT) void classifier_ce_kernel(T* __restrict__ logit
     mx = red[0];
 #pragma unroll
     for (int w = 1; w < NW; w++) mx = fmaxf(mx, red[w]);
+    const float mc = -mx * L2E;
     float sm = 0.f;
 #pragma unroll
     for (int k = 0; k < NV; k++) {
@@ -314,8 +324,7 @@ __global__ __launch_bounds__(NT) void classifier_ce_kernel(T* __restrict__ logit
             float f[VEC];
             unpack16<T>(reg[k], f);
 #pragma unroll
-            for (int e = 0; e < VEC; e++)
-                if (v * VEC + e < V) sm += __expf(f[e] - mx);
+            for (int e = 0; e < VEC; e++) sm += __builtin_amdgcn_exp2f(fmaf(f[e], L2E, mc));
         }
     }
     sm = wave_sum(sm);
@@ -327,6 +336,8 @@ __global__ __launch_bounds__(NT) void classifier_ce_kernel(T* __restrict__ logit
     for (int w = 0; w < NW; w++) tot += red[w];
     const float lse = mx + __logf(tot);
     if (tid == 0) losses[row] = lse - zt_s;
+    const float lc = -lse * L2E;
+    const int vt = tgt / VEC;
 #pragma unroll
     for (int k = 0; k < NV; k++) {
         const int v = tid + NT * k;
@@ -334,9 +345,11 @@ __global__ __launch_bounds__(NT) void classifier_ce_kernel(T* __restrict__ logit
             float f[VEC];
             unpack16<T>(reg[k], f);
 #pragma unroll
-            for (int e = 0; e < VEC; e++) {
-                const int col = v * VEC + e;
-                f[e] = col < V ? __expf(f[e] - lse) - (col == tgt ? 1.0f : 0.0f) : 0.0f;
+            for (int e = 0; e < VEC; e++) f[e] = __builtin_amdgcn_exp2f(fmaf(f[e], L2E, lc));
+            if (v == vt) {
+#pragma unroll
+                for (int e = 0; e < VEC; e++)
+                    if (v * VEC + e == tgt) f[e] -= 1.0f;
             }
             st16(z + (long)v * VEC, pack16<T>(f));
         }
@@ -492,7 +505,7 @@ template <typename T>
 int classifier_ce_launch(T* logits, float* losses, const int* targets, int N, int V, int Vp, int* flag, hipStream_t s) {
     if (N == 0) return 0;
     if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((classifier_ce_kernel<T, 256, 26>), dim3(N), dim3(256), 0, s, logits, losses, targets, V, Vp, flag);
+        hipLaunchKernelGGL((classifier_ce_kernel<T, 512, 13>), dim3(N), dim3(512), 0, s, logits, losses, targets, V, Vp, flag);
     } else {
         hipLaunchKernelGGL((classifier_ce_kernel<T, 1024, 13>), dim3(N), dim3(1024), 0, s, logits, losses, targets, V, Vp, flag);
     }

@@ -364,7 +364,7 @@ __global__ __launch_bounds__((Tile<T, BM, BN, WT>::NT), (Tile<T, BM, BN, WT>::OC
                 if (ok) load4<T>((const T*)g.bias + n, bb);
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    v[j][r] = gelu_f(g.alpha * acc[i][j][r] + bb[r]);
+                    v[j][r] = gelu_f<T>(g.alpha * acc[i][j][r] + bb[r]);
                     if (ok) mx = fmaxf(mx, v[j][r]);
                 }
                 if (ok && m < g.M) store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v[j]);
@@ -417,7 +417,7 @@ __global__ __launch_bounds__((Tile<T, BM, BN, WT>::NT), (Tile<T, BM, BN, WT>::OC
                     float pr[4];
                     load4<T>(pre, pr);  // GELU of the stored (rounded) pre-activation
 #pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] = gelu_f(pr[r]);
+                    for (int r = 0; r < 4; r++) v[r] = gelu_f<T>(pr[r]);
                 }
                 if constexpr (EPI == GEMM_BIAS_RESID) {
                     float res[4];
@@ -429,7 +429,7 @@ __global__ __launch_bounds__((Tile<T, BM, BN, WT>::NT), (Tile<T, BM, BN, WT>::OC
                     float pr[4];
                     load4<T>((const T*)g.aux_in + (size_t)m * g.ldaux + n, pr);
 #pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] *= gelu_grad_f(pr[r]);
+                    for (int r = 0; r < 4; r++) v[r] *= gelu_grad_f<T>(pr[r]);
                 }
                 store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v);
             }
@@ -487,7 +487,12 @@ const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {1.00, 0.79, 0.79}},
                             {256, 128, 64, 1, {0.81, 0.70, 0.66}},
                             {128, 256, 64, 1, {0.80, 0.90, 0.68}},
                             {128, 128, 64, 2, {0.87, 0.70, 0.70}},
-                            {256, 256, 128, 1, {0.96, 1.00, 1.00}}};
+                            {256, 256, 128, 1, {0.96, 1.00, 1.00}},
+#ifdef GEMM_ONLY_TILE_BM
+                            {256, 128, 128, 1, {1.0, 1.0, 1.0}},
+                            {128, 256, 128, 1, {1.0, 1.0, 1.0}},
+#endif
+};
 constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
 const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}}};
 
@@ -589,6 +594,10 @@ int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, i
     if constexpr (sizeof(T) == 2) {
         if (ch.wt == 128) {
             if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 128>(d, a, grid, epi, s);
+#ifdef GEMM_ONLY_TILE_BM
+            if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 128>(d, a, grid, epi, s);
+            if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 128>(d, a, grid, epi, s);
+#endif
             return (int)hipErrorInvalidValue;
         }
         if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, epi, s);

@@ -22,15 +22,18 @@
 
 namespace {
 
-constexpr int ROWS_PER_BLOCK_BWD = 32;
-template <typename T> struct LnCfg { static constexpr int NV = (sizeof(T) == 2) ? 4 : 8; };  // C <= 2048
+// 8 rows per backward workgroup (2 per wave): enough workgroups to keep
+// several waves per SIMD in flight on 8192 rows.
+constexpr int ROWS_PER_BLOCK_BWD = 8;
 
-template <typename T>
+// NV: 16-byte vectors per lane, ceil(C / (64 * VEC)), fixed at launch so the
+// row buffers take only the registers C needs.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out, float* __restrict__ mean,
                                                      float* __restrict__ rstd, const T* __restrict__ x,
                                                      const T* __restrict__ w, const T* __restrict__ b,
                                                      int N, int C) {
-    constexpr int VEC = VecT<T>::N, NV = LnCfg<T>::NV;
+    constexpr int VEC = VecT<T>::N;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= N) return;
@@ -80,13 +83,13 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out, float*
     }
 }
 
-template <typename T>
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T* __restrict__ dres_lp,
                                                      float* __restrict__ partial, const T* __restrict__ dy,
                                                      const T* __restrict__ x, const T* __restrict__ w,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
                                                      int N, int C, int accumulate) {
-    constexpr int VEC = VecT<T>::N, NV = LnCfg<T>::NV;
+    constexpr int VEC = VecT<T>::N;
     __shared__ float red[2 * 2048];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nvec = C / VEC;
@@ -181,22 +184,26 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T
 }
 
 // dw[c] += sum_blocks partial[blk][c]; db[c] += sum_blocks partial[blk][C + c].
-// 64 columns per workgroup, 4 phases of blocks per column (block k goes to
-// phase k % 4), phases combined in order 0..3 through LDS.
-__global__ __launch_bounds__(256) void ln_bwd_finish_kernel(float* __restrict__ dw, float* __restrict__ db,
-                                                            const float* __restrict__ partial, int C, int blocks) {
-    __shared__ float red[4][64];
+// 64 columns per workgroup, 16 phases of blocks per column (block k goes to
+// phase k % 16), phases combined in order 0..15 through LDS.
+constexpr int FIN_PH = 16;
+__global__ __launch_bounds__(64 * FIN_PH) void ln_bwd_finish_kernel(float* __restrict__ dw, float* __restrict__ db,
+                                                                    const float* __restrict__ partial, int C,
+                                                                    int blocks) {
+    __shared__ float red[FIN_PH][64];
     const int col = threadIdx.x & 63, ph = threadIdx.x >> 6;
     const int j = blockIdx.x * 64 + col;
     float s = 0.f;
     if (j < 2 * C) {
 #pragma unroll 4
-        for (int k = ph; k < blocks; k += 4) s += partial[(size_t)k * 2 * C + j];
+        for (int k = ph; k < blocks; k += FIN_PH) s += partial[(size_t)k * 2 * C + j];
     }
     red[ph][col] = s;
     __syncthreads();
     if (ph == 0 && j < 2 * C) {
-        const float t = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+        float t = red[0][col];
+#pragma unroll
+        for (int q = 1; q < FIN_PH; q++) t += red[q][col];
         if (j < C) dw[j] += t;
         else db[j - C] += t;
     }
@@ -204,16 +211,39 @@ __global__ __launch_bounds__(256) void ln_bwd_finish_kernel(float* __restrict__ 
 
 }  // namespace
 
+template <typename T, int NV>
+void ln_fwd_nv(T* out, float* mean, float* rstd, const T* x, const T* w, const T* b, int N, int C, hipStream_t s) {
+    hipLaunchKernelGGL((ln_fwd_kernel<T, NV>), dim3((N + 3) / 4), dim3(256), 0, s, out, mean, rstd, x, w, b, N, C);
+}
+
 template <typename T>
 int layernorm_fwd_launch(T* out, float* mean, float* rstd, const T* x, const T* w, const T* b,
                          int N, int C, hipStream_t s) {
     if (N <= 0) return 0;
-    hipLaunchKernelGGL(ln_fwd_kernel<T>, dim3((N + 3) / 4), dim3(256), 0, s, out, mean, rstd, x, w, b, N, C);
+    const int nv = (C / VecT<T>::N + 63) / 64;
+    switch (nv) {
+        case 1: ln_fwd_nv<T, 1>(out, mean, rstd, x, w, b, N, C, s); break;
+        case 2: ln_fwd_nv<T, 2>(out, mean, rstd, x, w, b, N, C, s); break;
+        case 3: ln_fwd_nv<T, 3>(out, mean, rstd, x, w, b, N, C, s); break;
+        case 4: ln_fwd_nv<T, 4>(out, mean, rstd, x, w, b, N, C, s); break;
+        default:
+            if constexpr (sizeof(T) == 4) {
+                if (nv <= 8) { ln_fwd_nv<T, 8>(out, mean, rstd, x, w, b, N, C, s); break; }
+            }
+            return (int)hipErrorInvalidValue;
+    }
     return (int)hipGetLastError();
 }
 
 size_t layernorm_bwd_workspace_bytes(int N, int C) {
     return (size_t)((N + ROWS_PER_BLOCK_BWD - 1) / ROWS_PER_BLOCK_BWD) * 2 * C * sizeof(float);
+}
+
+template <typename T, int NV>
+void ln_bwd_nv(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean, const float* rstd,
+               int N, int C, int accumulate, float* partial, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(blocks), dim3(256), 0, s, dres, dres_lp, partial, dy, x, w,
+                       mean, rstd, N, C, accumulate);
 }
 
 template <typename T>
@@ -222,9 +252,23 @@ int layernorm_bwd_launch(float* dres, T* dres_lp, float* dw, float* db, const T*
                          int accumulate, float* partial, hipStream_t s) {
     if (N <= 0) return 0;
     const int blocks = (N + ROWS_PER_BLOCK_BWD - 1) / ROWS_PER_BLOCK_BWD;
-    hipLaunchKernelGGL(ln_bwd_kernel<T>, dim3(blocks), dim3(256), 0, s, dres, dres_lp, partial, dy, x, w,
-                       mean, rstd, N, C, accumulate);
-    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + 63) / 64), dim3(256), 0, s, dw, db, partial, C, blocks);
+    const int nv = (C / VecT<T>::N + 63) / 64;
+    switch (nv) {
+        case 1: ln_bwd_nv<T, 1>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
+        case 2: ln_bwd_nv<T, 2>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
+        case 3: ln_bwd_nv<T, 3>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
+        case 4: ln_bwd_nv<T, 4>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
+        default:
+            if constexpr (sizeof(T) == 4) {
+                if (nv <= 8) {
+                    ln_bwd_nv<T, 8>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s);
+                    break;
+                }
+            }
+            return (int)hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + 63) / 64), dim3(64 * FIN_PH), 0, s, dw, db, partial, C,
+                       blocks);
     return (int)hipGetLastError();
 }
 
