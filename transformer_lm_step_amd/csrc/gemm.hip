@@ -173,6 +173,105 @@ DEV void slab_store(const uint4* r, T* __restrict__ s, int tid) {
     }
 }
 
+// Epilogue of one workgroup tile: lane holds C[m][n .. n+3] for its
+// TM x TN 16x16 MFMA tiles.
+template <typename T, typename TL, int EPI, typename OutT>
+DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int m0, int n0, int wm, int wn, int l16,
+                       int g4) {
+    constexpr int TM = TL::TM, TN = TL::TN;
+    if constexpr (EPI == GEMM_BIAS_GELU_SMX) {
+        // G = gelu(v + bias) stored, plus (max, sum exp(G - max)) of each row
+        // over this wave's 64 columns; a row's 64 values sit in the 4 lanes
+        // l16 + 16 g (4 tiles x 4 values each), combined with two shuffles.
+        static_assert(TL::WTN == 64, "partials are per 64 columns");
+        const int nw = n0 + wn * 64;
+        float2* part = (float2*)g.aux_out;
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+            const int m = m0 + wm * TL::WTM + 16 * i + l16;
+            float v[TN][4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int n = nw + 16 * j + 4 * g4;
+                const bool ok = n < g.N;
+                float bb[4] = {0.f, 0.f, 0.f, 0.f};
+                if (ok) load4<T>((const T*)g.bias + n, bb);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    v[j][r] = gelu_f<T>(g.alpha * acc[i][j][r] + bb[r]);
+                    if (ok) mx = fmaxf(mx, v[j][r]);
+                }
+                if (ok && m < g.M) store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v[j]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            float sm = 0.f;
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                if (nw + 16 * j + 4 * g4 < g.N)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) sm += expf(v[j][r] - mx);
+            sm += __shfl_xor(sm, 16, 64);
+            sm += __shfl_xor(sm, 32, 64);
+            if (g4 == 0 && m < g.M && nw < g.N) part[(size_t)m * g.ldaux + nw / 64] = make_float2(mx, sm);
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const int m = m0 + wm * TL::WTM + 16 * i + l16;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int n = n0 + wn * TL::WTN + 16 * j + 4 * g4;
+            if (n >= g.N) continue;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) v[r] = g.alpha * acc[i][j][r];
+            if constexpr (EPI == EPI_SPLIT) {
+                float* w = g.ws + (size_t)blockIdx.y * g.M * g.N + (size_t)m * g.N + n;
+                store4<float>(w, v);
+            } else if constexpr (EPI == GEMM_ACCUM) {
+                float* c = (float*)g.C + (size_t)m * g.ldc + n;
+                float o[4];
+                load4<float>(c, o);
+#pragma unroll
+                for (int r = 0; r < 4; r++) o[r] += v[r];
+                store4<float>(c, o);
+            } else {
+                if constexpr (EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU || EPI == GEMM_BIAS_RESID) {
+                    float bb[4];
+                    load4<T>((const T*)g.bias + n, bb);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) v[r] += bb[r];
+                }
+                if constexpr (EPI == GEMM_BIAS_GELU) {
+                    T* pre = (T*)g.aux_out + (size_t)m * g.ldaux + n;
+                    store4<T>(pre, v);
+                    float pr[4];
+                    load4<T>(pre, pr);  // GELU of the stored (rounded) pre-activation
+#pragma unroll
+                    for (int r = 0; r < 4; r++) v[r] = gelu_f<T>(pr[r]);
+                }
+                if constexpr (EPI == GEMM_BIAS_RESID) {
+                    float res[4];
+                    load4<T>((const T*)g.aux_in + (size_t)m * g.ldaux + n, res);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) v[r] += res[r];
+                }
+                if constexpr (EPI == GEMM_GELU_BWD) {
+                    float pr[4];
+                    load4<T>((const T*)g.aux_in + (size_t)m * g.ldaux + n, pr);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) v[r] *= gelu_grad_f<T>(pr[r]);
+                }
+                store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v);
+            }
+        }
+    }
+}
+
 template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
 __global__ __launch_bounds__((Tile<T, BM, BN, WT>::NT), (Tile<T, BM, BN, WT>::OCC)) void gemm_kernel(const Args g) {
     using TL = Tile<T, BM, BN, WT>;
@@ -343,98 +442,260 @@ __global__ __launch_bounds__((Tile<T, BM, BN, WT>::NT), (Tile<T, BM, BN, WT>::OC
         }
     }
 
-    // ---- epilogue: lane holds C[m][n .. n+3]
-    if constexpr (EPI == GEMM_BIAS_GELU_SMX) {
-        // G = gelu(v + bias) stored, plus (max, sum exp(G - max)) of each row
-        // over this wave's 64 columns; a row's 64 values sit in the 4 lanes
-        // l16 + 16 g (4 tiles x 4 values each), combined with two shuffles.
-        static_assert(TL::WTN == 64, "partials are per 64 columns");
-        const int nw = n0 + wn * 64;
-        float2* part = (float2*)g.aux_out;
+    gemm_epilogue<T, TL, EPI, OutT>(g, acc, m0, n0, wm, wn, l16, g4);
+}
+
+// ------------------------------------------------------------ direct to LDS --
+// bf16 products whose operand slabs go from global memory straight into LDS
+// (buffer loads with the LDS-destination bit): no staging registers, no LDS
+// store instructions, and no wait on a load until the barrier before the
+// stage that consumes it.  Each wave's 16-byte lane loads fill 1 KB of LDS
+// contiguously (lane i -> base + 16 i), so the LDS layout is chosen by which
+// global element each lane fetches:
+//  - a k-contiguous slab (R rows x 64 contraction elements) keeps rows of 128
+//    bytes with the 16-byte chunk c of row r stored at chunk c ^ (r & 7), so
+//    the fragment reads of 8 consecutive rows hit 8 different bank groups;
+//  - a k-strided slab (rows of the operand contiguous in memory) is stored as
+//    64 contraction rows of R elements, its 32-byte unit u of contraction row
+//    k at unit u ^ f(k), and fragments are read with the LDS transpose load
+//    (ds_read_b64_tr_b16: within 16 lanes, lane l gets element l%16 of four
+//    consecutive rows), two per fragment, which gives lane (row, group g) the
+//    contraction indices 8g..8g+7 -- the same slots as the k-contiguous read,
+//    so both layouts feed the same MFMA code.
+// Two stages in separate LDS arrays: loads for stage kt+1 are issued right
+// after the barrier that opens stage kt and waited for at the next one.
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+DEV constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+template <int R>
+DEV int dtl_fk(int k) {  // unit swizzle of contraction row k in a k-strided slab
+    return ((k & 3) | (((k >> 3) & 3) << 2)) & (R / 16 - 1);
+}
+
+template <int R_, bool KMAJ_, int NW_>
+struct DtlSlab {
+    static constexpr int R = R_, NW = NW_;
+    static constexpr bool KMAJ = KMAJ_;
+    static constexpr int NQ = R / 8 / NW;  // 1 KB load instructions per wave per stage
+    static_assert(NQ >= 1 && (R / 8) % NW == 0, "slab rows must split evenly over the waves");
+    uint32_t off[NQ];  // per-lane byte offset from the slab origin in global memory
+    int kc[KMAJ ? NQ : 1];
+    DEV void init(long ld, int lane, int wave) {
 #pragma unroll
-        for (int i = 0; i < TM; i++) {
-            const int m = m0 + wm * TL::WTM + 16 * i + l16;
-            float v[TN][4];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const int n = nw + 16 * j + 4 * g4;
-                const bool ok = n < g.N;
-                float bb[4] = {0.f, 0.f, 0.f, 0.f};
-                if (ok) load4<T>((const T*)g.bias + n, bb);
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    v[j][r] = gelu_f<T>(g.alpha * acc[i][j][r] + bb[r]);
-                    if (ok) mx = fmaxf(mx, v[j][r]);
-                }
-                if (ok && m < g.M) store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v[j]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            float sm = 0.f;
-#pragma unroll
-            for (int j = 0; j < TN; j++)
-                if (nw + 16 * j + 4 * g4 < g.N)
-#pragma unroll
-                    for (int r = 0; r < 4; r++) sm += expf(v[j][r] - mx);
-            sm += __shfl_xor(sm, 16, 64);
-            sm += __shfl_xor(sm, 32, 64);
-            if (g4 == 0 && m < g.M && nw < g.N) part[(size_t)m * g.ldaux + nw / 64] = make_float2(mx, sm);
-        }
-        return;
-    }
-#pragma unroll
-    for (int i = 0; i < TM; i++) {
-        const int m = m0 + wm * TL::WTM + 16 * i + l16;
-        if (m >= g.M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; j++) {
-            const int n = n0 + wn * TL::WTN + 16 * j + 4 * g4;
-            if (n >= g.N) continue;
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) v[r] = g.alpha * acc[i][j][r];
-            if constexpr (EPI == EPI_SPLIT) {
-                float* w = g.ws + (size_t)blockIdx.y * g.M * g.N + (size_t)m * g.N + n;
-                store4<float>(w, v);
-            } else if constexpr (EPI == GEMM_ACCUM) {
-                float* c = (float*)g.C + (size_t)m * g.ldc + n;
-                float o[4];
-                load4<float>(c, o);
-#pragma unroll
-                for (int r = 0; r < 4; r++) o[r] += v[r];
-                store4<float>(c, o);
+        for (int q = 0; q < NQ; q++) {
+            const int j = wave + NW * q;  // which 1 KB of the slab
+            if constexpr (KMAJ) {
+                const int r = 8 * j + (lane >> 3);
+                const int c = (lane & 7) ^ (lane >> 3);
+                kc[q] = 8 * c;
+                off[q] = (uint32_t)(((long)r * ld + 8 * c) * 2);
             } else {
-                if constexpr (EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU || EPI == GEMM_BIAS_RESID) {
-                    float bb[4];
-                    load4<T>((const T*)g.bias + n, bb);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] += bb[r];
-                }
-                if constexpr (EPI == GEMM_BIAS_GELU) {
-                    T* pre = (T*)g.aux_out + (size_t)m * g.ldaux + n;
-                    store4<T>(pre, v);
-                    float pr[4];
-                    load4<T>(pre, pr);  // GELU of the stored (rounded) pre-activation
-#pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] = gelu_f<T>(pr[r]);
-                }
-                if constexpr (EPI == GEMM_BIAS_RESID) {
-                    float res[4];
-                    load4<T>((const T*)g.aux_in + (size_t)m * g.ldaux + n, res);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] += res[r];
-                }
-                if constexpr (EPI == GEMM_GELU_BWD) {
-                    float pr[4];
-                    load4<T>((const T*)g.aux_in + (size_t)m * g.ldaux + n, pr);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] *= gelu_grad_f<T>(pr[r]);
-                }
-                store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v);
+                constexpr int KPI = 512 / R;  // contraction rows per 1 KB
+                const int p = 16 * lane;
+                const int k = j * KPI + p / (2 * R);
+                const int b = p % (2 * R);
+                const int u = (b >> 5) ^ dtl_fk<R>(k);
+                const int r = 16 * u + 8 * ((b >> 4) & 1);
+                off[q] = (uint32_t)(((long)k * ld + r) * 2);
             }
         }
     }
+};
+
+// Issue this wave's loads of the slab at (rows r0.., contraction k0..) into dst
+// (per-lane offsets and, k-contiguous, contraction indices from DtlSlab).
+template <int R, bool KMAJ, int NW>
+DEV void dtl_issue(const uint32_t* off, const int* kc, bf16_t* dst, const bf16_t* __restrict__ p, long ld, int r0,
+                   int Rmax, int k0, int K, int wave) {
+    constexpr int NQ = R / 8 / NW;
+    if constexpr (KMAJ) {
+        const long org = (long)r0 * ld + k0;
+        const uint32_t bytes = (uint32_t)max(0L, ((long)Rmax * ld - org) * 2);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p + org, bytes);
+        const int klim = K - k0;
+#pragma unroll
+        for (int q = 0; q < NQ; q++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (wave + NW * q) * 512), 16,
+                                                     kc[q] < klim ? off[q] : kBufOOB, 0, 0, 0);
+    } else {
+        const long org = (long)k0 * ld + r0;
+        const uint32_t bytes = (uint32_t)max(0L, ((long)K * ld - org) * 2);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p + org, bytes);
+#pragma unroll
+        for (int q = 0; q < NQ; q++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (wave + NW * q) * 512), 16, off[q], 0, 0,
+                                                     0);
+    }
+}
+
+// Per-lane element offsets of the fragment reads of one operand: KT tiles of 16
+// rows starting at wave row wb, both 32-deep MFMA steps of a stage.
+template <int R, bool KMAJ, int KT>
+struct DtlFrag {
+    int ofs[KT][2];  // [tile][step] (k-strided: the first of the two transpose reads)
+    DEV void init(int wb, int l16, int g4) {
+#pragma unroll
+        for (int t = 0; t < KT; t++) {
+            const int rb = wb + 16 * t;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                if constexpr (KMAJ) {
+                    ofs[t][ks] = (rb + l16) * 64 + (((4 * ks + g4) ^ (l16 & 7)) << 3);
+                } else {
+                    const int fk = ((l16 >> 2) | (g4 << 2)) & (R / 16 - 1);  // dtl_fk of every row read here
+                    const int k = 32 * ks + 8 * g4 + (l16 >> 2);
+                    ofs[t][ks] = k * R + ((((rb >> 4) ^ fk)) << 4) + 4 * (l16 & 3);
+                }
+            }
+        }
+    }
+};
+
+template <int R, bool KMAJ>
+DEV void dtl_frag_ld(Frag<bf16_t>& f, const bf16_t* s, int ofs) {
+    if constexpr (KMAJ) {
+        frag_ld(f, s + ofs);
+    } else {
+        const v4s_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(s + ofs));
+        const v4s_t b =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(s + ofs + 4 * R));
+        typedef short v8s_t __attribute__((ext_vector_type(8)));
+        const v8s_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+        f.v = __builtin_bit_cast(bf16x8_t, ab);
+    }
+}
+
+template <int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
+__global__ __launch_bounds__((Tile<bf16_t, BM, BN, WT>::NT), (Tile<bf16_t, BM, BN, WT>::OCC)) void
+gemm_dtl_kernel(const Args g) {
+    using T = bf16_t;
+    using TL = Tile<T, BM, BN, WT>;
+    constexpr int TM = TL::TM, TN = TL::TN, NT = TL::NT, NW = NT / 64, BK = 64;
+    static_assert(!BIAS || !AK, "the fused bias sum reads a k-strided A slab");
+    __shared__ __attribute__((aligned(1024))) T sA0[BM * BK];
+    __shared__ __attribute__((aligned(1024))) T sA1[BM * BK];
+    __shared__ __attribute__((aligned(1024))) T sB0[BN * BK];
+    __shared__ __attribute__((aligned(1024))) T sB1[BN * BK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % TL::WM, wn = wave / TL::WM;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    const int nb = gridDim.x;
+    int b = blockIdx.x;
+    const int full = (nb / 8) * 8;
+    if (b < full) b = (b % 8) * (nb / 8) + (b / 8);
+    const int GM = 8;
+    const int in_group = GM * tiles_n;
+    const int group = b / in_group;
+    const int first_m = group * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int tm = first_m + ((b % in_group) % gsz);
+    const int tn = (b % in_group) / gsz;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int ktiles = (g.K + BK - 1) / BK;
+    const int kt0 = blockIdx.y * g.kps;
+    const int kt1 = min(kt0 + g.kps, ktiles);
+    const T* __restrict__ A = (const T*)g.A;
+    const T* __restrict__ B = (const T*)g.B;
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    DtlSlab<BM, AK, TL::NT / 64> dA;
+    DtlSlab<BN, BKM, TL::NT / 64> dB;
+    dA.init(g.lda, lane, wave);
+    dB.init(g.ldb, lane, wave);
+    DtlFrag<BM, AK, TM> fA;
+    DtlFrag<BN, BKM, TN> fB;
+    fA.init(wm * TL::WTM, l16, g4);
+    fB.init(wn * TL::WTN, l16, g4);
+
+    // fused bias gradient: column sums over k of the k-strided A slab
+    constexpr int MQ = BM / 4, KG = NT / MQ, KPG = BK / KG;
+    const int bq = tid % MQ, bkg = tid / MQ;
+    float bs[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool do_bias = BIAS && tn == 0;
+
+    auto compute = [&](const T* a_s, const T* b_s) {
+        Frag<T> fa[2][TM], fb[2][TN];
+#pragma unroll
+        for (int t = 0; t < TN; t++) dtl_frag_ld<BN, BKM>(fb[0][t], b_s, fB.ofs[t][0]);
+#pragma unroll
+        for (int t = 0; t < TM; t++) dtl_frag_ld<BM, AK>(fa[0][t], a_s, fA.ofs[t][0]);
+#pragma unroll
+        for (int t = 0; t < TN; t++) dtl_frag_ld<BN, BKM>(fb[1][t], b_s, fB.ofs[t][1]);
+#pragma unroll
+        for (int t = 0; t < TM; t++) dtl_frag_ld<BM, AK>(fa[1][t], a_s, fA.ofs[t][1]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) mma(acc[i][j], fb[ks][j], fa[ks][i]);
+        if constexpr (BIAS) {
+#pragma unroll
+            for (int i = 0; i < KPG; i++) {
+                const int k = bkg * KPG + i;
+                const int m = 4 * bq;
+                const uint2 v = *reinterpret_cast<const uint2*>(
+                    a_s + k * BM + ((((m >> 4) ^ dtl_fk<BM>(k))) << 4) + (m & 15));
+                bs[0] += __uint_as_float(v.x << 16);
+                bs[1] += __uint_as_float(v.x & 0xffff0000u);
+                bs[2] += __uint_as_float(v.y << 16);
+                bs[3] += __uint_as_float(v.y & 0xffff0000u);
+            }
+        }
+    };
+
+    if (kt0 < kt1) {
+        dtl_issue<BM, AK, TL::NT / 64>(dA.off, dA.kc, sA0, A, g.lda, m0, g.M, kt0 * BK, g.K, wave);
+        dtl_issue<BN, BKM, TL::NT / 64>(dB.off, dB.kc, sB0, B, g.ldb, n0, g.N, kt0 * BK, g.K, wave);
+    }
+    for (int kt = kt0; kt < kt1; kt += 2) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (kt + 1 < kt1) {
+            dtl_issue<BM, AK, TL::NT / 64>(dA.off, dA.kc, sA1, A, g.lda, m0, g.M, (kt + 1) * BK, g.K, wave);
+            dtl_issue<BN, BKM, TL::NT / 64>(dB.off, dB.kc, sB1, B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, wave);
+        }
+        compute(sA0, sB0);
+        if (kt + 1 < kt1) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();
+            if (kt + 2 < kt1) {
+                dtl_issue<BM, AK, TL::NT / 64>(dA.off, dA.kc, sA0, A, g.lda, m0, g.M, (kt + 2) * BK, g.K, wave);
+                dtl_issue<BN, BKM, TL::NT / 64>(dB.off, dB.kc, sB0, B, g.ldb, n0, g.N, (kt + 2) * BK, g.K, wave);
+            }
+            compute(sA1, sB1);
+        }
+    }
+
+    if constexpr (BIAS) {
+        __syncthreads();  // every wave is done with the stage buffers
+        float* red = reinterpret_cast<float*>(sA0);  // KG x BM floats (<= BM * BK bf16)
+#pragma unroll
+        for (int e = 0; e < 4; e++) red[bkg * BM + 4 * bq + e] = bs[e];
+        __syncthreads();
+        if (do_bias && tid < BM) {
+            float t = 0.f;
+            for (int q = 0; q < KG; q++) t += red[q * BM + tid];
+            const int m = m0 + tid;
+            if (m < g.M) {
+                if constexpr (EPI == EPI_SPLIT) g.wsb[(size_t)blockIdx.y * g.M + m] = g.alpha * t;
+                else g.dbias[m] += g.alpha * t;
+            }
+        }
+    }
+    gemm_epilogue<T, TL, EPI, OutT>(g, acc, m0, n0, wm, wn, l16, g4);
 }
 
 // C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0)
@@ -542,10 +803,17 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     return best;
 }
 
+#ifndef GEMM_DTL
+#define GEMM_DTL 1
+#endif
+
 template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS = false>
 void launch_t(const Args& a, dim3 grid, hipStream_t s) {
     using TL = Tile<T, BM, BN, WT>;
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
+    if constexpr (sizeof(T) == 2 && GEMM_DTL)
+        hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
 }
 
 // Instantiated (layout, epilogue) pairs: forward products (A and B
