@@ -49,7 +49,28 @@ struct ACfg {
     static constexpr int RP = KD + 16 / (int)sizeof(T);  // pitch of row x d tiles
     static constexpr int TP = 64 + 16 / (int)sizeof(T);  // pitch of d x row tiles
     static constexpr int VEC = VecT<T>::N;
+    // bf16: operands needed as d x row (V^T, K^T, Q^T, dO^T) are read from the
+    // row x d tiles with the LDS transpose load instead of being staged twice
+    static constexpr bool TR = sizeof(T) == 2;
+    static constexpr int VP = HS + 16;  // pitch of the forward's V tile: HS values + 16 ones
 };
+
+// A 16-row x 32-contraction MFMA fragment of X^T from a row-major LDS tile
+// X[row][d] (8-byte aligned rows): slots 0..3 are rows k0..k0+3 and slots 4..7
+// rows k1..k1+3 of column d0 + l16.  ds_read_b64_tr_b16: within each group of
+// 16 lanes, lane l receives element l of the four 4-element pieces read by
+// lanes 4j..4j+3 (j = 0..3), so lane s reads row k + s/4, columns 4(s%4)...
+DEV void frag_tr(Frag<bf16_t>& f, const bf16_t* tile, int pitch, int k0, int k1, int d0, int l16) {
+    typedef short v4s_t __attribute__((ext_vector_type(4)));
+    typedef short v8s_t __attribute__((ext_vector_type(8)));
+    const int col = d0 + 4 * (l16 & 3);
+    const v4s_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s_t*)(tile + (k0 + (l16 >> 2)) * pitch + col));
+    const v4s_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s_t*)(tile + (k1 + (l16 >> 2)) * pitch + col));
+    const v8s_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.v = __builtin_bit_cast(bf16x8_t, ab);
+}
 
 // This lane's row (global index `row`) of a head slice as DSTEPS fragments over d.
 template <typename T, int HS>
@@ -65,11 +86,13 @@ DEV void row_frags(Frag<T>* f, const T* src, long rs, int row, int T_, int g4) {
 // Register-staged copies of the same two layouts, split into a load (issued
 // one block ahead, so its latency hides behind the current block's MFMAs) and
 // an LDS store.  FULL: rows row0..row0+63 are all < T (no row check).
-template <typename T, int HS>
+// COLS columns (zero past HS) of 64 rows into an LDS tile of pitch PITCH.
+template <typename T, int HS, int COLS = ACfg<T, HS>::KD, int PITCH = ACfg<T, HS>::RP>
 struct RowsStage {
     using A = ACfg<T, HS>;
-    static constexpr int VPR = A::KD / A::VEC;
-    static constexpr int N = 64 * VPR / 256;  // 64 * VPR is a multiple of 256 for every HS
+    static constexpr int VPR = COLS / A::VEC;
+    static constexpr int ITEMS = 64 * VPR;
+    static constexpr int N = (ITEMS + 255) / 256;
     uint4 r[N];
     template <bool FULL>
     DEV void load(const T* src, long rs, int row0, int T_, int tid) {
@@ -78,14 +101,16 @@ struct RowsStage {
             const int idx = tid + 256 * i;
             const int row = idx / VPR, d0 = (idx % VPR) * A::VEC;
             const int gr = row0 + row;
-            r[i] = ((FULL || gr < T_) && d0 < HS) ? ld16(src + (long)gr * rs + d0) : make_uint4(0, 0, 0, 0);
+            r[i] = ((ITEMS % 256 == 0 || idx < ITEMS) && (FULL || gr < T_) && d0 < HS)
+                       ? ld16(src + (long)gr * rs + d0)
+                       : make_uint4(0, 0, 0, 0);
         }
     }
     DEV void store(T* dst, int tid) const {
 #pragma unroll
         for (int i = 0; i < N; i++) {
             const int idx = tid + 256 * i;
-            st16(dst + (idx / VPR) * A::RP + (idx % VPR) * A::VEC, r[i]);
+            if (ITEMS % 256 == 0 || idx < ITEMS) st16(dst + (idx / VPR) * PITCH + (idx % VPR) * A::VEC, r[i]);
         }
     }
 };
@@ -135,7 +160,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
     using A = ACfg<T, HS>;
     constexpr int DT1 = A::DT + 1;  // output tiles incl. the row-sum tile
     __shared__ __attribute__((aligned(16))) T sK[64 * A::RP];
-    __shared__ __attribute__((aligned(16))) T sVt[(HS + 16) * A::TP];
+    // V as d x key (transposed staging) or, bf16, as key x d with 16 columns of ones
+    __shared__ __attribute__((aligned(16))) T sVt[A::TR ? 64 * A::VP : (HS + 16) * A::TP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int qb = gridDim.x - 1 - blockIdx.x;
@@ -147,7 +173,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
     const int q = qb * 64 + wave * 16 + l16;
 
     // the ones rows of the extended V^T (written once)
-    for (int i = tid; i < 16 * 64; i += 256) sVt[(HS + i / 64) * A::TP + (i % 64)] = from_f<T>(1.0f);
+    for (int i = tid; i < 16 * 64; i += 256) {
+        if constexpr (A::TR) sVt[(i / 16) * A::VP + HS + (i % 16)] = from_f<T>(1.0f);
+        else sVt[(HS + i / 64) * A::TP + (i % 64)] = from_f<T>(1.0f);
+    }
 
     Frag<T> fq[A::DSTEPS];
     row_frags<T, HS>(fq, Qh, rs, q, T_, g4);
@@ -158,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
     for (int dt = 0; dt < DT1; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     RowsStage<T, HS> pk;
-    RowsTStage<T, HS> pv;
+    std::conditional_t<A::TR, RowsStage<T, HS, HS, A::VP>, RowsTStage<T, HS>> pv;
     auto prefetch = [&](int kb) {
         if (kb < qb) {
             pk.template load<true>(Kh, rs, kb * 64, T_, tid);
@@ -221,9 +250,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
             frag_from(fp, pv);
 #pragma unroll
             for (int dt = 0; dt < DT1; dt++) {
-                const T* vr = sVt + (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
                 Frag<T> fv;
-                frag_ld2(fv, vr, vr + 16);
+                if constexpr (A::TR) {
+                    frag_tr(fv, sVt, A::VP, 32 * c + 4 * g4, 32 * c + 16 + 4 * g4, 16 * dt, l16);
+                } else {
+                    const T* vr = sVt + (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
+                    frag_ld2(fv, vr, vr + 16);
+                }
                 mma(o[dt], fv, fp);
             }
         }
@@ -281,8 +314,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
     using A = ACfg<T, HS>;
     __shared__ __attribute__((aligned(16))) T sQ[64 * A::RP];
     __shared__ __attribute__((aligned(16))) T sdO[64 * A::RP];
-    __shared__ __attribute__((aligned(16))) T sQt[HS * A::TP];
-    __shared__ __attribute__((aligned(16))) T sdOt[HS * A::TP];
+    __shared__ __attribute__((aligned(16))) T sQt[A::TR ? 8 : HS * A::TP];
+    __shared__ __attribute__((aligned(16))) T sdOt[A::TR ? 8 : HS * A::TP];
     __shared__ __attribute__((aligned(16))) float sL[64];
     __shared__ __attribute__((aligned(16))) float sD[64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -315,13 +348,17 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
         if ((qb + 1) * 64 <= T_) {
             pq.template load<true>(Qh, rs, qb * 64, T_, tid);
             pdo.template load<true>(dOh, C, qb * 64, T_, tid);
-            pqt.template load<true>(Qh, rs, qb * 64, T_, tid);
-            pdot.template load<true>(dOh, C, qb * 64, T_, tid);
+            if constexpr (!A::TR) {
+                pqt.template load<true>(Qh, rs, qb * 64, T_, tid);
+                pdot.template load<true>(dOh, C, qb * 64, T_, tid);
+            }
         } else {
             pq.template load<false>(Qh, rs, qb * 64, T_, tid);
             pdo.template load<false>(dOh, C, qb * 64, T_, tid);
-            pqt.template load<false>(Qh, rs, qb * 64, T_, tid);
-            pdot.template load<false>(dOh, C, qb * 64, T_, tid);
+            if constexpr (!A::TR) {
+                pqt.template load<false>(Qh, rs, qb * 64, T_, tid);
+                pdot.template load<false>(dOh, C, qb * 64, T_, tid);
+            }
         }
         const int qq = qb * 64 + (tid & 63);
         pl = qq < T_ ? lse_h[qq] : INFINITY;
@@ -332,8 +369,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
         __syncthreads();
         pq.store(sQ, tid);
         pdo.store(sdO, tid);
-        pqt.store(sQt, tid);
-        pdot.store(sdOt, tid);
+        if constexpr (!A::TR) {
+            pqt.store(sQt, tid);
+            pdot.store(sdOt, tid);
+        }
         if (tid < 64) {
             sL[tid] = pl;
             sD[tid] = pd;
@@ -382,12 +421,19 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
             frag_from(fs, sv);
 #pragma unroll
             for (int dt = 0; dt < A::DT; dt++) {
-                const int ofs = (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
                 Frag<T> fa;
-                frag_ld2(fa, sdOt + ofs, sdOt + ofs + 16);
-                mma(dv[dt], fa, fp);
-                frag_ld2(fa, sQt + ofs, sQt + ofs + 16);
-                mma(dk[dt], fa, fs);
+                if constexpr (A::TR) {
+                    frag_tr(fa, sdO, A::RP, 32 * c + 4 * g4, 32 * c + 16 + 4 * g4, 16 * dt, l16);
+                    mma(dv[dt], fa, fp);
+                    frag_tr(fa, sQ, A::RP, 32 * c + 4 * g4, 32 * c + 16 + 4 * g4, 16 * dt, l16);
+                    mma(dk[dt], fa, fs);
+                } else {
+                    const int ofs = (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
+                    frag_ld2(fa, sdOt + ofs, sdOt + ofs + 16);
+                    mma(dv[dt], fa, fp);
+                    frag_ld2(fa, sQt + ofs, sQt + ofs + 16);
+                    mma(dk[dt], fa, fs);
+                }
             }
         }
     };
@@ -415,7 +461,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
     using A = ACfg<T, HS>;
     __shared__ __attribute__((aligned(16))) T sK[64 * A::RP];
     __shared__ __attribute__((aligned(16))) T sV[64 * A::RP];
-    __shared__ __attribute__((aligned(16))) T sKt[HS * A::TP];
+    __shared__ __attribute__((aligned(16))) T sKt[A::TR ? 8 : HS * A::TP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int qb = gridDim.x - 1 - blockIdx.x;
@@ -442,11 +488,11 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
         if (kb < qb) {
             pk.template load<true>(Kh, rs, kb * 64, T_, tid);
             pv.template load<true>(Vh, rs, kb * 64, T_, tid);
-            pkt.template load<true>(Kh, rs, kb * 64, T_, tid);
+            if constexpr (!A::TR) pkt.template load<true>(Kh, rs, kb * 64, T_, tid);
         } else {
             pk.template load<false>(Kh, rs, kb * 64, T_, tid);
             pv.template load<false>(Vh, rs, kb * 64, T_, tid);
-            pkt.template load<false>(Kh, rs, kb * 64, T_, tid);
+            if constexpr (!A::TR) pkt.template load<false>(Kh, rs, kb * 64, T_, tid);
         }
     };
     prefetch(0);
@@ -454,7 +500,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
         __syncthreads();
         pk.store(sK, tid);
         pv.store(sV, tid);
-        pkt.store(sKt, tid);
+        if constexpr (!A::TR) pkt.store(sKt, tid);
         __syncthreads();
         if (kb < qb) prefetch(kb + 1);
         // S^T[key][q], dP^T[key][q]: lane holds key = 16kt + 4g4 + r, q = l16
@@ -490,9 +536,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
             frag_from(fs, sv);
 #pragma unroll
             for (int dt = 0; dt < A::DT; dt++) {
-                const T* kr = sKt + (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
                 Frag<T> fa;
-                frag_ld2(fa, kr, kr + 16);
+                if constexpr (A::TR) {
+                    frag_tr(fa, sK, A::RP, 32 * c + 4 * g4, 32 * c + 16 + 4 * g4, 16 * dt, l16);
+                } else {
+                    const T* kr = sKt + (16 * dt + l16) * A::TP + 32 * c + 4 * g4;
+                    frag_ld2(fa, kr, kr + 16);
+                }
                 mma(dq[dt], fa, fs);
             }
         }

@@ -735,20 +735,25 @@ struct Choice {
 };
 
 // Tile configurations per element type, with their measured relative per-CU
-// throughput per operand layout (MI355X, bf16, 8192 x 50304 x 768 classifier
-// products; time per round of resident workgroups, so wave quantisation is
-// left to the cost model; 1.00 = the best tile of that layout).  The 128-row
-// waves (8 per 256x256 tile) read 25% fewer LDS bytes per MFMA, which matters
-// most when both operands are transposed on their way into LDS.
+// throughput per operand layout (MI355X, bf16, direct-to-LDS kernel, time per
+// round of resident workgroups on the 8192 x 50304 x 768 classifier products,
+// so wave quantisation is left to the cost model; 1.00 = the best tile of that
+// layout; the 128x128 input-gradient figure is from the 8192 x 768 x 3072
+// products, where the classifier's is confounded by its K split; the smaller
+// weight-gradient tiles are set from the whole training step, where the
+// 128-row-wave tile with its K split is ~20% faster on those products than
+// 128x256 or 128x128 with theirs).  Forward:
+// 256x256 3.3 TFLOP/s per CU; weight gradient: 256x256
+// with 128-row waves 3.9 TFLOP/s per CU.
 struct TileCfg {
     int bm, bn, wt, occ;
     double speed[3];  // forward, input gradient, weight gradient
 };
-const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {1.00, 0.79, 0.79}},
-                            {256, 128, 64, 1, {0.81, 0.70, 0.66}},
-                            {128, 256, 64, 1, {0.80, 0.90, 0.68}},
-                            {128, 128, 64, 2, {0.87, 0.70, 0.70}},
-                            {256, 256, 128, 1, {0.96, 1.00, 1.00}},
+const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}},
+                            {256, 128, 64, 1, {0.75, 0.76, 0.66}},
+                            {128, 256, 64, 1, {0.71, 0.79, 0.70}},
+                            {128, 128, 64, 2, {0.81, 0.82, 0.70}},
+                            {256, 256, 128, 1, {1.00, 0.95, 1.00}},
 #ifdef GEMM_ONLY_TILE_BM
                             {256, 128, 128, 1, {1.0, 1.0, 1.0}},
                             {128, 256, 128, 1, {1.0, 1.0, 1.0}},
