@@ -226,7 +226,7 @@ def main():
     achieved = kflop / (kms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "gemm_kernel (classifier forward, 8192x50304x768 bf16)", "avg_ms": round(kms, 4)}
+                "kernel": "gemm_dtl_kernel (classifier forward, 8192x50304x768 bf16)", "avg_ms": round(kms, 4)}
     log(f"bench: classifier GEMM {kms:.3f} ms, {achieved:.1f} TFLOP/s")
     del x, w, y
 

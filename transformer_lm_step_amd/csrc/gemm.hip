@@ -699,8 +699,20 @@ gemm_dtl_kernel(const Args g) {
 }
 
 // C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0)
+// C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0).
+// Blocks past the first cblocks (when db is given) do the bias partials:
+// db[m] += sum_z wsb[z*M + m], z in increasing order.
 template <typename OutT, bool ACCUM>
-__global__ void splitk_reduce_kernel(OutT* __restrict__ C, const float* __restrict__ ws, size_t MN, int splits) {
+__global__ void splitk_reduce_kernel(OutT* __restrict__ C, const float* __restrict__ ws, size_t MN, int splits,
+                                     int cblocks, float* __restrict__ db, const float* __restrict__ wsb, int M) {
+    if ((int)blockIdx.x >= cblocks) {
+        const int m = ((int)blockIdx.x - cblocks) * blockDim.x + threadIdx.x;
+        if (m >= M) return;
+        float t = 0.f;
+        for (int z = 0; z < splits; z++) t += wsb[(size_t)z * M + m];
+        db[m] += t;
+        return;
+    }
     size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (i >= MN) return;
     float s[4];
@@ -718,15 +730,6 @@ __global__ void splitk_reduce_kernel(OutT* __restrict__ C, const float* __restri
         for (int r = 0; r < 4; r++) s[r] += c[r];
     }
     store4<OutT>(C + i, s);
-}
-
-// db[m] += sum_z wsb[z*M + m], z in increasing order
-__global__ void splitk_bias_reduce_kernel(float* __restrict__ db, const float* __restrict__ wsb, int M, int splits) {
-    const int m = blockIdx.x * blockDim.x + threadIdx.x;
-    if (m >= M) return;
-    float s = 0.f;
-    for (int z = 0; z < splits; z++) s += wsb[(size_t)z * M + m];
-    db[m] += s;
 }
 
 // ---------------------------------------------------------------- dispatch --
@@ -902,16 +905,14 @@ int gemm_launch_t(const GemmDesc& d, float* ws, size_t ws_bytes, int num_cus, hi
         if (a.dbias) a.wsb = ws + (size_t)ch.splits * MN;
         int e = launch_tile<T>(d, a, ch, dim3(tiles, ch.splits), EPI_SPLIT, s);
         if (e) return e;
-        const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
+        const int cblocks = (int)((MN / 4 + 255) / 256);
+        const int bblocks = a.dbias ? (d.M + 255) / 256 : 0;
         if (d.epi == GEMM_ACCUM)
-            hipLaunchKernelGGL((splitk_reduce_kernel<float, true>), dim3(blocks), dim3(256), 0, s, (float*)d.C, ws, MN,
-                               ch.splits);
+            hipLaunchKernelGGL((splitk_reduce_kernel<float, true>), dim3(cblocks + bblocks), dim3(256), 0, s,
+                               (float*)d.C, ws, MN, ch.splits, cblocks, d.dbias, a.wsb, d.M);
         else
-            hipLaunchKernelGGL((splitk_reduce_kernel<T, false>), dim3(blocks), dim3(256), 0, s, (T*)d.C, ws, MN,
-                               ch.splits);
-        if (a.dbias)
-            hipLaunchKernelGGL(splitk_bias_reduce_kernel, dim3((d.M + 255) / 256), dim3(256), 0, s, d.dbias, a.wsb,
-                               d.M, ch.splits);
+            hipLaunchKernelGGL((splitk_reduce_kernel<T, false>), dim3(cblocks), dim3(256), 0, s, (T*)d.C, ws, MN,
+                               ch.splits, cblocks, (float*)nullptr, (const float*)nullptr, 0);
         return (int)hipGetLastError();
     }
     a.kps = ktiles;
