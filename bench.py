@@ -127,6 +127,58 @@ def bench_fused(args):
     print(json.dumps(out), flush=True)
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "classifier_fwd_8192x50304x768_traffic.md")
+GEMM_SRC = os.path.join(HERE, "transformer_lm_step_amd", "csrc", "gemm.hip")
+
+
+def gemm_source_hash():
+    import hashlib
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the classifier forward product, as measured by
+    the FETCH_SIZE / WRITE_SIZE counter runs recorded in profiles/, if they were
+    taken on the current GEMM source; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(l.split(":", 1) for l in text.splitlines() if l.startswith(("gemm_source_sha256:", "traffic_bytes_per_launch:")))
+    if vals.get("gemm_source_sha256", "").strip() != gemm_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_probe():
+    """Kernels for the HBM-traffic counter runs: a 1 GiB device copy (the
+    reference of known size) and the classifier forward product, 3 launches each."""
+    import torch
+    from transformer_lm_step_amd import binding as Bnd
+    dev = torch.device("cuda:0")
+    n = 1 << 28  # 2^28 floats = 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    M, N, K = 8192, 50304, 768
+    x = torch.randn(M, K, device=dev).to(torch.bfloat16)
+    w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
+    y = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    sh = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        Bnd.gpt2_linear_forward(Bnd.GPT2_BF16, x.data_ptr(), w.data_ptr(), 0, y.data_ptr(), M, N, K, sh)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": "done", "gemm_source_sha256": gemm_source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +188,8 @@ def main():
     ap.add_argument("--seq", type=int, default=1024)
     ap.add_argument("--accum", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the kernels the HBM-traffic counter runs read")
     ap.add_argument("--workload", choices=("gpt2", "fused"), default="gpt2",
                     help="gpt2: the GPT-2 124M training step (default); fused: the standalone "
                          "Linear+GELU+softmax op")
@@ -144,6 +198,9 @@ def main():
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the data-parallel multi-GPU path is not implemented.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_probe:
+        traffic_probe()
+        return
     if args.workload == "fused":
         bench_fused(args)
         return
@@ -225,7 +282,7 @@ def main():
     kflop = 2.0 * M * N * K
     achieved = kflop / (kms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
                 "kernel": "gemm_dtl_kernel (classifier forward, 8192x50304x768 bf16)", "avg_ms": round(kms, 4)}
     log(f"bench: classifier GEMM {kms:.3f} ms, {achieved:.1f} TFLOP/s")
     del x, w, y

@@ -184,15 +184,17 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T
 }
 
 // dw[c] += sum_blocks partial[blk][c]; db[c] += sum_blocks partial[blk][C + c].
-// 64 columns per workgroup, 16 phases of blocks per column (block k goes to
-// phase k % 16), phases combined in order 0..15 through LDS.
-constexpr int FIN_PH = 16;
-__global__ __launch_bounds__(64 * FIN_PH) void ln_bwd_finish_kernel(float* __restrict__ dw, float* __restrict__ db,
-                                                                    const float* __restrict__ partial, int C,
-                                                                    int blocks) {
-    __shared__ float red[FIN_PH][64];
-    const int col = threadIdx.x & 63, ph = threadIdx.x >> 6;
-    const int j = blockIdx.x * 64 + col;
+// 16 columns per workgroup (so 2C/16 workgroups share the reads), 16 phases of
+// blocks per column (block k goes to phase k % 16), phases combined in order
+// 0..15 through LDS.
+constexpr int FIN_PH = 16, FIN_COLS = 16;
+__global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(float* __restrict__ dw,
+                                                                         float* __restrict__ db,
+                                                                         const float* __restrict__ partial, int C,
+                                                                         int blocks) {
+    __shared__ float red[FIN_PH][FIN_COLS];
+    const int col = threadIdx.x % FIN_COLS, ph = threadIdx.x / FIN_COLS;
+    const int j = blockIdx.x * FIN_COLS + col;
     float s = 0.f;
     if (j < 2 * C) {
 #pragma unroll 4
@@ -267,8 +269,8 @@ int layernorm_bwd_launch(float* dres, T* dres_lp, float* dw, float* db, const T*
             }
             return (int)hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + 63) / 64), dim3(64 * FIN_PH), 0, s, dw, db, partial, C,
-                       blocks);
+    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + FIN_COLS - 1) / FIN_COLS), dim3(FIN_COLS * FIN_PH), 0, s,
+                       dw, db, partial, C, blocks);
     return (int)hipGetLastError();
 }
 
