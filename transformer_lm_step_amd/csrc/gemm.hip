@@ -71,6 +71,12 @@ struct Tile {
     static constexpr int FBUF = DEPTH;
 };
 
+// Wave tile selector used by the kernels' template argument WT: 64 -> 64x64,
+// 128 -> 128x64 outputs per wave (128x128 waves need 256 accumulators per lane,
+// which the compiler only fits by spilling).
+template <typename T, int BM, int BN, int WT>
+using TileOf = Tile<T, BM, BN, (WT >= 128 ? 128 : 64), (WT == 256 ? 128 : 64)>;
+
 // Per-thread register count for staging an R x BK slab (both layouts).
 template <int R, int NT> struct StageRegs {
     static constexpr int KM = (R * 8 + NT - 1) / NT;            // k-major: R*8 vectors
@@ -273,8 +279,8 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
 }
 
 template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
-__global__ __launch_bounds__((Tile<T, BM, BN, WT>::NT), (Tile<T, BM, BN, WT>::OCC)) void gemm_kernel(const Args g) {
-    using TL = Tile<T, BM, BN, WT>;
+__global__ __launch_bounds__((TileOf<T, BM, BN, WT>::NT), (TileOf<T, BM, BN, WT>::OCC)) void gemm_kernel(const Args g) {
+    using TL = TileOf<T, BM, BN, WT>;
     constexpr int LDSK = TL::LDSK, BK = TL::BK, TM = TL::TM, TN = TL::TN, NT = TL::NT;
     __shared__ __attribute__((aligned(16))) T sA[2][BM * LDSK];
     __shared__ __attribute__((aligned(16))) T sB[2][BN * LDSK];
@@ -469,17 +475,38 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 DEV constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+// Stage depth BK (contraction elements per stage) and stage count NS per tile:
+// the 128x128 tiles (two workgroups per CU) keep four 32-deep stages so that
+// three are in flight while one is consumed; the larger tiles two 64-deep ones.
+#ifndef GEMM_DTL_BK128
+#define GEMM_DTL_BK128 64
+#endif
+#ifndef GEMM_DTL_NS128
+#define GEMM_DTL_NS128 2
+#endif
+template <int BM, int BN>
+struct DtlCfg {
+    static constexpr int BK = (BM == 128 && BN == 128) ? GEMM_DTL_BK128 : 64;
+    static constexpr int NS = (BM == 128 && BN == 128) ? GEMM_DTL_NS128 : 2;
+};
+
+// chunk swizzle of a k-contiguous slab row (16-byte chunks; 8 per 64-deep
+// row, 4 per 32-deep row): 8 consecutive rows land in 8 different bank groups
+template <int BK>
+DEV int dtl_swz(int r) {
+    return BK == 64 ? (r & 7) : ((r >> 1) & 3);
+}
 template <int R>
 DEV int dtl_fk(int k) {  // unit swizzle of contraction row k in a k-strided slab
     return ((k & 3) | (((k >> 3) & 3) << 2)) & (R / 16 - 1);
 }
 
-template <int R_, bool KMAJ_, int NW_>
+template <int R_, bool KMAJ_, int NW_, int BK_>
 struct DtlSlab {
-    static constexpr int R = R_, NW = NW_;
+    static constexpr int R = R_, NW = NW_, BK = BK_;
     static constexpr bool KMAJ = KMAJ_;
-    static constexpr int NQ = R / 8 / NW;  // 1 KB load instructions per wave per stage
-    static_assert(NQ >= 1 && (R / 8) % NW == 0, "slab rows must split evenly over the waves");
+    static constexpr int NQ = R * BK / 512 / NW;  // 1 KB load instructions per wave per stage
+    static_assert(NQ >= 1 && (R * BK / 512) % NW == 0, "slab must split evenly over the waves");
     uint32_t off[NQ];  // per-lane byte offset from the slab origin in global memory
     int kc[KMAJ ? NQ : 1];
     DEV void init(long ld, int lane, int wave) {
@@ -487,8 +514,10 @@ struct DtlSlab {
         for (int q = 0; q < NQ; q++) {
             const int j = wave + NW * q;  // which 1 KB of the slab
             if constexpr (KMAJ) {
-                const int r = 8 * j + (lane >> 3);
-                const int c = (lane & 7) ^ (lane >> 3);
+                constexpr int CPR = BK / 8;      // 16-byte chunks per row
+                constexpr int RPK = 64 / CPR;    // rows per 1 KB
+                const int r = RPK * j + lane / CPR;
+                const int c = (lane % CPR) ^ dtl_swz<BK>(r);
                 kc[q] = 8 * c;
                 off[q] = (uint32_t)(((long)r * ld + 8 * c) * 2);
             } else {
@@ -504,45 +533,56 @@ struct DtlSlab {
     }
 };
 
+// One 16-byte-per-lane buffer load into LDS at lds (wave-uniform; lane i
+// lands at lds + 16 i).  Written as inline assembly so that the compiler does
+// not track it: its own wait insertion cannot tell the stage buffers apart and
+// would wait for every load in flight before each fragment read.  The kernel
+// waits for these loads itself (vmcnt before each stage's barrier, and for all
+// of them before the loop ends), and issues no other vector memory access in
+// its main loop.
+DEV void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const void* lds) {
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                 "s"(__builtin_amdgcn_readfirstlane(a))
+                 : "memory", "m0");
+}
+
 // Issue this wave's loads of the slab at (rows r0.., contraction k0..) into dst
 // (per-lane offsets and, k-contiguous, contraction indices from DtlSlab).
-template <int R, bool KMAJ, int NW>
+template <int R, bool KMAJ, int NW, int BK>
 DEV void dtl_issue(const uint32_t* off, const int* kc, bf16_t* dst, const bf16_t* __restrict__ p, long ld, int r0,
                    int Rmax, int k0, int K, int wave) {
-    constexpr int NQ = R / 8 / NW;
+    constexpr int NQ = R * BK / 512 / NW;
     if constexpr (KMAJ) {
         const long org = (long)r0 * ld + k0;
         const uint32_t bytes = (uint32_t)max(0L, ((long)Rmax * ld - org) * 2);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(p + org, bytes);
         const int klim = K - k0;
 #pragma unroll
-        for (int q = 0; q < NQ; q++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (wave + NW * q) * 512), 16,
-                                                     kc[q] < klim ? off[q] : kBufOOB, 0, 0, 0);
+        for (int q = 0; q < NQ; q++) lds_dma16(rs, kc[q] < klim ? off[q] : kBufOOB, dst + (wave + NW * q) * 512);
     } else {
         const long org = (long)k0 * ld + r0;
         const uint32_t bytes = (uint32_t)max(0L, ((long)K * ld - org) * 2);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(p + org, bytes);
 #pragma unroll
-        for (int q = 0; q < NQ; q++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (wave + NW * q) * 512), 16, off[q], 0, 0,
-                                                     0);
+        for (int q = 0; q < NQ; q++) lds_dma16(rs, off[q], dst + (wave + NW * q) * 512);
     }
 }
 
 // Per-lane element offsets of the fragment reads of one operand: KT tiles of 16
-// rows starting at wave row wb, both 32-deep MFMA steps of a stage.
-template <int R, bool KMAJ, int KT>
+// rows starting at wave row wb, for each 32-deep MFMA step of a stage.
+template <int R, bool KMAJ, int KT, int BK>
 struct DtlFrag {
-    int ofs[KT][2];  // [tile][step] (k-strided: the first of the two transpose reads)
+    static constexpr int KS = BK / 32;
+    int ofs[KT][KS];  // [tile][step] (k-strided: the first of the two transpose reads)
     DEV void init(int wb, int l16, int g4) {
 #pragma unroll
         for (int t = 0; t < KT; t++) {
             const int rb = wb + 16 * t;
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
+            for (int ks = 0; ks < KS; ks++) {
                 if constexpr (KMAJ) {
-                    ofs[t][ks] = (rb + l16) * 64 + (((4 * ks + g4) ^ (l16 & 7)) << 3);
+                    ofs[t][ks] = (rb + l16) * BK + (((4 * ks + g4) ^ dtl_swz<BK>(rb + l16)) << 3);
                 } else {
                     const int fk = ((l16 >> 2) | (g4 << 2)) & (R / 16 - 1);  // dtl_fk of every row read here
                     const int k = 32 * ks + 8 * g4 + (l16 >> 2);
@@ -568,16 +608,24 @@ DEV void dtl_frag_ld(Frag<bf16_t>& f, const bf16_t* s, int ofs) {
 }
 
 template <int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
-__global__ __launch_bounds__((Tile<bf16_t, BM, BN, WT>::NT), (Tile<bf16_t, BM, BN, WT>::OCC)) void
+__global__ __launch_bounds__((TileOf<bf16_t, BM, BN, WT>::NT), (TileOf<bf16_t, BM, BN, WT>::OCC)) void
 gemm_dtl_kernel(const Args g) {
     using T = bf16_t;
-    using TL = Tile<T, BM, BN, WT>;
-    constexpr int TM = TL::TM, TN = TL::TN, NT = TL::NT, NW = NT / 64, BK = 64;
+    using TL = TileOf<T, BM, BN, WT>;
+    constexpr int TM = TL::TM, TN = TL::TN, NT = TL::NT, NW = NT / 64;
+    constexpr int BK = DtlCfg<BM, BN>::BK, NS = DtlCfg<BM, BN>::NS, KS = BK / 32;
     static_assert(!BIAS || !AK, "the fused bias sum reads a k-strided A slab");
+    // one LDS array per stage and operand, so the compiler can tell which
+    // buffer an LDS-destination load writes and which one a fragment read uses
     __shared__ __attribute__((aligned(1024))) T sA0[BM * BK];
     __shared__ __attribute__((aligned(1024))) T sA1[BM * BK];
+    __shared__ __attribute__((aligned(1024))) T sA2[NS > 2 ? BM * BK : 8];
+    __shared__ __attribute__((aligned(1024))) T sA3[NS > 3 ? BM * BK : 8];
     __shared__ __attribute__((aligned(1024))) T sB0[BN * BK];
     __shared__ __attribute__((aligned(1024))) T sB1[BN * BK];
+    __shared__ __attribute__((aligned(1024))) T sB2[NS > 2 ? BN * BK : 8];
+    __shared__ __attribute__((aligned(1024))) T sB3[NS > 3 ? BN * BK : 8];
+    __shared__ float sbias[BIAS ? (NT / (BM / 4)) * BM : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -598,9 +646,11 @@ gemm_dtl_kernel(const Args g) {
     const int tn = (b % in_group) / gsz;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const int ktiles = (g.K + BK - 1) / BK;
-    const int kt0 = blockIdx.y * g.kps;
-    const int kt1 = min(kt0 + g.kps, ktiles);
+    // g.kps counts 64-deep k-tiles (the unit of the K split); stages are BK deep
+    constexpr int SPT = 64 / BK;  // stages per 64-deep k-tile
+    const int ktiles = (g.K + 63) / 64;
+    const int kt0 = blockIdx.y * g.kps * SPT;
+    const int kt1 = min(blockIdx.y * g.kps + g.kps, ktiles) * SPT;
     const T* __restrict__ A = (const T*)g.A;
     const T* __restrict__ B = (const T*)g.B;
 
@@ -610,33 +660,38 @@ gemm_dtl_kernel(const Args g) {
 #pragma unroll
         for (int j = 0; j < TN; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    DtlSlab<BM, AK, TL::NT / 64> dA;
-    DtlSlab<BN, BKM, TL::NT / 64> dB;
+    DtlSlab<BM, AK, TL::NT / 64, BK> dA;
+    DtlSlab<BN, BKM, TL::NT / 64, BK> dB;
     dA.init(g.lda, lane, wave);
     dB.init(g.ldb, lane, wave);
-    DtlFrag<BM, AK, TM> fA;
-    DtlFrag<BN, BKM, TN> fB;
+    DtlFrag<BM, AK, TM, BK> fA;
+    DtlFrag<BN, BKM, TN, BK> fB;
     fA.init(wm * TL::WTM, l16, g4);
     fB.init(wn * TL::WTN, l16, g4);
+    constexpr int NQS = DtlSlab<BM, AK, TL::NT / 64, BK>::NQ + DtlSlab<BN, BKM, TL::NT / 64, BK>::NQ;
 
     // fused bias gradient: column sums over k of the k-strided A slab
     constexpr int MQ = BM / 4, KG = NT / MQ, KPG = BK / KG;
+    static_assert(!BIAS || KPG >= 1, "bias partial layout");
     const int bq = tid % MQ, bkg = tid / MQ;
     float bs[4] = {0.f, 0.f, 0.f, 0.f};
     const bool do_bias = BIAS && tn == 0;
 
+    auto issue = [&](int kt, T* a_dst, T* b_dst) {
+        dtl_issue<BM, AK, TL::NT / 64, BK>(dA.off, dA.kc, a_dst, A, g.lda, m0, g.M, kt * BK, g.K, wave);
+        dtl_issue<BN, BKM, TL::NT / 64, BK>(dB.off, dB.kc, b_dst, B, g.ldb, n0, g.N, kt * BK, g.K, wave);
+    };
     auto compute = [&](const T* a_s, const T* b_s) {
-        Frag<T> fa[2][TM], fb[2][TN];
+        Frag<T> fa[KS][TM], fb[KS][TN];
 #pragma unroll
-        for (int t = 0; t < TN; t++) dtl_frag_ld<BN, BKM>(fb[0][t], b_s, fB.ofs[t][0]);
+        for (int ks = 0; ks < KS; ks++) {
 #pragma unroll
-        for (int t = 0; t < TM; t++) dtl_frag_ld<BM, AK>(fa[0][t], a_s, fA.ofs[t][0]);
+            for (int t = 0; t < TN; t++) dtl_frag_ld<BN, BKM>(fb[ks][t], b_s, fB.ofs[t][ks]);
 #pragma unroll
-        for (int t = 0; t < TN; t++) dtl_frag_ld<BN, BKM>(fb[1][t], b_s, fB.ofs[t][1]);
+            for (int t = 0; t < TM; t++) dtl_frag_ld<BM, AK>(fa[ks][t], a_s, fA.ofs[t][ks]);
+        }
 #pragma unroll
-        for (int t = 0; t < TM; t++) dtl_frag_ld<BM, AK>(fa[1][t], a_s, fA.ofs[t][1]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++)
+        for (int ks = 0; ks < KS; ks++)
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -655,33 +710,57 @@ gemm_dtl_kernel(const Args g) {
             }
         }
     };
-
-    if (kt0 < kt1) {
-        dtl_issue<BM, AK, TL::NT / 64>(dA.off, dA.kc, sA0, A, g.lda, m0, g.M, kt0 * BK, g.K, wave);
-        dtl_issue<BN, BKM, TL::NT / 64>(dB.off, dB.kc, sB0, B, g.ldb, n0, g.N, kt0 * BK, g.K, wave);
+    // stage kt lives in buffer kt % NS.  Opening stage kt: wait for its loads
+    // (allowing the NS-2 later stages already issued to stay in flight; near
+    // the end, where fewer were issued, wait for all), barrier, then issue the
+    // loads of stage kt + NS - 1 into the buffer stage kt - 1 just released.
+    // The barrier is a bare s_barrier: __syncthreads()'s workgroup fence would
+    // also wait for the later stages' loads still in flight.  Each wave's vmcnt
+    // wait covers its own loads into stage kt, and the fragments of stage kt-1
+    // (the buffer about to be refilled) are consumed by MFMAs before it; the
+    // memory clobber keeps the compiler from moving LDS accesses across it.
+    auto open = [&](int kt) {
+        if (kt + NS - 2 < kt1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * NQS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("s_barrier" ::: "memory");
+    };
+#define GEMM_DTL_STAGE(I)                                                                          \
+    {                                                                                              \
+        const int kt = kb + (I);                                                                   \
+        if (kt < kt1) {                                                                            \
+            open(kt);                                                                              \
+            if (kt + NS - 1 < kt1) issue(kt + NS - 1, sA##I##p, sB##I##p);                         \
+            compute(sA##I, sB##I);                                                                 \
+        }                                                                                          \
     }
-    for (int kt = kt0; kt < kt1; kt += 2) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();
-        if (kt + 1 < kt1) {
-            dtl_issue<BM, AK, TL::NT / 64>(dA.off, dA.kc, sA1, A, g.lda, m0, g.M, (kt + 1) * BK, g.K, wave);
-            dtl_issue<BN, BKM, TL::NT / 64>(dB.off, dB.kc, sB1, B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, wave);
-        }
-        compute(sA0, sB0);
-        if (kt + 1 < kt1) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            __syncthreads();
-            if (kt + 2 < kt1) {
-                dtl_issue<BM, AK, TL::NT / 64>(dA.off, dA.kc, sA0, A, g.lda, m0, g.M, (kt + 2) * BK, g.K, wave);
-                dtl_issue<BN, BKM, TL::NT / 64>(dB.off, dB.kc, sB0, B, g.ldb, n0, g.N, (kt + 2) * BK, g.K, wave);
-            }
-            compute(sA1, sB1);
+    // buffers for "the stage NS - 1 ahead" of stage i: (i + NS - 1) % NS
+    T* const sA0p = NS == 2 ? sA1 : NS == 3 ? sA2 : sA3;
+    T* const sB0p = NS == 2 ? sB1 : NS == 3 ? sB2 : sB3;
+    T* const sA1p = NS == 2 ? sA0 : NS == 3 ? sA0 : sA0;
+    T* const sB1p = NS == 2 ? sB0 : NS == 3 ? sB0 : sB0;
+    T* const sA2p = NS == 3 ? sA1 : sA1;
+    T* const sB2p = NS == 3 ? sB1 : sB1;
+    T* const sA3p = sA2;
+    T* const sB3p = sB2;
+#pragma unroll
+    for (int i = 0; i < NS - 1; i++) {
+        const int kt = kt0 + i;
+        if (kt < kt1) {
+            T* ad = i == 0 ? sA0 : i == 1 ? sA1 : sA2;
+            T* bd = i == 0 ? sB0 : i == 1 ? sB1 : sB2;
+            issue(kt, ad, bd);
         }
     }
+    for (int kb = kt0; kb < kt1; kb += NS) {
+        GEMM_DTL_STAGE(0)
+        GEMM_DTL_STAGE(1)
+        if constexpr (NS > 2) GEMM_DTL_STAGE(2)
+        if constexpr (NS > 3) GEMM_DTL_STAGE(3)
+    }
+#undef GEMM_DTL_STAGE
 
     if constexpr (BIAS) {
-        __syncthreads();  // every wave is done with the stage buffers
-        float* red = reinterpret_cast<float*>(sA0);  // KG x BM floats (<= BM * BK bf16)
+        float* red = sbias;  // KG x BM floats
 #pragma unroll
         for (int e = 0; e < 4; e++) red[bkg * BM + 4 * bq + e] = bs[e];
         __syncthreads();
@@ -698,7 +777,6 @@ gemm_dtl_kernel(const Args g) {
     gemm_epilogue<T, TL, EPI, OutT>(g, acc, m0, n0, wm, wn, l16, g4);
 }
 
-// C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0)
 // C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0).
 // Blocks past the first cblocks (when db is given) do the bias partials:
 // db[m] += sum_z wsb[z*M + m], z in increasing order.
@@ -817,7 +895,7 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
 
 template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS = false>
 void launch_t(const Args& a, dim3 grid, hipStream_t s) {
-    using TL = Tile<T, BM, BN, WT>;
+    using TL = TileOf<T, BM, BN, WT>;
     if constexpr (sizeof(T) == 2 && GEMM_DTL)
         hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
     else
