@@ -87,6 +87,8 @@ DEV void row_frags(Frag<T>* f, const T* src, long rs, int row, int T_, int g4) {
 // one block ahead, so its latency hides behind the current block's MFMAs) and
 // an LDS store.  FULL: rows row0..row0+63 are all < T (no row check).
 // COLS columns (zero past HS) of 64 rows into an LDS tile of pitch PITCH.
+// Per-thread element offsets within a block are computed once (init); a load
+// only adds the block's row origin, a wave-uniform value.
 template <typename T, int HS, int COLS = ACfg<T, HS>::KD, int PITCH = ACfg<T, HS>::RP>
 struct RowsStage {
     using A = ACfg<T, HS>;
@@ -94,16 +96,26 @@ struct RowsStage {
     static constexpr int ITEMS = 64 * VPR;
     static constexpr int N = (ITEMS + 255) / 256;
     uint4 r[N];
-    template <bool FULL>
-    DEV void load(const T* src, long rs, int row0, int T_, int tid) {
+    uint32_t off[N];  // row * rs + d0 (elements)
+    int row[N];       // row within the block; >= 64 (or past HS) marks an idle slot
+    DEV void init(long rs, int tid) {
 #pragma unroll
         for (int i = 0; i < N; i++) {
             const int idx = tid + 256 * i;
-            const int row = idx / VPR, d0 = (idx % VPR) * A::VEC;
-            const int gr = row0 + row;
-            r[i] = ((ITEMS % 256 == 0 || idx < ITEMS) && (FULL || gr < T_) && d0 < HS)
-                       ? ld16(src + (long)gr * rs + d0)
-                       : make_uint4(0, 0, 0, 0);
+            const int rr = idx / VPR, d0 = (idx % VPR) * A::VEC;
+            const bool live = (ITEMS % 256 == 0 || idx < ITEMS) && d0 < HS;
+            row[i] = live ? rr : 1 << 20;
+            off[i] = live ? (uint32_t)(rr * rs + d0) : 0u;
+        }
+    }
+    template <bool FULL>
+    DEV void load(const T* src, long rs, int row0, int T_) {
+        const T* base = src + (long)row0 * rs;
+        const int lim = T_ - row0;
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const bool ok = FULL ? row[i] < 64 : row[i] < lim;
+            r[i] = ok ? ld16(base + off[i]) : make_uint4(0, 0, 0, 0);
         }
     }
     DEV void store(T* dst, int tid) const {
@@ -188,13 +200,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
 
     RowsStage<T, HS> pk;
     std::conditional_t<A::TR, RowsStage<T, HS, HS, A::VP>, RowsTStage<T, HS>> pv;
+    pk.init(rs, tid);
+    if constexpr (A::TR) pv.init(rs, tid);
     auto prefetch = [&](int kb) {
         if (kb < qb) {
-            pk.template load<true>(Kh, rs, kb * 64, T_, tid);
-            pv.template load<true>(Vh, rs, kb * 64, T_, tid);
+            pk.template load<true>(Kh, rs, kb * 64, T_);
+            if constexpr (A::TR) pv.template load<true>(Vh, rs, kb * 64, T_);
+            else pv.template load<true>(Vh, rs, kb * 64, T_, tid);
         } else {
-            pk.template load<false>(Kh, rs, kb * 64, T_, tid);
-            pv.template load<false>(Vh, rs, kb * 64, T_, tid);
+            pk.template load<false>(Kh, rs, kb * 64, T_);
+            if constexpr (A::TR) pv.template load<false>(Vh, rs, kb * 64, T_);
+            else pv.template load<false>(Vh, rs, kb * 64, T_, tid);
         }
     };
     prefetch(0);
@@ -342,19 +358,21 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
     }
     const int nqb = (T_ + 63) / 64;
     RowsStage<T, HS> pq, pdo;
+    pq.init(rs, tid);
+    pdo.init(C, tid);
     RowsTStage<T, HS> pqt, pdot;
     float pl = INFINITY, pd = 0.f;
     auto prefetch = [&](int qb) {
         if ((qb + 1) * 64 <= T_) {
-            pq.template load<true>(Qh, rs, qb * 64, T_, tid);
-            pdo.template load<true>(dOh, C, qb * 64, T_, tid);
+            pq.template load<true>(Qh, rs, qb * 64, T_);
+            pdo.template load<true>(dOh, C, qb * 64, T_);
             if constexpr (!A::TR) {
                 pqt.template load<true>(Qh, rs, qb * 64, T_, tid);
                 pdot.template load<true>(dOh, C, qb * 64, T_, tid);
             }
         } else {
-            pq.template load<false>(Qh, rs, qb * 64, T_, tid);
-            pdo.template load<false>(dOh, C, qb * 64, T_, tid);
+            pq.template load<false>(Qh, rs, qb * 64, T_);
+            pdo.template load<false>(dOh, C, qb * 64, T_);
             if constexpr (!A::TR) {
                 pqt.template load<false>(Qh, rs, qb * 64, T_, tid);
                 pdot.template load<false>(dOh, C, qb * 64, T_, tid);
@@ -484,14 +502,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
 
     RowsStage<T, HS> pk, pv;
     RowsTStage<T, HS> pkt;
+    pk.init(rs, tid);
+    pv.init(rs, tid);
     auto prefetch = [&](int kb) {
         if (kb < qb) {
-            pk.template load<true>(Kh, rs, kb * 64, T_, tid);
-            pv.template load<true>(Vh, rs, kb * 64, T_, tid);
+            pk.template load<true>(Kh, rs, kb * 64, T_);
+            pv.template load<true>(Vh, rs, kb * 64, T_);
             if constexpr (!A::TR) pkt.template load<true>(Kh, rs, kb * 64, T_, tid);
         } else {
-            pk.template load<false>(Kh, rs, kb * 64, T_, tid);
-            pv.template load<false>(Vh, rs, kb * 64, T_, tid);
+            pk.template load<false>(Kh, rs, kb * 64, T_);
+            pv.template load<false>(Vh, rs, kb * 64, T_);
             if constexpr (!A::TR) pkt.template load<false>(Kh, rs, kb * 64, T_, tid);
         }
     };

@@ -484,10 +484,13 @@ DEV constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((
 #ifndef GEMM_DTL_NS128
 #define GEMM_DTL_NS128 2
 #endif
+#ifndef GEMM_DTL_NS_RECT
+#define GEMM_DTL_NS_RECT 3
+#endif
 template <int BM, int BN>
 struct DtlCfg {
     static constexpr int BK = (BM == 128 && BN == 128) ? GEMM_DTL_BK128 : 64;
-    static constexpr int NS = (BM == 128 && BN == 128) ? GEMM_DTL_NS128 : 2;
+    static constexpr int NS = (BM == 128 && BN == 128) ? GEMM_DTL_NS128 : (BM != BN ? GEMM_DTL_NS_RECT : 2);
 };
 
 // chunk swizzle of a k-contiguous slab row (16-byte chunks; 8 per 64-deep
