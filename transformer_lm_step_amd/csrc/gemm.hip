@@ -40,6 +40,7 @@
 //    in split order, so results are deterministic.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -224,53 +225,117 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
         }
         return;
     }
+    // The epilogue's global reads (bias, residual, stored pre-activation,
+    // accumulator) are issued ahead of the stores they feed: the compiler cannot
+    // tell that the output aliases none of them and would otherwise order each
+    // read after the previous tile's store, one memory round trip per 16x16
+    // tile.
+    constexpr bool HAS_BIAS = EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU || EPI == GEMM_BIAS_RESID;
+    constexpr bool HAS_AUX = EPI == GEMM_BIAS_RESID || EPI == GEMM_GELU_BWD || EPI == GEMM_ACCUM;
+    using AuxT = std::conditional_t<EPI == GEMM_ACCUM, float, T>;
+    using Raw = std::conditional_t<sizeof(AuxT) == 2, uint2, float4>;
+    const int nb = n0 + wn * TL::WTN + 4 * g4;
+    const int mb = m0 + wm * TL::WTM + l16;
+    // (reads are unconditional, from a clamped in-range address, and unused
+    // lanes' values are discarded: a read under a branch would be waited for
+    // before the branch closes)
+    float bb[TN][4];
+    if constexpr (HAS_BIAS) {
+        using RawB = std::conditional_t<sizeof(T) == 2, uint2, float4>;
+        RawB rb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int n = nb + 16 * j;
+            rb[j] = *reinterpret_cast<const RawB*>((const T*)g.bias + (n < g.N ? n : 0));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            if constexpr (sizeof(T) == 2) {
+                const uint2 u = (const uint2&)rb[j];
+                bb[j][0] = __uint_as_float(u.x << 16); bb[j][1] = __uint_as_float(u.x & 0xffff0000u);
+                bb[j][2] = __uint_as_float(u.y << 16); bb[j][3] = __uint_as_float(u.y & 0xffff0000u);
+            } else {
+                const float4 u = (const float4&)rb[j];
+                bb[j][0] = u.x; bb[j][1] = u.y; bb[j][2] = u.z; bb[j][3] = u.w;
+            }
+        }
+    }
+    // auxiliary reads in groups of G tile rows (at most 32 registers per
+    // group); group gi + 1 is requested before group gi is stored.  With 16
+    // waves per workgroup (128 registers per lane) one tile row at a time.
+    constexpr bool TIGHT = TL::NT >= 1024;
+    constexpr int RPR = (int)sizeof(Raw) / 4;
+    constexpr int G = !HAS_AUX ? TM : TIGHT ? 1 : (TM * TN * RPR <= 32 ? TM : std::max(1, 32 / (TN * RPR)));
+    constexpr int NBUF = HAS_AUX && !TIGHT ? 2 : 1;
+    static_assert(TM % G == 0, "tile rows split evenly into groups");
+    Raw aux[NBUF][HAS_AUX ? G : 1][HAS_AUX ? TN : 1];
+    auto load_group = [&](int gi, Raw (&dst)[HAS_AUX ? G : 1][HAS_AUX ? TN : 1]) {
+        if constexpr (HAS_AUX) {
+            const AuxT* src = EPI == GEMM_ACCUM ? (const AuxT*)g.C : (const AuxT*)g.aux_in;
+            const size_t ld = EPI == GEMM_ACCUM ? (size_t)g.ldc : (size_t)g.ldaux;
+#pragma unroll
+            for (int ii = 0; ii < G; ii++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    const int m = mb + 16 * (gi * G + ii), n = nb + 16 * j;
+                    const bool ok = m < g.M && n < g.N;
+                    dst[ii][j] = *reinterpret_cast<const Raw*>(src + (ok ? (size_t)m * ld + n : 0));
+                }
+        }
+    };
+    if constexpr (!TIGHT) load_group(0, aux[0]);
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int m = m0 + wm * TL::WTM + 16 * i + l16;
+        if constexpr (HAS_AUX) {
+            if (TIGHT) load_group(i, aux[0]);
+            else if (i % G == 0 && i + G < TM) load_group(i / G + 1, aux[(i / G + 1) % NBUF]);
+        }
+        const int m = mb + 16 * i;
         if (m >= g.M) continue;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-            const int n = n0 + wn * TL::WTN + 16 * j + 4 * g4;
+            const int n = nb + 16 * j;
             if (n >= g.N) continue;
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) v[r] = g.alpha * acc[i][j][r];
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_AUX) {
+                const Raw& ru = aux[(i / G) % NBUF][i % G][j];
+                if constexpr (sizeof(AuxT) == 2) {
+                    const uint2 u = (const uint2&)ru;
+                    a[0] = __uint_as_float(u.x << 16); a[1] = __uint_as_float(u.x & 0xffff0000u);
+                    a[2] = __uint_as_float(u.y << 16); a[3] = __uint_as_float(u.y & 0xffff0000u);
+                } else {
+                    const float4 u = (const float4&)ru;
+                    a[0] = u.x; a[1] = u.y; a[2] = u.z; a[3] = u.w;
+                }
+            }
             if constexpr (EPI == EPI_SPLIT) {
                 float* w = g.ws + (size_t)blockIdx.y * g.M * g.N + (size_t)m * g.N + n;
                 store4<float>(w, v);
             } else if constexpr (EPI == GEMM_ACCUM) {
-                float* c = (float*)g.C + (size_t)m * g.ldc + n;
-                float o[4];
-                load4<float>(c, o);
 #pragma unroll
-                for (int r = 0; r < 4; r++) o[r] += v[r];
-                store4<float>(c, o);
+                for (int r = 0; r < 4; r++) v[r] += a[r];
+                store4<float>((float*)g.C + (size_t)m * g.ldc + n, v);
             } else {
-                if constexpr (EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU || EPI == GEMM_BIAS_RESID) {
-                    float bb[4];
-                    load4<T>((const T*)g.bias + n, bb);
+                if constexpr (HAS_BIAS) {
 #pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] += bb[r];
+                    for (int r = 0; r < 4; r++) v[r] += bb[j][r];
                 }
                 if constexpr (EPI == GEMM_BIAS_GELU) {
-                    T* pre = (T*)g.aux_out + (size_t)m * g.ldaux + n;
-                    store4<T>(pre, v);
-                    float pr[4];
-                    load4<T>(pre, pr);  // GELU of the stored (rounded) pre-activation
+                    store4<T>((T*)g.aux_out + (size_t)m * g.ldaux + n, v);
+                    // GELU of the stored (rounded) pre-activation
 #pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] = gelu_f<T>(pr[r]);
+                    for (int r = 0; r < 4; r++) v[r] = gelu_f<T>(to_f<T>(from_f<T>(v[r])));
                 }
                 if constexpr (EPI == GEMM_BIAS_RESID) {
-                    float res[4];
-                    load4<T>((const T*)g.aux_in + (size_t)m * g.ldaux + n, res);
 #pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] += res[r];
+                    for (int r = 0; r < 4; r++) v[r] += a[r];
                 }
                 if constexpr (EPI == GEMM_GELU_BWD) {
-                    float pr[4];
-                    load4<T>((const T*)g.aux_in + (size_t)m * g.ldaux + n, pr);
 #pragma unroll
-                    for (int r = 0; r < 4; r++) v[r] *= gelu_grad_f<T>(pr[r]);
+                    for (int r = 0; r < 4; r++) v[r] *= gelu_grad_f<T>(a[r]);
                 }
                 store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v);
             }
