@@ -891,7 +891,10 @@ struct Choice {
 // products, where the classifier's is confounded by its K split; the smaller
 // weight-gradient tiles are set from the whole training step, where the
 // 128-row-wave tile with its K split is ~20% faster on those products than
-// 128x256 or 128x128 with theirs).  Forward:
+// 128x256 or 128x128 with theirs; so are the forward figure of 256x128 and the
+// input-gradient figure of 128x256: inside the step the layer products read
+// operands that are no longer in cache, and these tiles, one workgroup per CU
+// with two stages in flight, run them 5-15% faster than 128x128).  Forward:
 // 256x256 3.3 TFLOP/s per CU; weight gradient: 256x256
 // with 128-row waves 3.9 TFLOP/s per CU.
 struct TileCfg {
@@ -899,8 +902,8 @@ struct TileCfg {
     double speed[3];  // forward, input gradient, weight gradient
 };
 const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}},
-                            {256, 128, 64, 1, {0.75, 0.76, 0.66}},
-                            {128, 256, 64, 1, {0.71, 0.79, 0.70}},
+                            {256, 128, 64, 1, {0.92, 0.76, 0.66}},
+                            {128, 256, 64, 1, {0.71, 0.92, 0.70}},
                             {128, 128, 64, 2, {0.81, 0.82, 0.70}},
                             {256, 256, 128, 1, {1.00, 0.95, 1.00}},
 #ifdef GEMM_ONLY_TILE_BM
