@@ -150,3 +150,20 @@ def fused_op_inputs(M: int, K: int, N: int, seed: int = DATA_SEED):
     W = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(1.0 / math.sqrt(K)))
     b = rng.normal(0.0, 0.02, N).astype(np.float32)
     return X, W.astype(np.float32), b
+
+
+def linear_inputs(M: int, K: int, N: int, seed: int = DATA_SEED):
+    """Operands of one Linear layer, all bf16-exact (float32 arrays).
+
+    x ~ N(0, 1) [M,K]; w ~ N(0, 0.02) [N,K] (the GPT-2 init scale);
+    bias ~ N(0, 0.02) [N]; dy ~ N(0, 1) [M,N]; dw0 ~ N(0, 0.01) [N,K] and
+    db0 ~ N(0, 0.01) [N] as gradients already accumulated (fp32).
+    """
+    rng = np.random.default_rng(seed)
+    x = round_to_bf16(rng.standard_normal((M, K), dtype=np.float32))
+    w = round_to_bf16(rng.normal(0.0, 0.02, (N, K)).astype(np.float32))
+    bias = round_to_bf16(rng.normal(0.0, 0.02, N).astype(np.float32))
+    dy = round_to_bf16(rng.standard_normal((M, N), dtype=np.float32))
+    dw0 = rng.normal(0.0, 0.01, (N, K)).astype(np.float32)
+    db0 = rng.normal(0.0, 0.01, N).astype(np.float32)
+    return x, w, bias, dy, dw0, db0

@@ -675,6 +675,20 @@ DEV void dtl_frag_ld(Frag<bf16_t>& f, const bf16_t* s, int ofs) {
     }
 }
 
+// Whether a tile shape and epilogue run the persistent tile loop (launches
+// then have at most one workgroup per resident slot).  Only epilogues that
+// read no activations do: a read issued behind the next tile's loads waits
+// for them (vector memory operations complete in order), and the next tile's
+// first stage waits for the stores before it, so an epilogue that reads
+// (residual, stored pre-activation, accumulator) measured slower persistent;
+// the fused bias sum and split partials stay one tile per workgroup too.
+template <int BM, int BN, int WT, int EPI, bool BIAS>
+constexpr bool dtl_persistent() {
+    constexpr int NT = TileOf<bf16_t, BM, BN, WT>::NT;
+    if (BIAS) return false;
+    return EPI == GEMM_STORE || EPI == GEMM_BIAS || (EPI == GEMM_BIAS_GELU && NT <= 512);
+}
+
 template <int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
 __global__ __launch_bounds__((TileOf<bf16_t, BM, BN, WT>::NT), (TileOf<bf16_t, BM, BN, WT>::OCC)) void
 gemm_dtl_kernel(const Args g) {
@@ -700,19 +714,30 @@ gemm_dtl_kernel(const Args g) {
     const int wm = wave % TL::WM, wn = wave / TL::WM;
     const int l16 = lane & 15, g4 = lane >> 4;
 
+    // Tiles are numbered u = 0 .. ntiles-1 and mapped so that the tiles of
+    // one XCD (u % 8, as workgroups are handed out round-robin) form a
+    // contiguous run, walked in groups of 8 row-tiles.  Persistent launches
+    // have fewer workgroups than tiles: workgroup w takes tiles w, w + G,
+    // w + 2G, ... (G = gridDim.x, a multiple of 8, so every tile stays on the
+    // XCD the numbering intends), and the first stages of its next tile are
+    // requested before the epilogue of the current one.
+    constexpr bool PERSIST = dtl_persistent<BM, BN, WT, EPI, BIAS>();
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-    const int nb = gridDim.x;
-    int b = blockIdx.x;
-    const int full = (nb / 8) * 8;
-    if (b < full) b = (b % 8) * (nb / 8) + (b / 8);
-    const int GM = 8;
-    const int in_group = GM * tiles_n;
-    const int group = b / in_group;
-    const int first_m = group * GM;
-    const int gsz = min(tiles_m - first_m, GM);
-    const int tm = first_m + ((b % in_group) % gsz);
-    const int tn = (b % in_group) / gsz;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int ntiles = tiles_m * tiles_n;
+    auto tile_of = [&](int u, int& tm_, int& tn_) {
+        const int full = (ntiles / 8) * 8;
+        if (u < full) u = (u % 8) * (ntiles / 8) + (u / 8);
+        const int GM = 8;
+        const int in_group = GM * tiles_n;
+        const int first_m = (u / in_group) * GM;
+        const int gsz = min(tiles_m - first_m, GM);
+        tm_ = first_m + ((u % in_group) % gsz);
+        tn_ = (u % in_group) / gsz;
+    };
+    int u = blockIdx.x;
+    int tm, tn;
+    tile_of(u, tm, tn);
+    int m0 = tm * BM, n0 = tn * BN;
 
     // g.kps counts 64-deep k-tiles (the unit of the K split); stages are BK deep
     constexpr int SPT = 64 / BK;  // stages per 64-deep k-tile
@@ -723,10 +748,6 @@ gemm_dtl_kernel(const Args g) {
     const T* __restrict__ B = (const T*)g.B;
 
     f32x4_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int j = 0; j < TN; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     DtlSlab<BM, AK, TL::NT / 64, BK> dA;
     DtlSlab<BN, BKM, TL::NT / 64, BK> dB;
@@ -745,10 +766,11 @@ gemm_dtl_kernel(const Args g) {
     float bs[4] = {0.f, 0.f, 0.f, 0.f};
     const bool do_bias = BIAS && tn == 0;
 
-    auto issue = [&](int kt, T* a_dst, T* b_dst) {
-        dtl_issue<BM, AK, TL::NT / 64, BK>(dA.off, dA.kc, a_dst, A, g.lda, m0, g.M, kt * BK, g.K, wave);
-        dtl_issue<BN, BKM, TL::NT / 64, BK>(dB.off, dB.kc, b_dst, B, g.ldb, n0, g.N, kt * BK, g.K, wave);
+    auto issue_at = [&](int kt, T* a_dst, T* b_dst, int mm0, int nn0) {
+        dtl_issue<BM, AK, TL::NT / 64, BK>(dA.off, dA.kc, a_dst, A, g.lda, mm0, g.M, kt * BK, g.K, wave);
+        dtl_issue<BN, BKM, TL::NT / 64, BK>(dB.off, dB.kc, b_dst, B, g.ldb, nn0, g.N, kt * BK, g.K, wave);
     };
+    auto issue = [&](int kt, T* a_dst, T* b_dst) { issue_at(kt, a_dst, b_dst, m0, n0); };
     auto compute = [&](const T* a_s, const T* b_s) {
         Frag<T> fa[KS][TM], fb[KS][TN];
 #pragma unroll
@@ -810,39 +832,66 @@ gemm_dtl_kernel(const Args g) {
     T* const sB2p = NS == 3 ? sB1 : sB1;
     T* const sA3p = sA2;
     T* const sB3p = sB2;
+    // the first NS - 1 stages of the tile at (mm0, nn0)
+    auto prologue = [&](int mm0, int nn0) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; i++) {
-        const int kt = kt0 + i;
-        if (kt < kt1) {
-            T* ad = i == 0 ? sA0 : i == 1 ? sA1 : sA2;
-            T* bd = i == 0 ? sB0 : i == 1 ? sB1 : sB2;
-            issue(kt, ad, bd);
-        }
-    }
-    for (int kb = kt0; kb < kt1; kb += NS) {
-        GEMM_DTL_STAGE(0)
-        GEMM_DTL_STAGE(1)
-        if constexpr (NS > 2) GEMM_DTL_STAGE(2)
-        if constexpr (NS > 3) GEMM_DTL_STAGE(3)
-    }
-#undef GEMM_DTL_STAGE
-
-    if constexpr (BIAS) {
-        float* red = sbias;  // KG x BM floats
-#pragma unroll
-        for (int e = 0; e < 4; e++) red[bkg * BM + 4 * bq + e] = bs[e];
-        __syncthreads();
-        if (do_bias && tid < BM) {
-            float t = 0.f;
-            for (int q = 0; q < KG; q++) t += red[q * BM + tid];
-            const int m = m0 + tid;
-            if (m < g.M) {
-                if constexpr (EPI == EPI_SPLIT) g.wsb[(size_t)blockIdx.y * g.M + m] = g.alpha * t;
-                else g.dbias[m] += g.alpha * t;
+        for (int i = 0; i < NS - 1; i++) {
+            const int kt = kt0 + i;
+            if (kt < kt1) {
+                T* ad = i == 0 ? sA0 : i == 1 ? sA1 : sA2;
+                T* bd = i == 0 ? sB0 : i == 1 ? sB1 : sB2;
+                issue_at(kt, ad, bd, mm0, nn0);
             }
         }
+    };
+    prologue(m0, n0);
+    while (true) {
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kb = kt0; kb < kt1; kb += NS) {
+            GEMM_DTL_STAGE(0)
+            GEMM_DTL_STAGE(1)
+            if constexpr (NS > 2) GEMM_DTL_STAGE(2)
+            if constexpr (NS > 3) GEMM_DTL_STAGE(3)
+        }
+        // next tile: once every wave is done with the stage buffers (the last
+        // stages were waited for with vmcnt(0), so no load into them is in
+        // flight), request its first stages, then store this one.  The next
+        // tile's first stage waits for everything older than its later stages,
+        // these stores included.
+        const int un = u + (int)gridDim.x;
+        const bool more = PERSIST && un < ntiles;
+        int tm1 = 0, tn1 = 0;
+        if (more) {
+            tile_of(un, tm1, tn1);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads are done
+            asm volatile("s_barrier" ::: "memory");
+            prologue(tm1 * BM, tn1 * BN);
+        }
+        if constexpr (BIAS) {
+            float* red = sbias;  // KG x BM floats
+#pragma unroll
+            for (int e = 0; e < 4; e++) red[bkg * BM + 4 * bq + e] = bs[e];
+            __syncthreads();
+            if (do_bias && tid < BM) {
+                float t = 0.f;
+                for (int q = 0; q < KG; q++) t += red[q * BM + tid];
+                const int m = m0 + tid;
+                if (m < g.M) {
+                    if constexpr (EPI == EPI_SPLIT) g.wsb[(size_t)blockIdx.y * g.M + m] = g.alpha * t;
+                    else g.dbias[m] += g.alpha * t;
+                }
+            }
+        }
+        gemm_epilogue<T, TL, EPI, OutT>(g, acc, m0, n0, wm, wn, l16, g4);
+        if (!more) break;
+        u = un;
+        m0 = tm1 * BM;
+        n0 = tn1 * BN;
     }
-    gemm_epilogue<T, TL, EPI, OutT>(g, acc, m0, n0, wm, wn, l16, g4);
+#undef GEMM_DTL_STAGE
 }
 
 // C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0).
@@ -880,7 +929,7 @@ __global__ void splitk_reduce_kernel(OutT* __restrict__ C, const float* __restri
 
 // ---------------------------------------------------------------- dispatch --
 struct Choice {
-    int bm, bn, wt, splits;
+    int bm, bn, wt, splits, occ, num_cus;
 };
 
 // Tile configurations per element type, with their measured relative per-CU
@@ -929,7 +978,7 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     const int lay = d.a_kmajor && d.b_kmajor ? 0 : (d.a_kmajor ? 1 : 2);
     const double flop_rate = 2.5e15 / 256.0;  // per CU, dense bf16
     const double hbm = 5.0e12;                // bytes/s usable
-    Choice best = {cfgs[0].bm, cfgs[0].bn, cfgs[0].wt, 1};
+    Choice best = {cfgs[0].bm, cfgs[0].bn, cfgs[0].wt, 1, cfgs[0].occ, num_cus};
     double best_cost = 1e300;
     for (int c = 0; c < ncfg; c++) {
         const TileCfg& t = cfgs[c];
@@ -953,7 +1002,7 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
             if (sp > 1) cost += (double)(sp + 1) * d.M * d.N * 4.0 / hbm;
             if (cost < best_cost * 0.999) {
                 best_cost = cost;
-                best = {t.bm, t.bn, t.wt, sp};
+                best = {t.bm, t.bn, t.wt, sp, t.occ, num_cus};
             }
         }
     }
@@ -965,11 +1014,12 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
 #endif
 
 template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS = false>
-void launch_t(const Args& a, dim3 grid, hipStream_t s) {
+void launch_t(const Args& a, dim3 grid, int slots, hipStream_t s) {
     using TL = TileOf<T, BM, BN, WT>;
-    if constexpr (sizeof(T) == 2 && GEMM_DTL)
+    if constexpr (sizeof(T) == 2 && GEMM_DTL) {
+        if (dtl_persistent<BM, BN, WT, EPI, BIAS>() && grid.y == 1) grid.x = std::min((int)grid.x, slots);
         hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
-    else
+    } else
         hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
 }
 
@@ -977,37 +1027,37 @@ void launch_t(const Args& a, dim3 grid, hipStream_t s) {
 // k-contiguous), input-gradient products (A k-contiguous, B k-strided) and
 // weight-gradient products (both k-strided).
 template <typename T, int BM, int BN, int WT>
-int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int epi, hipStream_t s) {
+int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int slots, int epi, hipStream_t s) {
     const int lay = (d.a_kmajor ? 2 : 0) | (d.b_kmajor ? 1 : 0);
     if (lay == 3) {
         switch (epi) {
-            case GEMM_STORE: launch_t<T, BM, BN, WT, true, true, GEMM_STORE, T>(a, grid, s); return 0;
-            case GEMM_BIAS: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS, T>(a, grid, s); return 0;
-            case GEMM_BIAS_GELU: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_GELU, T>(a, grid, s); return 0;
-            case GEMM_BIAS_RESID: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_RESID, T>(a, grid, s); return 0;
+            case GEMM_STORE: launch_t<T, BM, BN, WT, true, true, GEMM_STORE, T>(a, grid, slots, s); return 0;
+            case GEMM_BIAS: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS, T>(a, grid, slots, s); return 0;
+            case GEMM_BIAS_GELU: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_GELU, T>(a, grid, slots, s); return 0;
+            case GEMM_BIAS_RESID: launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_RESID, T>(a, grid, slots, s); return 0;
             case GEMM_BIAS_GELU_SMX:
                 if constexpr (sizeof(T) == 4) {
-                    launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_GELU_SMX, T>(a, grid, s);
+                    launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_GELU_SMX, T>(a, grid, slots, s);
                     return 0;
                 }
                 break;
         }
     } else if (lay == 2) {
         switch (epi) {
-            case GEMM_STORE: launch_t<T, BM, BN, WT, true, false, GEMM_STORE, T>(a, grid, s); return 0;
-            case GEMM_GELU_BWD: launch_t<T, BM, BN, WT, true, false, GEMM_GELU_BWD, T>(a, grid, s); return 0;
-            case EPI_SPLIT: launch_t<T, BM, BN, WT, true, false, EPI_SPLIT, float>(a, grid, s); return 0;
+            case GEMM_STORE: launch_t<T, BM, BN, WT, true, false, GEMM_STORE, T>(a, grid, slots, s); return 0;
+            case GEMM_GELU_BWD: launch_t<T, BM, BN, WT, true, false, GEMM_GELU_BWD, T>(a, grid, slots, s); return 0;
+            case EPI_SPLIT: launch_t<T, BM, BN, WT, true, false, EPI_SPLIT, float>(a, grid, slots, s); return 0;
         }
     } else if (lay == 0) {
         const bool bias = a.dbias != nullptr;
         switch (epi) {
             case GEMM_ACCUM:
-                if (bias) launch_t<T, BM, BN, WT, false, false, GEMM_ACCUM, float, true>(a, grid, s);
-                else launch_t<T, BM, BN, WT, false, false, GEMM_ACCUM, float, false>(a, grid, s);
+                if (bias) launch_t<T, BM, BN, WT, false, false, GEMM_ACCUM, float, true>(a, grid, slots, s);
+                else launch_t<T, BM, BN, WT, false, false, GEMM_ACCUM, float, false>(a, grid, slots, s);
                 return 0;
             case EPI_SPLIT:
-                if (bias) launch_t<T, BM, BN, WT, false, false, EPI_SPLIT, float, true>(a, grid, s);
-                else launch_t<T, BM, BN, WT, false, false, EPI_SPLIT, float, false>(a, grid, s);
+                if (bias) launch_t<T, BM, BN, WT, false, false, EPI_SPLIT, float, true>(a, grid, slots, s);
+                else launch_t<T, BM, BN, WT, false, false, EPI_SPLIT, float, false>(a, grid, slots, s);
                 return 0;
         }
     }
@@ -1016,20 +1066,22 @@ int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int epi, hipStream_t
 
 template <typename T>
 int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, int epi, hipStream_t s) {
+    // resident workgroup slots, a multiple of 8 (one XCD cycle)
+    const int slots = std::max(8, (ch.num_cus * ch.occ) / 8 * 8);
     if constexpr (sizeof(T) == 2) {
         if (ch.wt == 128) {
-            if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 128>(d, a, grid, epi, s);
+            if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 128>(d, a, grid, slots, epi, s);
 #ifdef GEMM_ONLY_TILE_BM
-            if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 128>(d, a, grid, epi, s);
-            if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 128>(d, a, grid, epi, s);
+            if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 128>(d, a, grid, slots, epi, s);
+            if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 128>(d, a, grid, slots, epi, s);
 #endif
             return (int)hipErrorInvalidValue;
         }
-        if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, epi, s);
-        if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 64>(d, a, grid, epi, s);
-        if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 64>(d, a, grid, epi, s);
+        if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, slots, epi, s);
+        if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 64>(d, a, grid, slots, epi, s);
+        if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 64>(d, a, grid, slots, epi, s);
     }
-    if (ch.bm == 128 && ch.bn == 128) return launch_epi<T, 128, 128, 64>(d, a, grid, epi, s);
+    if (ch.bm == 128 && ch.bn == 128) return launch_epi<T, 128, 128, 64>(d, a, grid, slots, epi, s);
     return (int)hipErrorInvalidValue;
 }
 
