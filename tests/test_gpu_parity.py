@@ -155,3 +155,31 @@ def test_loss_at_init_near_log_v():
     g = gpu_step(cfg, 0, params, batches)
     expect = math.log(cfg.vocab_size) + cfg.channels * 0.02 ** 2 / 2
     assert abs(g["means"][0] - expect) < 0.02
+
+
+# token patterns for the sorted, chunked token-embedding gradient: one id
+# everywhere (a single run over every 16-entry chunk), runs of 37 equal ids
+# (runs starting mid-chunk and crossing chunk boundaries), all ids distinct
+TOKEN_PATTERNS = ["one-id", "runs-37", "distinct"]
+
+
+@pytest.mark.parametrize("pattern", TOKEN_PATTERNS)
+def test_fp32_token_embedding_gradient_runs(pattern):
+    cfg, B, T = RAGGED64, 2, 150
+    say("case token runs", pattern)
+    params, [(x, y)] = make_inputs(cfg, B, T, perturb=True)
+    n = B * T
+    if pattern == "one-id":
+        ids = np.full(n, 5)
+    elif pattern == "runs-37":
+        ids = (np.arange(n) // 37 * 11) % cfg.vocab_size
+    else:
+        ids = np.random.default_rng(3).permutation(cfg.vocab_size)[:n]
+    x = ids.reshape(B, T).astype(np.int32)
+    o = oracle_step(cfg, params, [(x, y)], lr=1e-4)
+    g = gpu_step(cfg, 0, params, [(x, y)], lr=1e-4)
+    assert g["code"] == 0
+    for p in ("wte", "wpe"):
+        e = rel_l2(g["grads"][p], o["grads"][p])
+        say(pattern, p, "gradient rel-L2", e)
+        assert e < 1e-4, (pattern, p, e)

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict_
 }
 
 // Sort-based variant (B*T <= 16384), all deterministic:
-//  1. one workgroup sorts the keys (id << shift | position) in LDS (bitonic);
+//  1. the keys (id << shift | position) are sorted by rank (enc_rank_kernel):
 //     equal ids end up adjacent, in increasing position order;
 //  2. one wave per chunk of 16 sorted entries sums each run of equal ids in
 //     order.  A run that neither continues from the previous chunk nor into the
@@ -101,82 +101,100 @@ __global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict_
 //     piece goes to workspace (a run continuing from the previous chunk is a
 //     "head" piece, one that starts here and continues is a "tail" piece);
 //  3. for every tail piece, one wave adds the head pieces of the following
-//     chunks, in chunk order, and adds the total into dwte.
+//     chunks that continue the run, in chunk order, and adds the total into
+//     dwte.
 constexpr int ENC_CHUNK = 16;
 constexpr int ENC_SORT_MAX = 16384;
 
-__global__ __launch_bounds__(1024) void enc_sort_kernel(unsigned* __restrict__ sorted, const int* __restrict__ tok,
-                                                        int BT, int shift) {
-    __shared__ unsigned keys[ENC_SORT_MAX];
-    int n = 1;
-    while (n < BT) n <<= 1;
-    for (int i = threadIdx.x; i < n; i += 1024)
-        keys[i] = i < BT ? (((unsigned)tok[i] << shift) | (unsigned)i) : 0xffffffffu;
+// Keys (id << shift | position) are distinct, so a key's place in sorted
+// order is the number of keys below it.  Each workgroup stages all keys in LDS
+// and ranks 64 of them: lane l of wave w counts the keys below key
+// 64 * blockIdx.x + l among the w-th quarter of the keys (every lane of a wave
+// reads the same LDS words), and the four partial counts are added.
+__global__ __launch_bounds__(256) void enc_rank_kernel(unsigned* __restrict__ sorted, const int* __restrict__ tok,
+                                                       int BT, int shift) {
+    __shared__ __attribute__((aligned(16))) unsigned keys[ENC_SORT_MAX];
+    __shared__ int part[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n4 = (BT + 3) & ~3;
+    for (int j = threadIdx.x; j < n4; j += 256)
+        keys[j] = j < BT ? (((unsigned)tok[j] << shift) | (unsigned)j) : 0xffffffffu;
     __syncthreads();
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += 1024) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const unsigned a = keys[i], b = keys[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) {
-                        keys[i] = b;
-                        keys[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    const int i = blockIdx.x * 64 + lane;
+    const unsigned ki = i < BT ? keys[i] : 0u;
+    const int W = n4 / 4;  // 16-byte words of keys, split into quarters
+    const int j0 = 4 * (wave * W / 4), j1 = 4 * ((wave + 1) * W / 4);
+    int cnt = 0;
+#pragma unroll 8
+    for (int j = j0; j < j1; j += 4) {
+        const uint4 k4 = *reinterpret_cast<const uint4*>(&keys[j]);
+        cnt += (k4.x < ki) + (k4.y < ki) + (k4.z < ki) + (k4.w < ki);
     }
-    for (int i = threadIdx.x; i < BT; i += 1024) sorted[i] = keys[i];
+    part[wave][lane] = cnt;
+    __syncthreads();
+    if (wave == 0 && i < BT) sorted[part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = ki;
 }
 
+// One wave per chunk.  The chunk's keys sit one per lane; the dres row (and
+// the dwte row) of entry i + 1 are requested before entry i is added, so the
+// row reads overlap instead of forming a chain of round trips.
 __global__ __launch_bounds__(256) void enc_chunk_kernel(float* __restrict__ dwte, float* __restrict__ headws,
                                                         float* __restrict__ tailws, int* __restrict__ meta,
                                                         const float* __restrict__ dres,
                                                         const unsigned* __restrict__ sorted, int BT, int C,
                                                         int shift, int nch) {
     constexpr int NV = 8;
+    static_assert(ENC_CHUNK <= 64, "one key per lane");
     const int lane = threadIdx.x & 63;
     const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (c >= nch) return;
-    const int e0 = c * ENC_CHUNK, e1 = min(e0 + ENC_CHUNK, BT);
+    const int e0 = c * ENC_CHUNK, n = min(ENC_CHUNK, BT - e0);
     const unsigned pmask = (1u << shift) - 1u;
     const int prev = e0 > 0 ? (int)(sorted[e0 - 1] >> shift) : -1;
-    const int next = e1 < BT ? (int)(sorted[e1] >> shift) : -1;
+    const int next = e0 + n < BT ? (int)(sorted[e0 + n] >> shift) : -1;
+    const unsigned kl = lane < n ? sorted[e0 + lane] : 0u;
     const int nvec = C / 4;
-    float acc[NV][4];
+    auto key_at = [&](int i) { return (unsigned)__shfl((int)kl, i, 64); };
+    float acc[NV][4], x[NV][4], w[NV][4];
 #pragma unroll
     for (int k = 0; k < NV; k++) acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
-    int head_tok = -1, head_cont = 0, tail_tok = -1, run_start = e0;
-    for (int e = e0; e < e1; e++) {
-        const unsigned key = sorted[e];
-        const int v = (int)(key >> shift);
+    auto load_rows = [&](unsigned key, float (&xr)[NV][4], float (&wr)[NV][4]) {
         const float* r = dres + (long)(key & pmask) * C;
+        const float* q = dwte + (long)(key >> shift) * C;
 #pragma unroll
         for (int k = 0; k < NV; k++) {
             const int vv = lane + 64 * k;
             if (vv < nvec) {
-                float x[4];
-                load4<float>(r + vv * 4, x);
-#pragma unroll
-                for (int q = 0; q < 4; q++) acc[k][q] += x[q];
+                load4<float>(r + vv * 4, xr[k]);
+                load4<float>(q + vv * 4, wr[k]);
             }
         }
-        const bool end = (e == e1 - 1) || (int)(sorted[e + 1] >> shift) != v;
+    };
+    load_rows(key_at(0), x, w);
+    int head_tok = -1, head_cont = 0, tail_tok = -1, run_start = 0;
+    for (int i = 0; i < n; i++) {
+        const unsigned key = key_at(i);
+        const int v = (int)(key >> shift);
+        const bool last = i == n - 1;
+        const unsigned knext = key_at(last ? i : i + 1);
+        float xn[NV][4], wn[NV][4];
+        if (!last) load_rows(knext, xn, wn);
+#pragma unroll
+        for (int k = 0; k < NV; k++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) acc[k][q] += x[k][q];
+        const bool end = last || (int)(knext >> shift) != v;
         if (end) {
-            const bool head = run_start == e0 && prev == v;
-            const bool tail = e == e1 - 1 && next == v;
+            const bool head = run_start == 0 && prev == v;
+            const bool tail = last && next == v;
             float* dst = (!head && !tail) ? dwte + (long)v * C : (head ? headws : tailws) + (long)c * C;
 #pragma unroll
             for (int k = 0; k < NV; k++) {
                 const int vv = lane + 64 * k;
                 if (vv < nvec) {
-                    float o[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (!head && !tail) load4<float>(dst + vv * 4, o);
+                    float o[4];
 #pragma unroll
-                    for (int q = 0; q < 4; q++) o[q] += acc[k][q];
+                    for (int q = 0; q < 4; q++) o[q] = ((!head && !tail) ? w[k][q] : 0.f) + acc[k][q];
                     store4<float>(dst + vv * 4, o);
                 }
                 acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
@@ -187,7 +205,16 @@ __global__ __launch_bounds__(256) void enc_chunk_kernel(float* __restrict__ dwte
             } else if (tail) {
                 tail_tok = v;
             }
-            run_start = e + 1;
+            run_start = i + 1;
+        }
+        if (!last) {
+#pragma unroll
+            for (int k = 0; k < NV; k++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    x[k][q] = xn[k][q];
+                    w[k][q] = wn[k][q];
+                }
         }
     }
     if (lane == 0) {
@@ -197,15 +224,29 @@ __global__ __launch_bounds__(256) void enc_chunk_kernel(float* __restrict__ dwte
     }
 }
 
+// One wave per chunk with a tail piece of token v: the run continues as the
+// head pieces of chunks c+1 .. cl, where cl holds v's last entry (found by a
+// binary search over the sorted keys); those pieces are added in chunk order,
+// four reads in flight.
 __global__ __launch_bounds__(256) void enc_fix_kernel(float* __restrict__ dwte, const float* __restrict__ headws,
                                                       const float* __restrict__ tailws, const int* __restrict__ meta,
-                                                      int C, int nch) {
+                                                      const unsigned* __restrict__ sorted, int BT, int shift, int C,
+                                                      int nch) {
     constexpr int NV = 8;
     const int lane = threadIdx.x & 63;
     const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (c >= nch) return;
     const int v = meta[3 * c + 2];
     if (v < 0) return;
+    // first index with a key above every key of v
+    const unsigned lim = ((unsigned)(v + 1)) << shift;
+    int lo = (c + 1) * ENC_CHUNK, hi = BT;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sorted[mid] < lim) lo = mid + 1;
+        else hi = mid;
+    }
+    const int cl = (lo - 1) / ENC_CHUNK;
     const int nvec = C / 4;
     float acc[NV][4];
 #pragma unroll
@@ -214,7 +255,25 @@ __global__ __launch_bounds__(256) void enc_fix_kernel(float* __restrict__ dwte, 
         acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
         if (vv < nvec) load4<float>(tailws + (long)c * C + vv * 4, acc[k]);
     }
-    for (int c2 = c + 1; c2 < nch; c2++) {
+    int c2 = c + 1;
+    for (; c2 + 3 <= cl; c2 += 4) {
+        float h[4][NV][4];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int k = 0; k < NV; k++) {
+                const int vv = lane + 64 * k;
+                if (vv < nvec) load4<float>(headws + (long)(c2 + u) * C + vv * 4, h[u][k]);
+            }
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int k = 0; k < NV; k++)
+                if (lane + 64 * k < nvec)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) acc[k][q] += h[u][k][q];
+    }
+    for (; c2 <= cl; c2++) {
 #pragma unroll
         for (int k = 0; k < NV; k++) {
             const int vv = lane + 64 * k;
@@ -225,7 +284,6 @@ __global__ __launch_bounds__(256) void enc_fix_kernel(float* __restrict__ dwte, 
                 for (int q = 0; q < 4; q++) acc[k][q] += x[q];
             }
         }
-        if (!meta[3 * c2 + 1]) break;
     }
     float* w = dwte + (long)v * C;
 #pragma unroll
@@ -489,10 +547,11 @@ int encoder_bwd_launch(float* dwte, float* dwpe, const float* dres, const int* t
         w += ((size_t)nch * 12 + 255) / 256 * 256;
         float* headws = (float*)w;
         float* tailws = headws + (size_t)nch * C;
-        hipLaunchKernelGGL(enc_sort_kernel, dim3(1), dim3(1024), 0, s, sorted, tok, BT, shift);
+        hipLaunchKernelGGL(enc_rank_kernel, dim3((BT + 63) / 64), dim3(256), 0, s, sorted, tok, BT, shift);
         hipLaunchKernelGGL(enc_chunk_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, dres,
                            sorted, BT, C, shift, nch);
-        hipLaunchKernelGGL(enc_fix_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, C, nch);
+        hipLaunchKernelGGL(enc_fix_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, sorted, BT,
+                           shift, C, nch);
     } else {
         hipLaunchKernelGGL(encoder_bwd_wte_kernel, dim3((BT + 3) / 4), dim3(256), 0, s, dwte, dres, tok, BT, C);
     }
