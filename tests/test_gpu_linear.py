@@ -21,7 +21,7 @@ from helpers import rel_l2, say
 pytestmark = pytest.mark.gpu
 
 # (M, K, N): ragged layer-sized products, and a classifier-shaped one
-SHAPES = [(8232, 776, 3120), (8200, 3080, 776), (4104, 768, 50304)]
+SHAPES = [(8232, 776, 3120), (8200, 3080, 776), (4104, 768, 50304), (8232, 776, 1000)]
 
 
 def _rows(M, n, seed):

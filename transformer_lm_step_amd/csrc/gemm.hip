@@ -64,7 +64,7 @@ struct Tile {
     static constexpr int WM = BM / WTM, WN = BN / WTN;
     static constexpr int NT = 64 * WM * WN;          // threads per workgroup
     static constexpr int TM = WTM / 16, TN = WTN / 16;  // 16x16 MFMA tiles per wave
-    static constexpr int OCC = NT == 256 && WTM == 64 ? 2 : 1;  // workgroups per CU
+    static constexpr int OCC = NT == 256 && WTM == 64 && WTN == 64 ? 2 : 1;  // workgroups per CU
     // slab prefetch distance and fragment buffers, within the register budget
     // of NT/256 * OCC waves per SIMD
     static constexpr int DEPTH = WTM * WTN == 64 * 64 ? (NT <= 512 ? 2 : 1)
@@ -73,10 +73,10 @@ struct Tile {
 };
 
 // Wave tile selector used by the kernels' template argument WT: 64 -> 64x64,
-// 128 -> 128x64 outputs per wave (128x128 waves need 256 accumulators per lane,
-// which the compiler only fits by spilling).
+// 96 -> 64x96, 128 -> 128x64 outputs per wave (128x128 waves need 256
+// accumulators per lane, which the compiler only fits by spilling).
 template <typename T, int BM, int BN, int WT>
-using TileOf = Tile<T, BM, BN, (WT >= 128 ? 128 : 64), (WT == 256 ? 128 : 64)>;
+using TileOf = Tile<T, BM, BN, (WT >= 128 ? 128 : 64), (WT == 256 ? 128 : WT == 96 ? 96 : 64)>;
 
 // Per-thread register count for staging an R x BK slab (both layouts).
 template <int R, int NT> struct StageRegs {
@@ -950,11 +950,17 @@ struct TileCfg {
     int bm, bn, wt, occ;
     double speed[3];  // forward, input gradient, weight gradient
 };
+#ifndef GEMM_SPEED_192
+#define GEMM_SPEED_192 0.92
+#endif
 const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}},
                             {256, 128, 64, 1, {0.92, 0.76, 0.66}},
                             {128, 256, 64, 1, {0.71, 0.92, 0.70}},
                             {128, 128, 64, 2, {0.81, 0.82, 0.70}},
                             {256, 256, 128, 1, {1.00, 0.95, 1.00}},
+                            // forward products only: a k-strided slab needs
+                            // a power-of-two row count
+                            {128, 192, 96, 1, {GEMM_SPEED_192, 0.0, 0.0}},
 #ifdef GEMM_ONLY_TILE_BM
                             {256, 128, 128, 1, {1.0, 1.0, 1.0}},
                             {128, 256, 128, 1, {1.0, 1.0, 1.0}},
@@ -1029,6 +1035,9 @@ void launch_t(const Args& a, dim3 grid, int slots, hipStream_t s) {
 template <typename T, int BM, int BN, int WT>
 int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int slots, int epi, hipStream_t s) {
     const int lay = (d.a_kmajor ? 2 : 0) | (d.b_kmajor ? 1 : 0);
+    // k-strided slabs (input- and weight-gradient layouts) need power-of-two rows
+    constexpr bool KSTRIDED = (BM & (BM - 1)) == 0 && (BN & (BN - 1)) == 0;
+    if (lay != 3 && !KSTRIDED) return (int)hipErrorInvalidValue;
     if (lay == 3) {
         switch (epi) {
             case GEMM_STORE: launch_t<T, BM, BN, WT, true, true, GEMM_STORE, T>(a, grid, slots, s); return 0;
@@ -1042,6 +1051,8 @@ int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int slots, int epi, 
                 }
                 break;
         }
+    } else if constexpr (!KSTRIDED) {
+        return (int)hipErrorInvalidValue;
     } else if (lay == 2) {
         switch (epi) {
             case GEMM_STORE: launch_t<T, BM, BN, WT, true, false, GEMM_STORE, T>(a, grid, slots, s); return 0;
@@ -1077,6 +1088,7 @@ int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, i
 #endif
             return (int)hipErrorInvalidValue;
         }
+        if (ch.wt == 96 && ch.bm == 128 && ch.bn == 192) return launch_epi<T, 128, 192, 96>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 64>(d, a, grid, slots, epi, s);
