@@ -552,10 +552,18 @@ DEV constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((
 #ifndef GEMM_DTL_NS_RECT
 #define GEMM_DTL_NS_RECT 3
 #endif
+#ifndef GEMM_DTL_BK256
+#define GEMM_DTL_BK256 64
+#endif
+#ifndef GEMM_DTL_NS256
+#define GEMM_DTL_NS256 2
+#endif
 template <int BM, int BN>
 struct DtlCfg {
-    static constexpr int BK = (BM == 128 && BN == 128) ? GEMM_DTL_BK128 : 64;
-    static constexpr int NS = (BM == 128 && BN == 128) ? GEMM_DTL_NS128 : (BM != BN ? GEMM_DTL_NS_RECT : 2);
+    static constexpr int BK = (BM == 128 && BN == 128) ? GEMM_DTL_BK128 : (BM == 256 && BN == 256) ? GEMM_DTL_BK256 : 64;
+    static constexpr int NS = (BM == 128 && BN == 128) ? GEMM_DTL_NS128
+                              : (BM == 256 && BN == 256) ? GEMM_DTL_NS256
+                              : (BM != BN ? GEMM_DTL_NS_RECT : 2);
 };
 
 // chunk swizzle of a k-contiguous slab row (16-byte chunks; 8 per 64-deep
@@ -615,6 +623,16 @@ DEV void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const void* lds) {
                  : "memory", "m0");
 }
 
+// The buffer resource of an LDS-destination load must sit in scalar registers;
+// built from readfirstlane'd fields it does even where the compiler holds the
+// tile coordinates in vector registers (all lanes hold the same values).
+DEV __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t u = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
+
 // Issue this wave's loads of the slab at (rows r0.., contraction k0..) into dst
 // (per-lane offsets and, k-contiguous, contraction indices from DtlSlab).
 template <int R, bool KMAJ, int NW, int BK>
@@ -624,14 +642,14 @@ DEV void dtl_issue(const uint32_t* off, const int* kc, bf16_t* dst, const bf16_t
     if constexpr (KMAJ) {
         const long org = (long)r0 * ld + k0;
         const uint32_t bytes = (uint32_t)max(0L, ((long)Rmax * ld - org) * 2);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p + org, bytes);
+        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(p + org, bytes);
         const int klim = K - k0;
 #pragma unroll
         for (int q = 0; q < NQ; q++) lds_dma16(rs, kc[q] < klim ? off[q] : kBufOOB, dst + (wave + NW * q) * 512);
     } else {
         const long org = (long)k0 * ld + r0;
         const uint32_t bytes = (uint32_t)max(0L, ((long)K * ld - org) * 2);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p + org, bytes);
+        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(p + org, bytes);
 #pragma unroll
         for (int q = 0; q < NQ; q++) lds_dma16(rs, off[q], dst + (wave + NW * q) * 512);
     }
