@@ -552,6 +552,9 @@ DEV constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((
 #ifndef GEMM_DTL_NS_RECT
 #define GEMM_DTL_NS_RECT 3
 #endif
+#ifndef GEMM_HALF_LOADERS
+#define GEMM_HALF_LOADERS 1
+#endif
 #ifndef GEMM_DTL_BK256
 #define GEMM_DTL_BK256 64
 #endif
@@ -767,15 +770,26 @@ gemm_dtl_kernel(const Args g) {
 
     f32x4_t acc[TM][TN];
 
-    DtlSlab<BM, AK, TL::NT / 64, BK> dA;
-    DtlSlab<BN, BKM, TL::NT / 64, BK> dB;
-    dA.init(g.lda, lane, wave);
-    dB.init(g.ldb, lane, wave);
+    // Waves that issue the LDS-destination loads: in the 8-wave rectangular
+    // tiles only waves 0-3, one per SIMD, each issuing twice the share.  A
+    // 1 KB load holds the CU's vector-memory path for many cycles and a wave
+    // issues in order, so a loading wave stalls at the start of each stage;
+    // its SIMD partner (wave w + 4) runs its MFMAs meanwhile instead of
+    // stalling too (2-5% on those tiles; the 256x256 tile with 128-row waves
+    // has no registers for the doubled load offsets).
+    constexpr int NL = (NW == 8 && BM != BN && GEMM_HALF_LOADERS) ? 4 : NW;
+    const bool loads = NL == NW || wave < NL;
+    const int lw = NL == NW ? wave : wave % NL;
+    DtlSlab<BM, AK, NL, BK> dA;
+    DtlSlab<BN, BKM, NL, BK> dB;
+    dA.init(g.lda, lane, lw);
+    dB.init(g.ldb, lane, lw);
     DtlFrag<BM, AK, TM, BK> fA;
     DtlFrag<BN, BKM, TN, BK> fB;
     fA.init(wm * TL::WTM, l16, g4);
     fB.init(wn * TL::WTN, l16, g4);
-    constexpr int NQS = DtlSlab<BM, AK, TL::NT / 64, BK>::NQ + DtlSlab<BN, BKM, TL::NT / 64, BK>::NQ;
+    constexpr int NQS = DtlSlab<BM, AK, NL, BK>::NQ + DtlSlab<BN, BKM, NL, BK>::NQ;
+    static_assert((NS - 1) * NQS <= 63, "vmcnt range");
 
     // fused bias gradient: column sums over k of the k-strided A slab
     constexpr int MQ = BM / 4, KG = NT / MQ, KPG = BK / KG;
@@ -785,8 +799,10 @@ gemm_dtl_kernel(const Args g) {
     const bool do_bias = BIAS && tn == 0;
 
     auto issue_at = [&](int kt, T* a_dst, T* b_dst, int mm0, int nn0) {
-        dtl_issue<BM, AK, TL::NT / 64, BK>(dA.off, dA.kc, a_dst, A, g.lda, mm0, g.M, kt * BK, g.K, wave);
-        dtl_issue<BN, BKM, TL::NT / 64, BK>(dB.off, dB.kc, b_dst, B, g.ldb, nn0, g.N, kt * BK, g.K, wave);
+        if (loads) {
+            dtl_issue<BM, AK, NL, BK>(dA.off, dA.kc, a_dst, A, g.lda, mm0, g.M, kt * BK, g.K, wave);
+            dtl_issue<BN, BKM, NL, BK>(dB.off, dB.kc, b_dst, B, g.ldb, nn0, g.N, kt * BK, g.K, wave);
+        }
     };
     auto issue = [&](int kt, T* a_dst, T* b_dst) { issue_at(kt, a_dst, b_dst, m0, n0); };
     auto compute = [&](const T* a_s, const T* b_s) {
