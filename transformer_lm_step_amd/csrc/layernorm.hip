@@ -22,9 +22,15 @@
 
 namespace {
 
-// 8 rows per backward workgroup (2 per wave): enough workgroups to keep
-// several waves per SIMD in flight on 8192 rows.
+// Backward workgroups take 2 rows per wave: 16 waves (32 rows) when a row
+// fits in at most 2 vectors per lane (register budget of 16 waves), else 4
+// waves (8 rows, and the workspace is sized for this smaller count).  Fewer, larger workgroups leave fewer
+// per-workgroup partial sums for the finishing reduction to read.
 constexpr int ROWS_PER_BLOCK_BWD = 8;
+#ifndef LN_BWD_WAVES
+#define LN_BWD_WAVES 16
+#endif
+template <int NV> constexpr int ln_bwd_waves() { return NV <= 2 ? LN_BWD_WAVES : 4; }
 
 // NV: 16-byte vectors per lane, ceil(C / (64 * VEC)), fixed at launch so the
 // row buffers take only the registers C needs.
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out, float*
 }
 
 template <typename T, int NV>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T* __restrict__ dres_lp,
+__global__ __launch_bounds__(64 * ln_bwd_waves<NV>()) void ln_bwd_kernel(float* __restrict__ dres, T* __restrict__ dres_lp,
                                                      float* __restrict__ partial, const T* __restrict__ dy,
                                                      const T* __restrict__ x, const T* __restrict__ w,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -101,9 +107,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T
         for (int e = 0; e < VEC; e++) { dw_acc[i][e] = 0.f; db_acc[i][e] = 0.f; wv[i][e] = 0.f; }
         if (v < nvec) unpack16<T>(ld16(w + v * VEC), wv[i]);
     }
-    const int r0 = blockIdx.x * ROWS_PER_BLOCK_BWD;
-    const int r1 = min(r0 + ROWS_PER_BLOCK_BWD, N);
-    for (int row = r0 + wave; row < r1; row += 4) {
+    constexpr int NWV = ln_bwd_waves<NV>();
+    const int r0 = blockIdx.x * 2 * NWV;
+    const int r1 = min(r0 + 2 * NWV, N);
+    for (int row = r0 + wave; row < r1; row += NWV) {
         const float m = mean[row], rs = rstd[row];
         const T* xr = x + (size_t)row * C;
         const T* gr = dy + (size_t)row * C;
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T
             }
         }
     }
-    // combine the 4 waves in order 0,1,2,3
-    for (int wv_turn = 0; wv_turn < 4; wv_turn++) {
+    // combine the waves in order 0, 1, 2, ...
+    for (int wv_turn = 0; wv_turn < NWV; wv_turn++) {
         if (wave == wv_turn) {
 #pragma unroll
             for (int i = 0; i < NV; i++) {
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(float* __restrict__ dres, T
         __syncthreads();
     }
     float* p = partial + (size_t)blockIdx.x * 2 * C;
-    for (int c = threadIdx.x; c < C; c += 256) {
+    for (int c = threadIdx.x; c < C; c += 64 * NWV) {
         p[c] = red[c];
         p[C + c] = red[2048 + c];
     }
@@ -242,10 +249,13 @@ size_t layernorm_bwd_workspace_bytes(int N, int C) {
 }
 
 template <typename T, int NV>
-void ln_bwd_nv(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean, const float* rstd,
-               int N, int C, int accumulate, float* partial, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(blocks), dim3(256), 0, s, dres, dres_lp, partial, dy, x, w,
+int ln_bwd_nv(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean, const float* rstd,
+              int N, int C, int accumulate, float* partial, hipStream_t s) {
+    constexpr int NWV = ln_bwd_waves<NV>();
+    const int blocks = (N + 2 * NWV - 1) / (2 * NWV);
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(blocks), dim3(64 * NWV), 0, s, dres, dres_lp, partial, dy, x, w,
                        mean, rstd, N, C, accumulate);
+    return blocks;
 }
 
 template <typename T>
@@ -253,17 +263,17 @@ int layernorm_bwd_launch(float* dres, T* dres_lp, float* dw, float* db, const T*
                          const T* w, const float* mean, const float* rstd, int N, int C,
                          int accumulate, float* partial, hipStream_t s) {
     if (N <= 0) return 0;
-    const int blocks = (N + ROWS_PER_BLOCK_BWD - 1) / ROWS_PER_BLOCK_BWD;
     const int nv = (C / VecT<T>::N + 63) / 64;
+    int blocks = 0;
     switch (nv) {
-        case 1: ln_bwd_nv<T, 1>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
-        case 2: ln_bwd_nv<T, 2>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
-        case 3: ln_bwd_nv<T, 3>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
-        case 4: ln_bwd_nv<T, 4>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s); break;
+        case 1: blocks = ln_bwd_nv<T, 1>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+        case 2: blocks = ln_bwd_nv<T, 2>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+        case 3: blocks = ln_bwd_nv<T, 3>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+        case 4: blocks = ln_bwd_nv<T, 4>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
         default:
             if constexpr (sizeof(T) == 4) {
                 if (nv <= 8) {
-                    ln_bwd_nv<T, 8>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, blocks, s);
+                    blocks = ln_bwd_nv<T, 8>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s);
                     break;
                 }
             }
