@@ -647,8 +647,13 @@ DEV void dtl_issue(const uint32_t* off, const int* kc, bf16_t* dst, const bf16_t
         const uint32_t bytes = (uint32_t)max(0L, ((long)Rmax * ld - org) * 2);
         const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(p + org, bytes);
         const int klim = K - k0;
+        // every load of the wave starts at the same chunk of its row (the chunk
+        // swizzle repeats every 8 rows and each load is 512 / BK rows further
+        // on), so one offset and one contraction index serve all NQ loads
+        const uint32_t qstride = (uint32_t)((512 / BK) * NW * ld * 2);
+        const bool kin = kc[0] < klim;
 #pragma unroll
-        for (int q = 0; q < NQ; q++) lds_dma16(rs, kc[q] < klim ? off[q] : kBufOOB, dst + (wave + NW * q) * 512);
+        for (int q = 0; q < NQ; q++) lds_dma16(rs, kin ? off[0] + q * qstride : kBufOOB, dst + (wave + NW * q) * 512);
     } else {
         const long org = (long)k0 * ld + r0;
         const uint32_t bytes = (uint32_t)max(0L, ((long)K * ld - org) * 2);
@@ -731,7 +736,9 @@ gemm_dtl_kernel(const Args g) {
     __shared__ float sbias[BIAS ? (NT / (BM / 4)) * BM : 1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // (the wave index is the same in all lanes; readfirstlane lets the
+    // compiler see that, so branches on it are scalar)
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % TL::WM, wn = wave / TL::WM;
     const int l16 = lane & 15, g4 = lane >> 4;
 
@@ -775,9 +782,10 @@ gemm_dtl_kernel(const Args g) {
     // 1 KB load holds the CU's vector-memory path for many cycles and a wave
     // issues in order, so a loading wave stalls at the start of each stage;
     // its SIMD partner (wave w + 4) runs its MFMAs meanwhile instead of
-    // stalling too (2-5% on those tiles; the 256x256 tile with 128-row waves
-    // has no registers for the doubled load offsets).
-    constexpr int NL = (NW == 8 && BM != BN && GEMM_HALF_LOADERS) ? 4 : NW;
+    // stalling too (2-5% on those tiles).  The 256x256 tile with 128-row waves
+    // does it only with both operands k-contiguous: a k-strided slab keeps one
+    // offset register per load, and it has no registers for twice as many.
+    constexpr int NL = (NW == 8 && (BM != BN || (AK && BKM)) && GEMM_HALF_LOADERS) ? 4 : NW;
     const bool loads = NL == NW || wave < NL;
     const int lw = NL == NW ? wave : wave % NL;
     DtlSlab<BM, AK, NL, BK> dA;
