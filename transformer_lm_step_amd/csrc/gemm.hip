@@ -777,15 +777,13 @@ gemm_dtl_kernel(const Args g) {
 
     f32x4_t acc[TM][TN];
 
-    // Waves that issue the LDS-destination loads: in the 8-wave rectangular
-    // tiles only waves 0-3, one per SIMD, each issuing twice the share.  A
+    // Waves that issue the LDS-destination loads: in the 8-wave tiles only
+    // waves 0-3, one per SIMD, each issuing twice the share.  A
     // 1 KB load holds the CU's vector-memory path for many cycles and a wave
     // issues in order, so a loading wave stalls at the start of each stage;
     // its SIMD partner (wave w + 4) runs its MFMAs meanwhile instead of
-    // stalling too (2-5% on those tiles).  The 256x256 tile with 128-row waves
-    // does it only with both operands k-contiguous: a k-strided slab keeps one
-    // offset register per load, and it has no registers for twice as many.
-    constexpr int NL = (NW == 8 && (BM != BN || (AK && BKM)) && GEMM_HALF_LOADERS) ? 4 : NW;
+    // stalling too (2-8% on the 8-wave tiles).
+    constexpr int NL = (NW == 8 && GEMM_HALF_LOADERS) ? 4 : NW;
     const bool loads = NL == NW || wave < NL;
     const int lw = NL == NW ? wave : wave % NL;
     DtlSlab<BM, AK, NL, BK> dA;
