@@ -182,9 +182,9 @@ DEV void slab_store(const uint4* r, T* __restrict__ s, int tid) {
 
 // Epilogue of one workgroup tile: lane holds C[m][n .. n+3] for its
 // TM x TN 16x16 MFMA tiles.
-template <typename T, typename TL, int EPI, typename OutT>
+template <typename T, typename TL, int EPI, typename OutT, bool STG = false>
 DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int m0, int n0, int wm, int wn, int l16,
-                       int g4) {
+                       int g4, bf16_t* stage = nullptr) {
     constexpr int TM = TL::TM, TN = TL::TN;
     if constexpr (EPI == GEMM_BIAS_GELU_SMX) {
         // G = gelu(v + bias) stored, plus (max, sum exp(G - max)) of each row
@@ -283,6 +283,31 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
                 }
         }
     };
+    // bf16 outputs with a staging area (16 rows of this wave's columns in
+    // LDS): a 16-row slice of the wave's tile is written to LDS as computed
+    // (lane: one row, 4 columns per 16-column tile) and read back as 16-byte
+    // pieces of whole rows, so each store instruction writes full 128-byte
+    // lines instead of 32 bytes in each of 16 rows.
+    constexpr int SRP = TL::WTN + 8;            // staging row pitch (elements)
+    constexpr int SPR = TL::WTN / 8;            // 16-byte pieces per row
+    constexpr int SPI = (16 * SPR + 63) / 64;   // store instructions per slice
+    constexpr bool STAGED = STG && sizeof(OutT) == 2 && EPI != EPI_SPLIT && EPI != GEMM_ACCUM &&
+                            EPI != GEMM_BIAS_GELU_SMX;
+    auto put = [&](int j, const float* v) {  // this lane's 4 values of tile j into the slice
+        st8(stage + l16 * SRP + 16 * j + 4 * g4, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
+    };
+    auto flush = [&](void* dst, long ld, int mrow0, int ncol0) {  // slice rows -> memory
+#pragma unroll
+        for (int k = 0; k < SPI; k++) {
+            const int slot = (l16 + 16 * g4) + 64 * k;
+            const int row = slot / SPR, col = 8 * (slot % SPR);
+            if (slot < 16 * SPR) {
+                const uint4 d = ld16(stage + row * SRP + col);
+                const int m = mrow0 + row, n = ncol0 + col;
+                if (m < g.M && n < g.N) st16((bf16_t*)dst + (size_t)m * ld + n, d);
+            }
+        }
+    };
     if constexpr (!TIGHT) load_group(0, aux[0]);
 #pragma unroll
     for (int i = 0; i < TM; i++) {
@@ -291,6 +316,53 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
             else if (i % G == 0 && i + G < TM) load_group(i / G + 1, aux[(i / G + 1) % NBUF]);
         }
         const int m = mb + 16 * i;
+        if constexpr (STAGED) {
+            // every lane takes part in the slice exchange, in range or not
+            float vo[TN][4], vp[TN][4];
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) v[r] = g.alpha * acc[i][j][r];
+                float a[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (HAS_AUX) {
+                    const uint2 u = (const uint2&)aux[(i / G) % NBUF][i % G][j];
+                    a[0] = __uint_as_float(u.x << 16); a[1] = __uint_as_float(u.x & 0xffff0000u);
+                    a[2] = __uint_as_float(u.y << 16); a[3] = __uint_as_float(u.y & 0xffff0000u);
+                }
+                if constexpr (HAS_BIAS) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) v[r] += bb[j][r];
+                }
+                if constexpr (EPI == GEMM_BIAS_GELU) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        vp[j][r] = v[r];
+                        v[r] = gelu_f<T>(to_f<T>(from_f<T>(v[r])));
+                    }
+                }
+                if constexpr (EPI == GEMM_BIAS_RESID) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) v[r] += a[r];
+                }
+                if constexpr (EPI == GEMM_GELU_BWD) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) v[r] *= gelu_grad_f<T>(a[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) vo[j][r] = v[r];
+            }
+            const int mrow0 = m0 + wm * TL::WTM + 16 * i, ncol0 = n0 + wn * TL::WTN;
+            if constexpr (EPI == GEMM_BIAS_GELU) {
+#pragma unroll
+                for (int j = 0; j < TN; j++) put(j, vp[j]);
+                flush(g.aux_out, g.ldaux, mrow0, ncol0);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) put(j, vo[j]);
+            flush(g.C, g.ldc, mrow0, ncol0);
+            continue;
+        }
         if (m >= g.M) continue;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
@@ -925,7 +997,18 @@ gemm_dtl_kernel(const Args g) {
                 }
             }
         }
-        gemm_epilogue<T, TL, EPI, OutT>(g, acc, m0, n0, wm, wn, l16, g4);
+        // bf16 outputs are staged through the LDS buffer of stage NS - 1 (the
+        // larger of its two slabs), which no load targets until the next
+        // tile's first stage; every wave must be done reading it first
+        T* const lastA = NS == 2 ? sA1 : NS == 3 ? sA2 : sA3;
+        T* const lastB = NS == 2 ? sB1 : NS == 3 ? sB2 : sB3;
+        constexpr bool CAN_STAGE = NW * 16 * (TL::WTN + 8) <= (BM > BN ? BM : BN) * BK;
+        T* const stage = (BN >= BM ? lastB : lastA) + wave * 16 * (TL::WTN + 8);
+        if (CAN_STAGE && !more) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            asm volatile("s_barrier" ::: "memory");
+        }
+        gemm_epilogue<T, TL, EPI, OutT, CAN_STAGE>(g, acc, m0, n0, wm, wn, l16, g4, stage);
         if (!more) break;
         u = un;
         m0 = tm1 * BM;
