@@ -308,6 +308,23 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
             }
         }
     };
+    // fp32 outputs (split partials, accumulated weight gradients) the same
+    // way, 8 rows at a time (a staged row is 4x wider than a bf16 one)
+    constexpr bool STAGED32 = STG && sizeof(OutT) == 4 && (EPI == EPI_SPLIT || EPI == GEMM_ACCUM);
+    constexpr int SRP32 = TL::WTN + 4, SPR32 = TL::WTN / 4, SPI32 = (8 * SPR32 + 63) / 64;
+    float* const stage32 = (float*)stage;
+    auto flush32 = [&](float* dst, long ld, int mrow0, int ncol0) {
+#pragma unroll
+        for (int k = 0; k < SPI32; k++) {
+            const int slot = (l16 + 16 * g4) + 64 * k;
+            const int row = slot / SPR32, col = 4 * (slot % SPR32);
+            if (slot < 8 * SPR32) {
+                const uint4 d = ld16(stage32 + row * SRP32 + col);
+                const int m = mrow0 + row, n = ncol0 + col;
+                if (m < g.M && n < g.N) st16(dst + (size_t)m * ld + n, d);
+            }
+        }
+    };
     if constexpr (!TIGHT) load_group(0, aux[0]);
 #pragma unroll
     for (int i = 0; i < TM; i++) {
@@ -316,6 +333,32 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
             else if (i % G == 0 && i + G < TM) load_group(i / G + 1, aux[(i / G + 1) % NBUF]);
         }
         const int m = mb + 16 * i;
+        if constexpr (STAGED32) {
+            float vo[TN][4];
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) vo[j][r] = g.alpha * acc[i][j][r];
+                if constexpr (EPI == GEMM_ACCUM) {
+                    const float4 u = (const float4&)aux[(i / G) % NBUF][i % G][j];
+                    vo[j][0] += u.x; vo[j][1] += u.y; vo[j][2] += u.z; vo[j][3] += u.w;
+                }
+            }
+            float* const dst = EPI == EPI_SPLIT ? g.ws + (size_t)blockIdx.y * g.M * g.N : (float*)g.C;
+            const long ld = EPI == EPI_SPLIT ? (long)g.N : g.ldc;
+            const int mrow0 = m0 + wm * TL::WTM + 16 * i, ncol0 = n0 + wn * TL::WTN;
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                if ((l16 >> 3) == h) {
+#pragma unroll
+                    for (int j = 0; j < TN; j++)
+                        *reinterpret_cast<float4*>(stage32 + (l16 - 8 * h) * SRP32 + 16 * j + 4 * g4) =
+                            make_float4(vo[j][0], vo[j][1], vo[j][2], vo[j][3]);
+                }
+                flush32(dst, ld, mrow0 + 8 * h, ncol0);
+            }
+            continue;
+        }
         if constexpr (STAGED) {
             // every lane takes part in the slice exchange, in range or not
             float vo[TN][4], vp[TN][4];
