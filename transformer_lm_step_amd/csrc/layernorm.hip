@@ -22,13 +22,13 @@
 
 namespace {
 
-// Backward workgroups take 2 rows per wave: 16 waves (32 rows) when a row
-// fits in at most 2 vectors per lane (register budget of 16 waves), else 4
-// waves (8 rows, and the workspace is sized for this smaller count).  Fewer, larger workgroups leave fewer
+// Backward workgroups take 2 rows per wave: 8 waves (16 rows) when a row
+// fits in at most 2 vectors per lane, else 4 waves (8 rows, and the workspace
+// is sized for this smaller count).  Fewer, larger workgroups leave fewer
 // per-workgroup partial sums for the finishing reduction to read.
 constexpr int ROWS_PER_BLOCK_BWD = 8;
 #ifndef LN_BWD_WAVES
-#define LN_BWD_WAVES 16
+#define LN_BWD_WAVES 8
 #endif
 template <int NV> constexpr int ln_bwd_waves() { return NV <= 2 ? LN_BWD_WAVES : 4; }
 
