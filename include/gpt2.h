@@ -158,6 +158,15 @@ int gpt2_check_device_error(gpt2_ctx* ctx, void* hip_stream);
 enum { GPT2_T_LOGITS = 0, GPT2_T_LNF = 1, GPT2_T_RESIDUAL = 2, GPT2_T_DRESIDUAL = 3, GPT2_T_ENCODED = 4 };
 int gpt2_act_tensor(gpt2_ctx* ctx, int which, void** d_ptr, size_t* count);
 
+/* Timing hook (diagnostics): with n > 0, every later gpt2_forward records
+ * d_start_events[i] just before and d_end_events[i] just after its classifier
+ * product on its hip_stream, i = number of earlier forwards since this call,
+ * modulo n; hipEventElapsedTime of a pair then gives that product's duration
+ * inside the step.  The arrays hold n hipEvent_t handles each, owned by the
+ * caller and kept valid while the hook is set; n = 0 removes the hook.
+ * Errors: GPT2_E_ARG. */
+int gpt2_set_classifier_events(gpt2_ctx* ctx, void* const* d_start_events, void* const* d_end_events, int n);
+
 /* Frees the host-side context (no device memory is owned). */
 int gpt2_free(gpt2_ctx* ctx);
 

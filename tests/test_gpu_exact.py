@@ -95,3 +95,43 @@ def test_bad_token_raises_flag_and_state_rules():
     m.forward(torch.from_numpy(x.reshape(-1)).cuda(), torch.from_numpy(yb).cuda())
     assert m.check() == B.GPT2_E_TOKEN
     m.close()
+
+
+def test_classifier_event_hook():
+    """The timing hook records a start/end event pair around the classifier
+    product of each forward, cycling through the slots; n = 0 removes it."""
+    import ctypes
+    from transformer_lm_step_amd import binding as B
+    rt = ctypes.CDLL("libamdhip64.so")
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(4):
+        e = ctypes.c_void_p()
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    cfg = RAG
+    params, [(x, y)] = make_inputs(cfg, 2, 150, perturb=True)
+    m = _model(cfg, 0, 2, 150, params)
+    hook = B.gpt2_set_classifier_events(m.ctx, evs[:2], evs[2:])
+    xi = torch.from_numpy(x.reshape(-1)).cuda()
+    for _ in range(3):
+        m.forward(xi)
+    torch.cuda.synchronize()
+    for a, b in zip(evs[:2], evs[2:]):
+        t = ctypes.c_float()
+        assert rt.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        assert 0.0 < t.value < 1000.0
+    B.gpt2_set_classifier_events(m.ctx, [], [])
+    del hook
+    with pytest.raises(B.GPT2Error):
+        B.lib()  # the raw entry point rejects a negative count
+        rc = B.lib().gpt2_set_classifier_events(m.ctx, None, None, -1)
+        if rc != 0:
+            raise B.GPT2Error(rc, "gpt2_set_classifier_events")
+    m.forward(xi)
+    torch.cuda.synchronize()
+    m.close()
+    for e in evs:
+        rt.hipEventDestroy(e)

@@ -23,7 +23,7 @@ GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0
 EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
-    "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
+    "gpt2_set_classifier_events", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
     "gpt2_linear_backward_workspace", "fused_linear_gelu_softmax_f32",
     "fused_linear_gelu_softmax_f32_workspace",
 )
@@ -67,6 +67,7 @@ def _load():
         "gpt2_adamw_update": (i, [vp, f, f, f, f, f, i, vp]),
         "gpt2_check_device_error": (i, [vp, vp]),
         "gpt2_act_tensor": (i, [vp, i, ctypes.POINTER(vp), ctypes.POINTER(z)]),
+        "gpt2_set_classifier_events": (i, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i]),
         "gpt2_free": (i, [vp]),
         "gpt2_strerror": (ctypes.c_char_p, [i]),
         "gpt2_linear_forward": (i, [i, vp, vp, vp, vp, i, i, i, vp]),
@@ -164,6 +165,19 @@ def gpt2_act_tensor(ctx: int, which: int):
     n = ctypes.c_size_t()
     _check(_lib.gpt2_act_tensor(ctx, which, ctypes.byref(p), ctypes.byref(n)), "gpt2_act_tensor")
     return p.value, int(n.value)
+
+
+def gpt2_set_classifier_events(ctx: int, starts, ends):
+    """starts / ends: equal-length sequences of hipEvent_t handles (ints), or
+    empty to remove the hook.  The arrays are kept alive with the context
+    object that the caller holds (returned here; keep a reference)."""
+    n = len(starts)
+    if len(ends) != n:
+        raise ValueError("starts and ends differ in length")
+    a = (ctypes.c_void_p * max(n, 1))(*starts)
+    b = (ctypes.c_void_p * max(n, 1))(*ends)
+    _check(_lib.gpt2_set_classifier_events(ctx, a, b, n), "gpt2_set_classifier_events")
+    return a, b
 
 
 def gpt2_free(ctx: int):

@@ -161,6 +161,10 @@ struct gpt2_ctx {
     gpt2_buffers buf;
     Plan plan;
     int last_fwd_targets;  // -1: no forward yet, 0: without targets, 1: with
+    // timing hook around the classifier product (caller-owned events)
+    void* const* ev_start = nullptr;
+    void* const* ev_end = nullptr;
+    int ev_n = 0, ev_i = 0;
     char* acts() const { return (char*)buf.acts; }
     template <typename X> X* act(size_t ofs) const { return (X*)(acts() + ofs); }
     template <typename X> X* act_l(size_t ofs, size_t stride, int l) const { return (X*)(acts() + ofs + stride * l); }
@@ -253,7 +257,10 @@ int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, flo
     TRY(layernorm_fwd_launch<T>(lnf, c->act<float>(p.lnfm), c->act<float>(p.lnfr), resL, prm<T>(c, 14), prm<T>(c, 15),
                                 BT, C, s));
     T* logits = c->act<T>(p.logits);
+    const int ev = c->ev_n > 0 ? c->ev_i++ % c->ev_n : -1;
+    if (ev >= 0) TRY((int)hipEventRecord((hipEvent_t)c->ev_start[ev], s));
     TRY(gemm(c, fwd_desc(BT, Vp, C, lnf, prm<T>(c, 0), logits, GEMM_STORE, nullptr, nullptr, nullptr), s));
+    if (ev >= 0) TRY((int)hipEventRecord((hipEvent_t)c->ev_end[ev], s));
     if (targets) {
         float* losses = c->act<float>(p.losses);
         TRY(classifier_ce_launch<T>(logits, losses, targets, BT, V, Vp, c->flag(), s));
@@ -456,6 +463,15 @@ int gpt2_act_tensor(gpt2_ctx* c, int which, void** d_ptr, size_t* count) {
         case GPT2_T_ENCODED: *d_ptr = c->act<char>(p.enc); *count = p.BT * p.C; return GPT2_OK;
         default: return GPT2_E_ARG;
     }
+}
+
+int gpt2_set_classifier_events(gpt2_ctx* c, void* const* d_start_events, void* const* d_end_events, int n) {
+    if (!c || n < 0 || (n > 0 && (!d_start_events || !d_end_events))) return GPT2_E_ARG;
+    c->ev_start = n > 0 ? d_start_events : nullptr;
+    c->ev_end = n > 0 ? d_end_events : nullptr;
+    c->ev_n = n;
+    c->ev_i = 0;
+    return GPT2_OK;
 }
 
 int gpt2_free(gpt2_ctx* c) {
