@@ -29,7 +29,8 @@
 // a 16x16 score tile pair is fed straight back as the next MFMA's operand
 // (slot j of lane group g <-> row 32c + 16*(j/4) + 4g + j%4, the same map on
 // both operands).  Workgroups are issued longest-first along the causal
-// triangle.
+// triangle, with every row block of a (batch, head) pair on the same XCD
+// (attn_block).
 #include <math.h>
 
 #include <type_traits>
@@ -40,6 +41,23 @@
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
+
+// Row block `blk` (0 = the one with the most work) and (batch, head) of this
+// workgroup; the grid is one-dimensional, nb row blocks x B*NH pairs.  The
+// workgroup id runs over the pairs fastest, so all longest blocks are issued
+// first (the causal triangle's work per block ranges from 1 to nb tiles).
+// Consecutive ids go to the eight XCDs in turn, so when B*NH is a multiple of 8
+// every block of a pair runs on one XCD and the pair's K/V (forward, dQ) or
+// Q/dO (dK/dV) is fetched into that XCD's L2 once.  Issuing the blocks
+// row-fastest instead spreads a pair over all XCDs and gives XCD x only the
+// blocks x and x + 8 - up to 2.4 times another XCD's work.
+DEV void attn_block(int nb, int NH, int& blk, int& h, int& b) {
+    const int nhb = gridDim.x / nb;
+    blk = blockIdx.x / nhb;
+    const int hb = blockIdx.x - blk * nhb;
+    h = hb % NH;
+    b = hb / NH;
+}
 
 template <typename T, int HS>
 struct ACfg {
@@ -176,8 +194,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
     __shared__ __attribute__((aligned(16))) T sVt[A::TR ? 64 * A::VP : (HS + 16) * A::TP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int qb = gridDim.x - 1 - blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int nb = (T_ + 63) / 64;
+    int blk, h, b;
+    attn_block(nb, NH, blk, h, b);
+    const int qb = nb - 1 - blk;
     const long rs = 3L * C;
     const T* Qh = qkv + (long)b * T_ * rs + h * HS;
     const T* Kh = Qh + C;
@@ -336,8 +356,9 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
     __shared__ __attribute__((aligned(16))) float sD[64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int kb = blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int nqb = (T_ + 63) / 64;
+    int kb, h, b;
+    attn_block(nqb, NH, kb, h, b);
     const long rs = 3L * C;
     const T* Qh = qkv + (long)b * T_ * rs + h * HS;
     const T* Kh = Qh + C;
@@ -356,7 +377,6 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
         dk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         dv[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int nqb = (T_ + 63) / 64;
     RowsStage<T, HS> pq, pdo;
     pq.init(rs, tid);
     pdo.init(C, tid);
@@ -482,8 +502,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
     __shared__ __attribute__((aligned(16))) T sKt[A::TR ? 8 : HS * A::TP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int qb = gridDim.x - 1 - blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int nb = (T_ + 63) / 64;
+    int blk, h, b;
+    attn_block(nb, NH, blk, h, b);
+    const int qb = nb - 1 - blk;
     const long rs = 3L * C;
     const T* Qh = qkv + (long)b * T_ * rs + h * HS;
     const T* Kh = Qh + C;
@@ -583,7 +605,7 @@ template <typename T, int HS>
 int fwd_hs(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
     const int nb = (T_ + 63) / 64;
     const float sl2 = LOG2E / sqrtf((float)HS);
-    hipLaunchKernelGGL((attn_fwd_kernel<T, HS>), dim3(nb, NH, B), dim3(256), 0, s, out, lse, qkv, T_, C, NH, sl2);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, out, lse, qkv, T_, C, NH, sl2);
     return (int)hipGetLastError();
 }
 
@@ -596,9 +618,9 @@ int bwd_hs(T* dqkv, float* delta, const T* dout, const T* out, const T* qkv, con
     const long rows = (long)B * T_ * NH;
     hipLaunchKernelGGL((attn_delta_kernel<T, HS>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
                        delta, dout, out, B, T_, C, NH);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HS>), dim3(nb, NH, B), dim3(256), 0, s, dqkv, dout, qkv, lse,
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout, qkv, lse,
                        delta, T_, C, NH, sl2, scale);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HS>), dim3(nb, NH, B), dim3(256), 0, s, dqkv, dout, qkv, lse,
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout, qkv, lse,
                        delta, T_, C, NH, sl2, scale);
     return (int)hipGetLastError();
 }
