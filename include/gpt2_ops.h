@@ -37,6 +37,31 @@ int gpt2_linear_backward(int precision, const void* d_dy, const void* d_x, const
                          size_t work_bytes, void* hip_stream);
 size_t gpt2_linear_backward_workspace(int precision, int M, int N, int K);
 
+/* train_gpt2.cu, attention_forward (permute, Q K^T, softmax_forward_kernel5
+ * with the causal mask, P V, unpermute): for every batch b and head h, with
+ * q, k, v the channel slices h*HS .. h*HS+HS-1 (HS = C/NH) of the three
+ * thirds of qkv [B,T,3C],
+ *   out[b,t,h*HS + d] = sum_{s <= t} softmax_s(q_t . k_s / sqrt(HS)) v_s[d],
+ * out [B,T,C].  d_lse [B,NH,T] fp32 receives log2 of each row's softmax
+ * denominator, log2(sum_{s <= t} exp(q_t . k_s / sqrt(HS))), which
+ * gpt2_attention_backward reads.  precision GPT2_FP32 or GPT2_BF16 (bf16
+ * qkv and out, fp32 scores and accumulation).  HS in {16, 32, 64, 128}.
+ * Errors: GPT2_E_ARG (bad precision, NULL pointer, non-positive sizes),
+ * GPT2_E_SHAPE (C not a multiple of NH or unsupported HS), GPT2_E_ALIGN,
+ * GPT2_E_HIP. */
+int gpt2_attention_forward(int precision, const void* d_qkv, void* d_out, float* d_lse, int B, int T, int C, int NH,
+                           void* hip_stream);
+
+/* train_gpt2.cu, attention_backward (softmax_autoregressive_backward_kernel
+ * and the four batched products): dqkv [B,T,3C] (overwritten) = the gradient
+ * of sum(out * dout) with respect to qkv, from dout [B,T,C] and the
+ * forward's qkv, out and lse.  d_delta: B*NH*T fp32 workspace (per-row
+ * sum of dout * out; contents on return unspecified).  Types, HS and errors
+ * as gpt2_attention_forward. */
+int gpt2_attention_backward(int precision, const void* d_dout, const void* d_qkv, const void* d_out,
+                            const float* d_lse, void* d_dqkv, float* d_delta, int B, int T, int C, int NH,
+                            void* hip_stream);
+
 /* POPCORNBENCH l12_default_gpt trajectory page, the problem statement (a
  * Linear layer followed by tanh-form GELU and a softmax over dim 1), in fp32:
  *   Y[m, :] = softmax_n( GELU_tanh( sum_k X[m,k] W[n,k] + b[n] ) )

@@ -167,3 +167,17 @@ def linear_inputs(M: int, K: int, N: int, seed: int = DATA_SEED):
     dw0 = rng.normal(0.0, 0.01, (N, K)).astype(np.float32)
     db0 = rng.normal(0.0, 0.01, N).astype(np.float32)
     return x, w, bias, dy, dw0, db0
+
+
+def attention_inputs(B: int, T: int, C: int, score_scale: float = 1.0, seed: int = DATA_SEED):
+    """Operands of one causal attention layer, all bf16-exact (float32 arrays).
+
+    qkv [B,T,3C]: q ~ N(0, score_scale), k ~ N(0, 1), v ~ N(0, 1), so a
+    score q.k / sqrt(HS) is about N(0, score_scale^2); dout ~ N(0, 1) [B,T,C].
+    """
+    rng = np.random.default_rng(seed)
+    q = rng.normal(0.0, score_scale, (B, T, C))
+    kv = rng.standard_normal((B, T, 2 * C))
+    qkv = round_to_bf16(np.concatenate([q, kv], axis=2).astype(np.float32))
+    dout = round_to_bf16(rng.standard_normal((B, T, C), dtype=np.float32))
+    return qkv, dout

@@ -24,8 +24,8 @@ EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
     "gpt2_set_classifier_events", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
-    "gpt2_linear_backward_workspace", "fused_linear_gelu_softmax_f32",
-    "fused_linear_gelu_softmax_f32_workspace",
+    "gpt2_linear_backward_workspace", "gpt2_attention_forward", "gpt2_attention_backward",
+    "fused_linear_gelu_softmax_f32", "fused_linear_gelu_softmax_f32_workspace",
 )
 
 
@@ -73,6 +73,8 @@ def _load():
         "gpt2_linear_forward": (i, [i, vp, vp, vp, vp, i, i, i, vp]),
         "gpt2_linear_backward": (i, [i, vp, vp, vp, vp, vp, vp, i, i, i, f, vp, z, vp]),
         "gpt2_linear_backward_workspace": (z, [i, i, i, i]),
+        "gpt2_attention_forward": (i, [i, vp, vp, vp, i, i, i, i, vp]),
+        "gpt2_attention_backward": (i, [i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]),
         "fused_linear_gelu_softmax_f32": (i, [vp, vp, vp, vp, i, i, i, vp, z, vp]),
         "fused_linear_gelu_softmax_f32_workspace": (z, [i, i]),
     }
@@ -188,6 +190,18 @@ def gpt2_linear_forward(precision: int, d_x: int, d_w: int, d_bias: int, d_y: in
                         stream: int):
     _check(_lib.gpt2_linear_forward(precision, d_x, d_w, d_bias or None, d_y, M, N, K, stream or None),
            "gpt2_linear_forward")
+
+
+def gpt2_attention_forward(precision: int, d_qkv: int, d_out: int, d_lse: int, B: int, T: int, C: int, NH: int,
+                           stream: int):
+    _check(_lib.gpt2_attention_forward(precision, d_qkv, d_out, d_lse, B, T, C, NH, stream or None),
+           "gpt2_attention_forward")
+
+
+def gpt2_attention_backward(precision: int, d_dout: int, d_qkv: int, d_out: int, d_lse: int, d_dqkv: int,
+                            d_delta: int, B: int, T: int, C: int, NH: int, stream: int):
+    _check(_lib.gpt2_attention_backward(precision, d_dout, d_qkv, d_out, d_lse, d_dqkv, d_delta, B, T, C, NH,
+                                        stream or None), "gpt2_attention_backward")
 
 
 def gpt2_linear_backward_workspace(precision: int, M: int, N: int, K: int) -> int:

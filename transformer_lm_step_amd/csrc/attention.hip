@@ -38,9 +38,14 @@
 #include "device.h"
 #include "kernels.h"
 
+#ifndef ATTN_FWD_NS
+#define ATTN_FWD_NS 2
+#endif
+
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
+typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 // Row block `blk` (0 = the one with the most work) and (batch, head) of this
 // workgroup; the grid is one-dimensional, nb row blocks x B*NH pairs.  The
@@ -79,7 +84,6 @@ struct ACfg {
 // 16 lanes, lane l receives element l of the four 4-element pieces read by
 // lanes 4j..4j+3 (j = 0..3), so lane s reads row k + s/4, columns 4(s%4)...
 DEV void frag_tr(Frag<bf16_t>& f, const bf16_t* tile, int pitch, int k0, int k1, int d0, int l16) {
-    typedef short v4s_t __attribute__((ext_vector_type(4)));
     typedef short v8s_t __attribute__((ext_vector_type(8)));
     const int col = d0 + 4 * (l16 & 3);
     const v4s_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -308,6 +312,167 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
         for (int dt = 0; dt < A::DT; dt++) {
             float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
             store4<T>(orow + 16 * dt + 4 * g4, v);
+        }
+        if (g4 == 0) lse[((long)b * NH + h) * T_ + q] = m_run * sl2 + log2f(l_run);
+    }
+}
+
+// ------------------------------------------------- forward, bf16, HS = 64 --
+// The same computation as attn_fwd_kernel, with the K and V blocks copied from
+// global memory straight into LDS (buffer loads with the LDS-destination bit)
+// NS - 1 blocks ahead into NS stage buffers: no registers hold staged data, no
+// LDS store instructions are issued, and a wave waits for a block's loads only
+// when that block is about to be used.  One barrier per block makes the
+// block's loads (issued by all four waves) visible and frees the stage buffer
+// the next loads overwrite.  Each wave's 16-byte lane loads fill 1 KB (8 rows
+// of 128 bytes) contiguously, so the layout is set by which element a lane
+// fetches:
+//   K block: 16-byte chunk c of key row r at chunk c ^ (r & 7), so the S^T
+//            fragment reads of 8 consecutive rows hit 8 different bank groups;
+//   V block: 32-byte unit u (16 d values) of key row r at unit u ^ ((r >> 1) & 3),
+//            so each transposing read of V^T (rows 4g..4g+3 for lane group g)
+//            covers every bank once per 32 lanes.
+// Rows past T_ read as zeros (buffer range); the row sums come from an
+// all-ones operand held in registers instead of extra V columns.
+template <int NS>
+__global__ __launch_bounds__(256, 2) void attn_fwd_dtl_kernel(bf16_t* __restrict__ out, float* __restrict__ lse,
+                                                           const bf16_t* __restrict__ qkv, int T_, int C, int NH,
+                                                           float sl2) {
+    constexpr int HS = 64, BLK = 64 * HS;
+    __shared__ __attribute__((aligned(1024))) bf16_t sKV[NS][2][BLK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int nb = (T_ + 63) / 64;
+    int blk, h, b;
+    attn_block(nb, NH, blk, h, b);
+    const int qb = nb - 1 - blk;
+    const long rs = 3L * C;
+    const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
+    const bf16_t* Kh = Qh + C;
+    const bf16_t* Vh = Qh + 2 * C;
+    const int q = qb * 64 + wave * 16 + l16;
+
+    Frag<bf16_t> fq[2];
+    row_frags<bf16_t, HS>(fq, Qh, rs, q, T_, g4);
+
+    // byte offsets (from the block's first row) of this lane's two K and two
+    // V loads: load i of wave w fills rows 8 (w + 4 i) .. + 7 of the block
+    uint32_t koff[2], voff[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int r = 8 * (wave + 4 * i) + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int u = ((lane & 7) >> 1) ^ ((r >> 1) & 3);
+        koff[i] = (uint32_t)(((long)r * rs + 8 * c) * 2);
+        voff[i] = (uint32_t)(((long)r * rs + 16 * u + 8 * (lane & 1)) * 2);
+    }
+    auto issue = [&](int kb) {
+        const long org = (long)kb * 64 * rs;
+        const int rows = min(64, T_ - kb * 64);
+        const uint32_t bytes = (uint32_t)(((long)(rows - 1) * rs + HS) * 2);
+        const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(Kh + org, bytes);
+        const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(Vh + org, bytes);
+        bf16_t* st = sKV[kb % NS][0];
+#pragma unroll
+        for (int i = 0; i < 2; i++) lds_dma16(rk, koff[i], st + (wave + 4 * i) * 512);
+#pragma unroll
+        for (int i = 0; i < 2; i++) lds_dma16(rv, voff[i], st + BLK + (wave + 4 * i) * 512);
+    };
+    // fragment read offsets (elements): S^T operand K rows 16 kt + l16, chunk
+    // 4 ks + g4; V^T operand rows 32 c + 4 g4 + l16 / 4 (+ 16), d tile dt
+    int kofs[2], vofs[4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) kofs[ks] = l16 * 64 + (((4 * ks + g4) ^ (l16 & 7)) << 3);
+    const int vf = (2 * g4 + (l16 >> 3)) & 3;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) vofs[dt] = (4 * g4 + (l16 >> 2)) * 64 + ((dt ^ vf) << 4) + 4 * (l16 & 3);
+
+    Frag<bf16_t> fones;
+    fones.v = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+    float m_run = -INFINITY;
+    f32x4_t o[5];
+#pragma unroll
+    for (int dt = 0; dt < 5; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int p = 0; p < NS - 1; p++)
+        if (p <= qb) issue(p);
+    auto block = [&](int kb, auto diag) {
+        // this wave's loads of block kb are done once at most those of the
+        // blocks issued after it (up to NS - 2) are outstanding
+        if (NS > 2 && kb + NS - 2 <= qb) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 4));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + NS - 1 <= qb) issue(kb + NS - 1);
+        const bf16_t* sK = sKV[kb % NS][0];
+        const bf16_t* sV = sK + BLK;
+        f32x4_t s[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++) {
+            s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                Frag<bf16_t> fk;
+                frag_ld(fk, sK + kt * 1024 + kofs[ks]);
+                mma(s[kt], fk, fq[ks]);
+            }
+        }
+        if constexpr (decltype(diag)::value) {
+#pragma unroll
+            for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (kb * 64 + 16 * kt + 4 * g4 + r > q) s[kt][r] = -INFINITY;
+        }
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+            mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const float m_new = fmaxf(m_run, mloc);
+        if (__any(m_new > m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
+#pragma unroll
+            for (int dt = 0; dt < 5; dt++) o[dt] *= alpha;
+        }
+        m_run = m_new;
+        const float mc = -m_new * sl2;
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], sl2, mc));
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            float pv[8] = {s[2 * c][0], s[2 * c][1], s[2 * c][2], s[2 * c][3],
+                           s[2 * c + 1][0], s[2 * c + 1][1], s[2 * c + 1][2], s[2 * c + 1][3]};
+            Frag<bf16_t> fp;
+            frag_from(fp, pv);
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                const bf16_t* v0 = sV + c * 2048 + vofs[dt];
+                const v4s_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)v0);
+                const v4s_t bb =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(v0 + 1024));
+                Frag<bf16_t> fv;
+                fv.v = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, bb, 0, 1, 2, 3, 4, 5, 6, 7));
+                mma(o[dt], fv, fp);
+            }
+            mma(o[4], fones, fp);
+        }
+    };
+    for (int kb = 0; kb < qb; kb++) block(kb, std::false_type{});
+    block(qb, std::true_type{});
+
+    if (q < T_) {
+        const float l_run = o[4][0];
+        const float inv = 1.0f / l_run;
+        bf16_t* orow = out + ((long)b * T_ + q) * C + h * HS;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+            store4<bf16_t>(orow + 16 * dt + 4 * g4, v);
         }
         if (g4 == 0) lse[((long)b * NH + h) * T_ + q] = m_run * sl2 + log2f(l_run);
     }
@@ -605,6 +770,14 @@ template <typename T, int HS>
 int fwd_hs(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
     const int nb = (T_ + 63) / 64;
     const float sl2 = LOG2E / sqrtf((float)HS);
+    if constexpr (std::is_same_v<T, bf16_t> && HS == 64) {
+        // direct-to-LDS loads address a batch's rows with 32-bit byte offsets
+        if ((long)T_ * 3 * C * 2 < (1L << 31)) {
+            hipLaunchKernelGGL((attn_fwd_dtl_kernel<ATTN_FWD_NS>), dim3(nb * NH * B), dim3(256), 0, s, out, lse, qkv, T_,
+                               C, NH, sl2);
+            return (int)hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, out, lse, qkv, T_, C, NH, sl2);
     return (int)hipGetLastError();
 }

@@ -88,6 +88,35 @@ DEV uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 constexpr uint32_t kBufOOB = 0x80000000u;  // an offset past any range used here
 
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are outstanding (LDS and export counters left at their maxima)
+DEV constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// One 16-byte-per-lane buffer load into LDS at lds (wave-uniform; lane i
+// lands at lds + 16 i).  Written as inline assembly so that the compiler does
+// not track it: its own wait insertion cannot tell the stage buffers apart and
+// would wait for every load in flight before each fragment read.  A kernel
+// that uses it waits for these loads itself (vmcnt before the barrier of the
+// stage that consumes them, and for all of them before its loop ends), and
+// issues no other vector memory access while they are in flight: the
+// compiler's own vmcnt waits do not count them and would also wait for them.
+DEV void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const void* lds) {
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                 "s"(__builtin_amdgcn_readfirstlane(a))
+                 : "memory", "m0");
+}
+
+// The buffer resource of an LDS-destination load must sit in scalar registers;
+// built from readfirstlane'd fields it does even where the compiler holds the
+// tile coordinates in vector registers (all lanes hold the same values).
+DEV __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t u = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
+
 // v if ok, else zeros (component-wise select, no branch and no memory)
 DEV uint4 keep16(bool ok, const uint4& v) {
     const uint32_t m = ok ? 0xffffffffu : 0u;

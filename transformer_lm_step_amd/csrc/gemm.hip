@@ -653,7 +653,6 @@ __global__ __launch_bounds__((TileOf<T, BM, BN, WT>::NT), (TileOf<T, BM, BN, WT>
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-DEV constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Stage depth BK (contraction elements per stage) and stage count NS per tile:
 // the 128x128 tiles (two workgroups per CU) keep four 32-deep stages so that
@@ -726,30 +725,6 @@ struct DtlSlab {
         }
     }
 };
-
-// One 16-byte-per-lane buffer load into LDS at lds (wave-uniform; lane i
-// lands at lds + 16 i).  Written as inline assembly so that the compiler does
-// not track it: its own wait insertion cannot tell the stage buffers apart and
-// would wait for every load in flight before each fragment read.  The kernel
-// waits for these loads itself (vmcnt before each stage's barrier, and for all
-// of them before the loop ends), and issues no other vector memory access in
-// its main loop.
-DEV void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const void* lds) {
-    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
-                 "s"(__builtin_amdgcn_readfirstlane(a))
-                 : "memory", "m0");
-}
-
-// The buffer resource of an LDS-destination load must sit in scalar registers;
-// built from readfirstlane'd fields it does even where the compiler holds the
-// tile coordinates in vector registers (all lanes hold the same values).
-DEV __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t u = (uint64_t)(uintptr_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
-}
 
 // Issue this wave's loads of the slab at (rows r0.., contraction k0..) into dst
 // (per-lane offsets and, k-contiguous, contraction indices from DtlSlab).

@@ -79,3 +79,43 @@ extern "C" int gpt2_linear_backward(int precision, const void* dy, const void* x
     }
     return GPT2_OK;
 }
+
+namespace {
+int attn_args(int precision, int B, int T, int C, int NH) {
+    if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_E_ARG;
+    if (B <= 0 || T <= 0 || C <= 0 || NH <= 0) return GPT2_E_ARG;
+    if (C % NH) return GPT2_E_SHAPE;
+    const int hs = C / NH;
+    if (hs != 16 && hs != 32 && hs != 64 && hs != 128) return GPT2_E_SHAPE;
+    return GPT2_OK;
+}
+}  // namespace
+
+extern "C" int gpt2_attention_forward(int precision, const void* qkv, void* out, float* lse, int B, int T, int C,
+                                      int NH, void* hip_stream) {
+    const int e = attn_args(precision, B, T, C, NH);
+    if (e != GPT2_OK) return e;
+    if (!qkv || !out || !lse) return GPT2_E_ARG;
+    if (!al(qkv) || !al(out) || !al(lse)) return GPT2_E_ALIGN;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    const int r = precision == GPT2_BF16
+                      ? attention_fwd_launch<bf16_t>((bf16_t*)out, lse, (const bf16_t*)qkv, B, T, C, NH, s)
+                      : attention_fwd_launch<float>((float*)out, lse, (const float*)qkv, B, T, C, NH, s);
+    return r == 0 ? GPT2_OK : GPT2_E_HIP;
+}
+
+extern "C" int gpt2_attention_backward(int precision, const void* dout, const void* qkv, const void* out,
+                                       const float* lse, void* dqkv, float* delta, int B, int T, int C, int NH,
+                                       void* hip_stream) {
+    const int e = attn_args(precision, B, T, C, NH);
+    if (e != GPT2_OK) return e;
+    if (!dout || !qkv || !out || !lse || !dqkv || !delta) return GPT2_E_ARG;
+    if (!al(dout) || !al(qkv) || !al(out) || !al(lse) || !al(dqkv) || !al(delta)) return GPT2_E_ALIGN;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    const int r = precision == GPT2_BF16
+                      ? attention_bwd_launch<bf16_t>((bf16_t*)dqkv, delta, (const bf16_t*)dout, (const bf16_t*)out,
+                                                     (const bf16_t*)qkv, lse, B, T, C, NH, s)
+                      : attention_bwd_launch<float>((float*)dqkv, delta, (const float*)dout, (const float*)out,
+                                                    (const float*)qkv, lse, B, T, C, NH, s);
+    return r == 0 ? GPT2_OK : GPT2_E_HIP;
+}
