@@ -41,6 +41,9 @@
 #ifndef ATTN_FWD_NS
 #define ATTN_FWD_NS 2
 #endif
+#ifndef ATTN_BWD_NS
+#define ATTN_BWD_NS 2
+#endif
 
 namespace {
 
@@ -766,6 +769,297 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HS == 128) ? 1 : 2) void at
     }
 }
 
+// ------------------------------------------------ backward, bf16, HS = 64 --
+// The dK/dV and dQ kernels with their streamed blocks (Q and dO, or K and V)
+// copied straight into LDS like the forward's K and V.  Every streamed tile
+// is read both as rows (16-byte fragment reads) and transposed (the LDS
+// transpose read), so all use one layout: 64 rows of 128 bytes, 16-byte chunk
+// c of row r at chunk c ^ (r & 7).  Both reads then cover every bank once per
+// 32 lanes: a row read spreads 8 consecutive rows over 8 chunk positions, and
+// a transpose read (rows 4g..4g+3 for lane group g, a 32-byte d tile = two
+// chunks) lands its 8 rows on 8 different (row parity, chunk) pairs.
+
+// This wave's two 1 KB loads of a 64 x 64 bf16 tile in that layout.
+struct Tile64 {
+    uint32_t off[2];  // byte offsets from the tile's first row, row stride ld elements
+    DEV void init(long ld, int lane, int wave) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int r = 8 * (wave + 4 * i) + (lane >> 3);
+            const int c = (lane & 7) ^ (r & 7);
+            off[i] = (uint32_t)(((long)r * ld + 8 * c) * 2);
+        }
+    }
+    // rows row0 .. min(row0 + 64, T_) - 1 of src (row stride ld); rows past T_ read as zeros
+    DEV void issue(const bf16_t* src, long ld, int row0, int T_, bf16_t* dst, int wave) const {
+        const int rows = min(64, T_ - row0);
+        const uint32_t bytes = (uint32_t)(((long)(rows - 1) * ld + 64) * 2);
+        const __amdgpu_buffer_rsrc_t r = uniform_rsrc(src + (long)row0 * ld, bytes);
+#pragma unroll
+        for (int i = 0; i < 2; i++) lds_dma16(r, off[i], dst + (wave + 4 * i) * 512);
+    }
+};
+
+// Fragment read offsets (elements) within such a tile.  Row reads: rows
+// 16 t + l16 (t added as t * 1024), chunk 4 ks + g4.  Transpose reads of d tile
+// dt: rows 32 c + 4 g4 + l16 / 4 and 16 rows further (c added as c * 2048),
+// columns 16 dt + 4 (l16 % 4).
+struct Tile64Ofs {
+    int row[2], tr[4];
+    DEV void init(int l16, int g4) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) row[ks] = l16 * 64 + (((4 * ks + g4) ^ (l16 & 7)) << 3);
+        const int r = 4 * g4 + (l16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) tr[dt] = r * 64 + (((2 * dt + ((l16 >> 1) & 1)) ^ (r & 7)) << 3) + 4 * (l16 & 1);
+    }
+};
+
+DEV void tr_frag(Frag<bf16_t>& f, const bf16_t* p) {
+    const v4s_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)p);
+    const v4s_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(p + 1024));
+    f.v = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// dK/dV for one 64-key block over the query blocks at or after it; lse and
+// delta of the next query block are read into registers one block ahead and
+// put in LDS (two slots) before the barrier that opens the block.
+template <int NS>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dtl_kernel(bf16_t* __restrict__ dqkv,
+                                                                const bf16_t* __restrict__ dout,
+                                                                const bf16_t* __restrict__ qkv,
+                                                                const float* __restrict__ lse,
+                                                                const float* __restrict__ delta, int T_, int C,
+                                                                int NH, float sl2, float scale) {
+    constexpr int HS = 64, BLK = 64 * HS;
+    __shared__ __attribute__((aligned(1024))) bf16_t sQO[NS][2][BLK];
+    __shared__ __attribute__((aligned(16))) float sLD[NS][2][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int nqb = (T_ + 63) / 64;
+    int kb, h, b;
+    attn_block(nqb, NH, kb, h, b);
+    const long rs = 3L * C;
+    const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
+    const bf16_t* Kh = Qh + C;
+    const bf16_t* Vh = Qh + 2 * C;
+    const bf16_t* dOh = dout + (long)b * T_ * C + h * HS;
+    const float* lse_h = lse + ((long)b * NH + h) * T_;
+    const float* del_h = delta + ((long)b * NH + h) * T_;
+    const int key = kb * 64 + wave * 16 + l16;
+
+    Frag<bf16_t> fk[2], fv[2];
+    row_frags<bf16_t, HS>(fk, Kh, rs, key, T_, g4);
+    row_frags<bf16_t, HS>(fv, Vh, rs, key, T_, g4);
+    f32x4_t dk[4], dv[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) {
+        dk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dv[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    Tile64 tq, to;
+    tq.init(rs, lane, wave);
+    to.init(C, lane, wave);
+    Tile64Ofs ofs;
+    ofs.init(l16, g4);
+    auto issue = [&](int qb) {
+        bf16_t* st = sQO[qb % NS][0];
+        tq.issue(Qh, rs, qb * 64, T_, st, wave);
+        to.issue(dOh, C, qb * 64, T_, st + BLK, wave);
+    };
+    // query rows past T_: lse = +inf makes their P exactly zero
+    float pl = INFINITY, pd = 0.f;
+    auto load_ld = [&](int qb) {
+        const int qq = qb * 64 + lane;
+        pl = qq < T_ ? lse_h[qq] : INFINITY;
+        pd = qq < T_ ? del_h[qq] : 0.f;
+    };
+    if (wave == 0) load_ld(kb);
+#pragma unroll
+    for (int p = 0; p < NS - 1; p++)
+        if (kb + p < nqb) issue(kb + p);
+    auto block = [&](int qb, auto diag) {
+        float* sL = sLD[qb % NS][0];
+        float* sD = sLD[qb % NS][1];
+        if (wave == 0) {
+            sL[lane] = pl;
+            sD[lane] = pd;
+        }
+        if (NS > 2 && qb + NS - 2 < nqb) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 4));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the lse / delta writes are done
+        asm volatile("s_barrier" ::: "memory");
+        if (qb + NS - 1 < nqb) issue(qb + NS - 1);
+        if (wave == 0 && qb + 1 < nqb) load_ld(qb + 1);
+        const bf16_t* sQ = sQO[qb % NS][0];
+        const bf16_t* sdO = sQ + BLK;
+        // S[q][key] and dP[q][key]: lane holds q = 16qt + 4g4 + r, key = l16 (+ block offsets)
+        f32x4_t p[4], ds[4];
+#pragma unroll
+        for (int qt = 0; qt < 4; qt++) {
+            p[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ds[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                Frag<bf16_t> fa;
+                frag_ld(fa, sQ + qt * 1024 + ofs.row[ks]);
+                mma(p[qt], fa, fk[ks]);
+                frag_ld(fa, sdO + qt * 1024 + ofs.row[ks]);
+                mma(ds[qt], fa, fv[ks]);
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < 4; qt++) {
+            const float4 L4 = *reinterpret_cast<const float4*>(sL + 16 * qt + 4 * g4);
+            const float4 D4 = *reinterpret_cast<const float4*>(sD + 16 * qt + 4 * g4);
+            const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+            const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                float pr = __builtin_amdgcn_exp2f(fmaf(p[qt][r], sl2, -Lr[r]));
+                if constexpr (decltype(diag)::value)
+                    if (key > qb * 64 + 16 * qt + 4 * g4 + r) pr = 0.f;
+                p[qt][r] = pr;
+                ds[qt][r] = pr * (ds[qt][r] - Dr[r]);
+            }
+        }
+        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            float pv[8] = {p[2 * c][0], p[2 * c][1], p[2 * c][2], p[2 * c][3],
+                           p[2 * c + 1][0], p[2 * c + 1][1], p[2 * c + 1][2], p[2 * c + 1][3]};
+            float sv[8] = {ds[2 * c][0], ds[2 * c][1], ds[2 * c][2], ds[2 * c][3],
+                           ds[2 * c + 1][0], ds[2 * c + 1][1], ds[2 * c + 1][2], ds[2 * c + 1][3]};
+            Frag<bf16_t> fp, fs;
+            frag_from(fp, pv);
+            frag_from(fs, sv);
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                Frag<bf16_t> fa;
+                tr_frag(fa, sdO + c * 2048 + ofs.tr[dt]);
+                mma(dv[dt], fa, fp);
+                tr_frag(fa, sQ + c * 2048 + ofs.tr[dt]);
+                mma(dk[dt], fa, fs);
+            }
+        }
+    };
+    block(kb, std::true_type{});
+    for (int qb = kb + 1; qb < nqb; qb++) block(qb, std::false_type{});
+    if (key < T_) {
+        bf16_t* row = dqkv + ((long)b * T_ + key) * rs + h * HS;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            float kv[4] = {dk[dt][0] * scale, dk[dt][1] * scale, dk[dt][2] * scale, dk[dt][3] * scale};
+            float vv[4] = {dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]};
+            store4<bf16_t>(row + C + 16 * dt + 4 * g4, kv);
+            store4<bf16_t>(row + 2 * C + 16 * dt + 4 * g4, vv);
+        }
+    }
+}
+
+// dQ for one 64-query block over the key blocks at or before it.
+template <int NS>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_dtl_kernel(bf16_t* __restrict__ dqkv,
+                                                              const bf16_t* __restrict__ dout,
+                                                              const bf16_t* __restrict__ qkv,
+                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ delta, int T_, int C,
+                                                              int NH, float sl2, float scale) {
+    constexpr int HS = 64, BLK = 64 * HS;
+    __shared__ __attribute__((aligned(1024))) bf16_t sKV[NS][2][BLK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int nb = (T_ + 63) / 64;
+    int blk, h, b;
+    attn_block(nb, NH, blk, h, b);
+    const int qb = nb - 1 - blk;
+    const long rs = 3L * C;
+    const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
+    const bf16_t* Kh = Qh + C;
+    const bf16_t* Vh = Qh + 2 * C;
+    const bf16_t* dOh = dout + (long)b * T_ * C + h * HS;
+    const int q = qb * 64 + wave * 16 + l16;
+    const float Lq = q < T_ ? lse[((long)b * NH + h) * T_ + q] : INFINITY;
+    const float Dq = q < T_ ? delta[((long)b * NH + h) * T_ + q] : 0.f;
+
+    Frag<bf16_t> fq[2], fo[2];
+    row_frags<bf16_t, HS>(fq, Qh, rs, q, T_, g4);
+    row_frags<bf16_t, HS>(fo, dOh, C, q, T_, g4);
+    f32x4_t dq[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) dq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    Tile64 tkv;
+    tkv.init(rs, lane, wave);
+    Tile64Ofs ofs;
+    ofs.init(l16, g4);
+    auto issue = [&](int kb) {
+        bf16_t* st = sKV[kb % NS][0];
+        tkv.issue(Kh, rs, kb * 64, T_, st, wave);
+        tkv.issue(Vh, rs, kb * 64, T_, st + BLK, wave);
+    };
+#pragma unroll
+    for (int p = 0; p < NS - 1; p++)
+        if (p <= qb) issue(p);
+    auto block = [&](int kb, auto diag) {
+        if (NS > 2 && kb + NS - 2 <= qb) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 4));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + NS - 1 <= qb) issue(kb + NS - 1);
+        const bf16_t* sK = sKV[kb % NS][0];
+        const bf16_t* sV = sK + BLK;
+        // S^T[key][q], dP^T[key][q]: lane holds key = 16kt + 4g4 + r, q = l16
+        f32x4_t s[4], dp[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++) {
+            s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dp[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                Frag<bf16_t> fa;
+                frag_ld(fa, sK + kt * 1024 + ofs.row[ks]);
+                mma(s[kt], fa, fq[ks]);
+                frag_ld(fa, sV + kt * 1024 + ofs.row[ks]);
+                mma(dp[kt], fa, fo[ks]);
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], sl2, -Lq));
+                if constexpr (decltype(diag)::value)
+                    if (kb * 64 + 16 * kt + 4 * g4 + r > q) pr = 0.f;
+                s[kt][r] = pr * (dp[kt][r] - Dq);  // dS^T / scale
+            }
+        // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            float sv[8] = {s[2 * c][0], s[2 * c][1], s[2 * c][2], s[2 * c][3],
+                           s[2 * c + 1][0], s[2 * c + 1][1], s[2 * c + 1][2], s[2 * c + 1][3]};
+            Frag<bf16_t> fs;
+            frag_from(fs, sv);
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                Frag<bf16_t> fa;
+                tr_frag(fa, sK + c * 2048 + ofs.tr[dt]);
+                mma(dq[dt], fa, fs);
+            }
+        }
+    };
+    for (int kb = 0; kb < qb; kb++) block(kb, std::false_type{});
+    block(qb, std::true_type{});
+    if (q < T_) {
+        bf16_t* row = dqkv + ((long)b * T_ + q) * rs + h * HS;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            float v[4] = {dq[dt][0] * scale, dq[dt][1] * scale, dq[dt][2] * scale, dq[dt][3] * scale};
+            store4<bf16_t>(row + 16 * dt + 4 * g4, v);
+        }
+    }
+}
+
 template <typename T, int HS>
 int fwd_hs(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
     const int nb = (T_ + 63) / 64;
@@ -791,6 +1085,15 @@ int bwd_hs(T* dqkv, float* delta, const T* dout, const T* out, const T* qkv, con
     const long rows = (long)B * T_ * NH;
     hipLaunchKernelGGL((attn_delta_kernel<T, HS>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
                        delta, dout, out, B, T_, C, NH);
+    if constexpr (std::is_same_v<T, bf16_t> && HS == 64) {
+        if ((long)T_ * 3 * C * 2 < (1L << 31)) {
+            hipLaunchKernelGGL((attn_bwd_dkdv_dtl_kernel<ATTN_BWD_NS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv,
+                               dout, qkv, lse, delta, T_, C, NH, sl2, scale);
+            hipLaunchKernelGGL((attn_bwd_dq_dtl_kernel<ATTN_BWD_NS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout,
+                               qkv, lse, delta, T_, C, NH, sl2, scale);
+            return (int)hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout, qkv, lse,
                        delta, T_, C, NH, sl2, scale);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout, qkv, lse,

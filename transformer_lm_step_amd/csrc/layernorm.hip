@@ -191,10 +191,11 @@ __global__ __launch_bounds__(64 * ln_bwd_waves<NV>()) void ln_bwd_kernel(float* 
 }
 
 // dw[c] += sum_blocks partial[blk][c]; db[c] += sum_blocks partial[blk][C + c].
-// 16 columns per workgroup (so 2C/16 workgroups share the reads), 16 phases of
-// blocks per column (block k goes to phase k % 16), phases combined in order
-// 0..15 through LDS.
-constexpr int FIN_PH = 16, FIN_COLS = 16;
+// 16 columns per workgroup (so 2C/16 workgroups share the reads) and 64
+// phases of blocks per column (block k goes to phase k % 64); each thread
+// issues all of its reads before adding (one round trip instead of a chain),
+// and the phases are combined in order 0..63 through LDS.
+constexpr int FIN_PH = 64, FIN_COLS = 16, FIN_MAXR = 16;  // up to FIN_PH * FIN_MAXR partial rows at once
 __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(float* __restrict__ dw,
                                                                          float* __restrict__ db,
                                                                          const float* __restrict__ partial, int C,
@@ -204,14 +205,21 @@ __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(float*
     const int j = blockIdx.x * FIN_COLS + col;
     float s = 0.f;
     if (j < 2 * C) {
-#pragma unroll 4
-        for (int k = ph; k < blocks; k += FIN_PH) s += partial[(size_t)k * 2 * C + j];
+        for (int k0 = ph; k0 < blocks; k0 += FIN_PH * FIN_MAXR) {
+            float v[FIN_MAXR];
+#pragma unroll
+            for (int i = 0; i < FIN_MAXR; i++) {
+                const int k = k0 + i * FIN_PH;
+                v[i] = k < blocks ? partial[(size_t)k * 2 * C + j] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < FIN_MAXR; i++) s += v[i];
+        }
     }
     red[ph][col] = s;
     __syncthreads();
     if (ph == 0 && j < 2 * C) {
         float t = red[0][col];
-#pragma unroll
         for (int q = 1; q < FIN_PH; q++) t += red[q][col];
         if (j < C) dw[j] += t;
         else db[j - C] += t;
