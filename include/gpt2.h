@@ -58,7 +58,8 @@ enum {
     GPT2_E_STATE = -3,  /* call order violated (e.g. backward without a forward with targets) */
     GPT2_E_TOKEN = -4,  /* a token or target id outside [0, vocab_size) was seen on the device */
     GPT2_E_ALIGN = -5,  /* a pointer is not 256-byte aligned */
-    GPT2_E_HIP = -6     /* a HIP runtime call or kernel launch failed */
+    GPT2_E_HIP = -6,    /* a HIP runtime call or kernel launch failed */
+    GPT2_E_FILE = -7    /* a model file cannot be read or is not a valid model file */
 };
 
 typedef struct gpt2_ctx gpt2_ctx;
@@ -166,6 +167,30 @@ int gpt2_act_tensor(gpt2_ctx* ctx, int which, void** d_ptr, size_t* count);
  * caller and kept valid while the hook is set; n = 0 removes the hook.
  * Errors: GPT2_E_ARG. */
 int gpt2_set_classifier_events(gpt2_ctx* ctx, void* const* d_start_events, void* const* d_end_events, int n);
+
+/* Model files (train_gpt2.cu, gpt2_build_from_checkpoint): a header of 256
+ * little-endian int32 -- [0] magic 20240326, [1] version (3: fp32 parameters;
+ * 5: bf16 parameters, LayerNorm ones included), [2] max_seq_len,
+ * [3] vocab_size, [4] num_layers, [5] num_heads, [6] channels,
+ * [7] padded_vocab_size, the rest unused -- followed by the P parameters of
+ * that config in gpt2_param_layout order (4 or 2 bytes each).  Host-only
+ * calls: no device memory or stream is touched.
+ *
+ * gpt2_checkpoint_header reads the header into *cfg and the precision of the
+ * stored parameters (GPT2_FP32 for version 3, GPT2_BF16 for 5) into
+ * *file_precision.  Errors: GPT2_E_ARG (NULL argument), GPT2_E_FILE (the file
+ * cannot be opened or holds less than a header, bad magic or version, or a
+ * config that gpt2_query_sizes would reject for B = T = 1). */
+int gpt2_checkpoint_header(const char* path, gpt2_config* cfg, int* file_precision);
+
+/* Reads the P parameters into h_params (caller-owned host memory of count
+ * fp32 values): version 3 values as stored, version 5 values widened exactly
+ * from bf16.  count must equal P of the header's config.  The result is what
+ * gpt2_init expects, after a host-to-device copy, in `params` (GPT2_FP32) or
+ * `master` (GPT2_BF16).  Bytes after the parameters are ignored.
+ * Errors: as gpt2_checkpoint_header; GPT2_E_ARG also for count != P;
+ * GPT2_E_FILE also for a file shorter than the header plus P values. */
+int gpt2_checkpoint_read(const char* path, float* h_params, size_t count);
 
 /* Frees the host-side context (no device memory is owned). */
 int gpt2_free(gpt2_ctx* ctx);

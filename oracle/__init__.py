@@ -5,7 +5,9 @@ leg may import this package.  The product path (the HIP library and its
 binding) never does.
 
 The arithmetic lives in ``gpt2_oracle.c`` (plain single-threaded C, double
-precision).  This module only builds it, loads it and marshals numpy arrays.
+precision).  This module only builds it, loads it and marshals numpy arrays,
+plus one piece of byte work written here in numpy: reading a model file
+(``read_checkpoint``).
 Parity pins for every function are in ``tests/test_oracle_*.py``.
 """
 
@@ -133,6 +135,37 @@ def unpack(cfg, flat: np.ndarray, shapes: dict) -> dict:
     off, cnt, _ = param_layout(cfg)
     return {name: flat[off[i]: off[i] + cnt[i]].reshape(shapes[name])
             for i, name in enumerate(PARAM_NAMES)}
+
+
+class _Cfg:
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def read_checkpoint(path):
+    """train_gpt2.cu, gpt2_build_from_checkpoint: a header of 256 int32 (magic
+    20240326; version 3 = fp32 parameters, 5 = bf16 parameters; then
+    max_seq_len, vocab_size, num_layers, num_heads, channels,
+    padded_vocab_size), then all parameters of that config in ParameterTensors
+    order.  Returns (config fields as a dict, 0 for fp32 / 1 for bf16, the
+    parameters as float64).  bf16 values are widened exactly (a bf16 is the
+    upper half of the fp32 with the same value).  Raises ValueError for a bad
+    magic or version or a short file."""
+    with open(path, "rb") as f:
+        head = np.frombuffer(f.read(256 * 4), dtype="<i4")
+        if head.size != 256 or head[0] != 20240326 or head[1] not in (3, 5):
+            raise ValueError("not a model file")
+        names = ("max_seq_len", "vocab_size", "num_layers", "num_heads", "channels", "padded_vocab_size")
+        cfg = {n: int(head[2 + i]) for i, n in enumerate(names)}
+        _, _, P = param_layout(_Cfg(**cfg))
+        if head[1] == 3:
+            vals = np.frombuffer(f.read(4 * P), dtype="<f4")
+        else:
+            raw = np.frombuffer(f.read(2 * P), dtype="<u2")
+            vals = (raw.astype(np.uint32) << 16).view(np.float32)
+        if vals.size != P:
+            raise ValueError("model file shorter than its parameters")
+    return cfg, (0 if head[1] == 3 else 1), vals.astype(np.float64)
 
 
 # ---- per-definition entry points ------------------------------------------------

@@ -181,3 +181,24 @@ def attention_inputs(B: int, T: int, C: int, score_scale: float = 1.0, seed: int
     qkv = round_to_bf16(np.concatenate([q, kv], axis=2).astype(np.float32))
     dout = round_to_bf16(rng.standard_normal((B, T, C), dtype=np.float32))
     return qkv, dout
+
+
+def write_checkpoint(path: str, cfg: Config, flat_params: np.ndarray, version: int, header_extra=None):
+    """Writes a model file in the layout train_gpt2.cu's gpt2_build_from_checkpoint
+    reads: 256 little-endian int32 (magic 20240326, version, max_seq_len,
+    vocab_size, num_layers, num_heads, channels, padded_vocab_size, zeros),
+    then flat_params as float32 (version 3) or as bf16 (version 5: the upper
+    16 bits of each float32, so the values should already be bf16-exact).
+    header_extra: {index: value} overrides, for malformed-file tests."""
+    head = np.zeros(256, "<i4")
+    head[:8] = [20240326, version, cfg.max_seq_len, cfg.vocab_size, cfg.num_layers, cfg.num_heads,
+                cfg.channels, cfg.padded_vocab_size]
+    for k, v in (header_extra or {}).items():
+        head[k] = v
+    vals = np.ascontiguousarray(flat_params, dtype="<f4")
+    with open(path, "wb") as f:
+        f.write(head.tobytes())
+        if version == 5:
+            f.write((vals.view("<u4") >> 16).astype("<u2").tobytes())
+        else:
+            f.write(vals.tobytes())

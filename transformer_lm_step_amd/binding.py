@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libgpt2_hip.so")
 GPT2_FP32 = 0
 GPT2_BF16 = 1
 GPT2_OK, GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_STATE, GPT2_E_TOKEN, GPT2_E_ALIGN, GPT2_E_HIP = 0, -1, -2, -3, -4, -5, -6
+GPT2_E_FILE = -7
 GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0, 1, 2, 3, 4
 
 EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
-    "gpt2_set_classifier_events", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
+    "gpt2_set_classifier_events", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
     "gpt2_linear_backward_workspace", "gpt2_attention_forward", "gpt2_attention_backward",
     "fused_linear_gelu_softmax_f32", "fused_linear_gelu_softmax_f32_workspace",
 )
@@ -68,6 +69,8 @@ def _load():
         "gpt2_check_device_error": (i, [vp, vp]),
         "gpt2_act_tensor": (i, [vp, i, ctypes.POINTER(vp), ctypes.POINTER(z)]),
         "gpt2_set_classifier_events": (i, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i]),
+        "gpt2_checkpoint_header": (i, [ctypes.c_char_p, cfgp, ctypes.POINTER(i)]),
+        "gpt2_checkpoint_read": (i, [ctypes.c_char_p, vp, z]),
         "gpt2_free": (i, [vp]),
         "gpt2_strerror": (ctypes.c_char_p, [i]),
         "gpt2_linear_forward": (i, [i, vp, vp, vp, vp, i, i, i, vp]),
@@ -180,6 +183,23 @@ def gpt2_set_classifier_events(ctx: int, starts, ends):
     b = (ctypes.c_void_p * max(n, 1))(*ends)
     _check(_lib.gpt2_set_classifier_events(ctx, a, b, n), "gpt2_set_classifier_events")
     return a, b
+
+
+def gpt2_checkpoint_header(path: str):
+    """Returns (config as a dict of the gpt2_config fields, file precision)."""
+    c = gpt2_config()
+    prec = ctypes.c_int()
+    _check(_lib.gpt2_checkpoint_header(os.fsencode(path), ctypes.byref(c), ctypes.byref(prec)),
+           "gpt2_checkpoint_header")
+    return {n: getattr(c, n) for n, _ in gpt2_config._fields_}, int(prec.value)
+
+
+def gpt2_checkpoint_read(path: str, h_params) -> None:
+    """h_params: a C-contiguous float32 numpy array of P elements, filled in place."""
+    import numpy as np
+    if not (isinstance(h_params, np.ndarray) and h_params.dtype == np.float32 and h_params.flags.c_contiguous):
+        raise TypeError("h_params must be a C-contiguous float32 numpy array")
+    _check(_lib.gpt2_checkpoint_read(os.fsencode(path), h_params.ctypes.data, h_params.size), "gpt2_checkpoint_read")
 
 
 def gpt2_free(ctx: int):

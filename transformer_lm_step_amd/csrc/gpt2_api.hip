@@ -15,6 +15,7 @@
 //    the step).
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -327,6 +328,26 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     return GPT2_OK;
 }
 
+// Model-file header (train_gpt2.cu, gpt2_build_from_checkpoint): 256 int32.
+constexpr int kCkptMagic = 20240326, kCkptHeaderInts = 256;
+
+int read_ckpt_header(FILE* f, gpt2_config* cfg, int* prec) {
+    int32_t h[kCkptHeaderInts];
+    if (fread(h, sizeof(int32_t), kCkptHeaderInts, f) != (size_t)kCkptHeaderInts) return GPT2_E_FILE;
+    if (h[0] != kCkptMagic || (h[1] != 3 && h[1] != 5)) return GPT2_E_FILE;
+    gpt2_config c;
+    c.max_seq_len = h[2];
+    c.vocab_size = h[3];
+    c.num_layers = h[4];
+    c.num_heads = h[5];
+    c.channels = h[6];
+    c.padded_vocab_size = h[7];
+    if (check_config(&c, GPT2_FP32, 1, 1) != GPT2_OK) return GPT2_E_FILE;
+    *cfg = c;
+    *prec = h[1] == 3 ? GPT2_FP32 : GPT2_BF16;
+    return GPT2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -479,6 +500,51 @@ int gpt2_free(gpt2_ctx* c) {
     return GPT2_OK;
 }
 
+int gpt2_checkpoint_header(const char* path, gpt2_config* cfg, int* file_precision) {
+    if (!path || !cfg || !file_precision) return GPT2_E_ARG;
+    FILE* f = fopen(path, "rb");
+    if (!f) return GPT2_E_FILE;
+    const int rc = read_ckpt_header(f, cfg, file_precision);
+    fclose(f);
+    return rc;
+}
+
+int gpt2_checkpoint_read(const char* path, float* h_params, size_t count) {
+    if (!path || !h_params) return GPT2_E_ARG;
+    FILE* f = fopen(path, "rb");
+    if (!f) return GPT2_E_FILE;
+    gpt2_config c;
+    int prec = 0;
+    int rc = read_ckpt_header(f, &c, &prec);
+    if (rc == GPT2_OK) {
+        size_t off[16], cnt[16], P = 0;
+        param_layout(c, off, cnt, &P);
+        if (count != P) {
+            rc = GPT2_E_ARG;
+        } else if (prec == GPT2_FP32) {
+            if (fread(h_params, sizeof(float), P, f) != P) rc = GPT2_E_FILE;
+        } else {
+            // bf16 values, read in chunks and widened: a bf16 value is the
+            // upper 16 bits of the fp32 with the same value
+            constexpr size_t CH = 1 << 16;
+            uint16_t buf[CH];
+            for (size_t i = 0; i < P && rc == GPT2_OK; i += CH) {
+                const size_t n = std::min(CH, P - i);
+                if (fread(buf, sizeof(uint16_t), n, f) != n) {
+                    rc = GPT2_E_FILE;
+                    break;
+                }
+                for (size_t j = 0; j < n; j++) {
+                    const uint32_t u = (uint32_t)buf[j] << 16;
+                    memcpy(&h_params[i + j], &u, 4);
+                }
+            }
+        }
+    }
+    fclose(f);
+    return rc;
+}
+
 const char* gpt2_strerror(int code) {
     switch (code) {
         case GPT2_OK: return "ok";
@@ -488,6 +554,7 @@ const char* gpt2_strerror(int code) {
         case GPT2_E_TOKEN: return "token or target id outside [0, vocab_size)";
         case GPT2_E_ALIGN: return "pointer not 256-byte aligned";
         case GPT2_E_HIP: return "HIP runtime or kernel launch failure";
+        case GPT2_E_FILE: return "model file missing, unreadable or invalid";
         default: return "unknown error";
     }
 }

@@ -16,8 +16,27 @@ PARAM_NAMES = (
 )
 
 
+class Config:
+    """The six GPT2Config fields (train_gpt2.cu)."""
+
+    def __init__(self, max_seq_len, vocab_size, padded_vocab_size, num_layers, num_heads, channels):
+        self.max_seq_len, self.vocab_size, self.padded_vocab_size = max_seq_len, vocab_size, padded_vocab_size
+        self.num_layers, self.num_heads, self.channels = num_layers, num_heads, channels
+
+
 class GPT2:
     """One context over torch-allocated device buffers on the current device."""
+
+    @classmethod
+    def from_checkpoint(cls, path: str, precision: int, batch: int, seq_len: int, device="cuda"):
+        """A model whose initial parameters come from a model file (read on the
+        host by gpt2_checkpoint_read, then copied to the device by init)."""
+        fields, _ = B.gpt2_checkpoint_header(path)
+        cfg = Config(**fields)
+        model = cls(cfg, precision, batch, seq_len, device)
+        flat = np.empty(model.num_params, np.float32)
+        B.gpt2_checkpoint_read(path, flat)
+        return model.init(flat)
 
     def __init__(self, cfg, precision: int, batch: int, seq_len: int, device="cuda"):
         self.cfg, self.precision, self.B, self.T = cfg, precision, batch, seq_len
