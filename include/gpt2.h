@@ -168,6 +168,26 @@ int gpt2_act_tensor(gpt2_ctx* ctx, int which, void** d_ptr, size_t* count);
  * Errors: GPT2_E_ARG. */
 int gpt2_set_classifier_events(gpt2_ctx* ctx, void* const* d_start_events, void* const* d_end_events, int n);
 
+/* train_gpt2.cu, sample_softmax with the generation loop's indexing: for
+ * every batch row b, sets d_tokens[b*T + t] to the token drawn from the
+ * softmax over the first vocab_size logits of position t-1 of the last
+ * gpt2_forward, which must have been made without targets (GPT2_E_STATE
+ * otherwise).  The draw inverts the CDF with the coin d_coins[b] in [0, 1):
+ * the smallest i with coin * Z < p_0 + ... + p_i, where p_j = exp(z_j - max z)
+ * and Z = sum of all p_j (fp64 sums in a fixed order), or vocab_size - 1 if
+ * there is none.  d_tokens: device int32 [B,T] (typically the inputs of the
+ * next forward); d_coins: device fp32 [B]; 1 <= t < T.  Asynchronous on
+ * hip_stream.  Errors: GPT2_E_ARG, GPT2_E_STATE, GPT2_E_ALIGN, GPT2_E_HIP. */
+int gpt2_sample(gpt2_ctx* ctx, const float* d_coins, int32_t* d_tokens, int t, void* hip_stream);
+
+/* The page's generation loop: for t = t_begin .. t_end - 1, a forward without
+ * targets over all of d_tokens [B,T] (the page recomputes every position for
+ * each new token), then gpt2_sample(ctx, d_coins + (t - t_begin) * B,
+ * d_tokens, t).  d_coins: device fp32 [(t_end - t_begin) * B].  Positions
+ * t_begin .. t_end - 1 of every row are overwritten; 1 <= t_begin <= t_end <= T.
+ * Errors: as gpt2_forward and gpt2_sample. */
+int gpt2_generate(gpt2_ctx* ctx, int32_t* d_tokens, const float* d_coins, int t_begin, int t_end, void* hip_stream);
+
 /* Model files (train_gpt2.cu, gpt2_build_from_checkpoint): a header of 256
  * little-endian int32 -- [0] magic 20240326, [1] version (3: fp32 parameters;
  * 5: bf16 parameters, LayerNorm ones included), [2] max_seq_len,

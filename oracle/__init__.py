@@ -294,6 +294,30 @@ def gpt2_step(cfg, flat_params, inputs, targets=None, dloss=0.0, want_grads=True
             "logits": None if logits is None else logits.reshape(B, T, -1), "grads": g}
 
 
+def sample_softmax(logits, V, coin):
+    """train_gpt2.cu, sample_softmax: the index drawn from softmax(logits[:V])
+    by inverse CDF with coin in [0, 1): the smallest i with
+    coin * sum_j p_j < p_0 + ... + p_i (p_j = exp(z_j - max z); the maximum
+    cancels in exact arithmetic), V - 1 if none.  fp64, sums in index order."""
+    z = np.asarray(logits, np.float64)[:V]
+    cdf = np.cumsum(np.exp(z - z.max()))
+    i = int(np.searchsorted(cdf, float(coin) * cdf[-1], side="right"))
+    return min(i, V - 1)
+
+
+def generate(cfg, flat_params, tokens, coins, t_begin, t_end):
+    """train_gpt2.cu, the generation loop: for t = t_begin .. t_end - 1, a full
+    forward without targets over tokens [B,T], then every row b draws its
+    token at t from the logits at t - 1 with coin coins[t - t_begin][b].
+    Returns the updated tokens (int32 [B,T])."""
+    tokens = np.array(tokens, np.int32)
+    for t in range(t_begin, t_end):
+        z = gpt2_step(cfg, flat_params, tokens, want_grads=False, want_logits=True)["logits"]
+        for b in range(tokens.shape[0]):
+            tokens[b, t] = sample_softmax(z[b, t - 1], cfg.vocab_size, coins[t - t_begin][b])
+    return tokens
+
+
 def fused_linear_gelu_softmax(X, W, b, rows=None):
     X = _f64(X); W = _f64(W); b = _f64(b)
     M, K = X.shape; N = W.shape[0]

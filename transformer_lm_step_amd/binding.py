@@ -24,7 +24,7 @@ GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0
 EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
-    "gpt2_set_classifier_events", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
+    "gpt2_set_classifier_events", "gpt2_sample", "gpt2_generate", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
     "gpt2_linear_backward_workspace", "gpt2_attention_forward", "gpt2_attention_backward",
     "fused_linear_gelu_softmax_f32", "fused_linear_gelu_softmax_f32_workspace",
 )
@@ -69,6 +69,8 @@ def _load():
         "gpt2_check_device_error": (i, [vp, vp]),
         "gpt2_act_tensor": (i, [vp, i, ctypes.POINTER(vp), ctypes.POINTER(z)]),
         "gpt2_set_classifier_events": (i, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i]),
+        "gpt2_sample": (i, [vp, vp, vp, i, vp]),
+        "gpt2_generate": (i, [vp, vp, vp, i, i, vp]),
         "gpt2_checkpoint_header": (i, [ctypes.c_char_p, cfgp, ctypes.POINTER(i)]),
         "gpt2_checkpoint_read": (i, [ctypes.c_char_p, vp, z]),
         "gpt2_free": (i, [vp]),
@@ -183,6 +185,14 @@ def gpt2_set_classifier_events(ctx: int, starts, ends):
     b = (ctypes.c_void_p * max(n, 1))(*ends)
     _check(_lib.gpt2_set_classifier_events(ctx, a, b, n), "gpt2_set_classifier_events")
     return a, b
+
+
+def gpt2_sample(ctx: int, d_coins: int, d_tokens: int, t: int, stream: int):
+    _check(_lib.gpt2_sample(ctx, d_coins, d_tokens, t, stream or None), "gpt2_sample")
+
+
+def gpt2_generate(ctx: int, d_tokens: int, d_coins: int, t_begin: int, t_end: int, stream: int):
+    _check(_lib.gpt2_generate(ctx, d_tokens, d_coins, t_begin, t_end, stream or None), "gpt2_generate")
 
 
 def gpt2_checkpoint_header(path: str):

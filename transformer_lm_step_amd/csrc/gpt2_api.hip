@@ -500,6 +500,32 @@ int gpt2_free(gpt2_ctx* c) {
     return GPT2_OK;
 }
 
+int gpt2_sample(gpt2_ctx* c, const float* d_coins, int32_t* d_tokens, int t, void* hip_stream) {
+    if (!c || !d_coins || !d_tokens) return GPT2_E_ARG;
+    if (t < 1 || t >= c->T) return GPT2_E_ARG;
+    if (!aligned(d_tokens) || ((uintptr_t)d_coins % 4)) return GPT2_E_ALIGN;
+    if (c->last_fwd_targets != 0) return GPT2_E_STATE;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    const Plan& p = c->plan;
+    const int V = c->cfg.vocab_size, Vp = (int)p.Vp;
+    const int rc = c->prec == GPT2_BF16
+                       ? sample_launch<bf16_t>(d_tokens, c->act<bf16_t>(p.logits), d_coins, c->B, c->T, t, V, Vp, s)
+                       : sample_launch<float>(d_tokens, c->act<float>(p.logits), d_coins, c->B, c->T, t, V, Vp, s);
+    return hip_rc(rc);
+}
+
+int gpt2_generate(gpt2_ctx* c, int32_t* d_tokens, const float* d_coins, int t_begin, int t_end, void* hip_stream) {
+    if (!c || !d_tokens || !d_coins) return GPT2_E_ARG;
+    if (t_begin < 1 || t_end < t_begin || t_end > c->T) return GPT2_E_ARG;
+    for (int t = t_begin; t < t_end; t++) {
+        int rc = gpt2_forward(c, d_tokens, nullptr, nullptr, nullptr, hip_stream);
+        if (rc != GPT2_OK) return rc;
+        rc = gpt2_sample(c, d_coins + (size_t)(t - t_begin) * c->B, d_tokens, t, hip_stream);
+        if (rc != GPT2_OK) return rc;
+    }
+    return GPT2_OK;
+}
+
 int gpt2_checkpoint_header(const char* path, gpt2_config* cfg, int* file_precision) {
     if (!path || !cfg || !file_precision) return GPT2_E_ARG;
     FILE* f = fopen(path, "rb");

@@ -81,6 +81,11 @@ template <typename T>
 int classifier_ce_launch(T* logits, float* losses, const int* targets, int N, int V, int Vp,
                          int* flag, hipStream_t s);
 int mean_launch(float* out, const float* x, int n, hipStream_t s);
+
+// tokens[b*T + t] = the token drawn from softmax(logits[b, t-1, :V]) with coins[b]
+template <typename T>
+int sample_launch(int32_t* tokens, const T* logits, const float* coins, int B, int T_, int t, int V, int Vp,
+                  hipStream_t s);
 template <typename PT>
 int adamw_launch(PT* params, float* master, const float* grads, float* m, float* v, size_t n,
                  float lr, float beta1, float beta2, float c1, float c2, float eps, float wd,

@@ -106,6 +106,12 @@ class GPT2:
                        0 if losses is None else losses.data_ptr(), 0 if mean_loss is None else mean_loss.data_ptr(),
                        self.stream)
 
+    def sample(self, coins: torch.Tensor, tokens: torch.Tensor, t: int):
+        B.gpt2_sample(self.ctx, coins.data_ptr(), tokens.data_ptr(), t, self.stream)
+
+    def generate(self, tokens: torch.Tensor, coins: torch.Tensor, t_begin: int, t_end: int):
+        B.gpt2_generate(self.ctx, tokens.data_ptr(), coins.data_ptr(), t_begin, t_end, self.stream)
+
     def zero_grad(self):
         B.gpt2_zero_grad(self.ctx, self.stream)
 
