@@ -128,6 +128,94 @@ def bench_fused(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_generate(args):
+    """The page's generation loop on GPT-2 124M bf16 (B=8, T=1024): per new
+    token a forward without targets over all B x T positions, then one draw
+    per batch row on the device (gpt2_generate).  `steps` tokens per row are
+    generated after `warmup` untimed ones; value = generated tokens/s over all
+    rows.  The classifier product is again the dominant kernel (HIP events
+    around its launches in the timed forwards)."""
+    import torch
+    import synthetic as S
+    from transformer_lm_step_amd import binding as Bnd
+    from transformer_lm_step_amd.model import GPT2
+
+    cfg = S.GPT2_124M
+    B, T = args.batch, args.seq
+    if args.warmup + args.steps >= T:
+        raise SystemExit("generate: warmup + steps must stay below the sequence length")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    model = GPT2(cfg, Bnd.GPT2_BF16, B, T)
+    model.init(model.pack({k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}))
+    rng = np.random.default_rng(12)
+    t_begin = T - args.warmup - args.steps
+    start = S.token_stream(B * T, cfg.vocab_size, dist="zipf").reshape(B, T)
+    tok = torch.from_numpy(start.copy()).to(dev)
+    coins = torch.from_numpy(rng.random((args.warmup + args.steps) * B).astype(np.float32)).to(dev)
+    t_mid = t_begin + args.warmup
+    model.generate(tok, coins, t_begin, t_mid)
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    starts, ends = hip.create(args.steps), hip.create(args.steps)
+    hook = Bnd.gpt2_set_classifier_events(model.ctx, starts, ends)
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    model.generate(tok, coins[args.warmup * B:], t_mid, T)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    Bnd.gpt2_set_classifier_events(model.ctx, [], [])
+    del hook
+    if model.check() != 0:
+        raise RuntimeError("device-side error during generation")
+    ms = e0.elapsed_time(e1) / args.steps
+    kms = float(np.mean([hip.elapsed_ms(a, b) for a, b in zip(starts, ends)]))
+    hip.destroy(starts + ends)
+    # the draw alone: the sampling kernel over the last forward's logits
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(cur)
+    for _ in range(20):
+        model.sample(coins[:B], tok, T - 1)
+    s1.record(cur)
+    torch.cuda.synchronize()
+    sample_us = s0.elapsed_time(s1) / 20 * 1e3
+    gen = tok.cpu().numpy()
+    if not (np.all(gen >= 0) and np.all(gen < cfg.vocab_size)):
+        raise RuntimeError("generated ids outside the vocabulary")
+    tok_s = B / (ms / 1e3)
+    kflop = 2.0 * B * T * cfg.padded_vocab_size * cfg.channels
+    achieved = kflop / (kms / 1e3) / 1e12
+    log(f"bench: generate {ms:.3f} ms per token step ({tok_s:,.0f} tok/s), classifier {kms:.3f} ms, "
+        f"draw {sample_us:.1f} us")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        Tc, n = 64, 4
+        flat = oracle.pack_params(cfg, {k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()})
+        t0 = time.perf_counter()
+        oracle.generate(cfg, flat, start[:1, :Tc], rng.random((n, 1)), Tc - n, Tc)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} tokens of one row at T={Tc} (full forward per token, fp64, single thread), "
+                         f"{dt:.1f} s"}
+    out = {
+        "metric": "generated tokens/s, GPT-2 124M bf16, full B x T forward per token (page's loop)",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (Zipf(1.1) prompt tokens, random GPT-2 init, uniform coins)",
+        "config": {"workload": f"GPT-2 124M generation: B={B} rows, T={T}, one draw per row per forward"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_dtl_kernel (classifier forward, in the timed forwards)",
+                     "avg_ms": round(kms, 4), "launches": args.steps},
+        "sample_kernel_us": round(sample_us, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+
+
 class HipEvents:
     """hipEvent_t handles through the HIP runtime's C API (plumbing for the
     library's timing hook; torch creates its events lazily)."""
@@ -226,9 +314,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the kernels the HBM-traffic counter runs read")
-    ap.add_argument("--workload", choices=("gpt2", "fused"), default="gpt2",
+    ap.add_argument("--workload", choices=("gpt2", "fused", "generate"), default="gpt2",
                     help="gpt2: the GPT-2 124M training step (default); fused: the standalone "
-                         "Linear+GELU+softmax op")
+                         "Linear+GELU+softmax op; generate: the page's generation loop")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -239,6 +327,9 @@ def main():
         return
     if args.workload == "fused":
         bench_fused(args)
+        return
+    if args.workload == "generate":
+        bench_generate(args)
         return
 
     import torch

@@ -174,8 +174,8 @@ int gpt2_set_classifier_events(gpt2_ctx* ctx, void* const* d_start_events, void*
  * gpt2_forward, which must have been made without targets (GPT2_E_STATE
  * otherwise).  The draw inverts the CDF with the coin d_coins[b] in [0, 1):
  * the smallest i with coin * Z < p_0 + ... + p_i, where p_j = exp(z_j - max z)
- * and Z = sum of all p_j (fp64 sums in a fixed order), or vocab_size - 1 if
- * there is none.  d_tokens: device int32 [B,T] (typically the inputs of the
+ * and Z = sum of all p_j (fp64 sums in a fixed order, so the draw is
+ * deterministic), or vocab_size - 1 if there is none.  d_tokens: device int32 [B,T] (typically the inputs of the
  * next forward); d_coins: device fp32 [B]; 1 <= t < T.  Asynchronous on
  * hip_stream.  Errors: GPT2_E_ARG, GPT2_E_STATE, GPT2_E_ALIGN, GPT2_E_HIP. */
 int gpt2_sample(gpt2_ctx* ctx, const float* d_coins, int32_t* d_tokens, int t, void* hip_stream);
