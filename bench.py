@@ -314,6 +314,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the kernels the HBM-traffic counter runs read")
+    ap.add_argument("--sr", action="store_true",
+                    help="train without fp32 master weights (bf16 parameters, stochastic rounding in AdamW)")
     ap.add_argument("--workload", choices=("gpt2", "fused", "generate"), default="gpt2",
                     help="gpt2: the GPT-2 124M training step (default); fused: the standalone "
                          "Linear+GELU+softmax op; generate: the page's generation loop")
@@ -341,9 +343,10 @@ def main():
     B, T, accum = args.batch, args.seq, args.accum
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"bench: GPT-2 124M bf16 B={B} T={T} accum={accum} steps={args.steps} warmup={args.warmup}")
+    log(f"bench: GPT-2 124M bf16 B={B} T={T} accum={accum} steps={args.steps} warmup={args.warmup}"
+        + (" (no master weights, stochastic rounding)" if args.sr else ""))
 
-    model = GPT2(cfg, Bnd.GPT2_BF16, B, T)
+    model = GPT2(cfg, Bnd.GPT2_BF16_SR if args.sr else Bnd.GPT2_BF16, B, T)
     params = {k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}  # bf16-exact start
     model.init(model.pack(params))
     n_micro = (args.warmup + args.steps) * accum
@@ -418,7 +421,8 @@ def main():
         log(f"bench: oracle {cpu['value']:.3f} tok/s ({cpu['sample']})")
 
     out = {
-        "metric": "train tokens/sec + MFU, GPT-2 124M bf16 B=8 T=1024 on 1x MI355X",
+        "metric": "train tokens/sec + MFU, GPT-2 124M bf16 B=8 T=1024 on 1x MI355X"
+                  + (" (bf16 parameters without master weights, stochastic rounding)" if args.sr else ""),
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -48,8 +48,13 @@ typedef struct {
  *             products, no reduced-precision inputs).
  *  GPT2_BF16: bf16 parameters, activations and matrix-core products with fp32
  *             accumulation; fp32 master weights, fp32 gradients, fp32 AdamW
- *             state, fp32 LayerNorm statistics, losses and residual gradient. */
-enum { GPT2_FP32 = 0, GPT2_BF16 = 1 };
+ *             state, fp32 LayerNorm statistics, losses and residual gradient.
+ *  GPT2_BF16_SR: GPT2_BF16 without the fp32 master weights (train_gpt2.cu,
+ *             adamw_kernel3 without master_params): `master` is unused (0
+ *             bytes), the caller writes the bf16 initial values into `params`,
+ *             and each update rounds the new fp32 values to bf16
+ *             stochastically (see gpt2_adamw_update). */
+enum { GPT2_FP32 = 0, GPT2_BF16 = 1, GPT2_BF16_SR = 2 };
 
 enum {
     GPT2_OK = 0,
@@ -139,9 +144,28 @@ int gpt2_backward(gpt2_ctx* ctx, float dloss, void* hip_stream);
  * (sqrt(v/(1-b2^t)) + eps) + lr wd p, with one weight decay for all
  * parameters.  t is the 1-based step.  GPT2_BF16: the fp32 master weights are
  * updated and params receives their round-to-nearest-even bf16 value.
+ * GPT2_BF16_SR (the page's path without master weights): the update starts
+ * from the bf16 parameter and is evaluated in fp32 operation by operation as
+ * the page writes it (the moment updates as fused multiply-adds, bias
+ * corrections 1 - powf(b, t) in fp32, no other contraction); the result x is
+ * rounded to bf16 stochastically: with r the low 16 bits of a 32-bit noise
+ * value, x's low 16 bits are set to all ones if they exceed r (then rounded
+ * to nearest-even, i.e. up) and cleared otherwise, so x rounds up with
+ * probability (low 16 bits) / 65536.  The noise of parameter i is the
+ * page's Get2dNoiseUint applied twice at (i mod 512, i div 512) -- the
+ * page's 512-thread launch -- seeded first with s and then with the first
+ * value: SquirrelNoise5(p, SquirrelNoise5(p, s)), p = (i mod 512) +
+ * 198491317 (i div 512) mod 2^32.  s is drawn per call from the context's
+ * xorshift64* state (the page's random_u32; initial state 13371337, see
+ * gpt2_set_rng_state).
  * Errors: GPT2_E_ARG (t < 1), GPT2_E_HIP. */
 int gpt2_adamw_update(gpt2_ctx* ctx, float lr, float beta1, float beta2, float eps,
                       float weight_decay, int t, void* hip_stream);
+
+/* Sets (state != 0) and reads back (*old, if not NULL) the 64-bit xorshift64*
+ * state from which GPT2_BF16_SR updates draw their noise seeds (gpt2_init
+ * sets 13371337, the page's rng_state).  Errors: GPT2_E_ARG (NULL ctx). */
+int gpt2_set_rng_state(gpt2_ctx* ctx, uint64_t state, uint64_t* old);
 
 /* Synchronises hip_stream and reports device-side conditions raised since the
  * last call (GPT2_E_TOKEN for an out-of-range id), then clears them. */

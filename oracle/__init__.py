@@ -79,6 +79,13 @@ def _declare(L):
         "orc_crossentropy_forward": (_d, [_dp, _dp, _dp, _ip, _i, _i, _i]),
         "orc_crossentropy_backward": (None, [_dp, _dp, _ip, _d, _i, _i, _i]),
         "orc_adamw": (None, [_dp, _dp, _dp, _dp, _z, _d, _d, _d, _d, _d, _i]),
+        "orc_adamw_sr": (None, [ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_float),
+                                ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _z,
+                                ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, _i,
+                                ctypes.c_uint32]),
+        "orc_xorshift_u32": (ctypes.c_uint32, [ctypes.POINTER(ctypes.c_uint64)]),
+        "orc_noise2d": (ctypes.c_uint32, [_i, _i, ctypes.c_uint32]),
+        "orc_sr_bf16": (ctypes.c_uint16, [ctypes.c_float, ctypes.c_uint32]),
         "orc_gpt2_step": (_d, [ctypes.POINTER(OrcConfig), _dp, _ip, _ip, _i, _i, _d, _dp, _dp, _dp]),
         "orc_fused_linear_gelu_softmax": (None, [_dp, _dp, _dp, _dp, _i, _i, _i, _ip, _i]),
     }
@@ -292,6 +299,39 @@ def gpt2_step(cfg, flat_params, inputs, targets=None, dloss=0.0, want_grads=True
         raise ValueError("oracle rejected the arguments")
     return {"mean_loss": mean, "losses": losses.reshape(B, T) if tg is not None else None,
             "logits": None if logits is None else logits.reshape(B, T, -1), "grads": g}
+
+
+def adamw_sr(params_bf16, grads, m, v, lr, beta1, beta2, eps, wd, t, seed):
+    """train_gpt2.cu, adamw_kernel3 without master weights, in fp32 with the
+    page's stochastic rounding (see gpt2_oracle.c).  params_bf16: uint16 bf16
+    bit patterns; grads, m, v: float32.  Returns new (params, m, v)."""
+    p = np.array(params_bf16, dtype=np.uint16)
+    g = np.ascontiguousarray(grads, dtype=np.float32)
+    m2 = np.array(m, dtype=np.float32)
+    v2 = np.array(v, dtype=np.float32)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    lib().orc_adamw_sr(p.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), g.ctypes.data_as(f32p),
+                       m2.ctypes.data_as(f32p), v2.ctypes.data_as(f32p), p.size, lr, beta1, beta2, eps, wd, int(t),
+                       int(seed))
+    return p, m2, v2
+
+
+def xorshift_u32(state):
+    """train_gpt2.cu, random_u32.  Returns (value, new state)."""
+    s = ctypes.c_uint64(int(state))
+    r = lib().orc_xorshift_u32(ctypes.byref(s))
+    return int(r), int(s.value)
+
+
+def noise2d(x, y, seed):
+    """train_gpt2.cu, Get2dNoiseUint."""
+    return int(lib().orc_noise2d(int(x), int(y), int(seed)))
+
+
+def sr_bf16(x, r):
+    """train_gpt2.cu, stochastic_rounding of the fp32 value x with threshold r
+    (0 <= r < 2^16); returns the bf16 bit pattern."""
+    return int(lib().orc_sr_bf16(float(np.float32(x)), int(r)))
 
 
 def sample_softmax(logits, V, coin):

@@ -1,7 +1,9 @@
 /*
  * gpt2_oracle.c - CPU oracle for the GPT-2 training step (TEST INFRASTRUCTURE).
  *
- * Plain, slow, single-threaded C in double precision.  Each function writes out
+ * Plain, slow, single-threaded C in double precision (one exception:
+ * orc_adamw_sr works in fp32, the page's precision, because an fp32 value
+ * decides its stochastic rounding).  Each function writes out
  * one definition from the pages; comments name the page and the kernel or host
  * routine whose computation it follows.  Loops are in the order of the
  * definition; the only liberty taken is the loop nest of the two backward
@@ -18,6 +20,7 @@
 #include "gpt2_oracle.h"
 
 #include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -344,6 +347,94 @@ void orc_adamw(double* params, const double* grads, double* m, double* v, size_t
         v[i] = beta2 * v[i] + (1.0 - beta2) * g * g;
         double mhat = m[i] / c1, vhat = v[i] / c2;
         params[i] -= lr * (mhat / (sqrt(vhat) + eps) + weight_decay * params[i]);
+    }
+}
+
+/* SquirrelNoise5, Squirrel Eiserloh's published noise function (the one
+ * train_gpt2.cu uses): a 32-bit position is multiplied by a constant, the seed
+ * added, then the bits are mixed by right xor-shifts of 9, 11, 13, 15 and 17
+ * interleaved with adding, multiplying by and adding three more constants.
+ * All arithmetic modulo 2^32. */
+static uint32_t orc_squirrel5(uint32_t pos, uint32_t seed) {
+    uint32_t h = pos * 0xd2a80a3fu;
+    h += seed;
+    h ^= h >> 9;
+    h += 0xa884f197u;
+    h ^= h >> 11;
+    h *= 0x6c736f4bu;
+    h ^= h >> 13;
+    h += 0xb79f3abbu;
+    h ^= h >> 15;
+    h *= 0x1b56c4f5u;
+    h ^= h >> 17;
+    return h;
+}
+
+/* train_gpt2.cu, Get2dNoiseUint: position x + 198491317 y (mod 2^32). */
+uint32_t orc_noise2d(int x, int y, uint32_t seed) {
+    return orc_squirrel5((uint32_t)x + 198491317u * (uint32_t)y, seed);
+}
+
+/* train_gpt2.cu, random_u32: xorshift (shifts 12, 25, 27) of the 64-bit state,
+ * then the upper half of the state times 0x2545F4914F6CDD1D (xorshift*). */
+uint32_t orc_xorshift_u32(uint64_t* state) {
+    uint64_t s = *state;
+    s ^= s >> 12;
+    s ^= s << 25;
+    s ^= s >> 27;
+    *state = s;
+    return (uint32_t)((s * 0x2545F4914F6CDD1DULL) >> 32);
+}
+
+/* fp32 -> bf16, round to nearest even (finite inputs). */
+static uint16_t orc_bf16_rne(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* train_gpt2.cu, stochastic_rounding: the low 16 bits of x are set to ones
+ * if they exceed r (r < 2^16), cleared otherwise; then round to nearest-even
+ * bf16.  x rounds up exactly for the r below its low 16 bits. */
+uint16_t orc_sr_bf16(float x, uint32_t r) {
+    uint32_t bits;
+    memcpy(&bits, &x, 4);
+    bits = (bits & 0xffffu) > r ? (bits | 0xffffu) : (bits & 0xffff0000u);
+    float y;
+    memcpy(&y, &bits, 4);
+    return orc_bf16_rne(y);
+}
+
+/* train_gpt2.cu, adamw_kernel3 with master_params == NULL, in the page's
+ * precision (fp32, one rounding per operation; the moment updates are the
+ * page's lerp, two fused multiply-adds), with gpt2_update's corrections
+ * 1 - powf(beta, t) and stochastic_rounding: parameter i, launched by the page
+ * as thread i % 512 of block i / 512, draws the noise Get2dNoiseUint at that
+ * position with the per-call seed, and that value is the seed of a second
+ * Get2dNoiseUint at the same position (the page passes the first draw as the
+ * rounding's seed); the low 16 bits r of the second draw decide: the new
+ * value's low 16 bits are set to ones if they exceed r, cleared otherwise,
+ * and the result is rounded to nearest-even bf16.  params hold bf16 bit
+ * patterns. */
+void orc_adamw_sr(uint16_t* params, const float* grads, float* m, float* v, size_t n, float lr, float beta1,
+                  float beta2, float eps, float weight_decay, int t, uint32_t seed) {
+    const float c1 = 1.0f - powf(beta1, (float)t), c2 = 1.0f - powf(beta2, (float)t);
+    for (size_t i = 0; i < n; i++) {
+        const float g = grads[i];
+        m[i] = fmaf(beta1, m[i], fmaf(-beta1, g, g));
+        const float g2 = g * g;
+        v[i] = fmaf(beta2, v[i], fmaf(-beta2, g2, g2));
+        const float mhat = m[i] / c1, vhat = v[i] / c2;
+        uint32_t ob = (uint32_t)params[i] << 16;
+        float old;
+        memcpy(&old, &ob, 4);
+        const float den = sqrtf(vhat) + eps;
+        const float upd = mhat / den + weight_decay * old;
+        const float x = old - lr * upd;
+        const int tx = (int)(i % 512), bx = (int)(i / 512);
+        const uint32_t r = orc_noise2d(tx, bx, orc_noise2d(tx, bx, seed)) & 0xffffu;
+        params[i] = orc_sr_bf16(x, r);
     }
 }
 

@@ -17,6 +17,7 @@
 #define GPT2_ORACLE_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -110,6 +111,18 @@ double orc_gpt2_step(const orc_config* cfg, const double* params, const int* inp
  * all M rows in order. */
 void orc_fused_linear_gelu_softmax(double* Y, const double* X, const double* W, const double* b,
                                    int M, int K, int N, const int* rows, int nrows);
+
+/* train_gpt2.cu, adamw_kernel3 without master weights: the bf16 parameters
+ * (bit patterns) updated in fp32 -- the page's precision, since the fp32
+ * value decides the stochastic rounding -- and rounded back stochastically
+ * with SquirrelNoise5 noise; see gpt2_oracle.c.  m, v are fp32, "=". */
+void orc_adamw_sr(uint16_t* params, const float* grads, float* m, float* v, size_t n, float lr, float beta1,
+                  float beta2, float eps, float weight_decay, int t, uint32_t seed);
+/* train_gpt2.cu, random_u32 (xorshift*) and Get2dNoiseUint (SquirrelNoise5). */
+uint32_t orc_xorshift_u32(uint64_t* state);
+uint32_t orc_noise2d(int x, int y, uint32_t seed);
+/* train_gpt2.cu, stochastic_rounding of x with threshold r < 2^16 (bf16 bits). */
+uint16_t orc_sr_bf16(float x, uint32_t r);
 
 #ifdef __cplusplus
 }

@@ -89,7 +89,7 @@ def gpu_step(cfg, precision, params, batches, dloss=0.0, lr=1e-4, beta1=0.9, bet
     if model.precision == 1:
         newp = model.master().cpu().numpy().astype(np.float64)
     else:
-        newp = model.params().cpu().numpy().astype(np.float64)
+        newp = model.params().float().cpu().numpy().astype(np.float64)
     res = {"losses": losses, "means": means, "grads": model.unpack(grads), "params": model.unpack(newp),
            "m": model.unpack(model.adam_m().cpu().numpy().astype(np.float64)),
            "v": model.unpack(model.adam_v().cpu().numpy().astype(np.float64)),

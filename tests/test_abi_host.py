@@ -55,6 +55,8 @@ def test_query_sizes_plan():
     # activations: at least the logits (bf16) and 12 layers of the 8 per-layer tensors
     BT, C = 8 * 1024, 768
     assert s["acts"] >= BT * 50304 * 2 + 12 * BT * C * 2 * 16
+    sr = B.gpt2_query_sizes(S.GPT2_124M, B.GPT2_BF16_SR, 8, 1024)
+    assert sr["master"] == 0 and sr["params"] == s["params"] and sr["acts"] == s["acts"]
     s32 = B.gpt2_query_sizes(S.TINY, B.GPT2_FP32, 4, 64)
     assert s32["master"] == 0 and s32["params"] >= 136960 * 4
 

@@ -1,0 +1,84 @@
+"""bf16 training without master weights (GPT2_BF16_SR; train_gpt2.cu,
+adamw_kernel3's stochastic-rounding path): the device update against the
+oracle's fp32 update with the same rounding noise, bit for bit, over two
+steps (the seed state advancing between them) and after a reseed; the
+gradients of the mode equal those of GPT2_BF16 from the same parameters."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+from helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+
+
+def _micro(model, x, y):
+    import torch
+    dev = model.device
+    model.forward(torch.from_numpy(x.reshape(-1)).to(dev), torch.from_numpy(y.reshape(-1)).to(dev))
+    model.backward(0.0)
+
+
+def test_sr_update_matches_oracle_bitwise():
+    import torch
+    from transformer_lm_step_amd import binding as Bnd
+    from transformer_lm_step_amd.model import GPT2
+
+    cfg, B, T = S.TINY, 4, 64
+    params = {k: S.round_to_bf16(v) for k, v in S.init_params(cfg, seed=5, perturb=True).items()}
+    stream = S.token_stream(3 * B * T + 1, cfg.vocab_size, seed=6)
+    model = GPT2(cfg, Bnd.GPT2_BF16_SR, B, T)
+    model.init(model.pack(params))
+    assert model.sizes["master"] == 0
+    p = _bits(model.params())
+    m = np.zeros(model.num_params, np.float32)
+    v = np.zeros(model.num_params, np.float32)
+    state = 13371337
+    lr, b1, b2, eps, wd = 6e-4, 0.9, 0.95, 1e-8, 0.1
+    for t in (1, 2, 3):
+        if t == 3:
+            state = 0xDEADBEEF
+            assert Bnd.gpt2_set_rng_state(model.ctx, state) != 0
+        x, y = S.batch(stream, t - 1, B, T)
+        model.zero_grad()
+        _micro(model, x, y)
+        torch.cuda.synchronize()
+        g = model.grads().cpu().numpy().copy()
+        model.update(lr, b1, b2, eps, wd, t)
+        torch.cuda.synchronize()
+        seed, state = oracle.xorshift_u32(state)
+        p, m, v = oracle.adamw_sr(p, g, m, v, lr, b1, b2, eps, wd, t, seed)
+        got = _bits(model.params())
+        say("step", t, "seed", seed, "elements", got.size)
+        assert np.array_equal(got, p), (t, int((got != p).sum()))
+        assert np.array_equal(model.adam_m().cpu().numpy().view(np.uint32), m.view(np.uint32)), t
+        assert np.array_equal(model.adam_v().cpu().numpy().view(np.uint32), v.view(np.uint32)), t
+        assert Bnd.gpt2_set_rng_state(model.ctx) == state
+    model.close()
+
+
+def test_sr_mode_gradients_equal_bf16_mode():
+    import torch
+    from transformer_lm_step_amd import binding as Bnd
+    from transformer_lm_step_amd.model import GPT2
+
+    cfg, B, T = S.TINY, 2, 64
+    params = {k: S.round_to_bf16(v) for k, v in S.init_params(cfg, seed=9).items()}
+    x, y = S.batch(S.token_stream(B * T + 1, cfg.vocab_size, seed=4), 0, B, T)
+    grads = []
+    for prec in (Bnd.GPT2_BF16, Bnd.GPT2_BF16_SR):
+        model = GPT2(cfg, prec, B, T)
+        model.init(model.pack(params))
+        model.zero_grad()
+        _micro(model, x, y)
+        torch.cuda.synchronize()
+        grads.append(model.grads().cpu().numpy().copy())
+        model.close()
+    assert np.array_equal(grads[0].view(np.uint32), grads[1].view(np.uint32))

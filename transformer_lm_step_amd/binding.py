@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgpt2_hip.so")
 
 GPT2_FP32 = 0
 GPT2_BF16 = 1
+GPT2_BF16_SR = 2
 GPT2_OK, GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_STATE, GPT2_E_TOKEN, GPT2_E_ALIGN, GPT2_E_HIP = 0, -1, -2, -3, -4, -5, -6
 GPT2_E_FILE = -7
 GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0, 1, 2, 3, 4
@@ -24,7 +25,7 @@ GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0
 EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
-    "gpt2_set_classifier_events", "gpt2_sample", "gpt2_generate", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
+    "gpt2_set_classifier_events", "gpt2_set_rng_state", "gpt2_sample", "gpt2_generate", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
     "gpt2_linear_backward_workspace", "gpt2_attention_forward", "gpt2_attention_backward",
     "fused_linear_gelu_softmax_f32", "fused_linear_gelu_softmax_f32_workspace",
 )
@@ -69,6 +70,7 @@ def _load():
         "gpt2_check_device_error": (i, [vp, vp]),
         "gpt2_act_tensor": (i, [vp, i, ctypes.POINTER(vp), ctypes.POINTER(z)]),
         "gpt2_set_classifier_events": (i, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i]),
+        "gpt2_set_rng_state": (i, [vp, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]),
         "gpt2_sample": (i, [vp, vp, vp, i, vp]),
         "gpt2_generate": (i, [vp, vp, vp, i, i, vp]),
         "gpt2_checkpoint_header": (i, [ctypes.c_char_p, cfgp, ctypes.POINTER(i)]),
@@ -185,6 +187,13 @@ def gpt2_set_classifier_events(ctx: int, starts, ends):
     b = (ctypes.c_void_p * max(n, 1))(*ends)
     _check(_lib.gpt2_set_classifier_events(ctx, a, b, n), "gpt2_set_classifier_events")
     return a, b
+
+
+def gpt2_set_rng_state(ctx: int, state: int = 0) -> int:
+    """Sets the rounding-seed state (if state != 0); returns the previous one."""
+    old = ctypes.c_uint64()
+    _check(_lib.gpt2_set_rng_state(ctx, int(state), ctypes.byref(old)), "gpt2_set_rng_state")
+    return int(old.value)
 
 
 def gpt2_sample(ctx: int, d_coins: int, d_tokens: int, t: int, stream: int):

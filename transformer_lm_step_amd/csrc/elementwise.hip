@@ -482,6 +482,78 @@ __global__ void adamw_kernel(PT* __restrict__ params, float* __restrict__ master
     }
 }
 
+// train_gpt2.cu, adamw_kernel3 without master weights: the bf16 parameter is
+// updated in fp32 and rounded back to bf16 stochastically.
+//
+// SquirrelNoise5 (Squirrel Eiserloh's published noise function, version 5):
+// position times a constant, plus the seed, then alternating xor-shifts and
+// constant additions / multiplications.
+DEV uint32_t squirrel5(uint32_t pos, uint32_t seed) {
+    uint32_t x = pos * 0xd2a80a3fu + seed;
+    x ^= x >> 9;
+    x += 0xa884f197u;
+    x ^= x >> 11;
+    x *= 0x6c736f4bu;
+    x ^= x >> 13;
+    x += 0xb79f3abbu;
+    x ^= x >> 15;
+    x *= 0x1b56c4f5u;
+    x ^= x >> 17;
+    return x;
+}
+
+// One parameter, in the page's order of fp32 operations, none contracted
+// beyond the explicit fused multiply-adds of the moment updates.
+DEV bf16_t adamw_sr_one(uint32_t i, uint16_t p16, float g, float& m, float& v, float lr, float b1, float b2,
+                        float c1, float c2, float eps, float wd, uint32_t seed) {
+#pragma clang fp contract(off)
+    m = fmaf(b1, m, fmaf(-b1, g, g));
+    const float g2 = g * g;
+    v = fmaf(b2, v, fmaf(-b2, g2, g2));
+    const float mh = m / c1, vh = v / c2;
+    const float old = bf2f(p16);
+    const float den = sqrtf(vh) + eps;
+    const float step = mh / den + wd * old;
+    const float x = old - lr * step;
+    // noise of the page's 512-thread launch position (i mod 512, i div 512)
+    const uint32_t pos = (i & 511u) + 198491317u * (i >> 9);
+    const uint32_t r = squirrel5(pos, squirrel5(pos, seed)) & 0xffffu;
+    uint32_t bits = __float_as_uint(x);
+    bits = (bits & 0xffffu) > r ? (bits | 0xffffu) : (bits & 0xffff0000u);
+    return f2bf(__uint_as_float(bits));
+}
+
+__global__ void adamw_sr_kernel(bf16_t* __restrict__ params, const float* __restrict__ grads,
+                                float* __restrict__ mom, float* __restrict__ var, size_t n, float lr, float b1,
+                                float b2, float c1, float c2, float eps, float wd, uint32_t seed) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+    for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+        if (i + 4 <= n) {
+            float g[4], m[4], v[4];
+            load4<float>(grads + i, g);
+            load4<float>(mom + i, m);
+            load4<float>(var + i, v);
+            const uint2 pv = ld8(params + i);
+            const uint16_t pin[4] = {(uint16_t)(pv.x & 0xffffu), (uint16_t)(pv.x >> 16), (uint16_t)(pv.y & 0xffffu),
+                                     (uint16_t)(pv.y >> 16)};
+            uint16_t pout[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                pout[e] = adamw_sr_one((uint32_t)(i + e), pin[e], g[e], m[e], v[e], lr, b1, b2, c1, c2, eps, wd, seed);
+            store4<float>(mom + i, m);
+            store4<float>(var + i, v);
+            st8(params + i, make_uint2(pout[0] | ((uint32_t)pout[1] << 16), pout[2] | ((uint32_t)pout[3] << 16)));
+        } else {
+            for (size_t k = i; k < n; k++) {
+                float m = mom[k], v = var[k];
+                params[k] = adamw_sr_one((uint32_t)k, params[k], grads[k], m, v, lr, b1, b2, c1, c2, eps, wd, seed);
+                mom[k] = m;
+                var[k] = v;
+            }
+        }
+    }
+}
+
 __global__ void fill_f32_kernel(float* __restrict__ p, float value, size_t n) {
     const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
     for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
@@ -582,6 +654,14 @@ int adamw_launch(PT* params, float* master, const float* grads, float* m, float*
     if (n == 0) return 0;
     hipLaunchKernelGGL(adamw_kernel<PT>, dim3(grid_for((n + 3) / 4)), dim3(256), 0, s, params, master, grads, m, v, n,
                        lr, b1, b2, c1, c2, eps, wd);
+    return (int)hipGetLastError();
+}
+
+int adamw_sr_launch(bf16_t* params, const float* grads, float* m, float* v, size_t n, float lr, float b1, float b2,
+                    float c1, float c2, float eps, float wd, uint32_t seed, hipStream_t s) {
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(adamw_sr_kernel, dim3(grid_for((n + 3) / 4)), dim3(256), 0, s, params, grads, m, v, n, lr, b1, b2,
+                       c1, c2, eps, wd, seed);
     return (int)hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ void param_layout(const gpt2_config& c, size_t off[16], size_t cnt[16], size_t* 
 
 int check_config(const gpt2_config* cfg, int precision, int B, int T) {
     if (!cfg) return GPT2_E_ARG;
-    if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_E_ARG;
+    if (precision != GPT2_FP32 && precision != GPT2_BF16 && precision != GPT2_BF16_SR) return GPT2_E_ARG;
     if (cfg->num_layers < 1 || cfg->num_heads < 1 || cfg->channels < 1 || cfg->vocab_size < 1 ||
         cfg->max_seq_len < 1 || cfg->padded_vocab_size < cfg->vocab_size)
         return GPT2_E_ARG;
@@ -91,7 +91,7 @@ size_t dx_workspace(size_t BT, size_t IC, size_t OC, int esz, int epi) {
 
 Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     Plan p;
-    p.esz = precision == GPT2_BF16 ? 2 : 4;
+    p.esz = precision == GPT2_FP32 ? 4 : 2;
     p.B = B; p.T = T; p.BT = (size_t)B * T; p.C = c.channels; p.L = c.num_layers;
     p.Vp = c.padded_vocab_size; p.NH = c.num_heads;
     const size_t e = p.esz, BT = p.BT, C = p.C, L = p.L;
@@ -123,7 +123,7 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     p.losses = take(BT * 4);
     p.tok = take(BT * 4);
     p.dres32 = take(BT * C * 4);
-    p.dres_lp = precision == GPT2_BF16 ? take(BT * C * e) : p.dres32;
+    p.dres_lp = precision != GPT2_FP32 ? take(BT * C * e) : p.dres32;
     p.dbtc = take(p.s_btc);
     p.dbt4c = take(p.s_bt4c);
     p.dqkv = take(p.s_bt3c);
@@ -155,7 +155,9 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
 
 struct gpt2_ctx {
     gpt2_config cfg;
-    int prec;
+    int prec;              // arithmetic of the kernels: GPT2_FP32 or GPT2_BF16
+    bool sr = false;       // GPT2_BF16_SR: no master weights, stochastic rounding
+    uint64_t rng = 13371337;  // xorshift64* state of the rounding seeds
     int B, T;
     size_t P;
     size_t off[16], cnt[16];
@@ -176,6 +178,17 @@ struct gpt2_ctx {
 namespace {
 
 int hip_rc(int e) { return e == 0 ? GPT2_OK : GPT2_E_HIP; }
+
+// train_gpt2.cu, random_u32: Marsaglia's xorshift on 64 bits with the
+// xorshift* output multiplier, upper 32 bits of the product
+uint32_t xorshift_u32(uint64_t* st) {
+    uint64_t x = *st;
+    x ^= x >> 12;
+    x ^= x << 25;
+    x ^= x >> 27;
+    *st = x;
+    return (uint32_t)((x * 0x2545F4914F6CDD1DULL) >> 32);
+}
 #define TRY(x) do { int _e = (x); if (_e != 0) return GPT2_E_HIP; } while (0)
 
 template <typename T>
@@ -360,7 +373,7 @@ int gpt2_query_sizes(const gpt2_config* cfg, int precision, int B, int T, gpt2_s
     param_layout(*cfg, off, cnt, &P);
     Plan p = make_plan(*cfg, precision, B, T);
     out->params = align_up(P * p.esz);
-    out->master = precision == GPT2_BF16 ? align_up(P * 4) : 0;
+    out->master = precision == GPT2_BF16 ? align_up(P * 4) : 0;  // none for GPT2_FP32, GPT2_BF16_SR
     out->grads = out->adam_m = out->adam_v = align_up(P * 4);
     out->acts = p.acts_bytes;
     out->scratch = p.scratch_bytes;
@@ -390,12 +403,13 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, int precision, int B, int 
     gpt2_ctx* c = new (std::nothrow) gpt2_ctx();
     if (!c) return GPT2_E_ARG;
     c->cfg = *cfg;
-    c->prec = precision;
+    c->prec = precision == GPT2_FP32 ? GPT2_FP32 : GPT2_BF16;
+    c->sr = precision == GPT2_BF16_SR;
     c->B = B;
     c->T = T;
     param_layout(*cfg, c->off, c->cnt, &c->P);
     c->buf = *bufs;
-    if (precision == GPT2_FP32) c->buf.master = nullptr;
+    if (precision != GPT2_BF16) c->buf.master = nullptr;
     c->plan = make_plan(*cfg, precision, B, T);
     c->last_fwd_targets = -1;
     hipStream_t s = (hipStream_t)hip_stream;
@@ -445,9 +459,16 @@ int gpt2_adamw_update(gpt2_ctx* c, float lr, float beta1, float beta2, float eps
                       void* hip_stream) {
     if (!c || t < 1) return GPT2_E_ARG;
     if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f)) return GPT2_E_ARG;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (c->sr) {
+        const uint32_t seed = xorshift_u32(&c->rng);
+        const float c1 = 1.0f - powf(beta1, (float)t), c2 = 1.0f - powf(beta2, (float)t);
+        return hip_rc(adamw_sr_launch((bf16_t*)c->buf.params, (const float*)c->buf.grads, (float*)c->buf.adam_m,
+                                      (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps, weight_decay, seed,
+                                      s));
+    }
     const float c1 = (float)(1.0 - pow((double)beta1, t));
     const float c2 = (float)(1.0 - pow((double)beta2, t));
-    hipStream_t s = (hipStream_t)hip_stream;
     int e;
     if (c->prec == GPT2_BF16)
         e = adamw_launch<bf16_t>((bf16_t*)c->buf.params, (float*)c->buf.master, (const float*)c->buf.grads,
@@ -457,6 +478,13 @@ int gpt2_adamw_update(gpt2_ctx* c, float lr, float beta1, float beta2, float eps
         e = adamw_launch<float>((float*)c->buf.params, nullptr, (const float*)c->buf.grads, (float*)c->buf.adam_m,
                                 (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps, weight_decay, s);
     return hip_rc(e);
+}
+
+int gpt2_set_rng_state(gpt2_ctx* c, uint64_t state, uint64_t* old) {
+    if (!c) return GPT2_E_ARG;
+    if (old) *old = c->rng;
+    if (state) c->rng = state;
+    return GPT2_OK;
 }
 
 int gpt2_check_device_error(gpt2_ctx* c, void* hip_stream) {

@@ -90,6 +90,9 @@ template <typename PT>
 int adamw_launch(PT* params, float* master, const float* grads, float* m, float* v, size_t n,
                  float lr, float beta1, float beta2, float c1, float c2, float eps, float wd,
                  hipStream_t s);
+// bf16 parameters without master weights, stochastic rounding seeded by seed
+int adamw_sr_launch(bf16_t* params, const float* grads, float* m, float* v, size_t n, float lr, float b1, float b2,
+                    float c1, float c2, float eps, float wd, uint32_t seed, hipStream_t s);
 int fill_f32_launch(float* p, float value, size_t n, hipStream_t s);
 int fill_i32_launch(int* p, int value, size_t n, hipStream_t s);
 int cast_f32_to_bf16_launch(bf16_t* dst, const float* src, size_t n, hipStream_t s);

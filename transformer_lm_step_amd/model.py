@@ -60,7 +60,7 @@ class GPT2:
         return self.bufs[name][: n * torch.tensor([], dtype=dtype).element_size()].view(dtype)
 
     def params(self):
-        dt = torch.bfloat16 if self.precision == B.GPT2_BF16 else torch.float32
+        dt = torch.float32 if self.precision == B.GPT2_FP32 else torch.bfloat16
         return self._flat("params", dt, self.num_params)
 
     def master(self):
@@ -92,10 +92,14 @@ class GPT2:
 
     def init(self, flat_params_f32: np.ndarray):
         """Writes the initial fp32 parameters and creates the context (which
-        zeroes the AdamW state and, in bf16 mode, casts master -> params)."""
+        zeroes the AdamW state and, in bf16 mode, casts master -> params).
+        Without master weights (GPT2_BF16_SR) the values are written to params
+        as bf16 (exact for bf16-exact values)."""
         src = torch.from_numpy(np.ascontiguousarray(flat_params_f32, dtype=np.float32)).to(self.device)
         if self.precision == B.GPT2_BF16:
             self.master().copy_(src)
+        elif self.precision == B.GPT2_BF16_SR:
+            self.params().copy_(src.to(torch.bfloat16))
         else:
             self.params().copy_(src)
         self.ctx = B.gpt2_init(self.cfg, self.precision, self.B, self.T, self._ptrs(), self.stream)
