@@ -681,6 +681,8 @@ struct DtlCfg {
     static constexpr int NS = (BM == 128 && BN == 128) ? GEMM_DTL_NS128
                               : (BM == 256 && BN == 256) ? GEMM_DTL_NS256
                               : (BM != BN ? GEMM_DTL_NS_RECT : 2);
+    static_assert(NS >= 2 && NS <= 4, "the stage loop unrolls 2 to 4 stage buffers");
+    static_assert(BK == 32 || BK == 64, "stages are one or two 32-deep MFMA steps");
 };
 
 // chunk swizzle of a k-contiguous slab row (16-byte chunks; 8 per 64-deep
