@@ -958,13 +958,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dtl_kernel(bf16_t* __res
     }
 }
 
-// dQ for one 64-query block over the key blocks at or before it.
+// dQ for one 64-query block over the key blocks at or before it.  It also
+// computes the block's delta = rowsum(dO * O) itself (each query row belongs
+// to exactly one workgroup here) and stores it for the dK/dV kernel, which
+// runs after it: no separate delta pass.
 template <int NS>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dtl_kernel(bf16_t* __restrict__ dqkv,
                                                               const bf16_t* __restrict__ dout,
+                                                              const bf16_t* __restrict__ out,
                                                               const bf16_t* __restrict__ qkv,
                                                               const float* __restrict__ lse,
-                                                              const float* __restrict__ delta, int T_, int C,
+                                                              float* __restrict__ delta, int T_, int C,
                                                               int NH, float sl2, float scale) {
     constexpr int HS = 64, BLK = 64 * HS;
     __shared__ __attribute__((aligned(1024))) bf16_t sKV[NS][2][BLK];
@@ -982,11 +986,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dtl_kernel(bf16_t* __restr
     const bf16_t* dOh = dout + (long)b * T_ * C + h * HS;
     const int q = qb * 64 + wave * 16 + l16;
     const float Lq = q < T_ ? lse[((long)b * NH + h) * T_ + q] : INFINITY;
-    const float Dq = q < T_ ? delta[((long)b * NH + h) * T_ + q] : 0.f;
 
-    Frag<bf16_t> fq[2], fo[2];
+    Frag<bf16_t> fq[2], fo[2], fy[2];
     row_frags<bf16_t, HS>(fq, Qh, rs, q, T_, g4);
     row_frags<bf16_t, HS>(fo, dOh, C, q, T_, g4);
+    row_frags<bf16_t, HS>(fy, out + (long)b * T_ * C + h * HS, C, q, T_, g4);
+    // delta of this lane's query: its 16 of the 64 d values (d = 32 ks + 8 g4
+    // + j), then the four lane groups holding the query added in a fixed order
+    float Dq = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) Dq += (float)fo[ks].v[j] * (float)fy[ks].v[j];
+    Dq += __shfl_xor(Dq, 16, 64);
+    Dq += __shfl_xor(Dq, 32, 64);
+    if (q < T_ && g4 == 0) delta[((long)b * NH + h) * T_ + q] = Dq;
     f32x4_t dq[4];
 #pragma unroll
     for (int dt = 0; dt < 4; dt++) dq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1083,17 +1097,18 @@ int bwd_hs(T* dqkv, float* delta, const T* dout, const T* out, const T* qkv, con
     const float scale = 1.0f / sqrtf((float)HS);
     const float sl2 = LOG2E * scale;
     const long rows = (long)B * T_ * NH;
-    hipLaunchKernelGGL((attn_delta_kernel<T, HS>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
-                       delta, dout, out, B, T_, C, NH);
     if constexpr (std::is_same_v<T, bf16_t> && HS == 64) {
         if ((long)T_ * 3 * C * 2 < (1L << 31)) {
+            // dQ first: it writes delta, which dK/dV reads
+            hipLaunchKernelGGL((attn_bwd_dq_dtl_kernel<ATTN_BWD_NS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout,
+                               out, qkv, lse, delta, T_, C, NH, sl2, scale);
             hipLaunchKernelGGL((attn_bwd_dkdv_dtl_kernel<ATTN_BWD_NS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv,
                                dout, qkv, lse, delta, T_, C, NH, sl2, scale);
-            hipLaunchKernelGGL((attn_bwd_dq_dtl_kernel<ATTN_BWD_NS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout,
-                               qkv, lse, delta, T_, C, NH, sl2, scale);
             return (int)hipGetLastError();
         }
     }
+    hipLaunchKernelGGL((attn_delta_kernel<T, HS>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                       delta, dout, out, B, T_, C, NH);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout, qkv, lse,
                        delta, T_, C, NH, sl2, scale);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HS>), dim3(nb * NH * B), dim3(256), 0, s, dqkv, dout, qkv, lse,
