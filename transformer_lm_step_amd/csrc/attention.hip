@@ -13,7 +13,8 @@
 // running maximum and sum of an online softmax (base 2: scores are scaled by
 // log2(e)/sqrt(HS)) and stores lse2 = max + log2(sum); the backward rebuilds
 // P = exp2(S * log2(e)/sqrt(HS) - lse2) tile by tile.  rowsum(P * dP) equals
-// rowsum(dO * O), computed up front (delta).  The backward runs as two kernels
+// rowsum(dO * O) (delta): computed up front by its own pass, or (bf16, head
+// size 64) by the dQ kernel, which then runs first.  The backward runs as two kernels
 // so that every output element is produced by exactly one workgroup with a
 // fixed summation order (no atomics): one per 64-key block accumulating dK and
 // dV over the query blocks at or after it, one per 64-query block accumulating
