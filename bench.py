@@ -43,22 +43,21 @@ def flops_per_token(L, C, V, T):
     return 3.0 * (24.0 * L * C * C + 2.0 * C * V + 2.0 * L * (T + 1) * C)
 
 
-def cpu_baseline(cfg, budget_s=30.0):
+def cpu_baseline(cfg, T=128, name="124M"):
     """The CPU oracle (single-threaded C, fp64) on a bounded sample of the same
-    workload: one micro-step (forward + backward) of GPT-2 124M on B=1 x T
-    tokens (T = 128: about 15 s on the host cores)."""
+    workload: one micro-step (forward + backward) of the model on B=1 x T
+    tokens (124M at T = 128: about 15 s on the host cores)."""
     import oracle
     import synthetic as S
     params = S.init_params(cfg)
     flat = oracle.pack_params(cfg, {k: S.round_to_bf16(v) for k, v in params.items()})
-    T = 128
     stream = S.token_stream(T + 1, cfg.vocab_size, dist="zipf")
     x, y = S.batch(stream, 0, 1, T)
     t0 = time.perf_counter()
     oracle.gpt2_step(cfg, flat, x, y)
     dt = time.perf_counter() - t0
     return {"value": T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"one forward+backward micro-step of GPT-2 124M, B=1 T={T} (fp64, single thread), "
+            "sample": f"one forward+backward micro-step of GPT-2 {name}, B=1 T={T} (fp64, single thread), "
                       f"{dt:.1f} s"}
 
 
@@ -314,6 +313,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the kernels the HBM-traffic counter runs read")
+    ap.add_argument("--model", choices=("124m", "1558m"), default="124m",
+                    help="GPT-2 size of the training step (124M is the headline workload)")
     ap.add_argument("--sr", action="store_true",
                     help="train without fp32 master weights (bf16 parameters, stochastic rounding in AdamW)")
     ap.add_argument("--workload", choices=("gpt2", "fused", "generate"), default="gpt2",
@@ -339,11 +340,12 @@ def main():
     from transformer_lm_step_amd import binding as Bnd
     from transformer_lm_step_amd.model import GPT2
 
-    cfg = S.GPT2_124M
+    cfg = S.GPT2_124M if args.model == "124m" else S.GPT2_1558M
+    name = "124M" if args.model == "124m" else "1558M"
     B, T, accum = args.batch, args.seq, args.accum
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"bench: GPT-2 124M bf16 B={B} T={T} accum={accum} steps={args.steps} warmup={args.warmup}"
+    log(f"bench: GPT-2 {name} bf16 B={B} T={T} accum={accum} steps={args.steps} warmup={args.warmup}"
         + (" (no master weights, stochastic rounding)" if args.sr else ""))
 
     model = GPT2(cfg, Bnd.GPT2_BF16_SR if args.sr else Bnd.GPT2_BF16, B, T)
@@ -408,20 +410,22 @@ def main():
     M, N, K = BT, cfg.padded_vocab_size, cfg.channels
     kflop = 2.0 * M * N * K
     achieved = kflop / (kms / 1e3) / 1e12
+    # the recorded counter figure is for the 124M product at B*T = 8192
+    traffic = recorded_traffic() if (M, N, K) == (8192, 50304, 768) else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
-                "kernel": "gemm_dtl_kernel (classifier forward, 8192x50304x768 bf16, in-step launches)",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": f"gemm_dtl_kernel (classifier forward, {M}x{N}x{K} bf16, in-step launches)",
                 "avg_ms": round(kms, 4), "launches": n_ev}
     log(f"bench: classifier GEMM in the step {kms:.3f} ms, {achieved:.1f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle sample ...")
-        cpu = cpu_baseline(cfg)
+        cpu = cpu_baseline(cfg, 128, name) if args.model == "124m" else cpu_baseline(cfg, 4, name)
         log(f"bench: oracle {cpu['value']:.3f} tok/s ({cpu['sample']})")
 
     out = {
-        "metric": "train tokens/sec + MFU, GPT-2 124M bf16 B=8 T=1024 on 1x MI355X"
+        "metric": f"train tokens/sec + MFU, GPT-2 {name} bf16 B=8 T=1024 on 1x MI355X"
                   + (" (bf16 parameters without master weights, stochastic rounding)" if args.sr else ""),
         "value": round(tok_s, 1),
         "unit": "tokens/s",
@@ -434,7 +438,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (Zipf(1.1) token stream, random GPT-2 init)",
-        "config": {"workload": "GPT-2 124M training step: 2 micro-steps of B=8 T=1024 + AdamW",
+        "config": {"workload": f"GPT-2 {name} training step: {accum} micro-steps of B={B} T={T} + AdamW",
                    "global_batch": accum * B, "seq_len": T, "grad_accum": accum, "parallelism": "single GPU"},
         "mfu": round(mfu, 4),
         "flops_per_token": fpt,
