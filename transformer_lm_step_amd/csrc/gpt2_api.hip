@@ -44,7 +44,7 @@ struct Plan {
     // per-layer strides (bytes)
     size_t s_btc, s_bt3c, s_bt4c, s_bt, s_lse;
     // scratch
-    size_t flag, work, work_bytes, scratch_bytes;
+    size_t flag, work, work_bytes, work2, work2_bytes, scratch_bytes;
 };
 
 void param_layout(const gpt2_config& c, size_t off[16], size_t cnt[16], size_t* total) {
@@ -144,10 +144,20 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     w = std::max(w, dx_workspace(BT, C, 3 * C, p.esz, GEMM_STORE));
     w = std::max(w, layernorm_bwd_workspace_bytes((int)BT, (int)C));
     w = std::max(w, encoder_bwd_workspace_bytes((int)BT, (int)C));
+    // second workspace: split-K partials of the weight-gradient products,
+    // which run on their own stream beside the input-gradient chain
+    size_t w2 = 0;
+    w2 = std::max(w2, dw_workspace(p.Vp, C, BT, p.esz));
+    w2 = std::max(w2, dw_workspace(3 * C, C, BT, p.esz));
+    w2 = std::max(w2, dw_workspace(C, C, BT, p.esz));
+    w2 = std::max(w2, dw_workspace(4 * C, C, BT, p.esz));
+    w2 = std::max(w2, dw_workspace(C, 4 * C, BT, p.esz));
     p.flag = 0;
     p.work = kAlign;
     p.work_bytes = align_up(w);
-    p.scratch_bytes = kAlign + p.work_bytes;
+    p.work2 = p.work + p.work_bytes;
+    p.work2_bytes = align_up(w2);
+    p.scratch_bytes = p.work2 + p.work2_bytes;
     return p;
 }
 
@@ -173,6 +183,20 @@ struct gpt2_ctx {
     template <typename X> X* act_l(size_t ofs, size_t stride, int l) const { return (X*)(acts() + ofs + stride * l); }
     int* flag() const { return (int*)((char*)buf.scratch + plan.flag); }
     float* work() const { return (float*)((char*)buf.scratch + plan.work); }
+    float* work2() const { return (float*)((char*)buf.scratch + plan.work2); }
+    // the weight-gradient products of the backward pass run on `side`, forked
+    // from and joined back into the caller's stream with events: ev_in[k]
+    // marks where product k's inputs are ready, ev_done[k] its completion
+    // (k: 0 classifier, 1 fcproj, 2 fc, 3 attproj, 4 qkv)
+    hipStream_t side = nullptr;
+    hipEvent_t ev_in[5] = {}, ev_done[5] = {};
+    ~gpt2_ctx() {
+        for (int k = 0; k < 5; k++) {
+            if (ev_in[k]) (void)hipEventDestroy(ev_in[k]);
+            if (ev_done[k]) (void)hipEventDestroy(ev_done[k]);
+        }
+        if (side) (void)hipStreamDestroy(side);
+    }
 };
 
 namespace {
@@ -232,6 +256,20 @@ GemmDesc dw_desc(int BT, int IC, int OC, const void* dY, const void* X, float* d
 int gemm(gpt2_ctx* c, const GemmDesc& d, hipStream_t s) {
     return gemm_launch(d, c->plan.esz, c->work(), c->plan.work_bytes, kPlanCUs, s);
 }
+
+// Weight-gradient product k on the side stream, after everything enqueued on
+// s so far.  (A stream wait takes the event as last recorded when the wait is
+// enqueued, so each event is re-recorded once per layer.)
+int gemm_side(gpt2_ctx* c, int k, const GemmDesc& d, hipStream_t s) {
+    TRY((int)hipEventRecord(c->ev_in[k], s));
+    TRY((int)hipStreamWaitEvent(c->side, c->ev_in[k], 0));
+    TRY(gemm_launch(d, c->plan.esz, c->work2(), c->plan.work2_bytes, kPlanCUs, c->side));
+    TRY((int)hipEventRecord(c->ev_done[k], c->side));
+    return 0;
+}
+
+// s waits until side-stream product k (and everything before it there) is done
+int wait_side(gpt2_ctx* c, int k, hipStream_t s) { return (int)hipStreamWaitEvent(s, c->ev_done[k], 0); }
 
 template <typename T>
 int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, float* d_losses, float* d_mean,
@@ -301,8 +339,12 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     T* dres_lp_out = lowp ? dres_lp : nullptr;
     float* work = c->work();
     // classifier (tied weights): dlnf = alpha * dlogits wte; dwte += alpha * dlogits^T lnf
+    // Weight gradients run on the side stream.  Their inputs stay unchanged
+    // until the waits below: dres_lp until the next LayerNorm backward, dbt4c
+    // and dqkv until the next layer's fcproj input gradient and attention
+    // backward; wte's gradient is also written by the encoder backward.
+    TRY(gemm_side(c, 0, dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr), s));
     TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s));
-    TRY(gemm(c, dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr), s));
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
     TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
                                 c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s));
@@ -316,27 +358,34 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
         const T* fch = c->act_l<T>(p.fch, p.s_bt4c, l);
         const T* fchg = c->act_l<T>(p.fchg, p.s_bt4c, l);
         // fcproj (+ GELU backward fused into its input-gradient product)
+        TRY(gemm_side(c, 1, dw_desc(BT, 4 * C, C, dres_lp, fchg, grd(c, 12, l, 4 * CC), 1.0f, grd(c, 13, l, C)), s));
+        if (l < L - 1) TRY(wait_side(c, 2, s));  // layer l + 1's fc weight gradient has read dbt4c
         TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_lp, prm<T>(c, 12, l, 4 * CC), dbt4c, GEMM_GELU_BWD, fch, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, 4 * C, C, dres_lp, fchg, grd(c, 12, l, 4 * CC), 1.0f, grd(c, 13, l, C)), s));
         // fc
+        TRY(gemm_side(c, 2, dw_desc(BT, C, 4 * C, dbt4c, ln2, grd(c, 10, l, 4 * CC), 1.0f, grd(c, 11, l, 4 * C)), s));
         TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c, prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, C, 4 * C, dbt4c, ln2, grd(c, 10, l, 4 * CC), 1.0f, grd(c, 11, l, 4 * C)), s));
+        TRY(wait_side(c, 1, s));  // the fcproj weight gradient has read dres_lp
         TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
                                     prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
                                     c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s));
         // attproj
+        TRY(gemm_side(c, 3, dw_desc(BT, C, C, dres_lp, atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C)), s));
         TRY(gemm(c, dx_desc(BT, C, C, dres_lp, prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, C, C, dres_lp, atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C)), s));
         // attention
+        if (l < L - 1) TRY(wait_side(c, 4, s));  // layer l + 1's qkv weight gradient has read dqkv
         TRY(attention_bwd_launch<T>(dqkv, c->act<float>(p.delta), dbtc, atty, qkv, c->act_l<float>(p.lse, p.s_lse, l),
                                     B, Tn, C, NH, s));
         // qkv
+        TRY(gemm_side(c, 4, dw_desc(BT, C, 3 * C, dqkv, ln1, grd(c, 4, l, 3 * CC), 1.0f, grd(c, 5, l, 3 * C)), s));
         TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv, prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(gemm(c, dw_desc(BT, C, 3 * C, dqkv, ln1, grd(c, 4, l, 3 * CC), 1.0f, grd(c, 5, l, 3 * C)), s));
+        TRY(wait_side(c, 3, s));  // the attproj weight gradient has read dres_lp
         TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 2, l, C), grd(c, 3, l, C), dbtc, res,
                                     prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
                                     c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, work, s));
     }
+    // join: the side stream's last product (layer 0's qkv, or the classifier
+    // if there are no layers) is done, and with it every earlier one
+    TRY(wait_side(c, L > 0 ? 4 : 0, s));
     TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, work, s));
     return GPT2_OK;
 }
@@ -414,6 +463,13 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, int precision, int B, int 
     c->last_fwd_targets = -1;
     hipStream_t s = (hipStream_t)hip_stream;
     int e = 0;
+    // default priority; non-blocking, so that it never waits on the legacy
+    // default stream implicitly (only on the events of the backward pass)
+    e |= (int)hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+    for (int k = 0; k < 5 && !e; k++) {
+        e |= (int)hipEventCreateWithFlags(&c->ev_in[k], hipEventDisableTiming);
+        e |= (int)hipEventCreateWithFlags(&c->ev_done[k], hipEventDisableTiming);
+    }
     e |= fill_f32_launch((float*)c->buf.adam_m, 0.f, c->P, s);
     e |= fill_f32_launch((float*)c->buf.adam_v, 0.f, c->P, s);
     e |= fill_i32_launch(c->flag(), 0, 64, s);
