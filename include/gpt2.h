@@ -83,7 +83,8 @@ typedef struct {
  *  grads, adam_m, adam_v : fp32, flat, same layout.
  *  acts   : forward activations and backward scratch (opaque except for the
  *           tensors gpt2_act_tensor exposes).
- *  scratch: split-K and reduction workspace (opaque). */
+ *  scratch: split-K and reduction workspaces (opaque; one for the
+ *           input-gradient chain, one for the weight-gradient stream). */
 typedef struct {
     void *params, *master, *grads, *adam_m, *adam_v, *acts, *scratch;
 } gpt2_buffers;
@@ -108,6 +109,8 @@ int gpt2_param_layout(const gpt2_config* cfg, size_t offset[16], size_t count[16
  * Shape limits: channels % num_heads == 0; head size C/NH a multiple of 16 and
  * at most 128; channels and padded_vocab_size multiples of 8;
  * 1 <= T <= max_seq_len; B >= 1; padded_vocab_size <= 53248.
+ * Also creates the context's internal stream (default priority, not blocking
+ * on the null stream) and its events, used by gpt2_backward.
  * Errors: GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_ALIGN, GPT2_E_HIP. */
 int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, int precision, int B, int T,
               const gpt2_buffers* bufs, void* hip_stream);
@@ -135,6 +138,10 @@ int gpt2_zero_grad(gpt2_ctx* ctx, void* hip_stream);
  * loss gradient: dloss <= 0 means 1/(B*T), the page's fixed choice; with
  * accumulation over n micro-steps pass 1/(n*B*T).  The residual-stream
  * gradient is kept in fp32 and re-initialised by every backward.
+ * The weight-gradient products run on a second stream that the context owns,
+ * forked from hip_stream with events and joined back into it before the
+ * call's last kernel: to the caller the whole pass is still ordered on
+ * hip_stream.
  * Errors: GPT2_E_ARG, GPT2_E_STATE (the last forward had no targets),
  * GPT2_E_HIP. */
 int gpt2_backward(gpt2_ctx* ctx, float dloss, void* hip_stream);
@@ -236,7 +243,9 @@ int gpt2_checkpoint_header(const char* path, gpt2_config* cfg, int* file_precisi
  * GPT2_E_FILE also for a file shorter than the header plus P values. */
 int gpt2_checkpoint_read(const char* path, float* h_params, size_t count);
 
-/* Frees the host-side context (no device memory is owned). */
+/* Frees the context: its host state and its internal stream and events (no
+ * device memory is owned).  Work already enqueued is not waited for: the
+ * caller synchronises hip_stream first. */
 int gpt2_free(gpt2_ctx* ctx);
 
 const char* gpt2_strerror(int code);
