@@ -32,6 +32,10 @@ constexpr int kPlanCUs = 256;  // split-K planning constant (MI355X: 256 CUs)
 // splits and workgroups leave the other half to the chain (a 124M bf16 step
 // takes 20.9 ms this way, 22.2 ms planned for 256 and 21.2 for 64, 96 or 192).
 constexpr int kSideCUs = 128;
+// ... and the input-gradient products of the backward pass as if they had
+// three quarters of it (20.6 ms against 21.0 planned for 256 CUs, 20.9 for
+// 224; 160 or 128 pick splits that make the step 1.5-2 ms slower).
+constexpr int kChainCUs = 192;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -91,7 +95,7 @@ size_t dw_workspace(size_t OC, size_t IC, size_t BT, int esz) {
 size_t dx_workspace(size_t BT, size_t IC, size_t OC, int esz, int epi) {
     GemmDesc d = {};
     d.M = (int)BT; d.N = (int)IC; d.K = (int)OC; d.ldc = (long)IC; d.epi = epi; d.split_ok = 1;
-    return gemm_workspace_bytes(d, esz, kPlanCUs);
+    return gemm_workspace_bytes(d, esz, kChainCUs);
 }
 
 Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
@@ -254,8 +258,8 @@ GemmDesc dw_desc(int BT, int IC, int OC, const void* dY, const void* X, float* d
     return d;
 }
 
-int gemm(gpt2_ctx* c, const GemmDesc& d, hipStream_t s) {
-    return gemm_launch(d, c->plan.esz, c->work(), c->plan.work_bytes, kPlanCUs, s);
+int gemm(gpt2_ctx* c, const GemmDesc& d, hipStream_t s, int cus = kPlanCUs) {
+    return gemm_launch(d, c->plan.esz, c->work(), c->plan.work_bytes, cus, s);
 }
 
 // Weight-gradient product k on the side stream, after everything enqueued on
@@ -345,7 +349,7 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     // and dqkv until the next layer's fcproj input gradient and attention
     // backward; wte's gradient is also written by the encoder backward.
     TRY(gemm_side(c, 0, dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr), s));
-    TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s));
+    TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s, kChainCUs));
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
     TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
                                 c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s));
@@ -361,24 +365,24 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
         // fcproj (+ GELU backward fused into its input-gradient product)
         TRY(gemm_side(c, 1, dw_desc(BT, 4 * C, C, dres_lp, fchg, grd(c, 12, l, 4 * CC), 1.0f, grd(c, 13, l, C)), s));
         if (l < L - 1) TRY(wait_side(c, 2, s));  // layer l + 1's fc weight gradient has read dbt4c
-        TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_lp, prm<T>(c, 12, l, 4 * CC), dbt4c, GEMM_GELU_BWD, fch, 1.0f), s));
+        TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_lp, prm<T>(c, 12, l, 4 * CC), dbt4c, GEMM_GELU_BWD, fch, 1.0f), s, kChainCUs));
         // fc
         TRY(gemm_side(c, 2, dw_desc(BT, C, 4 * C, dbt4c, ln2, grd(c, 10, l, 4 * CC), 1.0f, grd(c, 11, l, 4 * C)), s));
-        TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c, prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c, prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s, kChainCUs));
         TRY(wait_side(c, 1, s));  // the fcproj weight gradient has read dres_lp
         TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
                                     prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
                                     c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s));
         // attproj
         TRY(gemm_side(c, 3, dw_desc(BT, C, C, dres_lp, atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C)), s));
-        TRY(gemm(c, dx_desc(BT, C, C, dres_lp, prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(gemm(c, dx_desc(BT, C, C, dres_lp, prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s, kChainCUs));
         // attention
         if (l < L - 1) TRY(wait_side(c, 4, s));  // layer l + 1's qkv weight gradient has read dqkv
         TRY(attention_bwd_launch<T>(dqkv, c->act<float>(p.delta), dbtc, atty, qkv, c->act_l<float>(p.lse, p.s_lse, l),
                                     B, Tn, C, NH, s));
         // qkv
         TRY(gemm_side(c, 4, dw_desc(BT, C, 3 * C, dqkv, ln1, grd(c, 4, l, 3 * CC), 1.0f, grd(c, 5, l, 3 * C)), s));
-        TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv, prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv, prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s, kChainCUs));
         TRY(wait_side(c, 3, s));  // the attproj weight gradient has read dres_lp
         TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 2, l, C), grd(c, 3, l, C), dbtc, res,
                                     prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
