@@ -318,6 +318,18 @@ __global__ void encoder_bwd_wpe_kernel(float* __restrict__ dwpe, const float* __
     store4<float>(dwpe + t * C + c, o);
 }
 
+// The logits row is read once and its gradient written once: non-temporal
+// accesses (400 -> 363 us per 8192 x 50304 bf16 launch inside the step).
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+DEV uint4 ld16_stream(const void* p) {
+    const u32x4_nt t = __builtin_nontemporal_load((const u32x4_nt*)p);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+DEV void st16_stream(void* p, const uint4& v) {
+    const u32x4_nt t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, (u32x4_nt*)p);
+}
+
 // ---------------------------------------------------- softmax + cross-ent. --
 // train_gpt2.cu, fused_classifier_kernel3 and prepare_softmax_blockwide:
 // one workgroup per row.  The row (Vp logits) is read once into registers;
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T*
     for (int k = 0; k < NV; k++) {
         const int v = tid + NT * k;
         if (v < nvec) {
-            reg[k] = ld16(z + (long)v * VEC);
+            reg[k] = ld16_stream(z + (long)v * VEC);
             float f[VEC];
             unpack16<T>(reg[k], f);
             if ((v + 1) * VEC > V) {
@@ -409,7 +421,7 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T*
                 for (int e = 0; e < VEC; e++)
                     if (v * VEC + e == tgt) f[e] -= 1.0f;
             }
-            st16(z + (long)v * VEC, pack16<T>(f));
+            st16_stream(z + (long)v * VEC, pack16<T>(f));
         }
     }
 }
