@@ -183,3 +183,40 @@ def test_fp32_token_embedding_gradient_runs(pattern):
         e = rel_l2(g["grads"][p], o["grads"][p])
         say(pattern, p, "gradient rel-L2", e)
         assert e < 1e-4, (pattern, p, e)
+
+
+def test_caller_stream_without_host_syncs_matches_bitwise():
+    """Two accumulated micro-steps and the update enqueued back to back on a
+    non-default caller stream (the backward forks its weight-gradient products
+    onto the context's own stream and joins them back), with no host
+    synchronisation until the end: bit-identical to the synchronised run."""
+    import torch
+    from transformer_lm_step_amd.model import GPT2
+    cfg, B, T = RAGGED64, 2, 150
+    say("case caller stream bf16")
+    params, batches = make_inputs(cfg, B, T, n_micro=2, perturb=True, bf16=True)
+    ref = gpu_step(cfg, 1, params, batches, dloss=1.0 / (2 * B * T), wd=0.1, t=1)
+    model = GPT2(cfg, 1, B, T)
+    model.init(model.pack(params))
+    torch.cuda.synchronize()
+    dev = model.device
+    xs = [torch.from_numpy(x.reshape(-1)).to(dev) for x, _ in batches]
+    ys = [torch.from_numpy(y.reshape(-1)).to(dev) for _, y in batches]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        model.zero_grad()
+        for xi, yi in zip(xs, ys):
+            model.forward(xi, yi, None, None)
+            model.backward(1.0 / (2 * B * T))
+        grads = model.grads().clone()
+        model.update(1e-4, 0.9, 0.999, 1e-8, 0.1, 1)
+        newp = model.master().clone()
+    s.synchronize()
+    assert model.check() == 0
+    g = model.unpack(grads.cpu().numpy().astype(np.float64))
+    p_ = model.unpack(newp.cpu().numpy().astype(np.float64))
+    model.close()
+    for p in PARAM_NAMES:
+        assert np.array_equal(g[p], ref["grads"][p]), p
+        assert np.array_equal(p_[p], ref["params"][p]), p
