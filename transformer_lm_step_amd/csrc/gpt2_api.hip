@@ -388,10 +388,13 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
                                     prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
                                     c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, work, s));
     }
-    // join: the side stream's last product (layer 0's qkv, or the classifier
-    // if there are no layers) is done, and with it every earlier one
-    TRY(wait_side(c, L > 0 ? 4 : 0, s));
+    // the encoder backward adds into wte's gradient after the classifier's
+    // weight gradient (the side stream's first product) and overlaps the
+    // side stream's last ones; then join: the side stream's last product
+    // (layer 0's qkv) is done, and with it every earlier one
+    TRY(wait_side(c, 0, s));
     TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, work, s));
+    TRY(wait_side(c, 4, s));
     return GPT2_OK;
 }
 
