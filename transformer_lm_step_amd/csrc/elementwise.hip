@@ -559,9 +559,9 @@ __global__ void adamw_sr_kernel(bf16_t* __restrict__ params, const float* __rest
     for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
         if (i + 4 <= n) {
             float g[4], m[4], v[4];
-            load4<float>(grads + i, g);
-            load4<float>(mom + i, m);
-            load4<float>(var + i, v);
+            load4_stream(grads + i, g);
+            load4_stream(mom + i, m);
+            load4_stream(var + i, v);
             const uint2 pv = ld8(params + i);
             const uint16_t pin[4] = {(uint16_t)(pv.x & 0xffffu), (uint16_t)(pv.x >> 16), (uint16_t)(pv.y & 0xffffu),
                                      (uint16_t)(pv.y >> 16)};
@@ -569,8 +569,8 @@ __global__ void adamw_sr_kernel(bf16_t* __restrict__ params, const float* __rest
 #pragma unroll
             for (int e = 0; e < 4; e++)
                 pout[e] = adamw_sr_one((uint32_t)(i + e), pin[e], g[e], m[e], v[e], lr, b1, b2, c1, c2, eps, wd, seed);
-            store4<float>(mom + i, m);
-            store4<float>(var + i, v);
+            store4_stream(mom + i, m);
+            store4_stream(var + i, v);
             st8(params + i, make_uint2(pout[0] | ((uint32_t)pout[1] << 16), pout[2] | ((uint32_t)pout[3] << 16)));
         } else {
             for (size_t k = i; k < n; k++) {
@@ -691,7 +691,9 @@ int adamw_launch(PT* params, float* master, const float* grads, float* m, float*
 int adamw_sr_launch(bf16_t* params, const float* grads, float* m, float* v, size_t n, float lr, float b1, float b2,
                     float c1, float c2, float eps, float wd, uint32_t seed, hipStream_t s) {
     if (n == 0) return 0;
-    hipLaunchKernelGGL(adamw_sr_kernel, dim3(grid_for((n + 3) / 4)), dim3(256), 0, s, params, grads, m, v, n, lr, b1, b2,
+    const size_t blocks = ((n + 3) / 4 + 255) / 256;  // one pass: 4 parameters per thread
+    if (blocks > 0x7fffffffu) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(adamw_sr_kernel, dim3((unsigned)blocks), dim3(256), 0, s, params, grads, m, v, n, lr, b1, b2,
                        c1, c2, eps, wd, seed);
     return (int)hipGetLastError();
 }
