@@ -139,9 +139,9 @@ int gpt2_zero_grad(gpt2_ctx* ctx, void* hip_stream);
  * accumulation over n micro-steps pass 1/(n*B*T).  The residual-stream
  * gradient is kept in fp32 and re-initialised by every backward.
  * The weight-gradient products run on a second stream that the context owns,
- * forked from hip_stream with events and joined back into it before the
- * call's last kernel: to the caller the whole pass is still ordered on
- * hip_stream.
+ * forked from hip_stream with events and joined back into it (a wait on
+ * hip_stream for that stream's last event) as the call's last enqueued
+ * operation: to the caller the whole pass is still ordered on hip_stream.
  * Errors: GPT2_E_ARG, GPT2_E_STATE (the last forward had no targets),
  * GPT2_E_HIP. */
 int gpt2_backward(gpt2_ctx* ctx, float dloss, void* hip_stream);
