@@ -87,6 +87,13 @@ DEV uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 constexpr uint32_t kBufOOB = 0x80000000u;  // an offset past any range used here
+// Byte range of a buffer resource from the valid bytes past its base: clamped
+// to [0, 2^31 - 1], so that it fits the 32-bit field and kBufOOB stays past
+// it.  Operands larger than 2 GiB keep their full extent reachable, since
+// every per-lane offset inside one staged slab is far below 2 GiB.
+DEV uint32_t rsrc_range(long bytes) {
+    return (uint32_t)(bytes < 0 ? 0L : bytes > 0x7fffffffL ? 0x7fffffffL : bytes);
+}
 
 // s_waitcnt immediate that waits until at most n vector memory operations of
 // this wave are outstanding (LDS and export counters left at their maxima)

@@ -86,6 +86,7 @@ template <int R, int NT> struct StageRegs {
 };
 
 enum { EPI_SPLIT = 100 };
+constexpr int kMaxGroup = 8;  // problem classes of one grouped launch
 
 struct Args {
     const void* A; long lda;
@@ -142,7 +143,7 @@ DEV void slab_load(uint4* r, const SlabAddr<T, R, KMAJ, NT>& ad, const T* __rest
     if constexpr (KMAJ) {
         const T* base = p + (long)r0 * ld + k0;
         const long end = (long)Rmax * ld;  // elements
-        const uint32_t bytes = (uint32_t)max(0L, (end - ((long)r0 * ld + k0)) * (long)sizeof(T));
+        const uint32_t bytes = rsrc_range((end - ((long)r0 * ld + k0)) * (long)sizeof(T));
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
         const int klim = K - k0;
 #pragma unroll
@@ -150,7 +151,7 @@ DEV void slab_load(uint4* r, const SlabAddr<T, R, KMAJ, NT>& ad, const T* __rest
     } else {
         const T* base = p + (long)k0 * ld + r0;
         const long end = (long)K * ld;
-        const uint32_t bytes = (uint32_t)max(0L, (end - ((long)k0 * ld + r0)) * (long)sizeof(T));
+        const uint32_t bytes = rsrc_range((end - ((long)k0 * ld + r0)) * (long)sizeof(T));
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
 #pragma unroll
         for (int i = 0; i < 4 * StageRegs<R, NT>::KS_BLOCKS; i++) r[i] = buf_ld16(rs, ad.off[i]);
@@ -736,7 +737,7 @@ DEV void dtl_issue(const uint32_t* off, const int* kc, bf16_t* dst, const bf16_t
     constexpr int NQ = R * BK / 512 / NW;
     if constexpr (KMAJ) {
         const long org = (long)r0 * ld + k0;
-        const uint32_t bytes = (uint32_t)max(0L, ((long)Rmax * ld - org) * 2);
+        const uint32_t bytes = rsrc_range(((long)Rmax * ld - org) * 2);
         const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(p + org, bytes);
         const int klim = K - k0;
         // every load of the wave starts at the same chunk of its row (the chunk
@@ -748,7 +749,7 @@ DEV void dtl_issue(const uint32_t* off, const int* kc, bf16_t* dst, const bf16_t
         for (int q = 0; q < NQ; q++) lds_dma16(rs, kin ? off[0] + q * qstride : kBufOOB, dst + (wave + NW * q) * 512);
     } else {
         const long org = (long)k0 * ld + r0;
-        const uint32_t bytes = (uint32_t)max(0L, ((long)K * ld - org) * 2);
+        const uint32_t bytes = rsrc_range(((long)K * ld - org) * 2);
         const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(p + org, bytes);
 #pragma unroll
         for (int q = 0; q < NQ; q++) lds_dma16(rs, off[q], dst + (wave + NW * q) * 512);
@@ -807,10 +808,41 @@ constexpr bool dtl_persistent() {
     return EPI == GEMM_STORE || EPI == GEMM_BIAS || (EPI == GEMM_BIAS_GELU && NT <= 512);
 }
 
-template <int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS>
+// One launch for a list of weight-gradient products: problem class c holds
+// count[c] products of one shape at fixed strides (the layers of the model),
+// and global tile u belongs to class c when begin[c] <= u < begin[c + 1].
+// Every product accumulates into its own fp32 gradient, so one tile per
+// workgroup and no K split: the whole contraction (B*T) runs in one tile.
+struct GroupArgs {
+    const void* A[kMaxGroup];
+    const void* B[kMaxGroup];
+    float* C[kMaxGroup];
+    float* dbias[kMaxGroup];
+    long lda[kMaxGroup], ldb[kMaxGroup], ldc[kMaxGroup];
+    long sA[kMaxGroup], sB[kMaxGroup], sC[kMaxGroup], sBias[kMaxGroup];  // per-product strides (elements)
+    int M[kMaxGroup], N[kMaxGroup], K[kMaxGroup], tiles_m[kMaxGroup], tiles_n[kMaxGroup];
+    float alpha[kMaxGroup];
+    int begin[kMaxGroup + 1];
+    int np, total;
+};
+
+// a[c] for a wave-uniform c (a chain of scalar selects, no indexed load)
+template <typename X, int N>
+DEV X pick(const X (&a)[N], int c) {
+    X r = a[0];
+#pragma unroll
+    for (int i = 1; i < N; i++) r = c == i ? a[i] : r;
+    return r;
+}
+
+template <bool GRP>
+using KernArgs = std::conditional_t<GRP, GroupArgs, Args>;
+
+template <int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS, bool GRP = false>
 __global__ __launch_bounds__((TileOf<bf16_t, BM, BN, WT>::NT), (TileOf<bf16_t, BM, BN, WT>::OCC)) void
-gemm_dtl_kernel(const Args g) {
+gemm_dtl_kernel(const KernArgs<GRP> ka) {
     using T = bf16_t;
+    static_assert(!GRP || (EPI == GEMM_ACCUM && !AK && !BKM), "grouped launches are weight-gradient products");
     using TL = TileOf<T, BM, BN, WT>;
     constexpr int TM = TL::TM, TN = TL::TN, NT = TL::NT, NW = NT / 64;
     constexpr int BK = DtlCfg<BM, BN>::BK, NS = DtlCfg<BM, BN>::NS, KS = BK / 32;
@@ -841,7 +873,36 @@ gemm_dtl_kernel(const Args g) {
     // w + 2G, ... (G = gridDim.x, a multiple of 8, so every tile stays on the
     // XCD the numbering intends), and the first stages of its next tile are
     // requested before the epilogue of the current one.
-    constexpr bool PERSIST = dtl_persistent<BM, BN, WT, EPI, BIAS>();
+    constexpr bool PERSIST = !GRP && dtl_persistent<BM, BN, WT, EPI, BIAS>();
+    Args g;
+    int u = blockIdx.x;
+    int tm, tn;
+    if constexpr (GRP) {
+        // global tile u (XCD-contiguous runs as below) -> class c, product l,
+        // tile (tm, tn) of that product, row tiles fastest (neighbouring
+        // workgroups share the B panel)
+        const int nt = ka.total, full = (nt / 8) * 8;
+        if (u < full) u = (u % 8) * (nt / 8) + (u / 8);
+        int c = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxGroup; i++) c = (i < ka.np && u >= ka.begin[i]) ? i : c;
+        const int tmc = pick(ka.tiles_m, c), per = tmc * pick(ka.tiles_n, c);
+        const int v = u - pick(ka.begin, c), l = v / per, w = v % per;
+        tm = w % tmc;
+        tn = w / tmc;
+        g.A = (const T*)pick(ka.A, c) + l * pick(ka.sA, c);
+        g.B = (const T*)pick(ka.B, c) + l * pick(ka.sB, c);
+        g.C = pick(ka.C, c) + l * pick(ka.sC, c);
+        float* const db = pick(ka.dbias, c);
+        g.dbias = db ? db + l * pick(ka.sBias, c) : nullptr;
+        g.lda = pick(ka.lda, c); g.ldb = pick(ka.ldb, c); g.ldc = pick(ka.ldc, c);
+        g.M = pick(ka.M, c); g.N = pick(ka.N, c); g.K = pick(ka.K, c);
+        g.alpha = pick(ka.alpha, c);
+        g.kps = (g.K + 63) / 64;
+        g.bias = nullptr; g.aux_in = nullptr; g.aux_out = nullptr; g.ldaux = 0; g.ws = nullptr; g.wsb = nullptr;
+    } else {
+        g = ka;
+    }
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
     auto tile_of = [&](int u, int& tm_, int& tn_) {
@@ -854,9 +915,7 @@ gemm_dtl_kernel(const Args g) {
         tm_ = first_m + ((u % in_group) % gsz);
         tn_ = (u % in_group) / gsz;
     };
-    int u = blockIdx.x;
-    int tm, tn;
-    tile_of(u, tm, tn);
+    if constexpr (!GRP) tile_of(u, tm, tn);
     int m0 = tm * BM, n0 = tn * BN;
 
     // g.kps counts 64-deep k-tiles (the unit of the K split); stages are BK deep
@@ -894,7 +953,7 @@ gemm_dtl_kernel(const Args g) {
     static_assert(!BIAS || KPG >= 1, "bias partial layout");
     const int bq = tid % MQ, bkg = tid / MQ;
     float bs[4] = {0.f, 0.f, 0.f, 0.f};
-    const bool do_bias = BIAS && tn == 0;
+    const bool do_bias = BIAS && tn == 0 && g.dbias != nullptr;
 
     auto issue_at = [&](int kt, T* a_dst, T* b_dst, int mm0, int nn0) {
         if (loads) {
@@ -1284,6 +1343,35 @@ int gemm_launch_t(const GemmDesc& d, float* ws, size_t ws_bytes, int num_cus, hi
 }
 
 }  // namespace
+
+int gemm_dw_group_launch(const GemmGroupItem* items, int n, hipStream_t s) {
+    constexpr int BM = 256, BN = 256, WT = 128;
+    if (n < 1 || n > kMaxGroup || !items) return (int)hipErrorInvalidValue;
+    GroupArgs ga = {};
+    long total = 0;
+    for (int i = 0; i < n; i++) {
+        const GemmGroupItem& it = items[i];
+        if (it.M < 0 || it.N < 0 || it.K < 0 || it.count < 0) return (int)hipErrorInvalidValue;
+        ga.A[i] = it.A; ga.B[i] = it.B; ga.C[i] = it.C; ga.dbias[i] = it.dbias;
+        ga.lda[i] = it.lda; ga.ldb[i] = it.ldb; ga.ldc[i] = it.ldc;
+        ga.sA[i] = it.sA; ga.sB[i] = it.sB; ga.sC[i] = it.sC; ga.sBias[i] = it.sBias;
+        ga.M[i] = it.M; ga.N[i] = it.N; ga.K[i] = it.K; ga.alpha[i] = it.alpha;
+        ga.tiles_m[i] = (it.M + BM - 1) / BM;
+        ga.tiles_n[i] = (it.N + BN - 1) / BN;
+        ga.begin[i] = (int)total;
+        total += (long)ga.tiles_m[i] * ga.tiles_n[i] * it.count;
+        if (total > (1L << 30)) return (int)hipErrorInvalidValue;
+    }
+    for (int i = n; i <= kMaxGroup; i++) ga.begin[i] = (int)total;
+    for (int i = n; i < kMaxGroup; i++) ga.tiles_m[i] = ga.tiles_n[i] = 1;
+    ga.np = n;
+    ga.total = (int)total;
+    if (total == 0) return 0;
+    using TL = TileOf<bf16_t, BM, BN, WT>;
+    hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, WT, false, false, GEMM_ACCUM, float, true, true>), dim3((unsigned)total),
+                       dim3(TL::NT), 0, s, ga);
+    return (int)hipGetLastError();
+}
 
 size_t gemm_workspace_bytes(const GemmDesc& d, int elem_bytes, int num_cus) {
     const Choice ch = choose(d, elem_bytes, num_cus);

@@ -27,15 +27,6 @@
 namespace {
 
 constexpr int kPlanCUs = 256;  // split-K planning constant (MI355X: 256 CUs)
-// The weight-gradient products run beside the input-gradient chain and are
-// planned (tile, K split, persistent grid) as if they had half the chip: fewer
-// splits and workgroups leave the other half to the chain (a 124M bf16 step
-// takes 20.9 ms this way, 22.2 ms planned for 256 and 21.2 for 64, 96 or 192).
-constexpr int kSideCUs = 128;
-// ... and the input-gradient products of the backward pass as if they had
-// three quarters of it (20.6 ms against 21.0 planned for 256 CUs, 20.9 for
-// 224; 160 or 128 pick splits that make the step 1.5-2 ms slower).
-constexpr int kChainCUs = 192;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -53,7 +44,7 @@ struct Plan {
     // per-layer strides (bytes)
     size_t s_btc, s_bt3c, s_bt4c, s_bt, s_lse;
     // scratch
-    size_t flag, work, work_bytes, work2, work2_bytes, scratch_bytes;
+    size_t flag, work, work_bytes, scratch_bytes;
 };
 
 void param_layout(const gpt2_config& c, size_t off[16], size_t cnt[16], size_t* total) {
@@ -85,17 +76,18 @@ int check_config(const gpt2_config* cfg, int precision, int B, int T) {
     return GPT2_OK;
 }
 
-// split-K workspace of dW[OC,IC] += dY^T X (M=OC, N=IC, K=BT) and of
-// dX[BT,IC] = dY W (M=BT, N=IC, K=OC)
+// split-K workspace of dW[OC,IC] += dY^T X (M=OC, N=IC, K=BT; fp32 mode,
+// where the weight gradients are separate launches) and of dX[BT,IC] = dY W
+// (M=BT, N=IC, K=OC)
 size_t dw_workspace(size_t OC, size_t IC, size_t BT, int esz) {
     GemmDesc d = {};
     d.M = (int)OC; d.N = (int)IC; d.K = (int)BT; d.ldc = (long)IC; d.epi = GEMM_ACCUM; d.split_ok = 1;
-    return gemm_workspace_bytes(d, esz, kSideCUs);
+    return gemm_workspace_bytes(d, esz, kPlanCUs);
 }
 size_t dx_workspace(size_t BT, size_t IC, size_t OC, int esz, int epi) {
     GemmDesc d = {};
     d.M = (int)BT; d.N = (int)IC; d.K = (int)OC; d.ldc = (long)IC; d.epi = epi; d.split_ok = 1;
-    return gemm_workspace_bytes(d, esz, kChainCUs);
+    return gemm_workspace_bytes(d, esz, kPlanCUs);
 }
 
 Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
@@ -132,15 +124,21 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     p.losses = take(BT * 4);
     p.tok = take(BT * 4);
     p.dres32 = take(BT * C * 4);
-    p.dres_lp = precision != GPT2_FP32 ? take(BT * C * e) : p.dres32;
+    // In bf16 mode every layer's weight gradients run in one launch at the
+    // end of the backward pass, so the output gradients they read are kept
+    // per layer: the residual gradient's bf16 copy entering fcproj (slot 2l)
+    // and entering attproj (slot 2l + 1), fc's pre-activation gradient and
+    // the qkv gradient.  In fp32 mode one buffer of each is reused.
+    const bool keep = precision != GPT2_FP32;
+    p.dres_lp = keep ? take(2 * L * p.s_btc) : p.dres32;
     p.dbtc = take(p.s_btc);
-    p.dbt4c = take(p.s_bt4c);
-    p.dqkv = take(p.s_bt3c);
+    p.dbt4c = take((keep ? L : 1) * p.s_bt4c);
+    p.dqkv = take((keep ? L : 1) * p.s_bt3c);
     p.delta = take(p.s_lse);
     p.acts_bytes = o;
     // scratch: device flag + a workspace shared (in stream order) by the
-    // input-gradient split-K partials, LayerNorm-backward partials and the
-    // encoder-backward sort
+    // split-K partials, LayerNorm-backward partials and the encoder-backward
+    // sort
     size_t w = 0;
     w = std::max(w, dx_workspace(BT, C, p.Vp, p.esz, GEMM_STORE));
     w = std::max(w, dx_workspace(BT, 4 * C, C, p.esz, GEMM_GELU_BWD));
@@ -149,20 +147,17 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     w = std::max(w, dx_workspace(BT, C, 3 * C, p.esz, GEMM_STORE));
     w = std::max(w, layernorm_bwd_workspace_bytes((int)BT, (int)C));
     w = std::max(w, encoder_bwd_workspace_bytes((int)BT, (int)C));
-    // second workspace: split-K partials of the weight-gradient products,
-    // which run on their own stream beside the input-gradient chain
-    size_t w2 = 0;
-    w2 = std::max(w2, dw_workspace(p.Vp, C, BT, p.esz));
-    w2 = std::max(w2, dw_workspace(3 * C, C, BT, p.esz));
-    w2 = std::max(w2, dw_workspace(C, C, BT, p.esz));
-    w2 = std::max(w2, dw_workspace(4 * C, C, BT, p.esz));
-    w2 = std::max(w2, dw_workspace(C, 4 * C, BT, p.esz));
+    if (!keep) {
+        w = std::max(w, dw_workspace(p.Vp, C, BT, p.esz));
+        w = std::max(w, dw_workspace(3 * C, C, BT, p.esz));
+        w = std::max(w, dw_workspace(C, C, BT, p.esz));
+        w = std::max(w, dw_workspace(4 * C, C, BT, p.esz));
+        w = std::max(w, dw_workspace(C, 4 * C, BT, p.esz));
+    }
     p.flag = 0;
     p.work = kAlign;
     p.work_bytes = align_up(w);
-    p.work2 = p.work + p.work_bytes;
-    p.work2_bytes = align_up(w2);
-    p.scratch_bytes = p.work2 + p.work2_bytes;
+    p.scratch_bytes = p.work + p.work_bytes;
     return p;
 }
 
@@ -188,20 +183,6 @@ struct gpt2_ctx {
     template <typename X> X* act_l(size_t ofs, size_t stride, int l) const { return (X*)(acts() + ofs + stride * l); }
     int* flag() const { return (int*)((char*)buf.scratch + plan.flag); }
     float* work() const { return (float*)((char*)buf.scratch + plan.work); }
-    float* work2() const { return (float*)((char*)buf.scratch + plan.work2); }
-    // the weight-gradient products of the backward pass run on `side`, forked
-    // from and joined back into the caller's stream with events: ev_in[k]
-    // marks where product k's inputs are ready, ev_done[k] its completion
-    // (k: 0 classifier, 1 fcproj, 2 fc, 3 attproj, 4 qkv)
-    hipStream_t side = nullptr;
-    hipEvent_t ev_in[5] = {}, ev_done[5] = {};
-    ~gpt2_ctx() {
-        for (int k = 0; k < 5; k++) {
-            if (ev_in[k]) (void)hipEventDestroy(ev_in[k]);
-            if (ev_done[k]) (void)hipEventDestroy(ev_done[k]);
-        }
-        if (side) (void)hipStreamDestroy(side);
-    }
 };
 
 namespace {
@@ -262,20 +243,6 @@ int gemm(gpt2_ctx* c, const GemmDesc& d, hipStream_t s, int cus = kPlanCUs) {
     return gemm_launch(d, c->plan.esz, c->work(), c->plan.work_bytes, cus, s);
 }
 
-// Weight-gradient product k on the side stream, after everything enqueued on
-// s so far.  (A stream wait takes the event as last recorded when the wait is
-// enqueued, so each event is re-recorded once per layer.)
-int gemm_side(gpt2_ctx* c, int k, const GemmDesc& d, hipStream_t s) {
-    TRY((int)hipEventRecord(c->ev_in[k], s));
-    TRY((int)hipStreamWaitEvent(c->side, c->ev_in[k], 0));
-    TRY(gemm_launch(d, c->plan.esz, c->work2(), c->plan.work2_bytes, kSideCUs, c->side));
-    TRY((int)hipEventRecord(c->ev_done[k], c->side));
-    return 0;
-}
-
-// s waits until side-stream product k (and everything before it there) is done
-int wait_side(gpt2_ctx* c, int k, hipStream_t s) { return (int)hipStreamWaitEvent(s, c->ev_done[k], 0); }
-
 template <typename T>
 int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, float* d_losses, float* d_mean,
                  hipStream_t s) {
@@ -332,26 +299,28 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     const Plan& p = c->plan;
     const int B = c->B, Tn = c->T, BT = (int)p.BT, C = (int)p.C, L = (int)p.L, NH = (int)p.NH, Vp = (int)p.Vp;
     const size_t CC = (size_t)C * C;
-    const bool lowp = c->prec == GPT2_BF16;
+    // bf16: weight gradients of all layers in one launch at the end, from
+    // output gradients kept per layer; fp32: each right after its input
+    const bool grouped = c->prec == GPT2_BF16;
     const float alpha = dloss > 0.f ? dloss : 1.0f / (float)BT;
     T* logits = c->act<T>(p.logits);  // holds softmax - onehot
     T* lnf = c->act<T>(p.lnf);
     T* dbtc = c->act<T>(p.dbtc);
-    T* dbt4c = c->act<T>(p.dbt4c);
-    T* dqkv = c->act<T>(p.dqkv);
     float* dres = c->act<float>(p.dres32);
-    T* dres_lp = lowp ? c->act<T>(p.dres_lp) : (T*)dres;
-    T* dres_lp_out = lowp ? dres_lp : nullptr;
+    // per-layer slots (bf16) or the single buffer (fp32)
+    auto dres_in = [&](int l, int which) {  // 0: entering fcproj, 1: entering attproj
+        return grouped ? c->act<T>(p.dres_lp + (2 * (size_t)l + which) * p.s_btc) : (T*)dres;
+    };
+    auto dbt4c = [&](int l) { return c->act<T>(p.dbt4c + (grouped ? (size_t)l * p.s_bt4c : 0)); };
+    auto dqkv = [&](int l) { return c->act<T>(p.dqkv + (grouped ? (size_t)l * p.s_bt3c : 0)); };
+    auto lp_out = [&](int l, int which) { return grouped ? dres_in(l, which) : (T*)nullptr; };
     float* work = c->work();
+    auto dw_now = [&](const GemmDesc& d) { return grouped ? 0 : gemm(c, d, s); };
     // classifier (tied weights): dlnf = alpha * dlogits wte; dwte += alpha * dlogits^T lnf
-    // Weight gradients run on the side stream.  Their inputs stay unchanged
-    // until the waits below: dres_lp until the next LayerNorm backward, dbt4c
-    // and dqkv until the next layer's fcproj input gradient and attention
-    // backward; wte's gradient is also written by the encoder backward.
-    TRY(gemm_side(c, 0, dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr), s));
-    TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s, kChainCUs));
+    TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s));
+    TRY(dw_now(dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr)));
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
-    TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
+    TRY(layernorm_bwd_launch<T>(dres, lp_out(L - 1, 0), grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
                                 c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s));
     for (int l = L - 1; l >= 0; l--) {
         const T* res = l == 0 ? c->act<T>(p.enc) : c->act_l<T>(p.res3, p.s_btc, l - 1);
@@ -363,38 +332,57 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
         const T* fch = c->act_l<T>(p.fch, p.s_bt4c, l);
         const T* fchg = c->act_l<T>(p.fchg, p.s_bt4c, l);
         // fcproj (+ GELU backward fused into its input-gradient product)
-        TRY(gemm_side(c, 1, dw_desc(BT, 4 * C, C, dres_lp, fchg, grd(c, 12, l, 4 * CC), 1.0f, grd(c, 13, l, C)), s));
-        if (l < L - 1) TRY(wait_side(c, 2, s));  // layer l + 1's fc weight gradient has read dbt4c
-        TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_lp, prm<T>(c, 12, l, 4 * CC), dbt4c, GEMM_GELU_BWD, fch, 1.0f), s, kChainCUs));
+        TRY(dw_now(dw_desc(BT, 4 * C, C, dres_in(l, 0), fchg, grd(c, 12, l, 4 * CC), 1.0f, grd(c, 13, l, C))));
+        TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_in(l, 0), prm<T>(c, 12, l, 4 * CC), dbt4c(l), GEMM_GELU_BWD, fch, 1.0f),
+                 s));
         // fc
-        TRY(gemm_side(c, 2, dw_desc(BT, C, 4 * C, dbt4c, ln2, grd(c, 10, l, 4 * CC), 1.0f, grd(c, 11, l, 4 * C)), s));
-        TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c, prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s, kChainCUs));
-        TRY(wait_side(c, 1, s));  // the fcproj weight gradient has read dres_lp
-        TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
+        TRY(dw_now(dw_desc(BT, C, 4 * C, dbt4c(l), ln2, grd(c, 10, l, 4 * CC), 1.0f, grd(c, 11, l, 4 * C))));
+        TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c(l), prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(layernorm_bwd_launch<T>(dres, lp_out(l, 1), grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
                                     prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
                                     c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s));
         // attproj
-        TRY(gemm_side(c, 3, dw_desc(BT, C, C, dres_lp, atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C)), s));
-        TRY(gemm(c, dx_desc(BT, C, C, dres_lp, prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s, kChainCUs));
+        TRY(dw_now(dw_desc(BT, C, C, dres_in(l, 1), atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C))));
+        TRY(gemm(c, dx_desc(BT, C, C, dres_in(l, 1), prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
         // attention
-        if (l < L - 1) TRY(wait_side(c, 4, s));  // layer l + 1's qkv weight gradient has read dqkv
-        TRY(attention_bwd_launch<T>(dqkv, c->act<float>(p.delta), dbtc, atty, qkv, c->act_l<float>(p.lse, p.s_lse, l),
-                                    B, Tn, C, NH, s));
+        TRY(attention_bwd_launch<T>(dqkv(l), c->act<float>(p.delta), dbtc, atty, qkv,
+                                    c->act_l<float>(p.lse, p.s_lse, l), B, Tn, C, NH, s));
         // qkv
-        TRY(gemm_side(c, 4, dw_desc(BT, C, 3 * C, dqkv, ln1, grd(c, 4, l, 3 * CC), 1.0f, grd(c, 5, l, 3 * C)), s));
-        TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv, prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s, kChainCUs));
-        TRY(wait_side(c, 3, s));  // the attproj weight gradient has read dres_lp
-        TRY(layernorm_bwd_launch<T>(dres, dres_lp_out, grd(c, 2, l, C), grd(c, 3, l, C), dbtc, res,
-                                    prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
+        TRY(dw_now(dw_desc(BT, C, 3 * C, dqkv(l), ln1, grd(c, 4, l, 3 * CC), 1.0f, grd(c, 5, l, 3 * C))));
+        TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv(l), prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(layernorm_bwd_launch<T>(dres, l > 0 ? lp_out(l - 1, 0) : (T*)nullptr, grd(c, 2, l, C), grd(c, 3, l, C),
+                                    dbtc, res, prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
                                     c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, work, s));
     }
+    if (grouped) {
+        // dW += dY^T X (M = OC, N = IC, K = BT) and db += column sums of dY,
+        // every layer at once; the classifier's tied-weight gradient first in
+        // the tile order (its 197 x 3 tiles are the largest product)
+        const long sbtc = (long)(p.s_btc / sizeof(T)), sbt4c = (long)(p.s_bt4c / sizeof(T));
+        const long sbt3c = (long)(p.s_bt3c / sizeof(T));
+        GemmGroupItem it[5];
+        auto item = [&](GemmGroupItem& g, const void* A, long lda, long sA, const void* Bm, long ldb, long sB, float* Cm,
+                        long sC, float* db, long sdb, int M, int N, int cnt, float a) {
+            g.A = A; g.lda = lda; g.sA = sA; g.B = Bm; g.ldb = ldb; g.sB = sB; g.C = Cm; g.ldc = N; g.sC = sC;
+            g.dbias = db; g.sBias = sdb; g.M = M; g.N = N; g.K = BT; g.count = cnt; g.alpha = a;
+        };
+        item(it[0], logits, Vp, 0, lnf, C, 0, grd(c, 0), 0, nullptr, 0, Vp, C, 1, alpha);
+        // fcproj: dY = residual gradient entering it (slots 2l), X = fc GELU output
+        item(it[1], dres_in(0, 0), C, 2 * sbtc, c->act<T>(p.fchg), 4 * C, sbt4c, grd(c, 12), (long)(4 * CC),
+             grd(c, 13), C, C, 4 * C, L, 1.0f);
+        // fc: dY = pre-activation gradient, X = ln2
+        item(it[2], dbt4c(0), 4 * C, sbt4c, c->act<T>(p.ln2), C, sbtc, grd(c, 10), (long)(4 * CC), grd(c, 11), 4 * C,
+             4 * C, C, L, 1.0f);
+        // attproj: dY = residual gradient entering it (slots 2l + 1), X = attention output
+        item(it[3], dres_in(0, 1), C, 2 * sbtc, c->act<T>(p.atty), C, sbtc, grd(c, 6), (long)CC, grd(c, 7), C, C, C,
+             L, 1.0f);
+        // qkv: dY = qkv gradient, X = ln1
+        item(it[4], dqkv(0), 3 * C, sbt3c, c->act<T>(p.ln1), C, sbtc, grd(c, 4), (long)(3 * CC), grd(c, 5), 3 * C,
+             3 * C, C, L, 1.0f);
+        TRY(gemm_dw_group_launch(it, 5, s));
+    }
     // the encoder backward adds into wte's gradient after the classifier's
-    // weight gradient (the side stream's first product) and overlaps the
-    // side stream's last ones; then join: the side stream's last product
-    // (layer 0's qkv) is done, and with it every earlier one
-    TRY(wait_side(c, 0, s));
     TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, work, s));
-    TRY(wait_side(c, 4, s));
     return GPT2_OK;
 }
 
@@ -471,13 +459,6 @@ int gpt2_init(gpt2_ctx** out, const gpt2_config* cfg, int precision, int B, int 
     c->last_fwd_targets = -1;
     hipStream_t s = (hipStream_t)hip_stream;
     int e = 0;
-    // default priority; non-blocking, so that it never waits on the legacy
-    // default stream implicitly (only on the events of the backward pass)
-    e |= (int)hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
-    for (int k = 0; k < 5 && !e; k++) {
-        e |= (int)hipEventCreateWithFlags(&c->ev_in[k], hipEventDisableTiming);
-        e |= (int)hipEventCreateWithFlags(&c->ev_done[k], hipEventDisableTiming);
-    }
     e |= fill_f32_launch((float*)c->buf.adam_m, 0.f, c->P, s);
     e |= fill_f32_launch((float*)c->buf.adam_v, 0.f, c->P, s);
     e |= fill_i32_launch(c->flag(), 0, 64, s);

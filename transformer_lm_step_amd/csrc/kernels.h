@@ -36,11 +36,27 @@ struct GemmDesc {
     float* dbias;             // GEMM_ACCUM only (may be NULL): dbias[m] += alpha * sum_k A(m,k)
     int split_ok;             // GEMM_STORE / GEMM_ACCUM may split K (needs workspace)
 };
-// Workspace (fp32) needed by gemm_launch for split-K (0 if it will not split).
+// Weight-gradient products of several layers in one launch (bf16 operands,
+// both contraction-strided; fp32 gradients):
+//   C_l[m,n] += alpha * sum_k A_l[k*lda + m] * B_l[k*ldb + n]
+//   dbias_l[m] += alpha * sum_k A_l[k*lda + m]          (when dbias != NULL)
+// for product l = 0 .. count-1 of each item, with X_l = X + l * sX (elements).
+// Up to 8 items; no K split and no workspace (one 256x256 tile per workgroup
+// over the whole contraction).  Returns 0 or a hipError_t.
+struct GemmGroupItem {
+    const void* A; long lda; long sA;
+    const void* B; long ldb; long sB;
+    float* C; long ldc; long sC;
+    float* dbias; long sBias;
+    int M, N, K, count;
+    float alpha;
+};
+int gemm_dw_group_launch(const GemmGroupItem* items, int n, hipStream_t s);
 // Row softmax from the per-64-column partials of GEMM_BIAS_GELU_SMX:
 // Y[m, :] = exp(Y[m, :] - M_m) / S_m, in place (fp32, N % 4 == 0).
 int softmax_finish_launch(float* Y, const float2* part, int M, int N, int np, hipStream_t s);
 
+// Workspace (fp32) needed by gemm_launch for split-K (0 if it will not split).
 size_t gemm_workspace_bytes(const GemmDesc& d, int elem_bytes, int num_cus);
 // Returns 0 or a hipError_t.  ws may be NULL if gemm_workspace_bytes(d) == 0.
 int gemm_launch(const GemmDesc& d, int elem_bytes, float* ws, size_t ws_bytes, int num_cus, hipStream_t s);
