@@ -183,7 +183,11 @@ DEV void slab_store(const uint4* r, T* __restrict__ s, int tid) {
 
 // Epilogue of one workgroup tile: lane holds C[m][n .. n+3] for its
 // TM x TN 16x16 MFMA tiles.
-template <typename T, typename TL, int EPI, typename OutT, bool STG = false>
+// XS (bf16 outputs staged through LDS): the bias is already in the
+// accumulators, and every store is a buffer store whose out-of-range lanes
+// are sent past the resource range, so each wave issues exactly
+// TM * SPI (twice that with the GELU pre-activation) store instructions.
+template <typename T, typename TL, int EPI, typename OutT, bool STG = false, bool XS = false>
 DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int m0, int n0, int wm, int wn, int l16,
                        int g4, bf16_t* stage = nullptr) {
     constexpr int TM = TL::TM, TN = TL::TN;
@@ -231,7 +235,7 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
     // tell that the output aliases none of them and would otherwise order each
     // read after the previous tile's store, one memory round trip per 16x16
     // tile.
-    constexpr bool HAS_BIAS = EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU || EPI == GEMM_BIAS_RESID;
+    constexpr bool HAS_BIAS = !XS && (EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU || EPI == GEMM_BIAS_RESID);
     constexpr bool HAS_AUX = EPI == GEMM_BIAS_RESID || EPI == GEMM_GELU_BWD || EPI == GEMM_ACCUM;
     using AuxT = std::conditional_t<EPI == GEMM_ACCUM, float, T>;
     using Raw = std::conditional_t<sizeof(AuxT) == 2, uint2, float4>;
@@ -298,6 +302,22 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
         st8(stage + l16 * SRP + 16 * j + 4 * g4, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
     };
     auto flush = [&](void* dst, long ld, int mrow0, int ncol0) {  // slice rows -> memory
+        if constexpr (XS) {
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc((bf16_t*)dst + (size_t)mrow0 * ld, rsrc_range(((long)g.M - mrow0) * ld * 2));
+#pragma unroll
+            for (int k = 0; k < SPI; k++) {
+                const int slot = (l16 + 16 * g4) + 64 * k;
+                const bool in = slot < 16 * SPR;
+                const int sl = in ? slot : 0;
+                const int row = sl / SPR, col = 8 * (sl % SPR);
+                const uint4 d = ld16(stage + row * SRP + col);
+                const bool ok = in && ncol0 + col < g.N;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, d), rs,
+                                                       ok ? (int)((row * ld + ncol0 + col) * 2) : (int)kBufOOB, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < SPI; k++) {
             const int slot = (l16 + 16 * g4) + 64 * k;
@@ -801,6 +821,23 @@ DEV void dtl_frag_ld(Frag<bf16_t>& f, const bf16_t* s, int ofs) {
 // first stage waits for the stores before it, so an epilogue that reads
 // (residual, stored pre-activation, accumulator) measured slower persistent;
 // the fused bias sum and split partials stay one tile per workgroup too.
+// Whether a tile keeps two stages of fragments in registers (the stage loop
+// that reads stage kt + 1's fragments before stage kt's MFMAs): only where
+// both sets and the accumulators fit the registers each wave has at the
+// tile's occupancy (512 per SIMD lane shared by the waves on that SIMD).
+// Two waves per SIMD leave 256 registers per lane; there the epilogues of
+// the forward layouts (bias, GELU, residual reads) and the fused bias sum
+// still spill, so only the input-gradient layout's stores take it.
+template <int BM, int BN, int WT, bool AK, bool BKM, int EPI>
+constexpr bool dtl_rp() {
+    using TL = TileOf<bf16_t, BM, BN, WT>;
+    constexpr int per_simd = (TL::NT / 64) * TL::OCC / 4;
+    constexpr int regs = 512 / (per_simd < 1 ? 1 : per_simd);
+    constexpr int KS = DtlCfg<BM, BN>::BK / 32;
+    constexpr bool fits = 2 * (TL::TM + TL::TN) * KS * 4 + TL::TM * TL::TN * 4 + 48 <= regs;
+    return per_simd <= 1 ? fits : fits && AK && !BKM && (EPI == GEMM_STORE || EPI == GEMM_GELU_BWD);
+}
+
 template <int BM, int BN, int WT, int EPI, bool BIAS>
 constexpr bool dtl_persistent() {
     constexpr int NT = TileOf<bf16_t, BM, BN, WT>::NT;
@@ -874,13 +911,31 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
     // XCD the numbering intends), and the first stages of its next tile are
     // requested before the epilogue of the current one.
     constexpr bool PERSIST = !GRP && dtl_persistent<BM, BN, WT, EPI, BIAS>();
+    constexpr bool RP = dtl_rp<BM, BN, WT, AK, BKM, EPI>();
+    // bf16 outputs are staged through the LDS buffer of stage NS - 1 (the
+    // larger of its two slabs), which no load targets until the next tile's
+    // first stage
+    constexpr bool CAN_STAGE = NW * 16 * (TL::WTN + 8) <= (BM > BN ? BM : BN) * BK;
+    // Persistent bf16-output tiles (XS): the bias is the accumulators' initial
+    // value, and the epilogue's stores stay in flight while the next tile
+    // starts -- each wave issues exactly XS_STORES of them, so the waits of
+    // the next tile's first stages allow that many younger operations.
+    constexpr bool XS = PERSIST && CAN_STAGE && std::is_same<OutT, bf16_t>::value &&
+                        (EPI == GEMM_STORE || EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU);
+    constexpr int XS_SPI = (16 * (TL::WTN / 8) + 63) / 64;
+    constexpr int XS_STORES = XS ? TM * XS_SPI * (EPI == GEMM_BIAS_GELU ? 2 : 1) : 0;
+    constexpr bool ACC_BIAS = XS && (EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU);
+    static_assert(BN <= 512, "one 1 KB load holds a tile's bias columns");
+    __shared__ __attribute__((aligned(1024))) T sBiasRow[ACC_BIAS ? 512 : 8];  // the tile's bias columns
     Args g;
     int u = blockIdx.x;
     int tm, tn;
     if constexpr (GRP) {
         // global tile u (XCD-contiguous runs as below) -> class c, product l,
-        // tile (tm, tn) of that product, row tiles fastest (neighbouring
-        // workgroups share the B panel)
+        // tile (tm, tn) of that product.  Neighbouring tiles (same XCD, run
+        // at the same time) share the panel of the larger operand: column
+        // tiles fastest when A (M x K) is the larger, row tiles fastest
+        // otherwise, so that panel is fetched from HBM once per product
         const int nt = ka.total, full = (nt / 8) * 8;
         if (u < full) u = (u % 8) * (nt / 8) + (u / 8);
         int c = 0;
@@ -888,8 +943,14 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
         for (int i = 1; i < kMaxGroup; i++) c = (i < ka.np && u >= ka.begin[i]) ? i : c;
         const int tmc = pick(ka.tiles_m, c), per = tmc * pick(ka.tiles_n, c);
         const int v = u - pick(ka.begin, c), l = v / per, w = v % per;
-        tm = w % tmc;
-        tn = w / tmc;
+        if (pick(ka.M, c) >= pick(ka.N, c)) {
+            const int tnc = per / tmc;
+            tn = w % tnc;
+            tm = w / tnc;
+        } else {
+            tm = w % tmc;
+            tn = w / tmc;
+        }
         g.A = (const T*)pick(ka.A, c) + l * pick(ka.sA, c);
         g.B = (const T*)pick(ka.B, c) + l * pick(ka.sB, c);
         g.C = pick(ka.C, c) + l * pick(ka.sC, c);
@@ -962,21 +1023,11 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
         }
     };
     auto issue = [&](int kt, T* a_dst, T* b_dst) { issue_at(kt, a_dst, b_dst, m0, n0); };
-    auto compute = [&](const T* a_s, const T* b_s) {
+    // one stage's fragments of this wave (both operands, every 32-deep step)
+    struct FragSet {
         Frag<T> fa[KS][TM], fb[KS][TN];
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-#pragma unroll
-            for (int t = 0; t < TN; t++) dtl_frag_ld<BN, BKM>(fb[ks][t], b_s, fB.ofs[t][ks]);
-#pragma unroll
-            for (int t = 0; t < TM; t++) dtl_frag_ld<BM, AK>(fa[ks][t], a_s, fA.ofs[t][ks]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int j = 0; j < TN; j++) mma(acc[i][j], fb[ks][j], fa[ks][i]);
+    };
+    auto bias_sum = [&](const T* a_s) {
         if constexpr (BIAS) {
 #pragma unroll
             for (int i = 0; i < KPG; i++) {
@@ -991,6 +1042,29 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
             }
         }
     };
+    auto read_frags = [&](const T* a_s, const T* b_s, FragSet& f) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+#pragma unroll
+            for (int t = 0; t < TN; t++) dtl_frag_ld<BN, BKM>(f.fb[ks][t], b_s, fB.ofs[t][ks]);
+#pragma unroll
+            for (int t = 0; t < TM; t++) dtl_frag_ld<BM, AK>(f.fa[ks][t], a_s, fA.ofs[t][ks]);
+        }
+        bias_sum(a_s);
+    };
+    auto mfmas = [&](const FragSet& f) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) mma(acc[i][j], f.fb[ks][j], f.fa[ks][i]);
+    };
+    auto compute = [&](const T* a_s, const T* b_s) {
+        FragSet f;
+        read_frags(a_s, b_s, f);
+        mfmas(f);
+    };
     // stage kt lives in buffer kt % NS.  Opening stage kt: wait for its loads
     // (allowing the NS-2 later stages already issued to stay in flight; near
     // the end, where fewer were issued, wait for all), barrier, then issue the
@@ -1000,11 +1074,33 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
     // wait covers its own loads into stage kt, and the fragments of stage kt-1
     // (the buffer about to be refilled) are consumed by MFMAs before it; the
     // memory clobber keeps the compiler from moving LDS accesses across it.
+    // pend: the previous tile's epilogue stores (XS) were issued after the
+    // loads of this tile's first NS - 1 stages, so those stages' waits allow
+    // them to stay outstanding (vector memory operations complete in order)
+    bool pend = false;
+    // (LGK: 0xffff leaves the LDS counter alone, 0xc0ff also waits for this
+    // wave's LDS reads)
+    auto wait_stage = [&](int kt, auto lgk) {
+        constexpr int LGK = decltype(lgk)::value;
+        constexpr int base = (NS - 2) * NQS;
+        constexpr int with = base + XS_STORES > 63 ? 63 : base + XS_STORES;
+        if (kt + NS - 2 >= kt1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & LGK);
+        else if (XS_STORES > 0 && pend && kt - kt0 <= NS - 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(with) & LGK);
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(base) & LGK);
+    };
     auto open = [&](int kt) {
-        if (kt + NS - 2 < kt1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * NQS));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        wait_stage(kt, std::integral_constant<int, 0xffff>());
         asm volatile("s_barrier" ::: "memory");
     };
+    // RP: wait until stage kt has landed (the stages issued after it may stay
+    // in flight), with this wave's fragment reads of the stage before
+    // complete, then barrier
+    auto open_rp = [&](int kt) {
+        wait_stage(kt, std::integral_constant<int, 0xc0ff>());
+        asm volatile("s_barrier" ::: "memory");
+    };
+    auto bufA = [&](int b) { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
+    auto bufB = [&](int b) { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 #define GEMM_DTL_STAGE(I)                                                                          \
     {                                                                                              \
         const int kt = kb + (I);                                                                   \
@@ -1035,18 +1131,80 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
             }
         }
     };
+    // ACC_BIAS: the tile's bias columns go to LDS with the first stage's
+    // loads (one 1 KB load, ahead of them, so the wait for that stage covers
+    // it) and are added to the accumulators after the last stage, so the
+    // epilogue reads nothing from global memory
+    auto bias_issue = [&](int nn0) {
+        if constexpr (ACC_BIAS) {
+            if (wave == 0) {
+                const __amdgpu_buffer_rsrc_t rs =
+                    uniform_rsrc((const T*)g.bias + nn0, rsrc_range(((long)g.N - nn0) * 2));
+                lds_dma16(rs, (uint32_t)lane * 16, sBiasRow);
+            }
+        }
+    };
+    auto add_bias = [&]() {
+        if constexpr (ACC_BIAS) {
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const uint2 u2 = ld8(sBiasRow + wn * TL::WTN + 4 * g4 + 16 * j);
+                const f32x4_t b0 = {__uint_as_float(u2.x << 16), __uint_as_float(u2.x & 0xffff0000u),
+                                    __uint_as_float(u2.y << 16), __uint_as_float(u2.y & 0xffff0000u)};
+#pragma unroll
+                for (int i = 0; i < TM; i++) acc[i][j] += b0;
+            }
+        }
+    };
+    bias_issue(n0);
     prologue(m0, n0);
     while (true) {
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int j = 0; j < TN; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int kb = kt0; kb < kt1; kb += NS) {
-            GEMM_DTL_STAGE(0)
-            GEMM_DTL_STAGE(1)
-            if constexpr (NS > 2) GEMM_DTL_STAGE(2)
-            if constexpr (NS > 3) GEMM_DTL_STAGE(3)
+        if (ACC_BIAS && kt0 >= kt1) {  // no stage waited for the bias load (empty contraction)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            asm volatile("s_barrier" ::: "memory");
         }
+        if constexpr (RP) {
+            // Fragments one stage ahead in registers: the reads of stage kt + 1
+            // are issued before the MFMAs of stage kt, so their LDS latency is
+            // covered by that stage's matrix work.  Stage kt's buffer is free
+            // once every wave holds its fragments (lgkmcnt(0) before the
+            // barrier), so the loads of stage kt + NS go into it right away.
+            FragSet f0, f1;
+            open_rp(kt0);
+            if (kt0 + NS - 1 < kt1) issue(kt0 + NS - 1, bufA(NS - 1), bufB(NS - 1));
+            if (kt0 < kt1) read_frags(sA0, sB0, f0);
+            constexpr int U = NS == 3 ? 6 : NS;  // stages per unrolled pass (even, a multiple of NS)
+            for (int kb = kt0; kb < kt1; kb += U) {
+#pragma unroll
+                for (int i = 0; i < U; i++) {
+                    const int kt = kb + i;
+                    if (kt < kt1) {
+                        FragSet& fc = (i & 1) ? f1 : f0;
+                        FragSet& fn = (i & 1) ? f0 : f1;
+                        if (kt + 1 < kt1) {
+                            open_rp(kt + 1);
+                            if (kt + NS < kt1) issue(kt + NS, bufA(i % NS), bufB(i % NS));
+                            read_frags(bufA((i + 1) % NS), bufB((i + 1) % NS), fn);
+                        }
+                        mfmas(fc);
+                    }
+                }
+            }
+        } else {
+            for (int kb = kt0; kb < kt1; kb += NS) {
+                GEMM_DTL_STAGE(0)
+                GEMM_DTL_STAGE(1)
+                if constexpr (NS > 2) GEMM_DTL_STAGE(2)
+                if constexpr (NS > 3) GEMM_DTL_STAGE(3)
+            }
+        }
+        // the bias (its load landed before the first stage's), added after the
+        // sum as the epilogue would: the same rounding
+        add_bias();
         // next tile: once every wave is done with the stage buffers (the last
         // stages were waited for with vmcnt(0), so no load into them is in
         // flight), request its first stages, then store this one.  The next
@@ -1059,6 +1217,7 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
             tile_of(un, tm1, tn1);
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads are done
             asm volatile("s_barrier" ::: "memory");
+            bias_issue(tn1 * BN);
             prologue(tm1 * BM, tn1 * BN);
         }
         if constexpr (BIAS) {
@@ -1076,19 +1235,17 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
                 }
             }
         }
-        // bf16 outputs are staged through the LDS buffer of stage NS - 1 (the
-        // larger of its two slabs), which no load targets until the next
-        // tile's first stage; every wave must be done reading it first
+        // the staging buffer: every wave must be done reading it first
         T* const lastA = NS == 2 ? sA1 : NS == 3 ? sA2 : sA3;
         T* const lastB = NS == 2 ? sB1 : NS == 3 ? sB2 : sB3;
-        constexpr bool CAN_STAGE = NW * 16 * (TL::WTN + 8) <= (BM > BN ? BM : BN) * BK;
         T* const stage = (BN >= BM ? lastB : lastA) + wave * 16 * (TL::WTN + 8);
         if (CAN_STAGE && !more) {
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
             asm volatile("s_barrier" ::: "memory");
         }
-        gemm_epilogue<T, TL, EPI, OutT, CAN_STAGE>(g, acc, m0, n0, wm, wn, l16, g4, stage);
+        gemm_epilogue<T, TL, EPI, OutT, CAN_STAGE, XS>(g, acc, m0, n0, wm, wn, l16, g4, stage);
         if (!more) break;
+        pend = true;
         u = un;
         m0 = tm1 * BM;
         n0 = tn1 * BN;
@@ -1318,6 +1475,11 @@ int gemm_launch_t(const GemmDesc& d, float* ws, size_t ws_bytes, int num_cus, hi
     a.dbias = d.epi == GEMM_ACCUM ? d.dbias : nullptr;
     a.wsb = nullptr;
     if (tiles == 0) return 0;
+    // the bias is added to the unscaled sum (bf16 tiles start their
+    // accumulators at it), so products with a bias take alpha = 1
+    if ((d.epi == GEMM_BIAS || d.epi == GEMM_BIAS_GELU || d.epi == GEMM_BIAS_RESID || d.epi == GEMM_BIAS_GELU_SMX) &&
+        d.alpha != 1.0f)
+        return (int)hipErrorInvalidValue;
     if (ch.splits > 1) {
         const size_t MN = (size_t)d.M * d.N;
         const size_t need = (size_t)ch.splits * (MN + d.M) * sizeof(float);

@@ -174,6 +174,7 @@ struct gpt2_ctx {
     gpt2_buffers buf;
     Plan plan;
     int last_fwd_targets;  // -1: no forward yet, 0: without targets, 1: with
+    float dw_alpha = 1.0f;  // the classifier weight gradient's scale in the current backward
     // timing hook around the classifier product (caller-owned events)
     void* const* ev_start = nullptr;
     void* const* ev_end = nullptr;
@@ -294,6 +295,44 @@ int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, flo
     return GPT2_OK;
 }
 
+// dW += dY^T X (M = OC, N = IC, K = BT) and db += column sums of dY for
+// layers l0 .. l1 - 1 in one launch (and the classifier's tied-weight
+// gradient first in the tile order when cls: its 197 x 3 tiles are the
+// largest product)
+int dw_group(gpt2_ctx* c, int l0, int l1, bool cls, hipStream_t s) {
+    const Plan& p = c->plan;
+    const int BT = (int)p.BT, C = (int)p.C, Vp = (int)p.Vp;
+    const size_t CC = (size_t)C * C, e = 2;
+    const long sbtc = (long)(p.s_btc / e), sbt4c = (long)(p.s_bt4c / e), sbt3c = (long)(p.s_bt3c / e);
+    const float alpha = c->dw_alpha;
+    GemmGroupItem it[5];
+    int n = 0;
+    auto item = [&](const void* A, long lda, long sA, const void* Bm, long ldb, long sB, float* Cm, long sC, float* db,
+                    long sdb, int M, int N, int cnt, float a) {
+        GemmGroupItem& g = it[n++];
+        g.A = A; g.lda = lda; g.sA = sA; g.B = Bm; g.ldb = ldb; g.sB = sB; g.C = Cm; g.ldc = N; g.sC = sC;
+        g.dbias = db; g.sBias = sdb; g.M = M; g.N = N; g.K = BT; g.count = cnt; g.alpha = a;
+    };
+    const int cnt = l1 - l0;
+    auto act = [&](size_t ofs, size_t stride, int l) { return (const bf16_t*)(c->acts() + ofs + stride * l); };
+    if (cls) item(c->act<bf16_t>(p.logits), Vp, 0, c->act<bf16_t>(p.lnf), C, 0, grd(c, 0), 0, nullptr, 0, Vp, C, 1, alpha);
+    if (cnt > 0) {
+        // fcproj: dY = residual gradient entering it (slots 2l), X = fc GELU output
+        item(act(p.dres_lp, 2 * p.s_btc, l0), C, 2 * sbtc, act(p.fchg, p.s_bt4c, l0), 4 * C, sbt4c,
+             grd(c, 12, l0, 4 * CC), (long)(4 * CC), grd(c, 13, l0, C), C, C, 4 * C, cnt, 1.0f);
+        // fc: dY = pre-activation gradient, X = ln2
+        item(act(p.dbt4c, p.s_bt4c, l0), 4 * C, sbt4c, act(p.ln2, p.s_btc, l0), C, sbtc, grd(c, 10, l0, 4 * CC),
+             (long)(4 * CC), grd(c, 11, l0, 4 * C), 4 * C, 4 * C, C, cnt, 1.0f);
+        // attproj: dY = residual gradient entering it (slots 2l + 1), X = attention output
+        item(act(p.dres_lp + p.s_btc, 2 * p.s_btc, l0), C, 2 * sbtc, act(p.atty, p.s_btc, l0), C, sbtc,
+             grd(c, 6, l0, CC), (long)CC, grd(c, 7, l0, C), C, C, C, cnt, 1.0f);
+        // qkv: dY = qkv gradient, X = ln1
+        item(act(p.dqkv, p.s_bt3c, l0), 3 * C, sbt3c, act(p.ln1, p.s_btc, l0), C, sbtc, grd(c, 4, l0, 3 * CC),
+             (long)(3 * CC), grd(c, 5, l0, 3 * C), 3 * C, 3 * C, C, cnt, 1.0f);
+    }
+    return n ? gemm_dw_group_launch(it, n, s) : 0;
+}
+
 template <typename T>
 int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     const Plan& p = c->plan;
@@ -303,6 +342,7 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     // output gradients kept per layer; fp32: each right after its input
     const bool grouped = c->prec == GPT2_BF16;
     const float alpha = dloss > 0.f ? dloss : 1.0f / (float)BT;
+    c->dw_alpha = alpha;
     T* logits = c->act<T>(p.logits);  // holds softmax - onehot
     T* lnf = c->act<T>(p.lnf);
     T* dbtc = c->act<T>(p.dbtc);
@@ -353,34 +393,11 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
         TRY(layernorm_bwd_launch<T>(dres, l > 0 ? lp_out(l - 1, 0) : (T*)nullptr, grd(c, 2, l, C), grd(c, 3, l, C),
                                     dbtc, res, prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
                                     c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, work, s));
+
     }
-    if (grouped) {
-        // dW += dY^T X (M = OC, N = IC, K = BT) and db += column sums of dY,
-        // every layer at once; the classifier's tied-weight gradient first in
-        // the tile order (its 197 x 3 tiles are the largest product)
-        const long sbtc = (long)(p.s_btc / sizeof(T)), sbt4c = (long)(p.s_bt4c / sizeof(T));
-        const long sbt3c = (long)(p.s_bt3c / sizeof(T));
-        GemmGroupItem it[5];
-        auto item = [&](GemmGroupItem& g, const void* A, long lda, long sA, const void* Bm, long ldb, long sB, float* Cm,
-                        long sC, float* db, long sdb, int M, int N, int cnt, float a) {
-            g.A = A; g.lda = lda; g.sA = sA; g.B = Bm; g.ldb = ldb; g.sB = sB; g.C = Cm; g.ldc = N; g.sC = sC;
-            g.dbias = db; g.sBias = sdb; g.M = M; g.N = N; g.K = BT; g.count = cnt; g.alpha = a;
-        };
-        item(it[0], logits, Vp, 0, lnf, C, 0, grd(c, 0), 0, nullptr, 0, Vp, C, 1, alpha);
-        // fcproj: dY = residual gradient entering it (slots 2l), X = fc GELU output
-        item(it[1], dres_in(0, 0), C, 2 * sbtc, c->act<T>(p.fchg), 4 * C, sbt4c, grd(c, 12), (long)(4 * CC),
-             grd(c, 13), C, C, 4 * C, L, 1.0f);
-        // fc: dY = pre-activation gradient, X = ln2
-        item(it[2], dbt4c(0), 4 * C, sbt4c, c->act<T>(p.ln2), C, sbtc, grd(c, 10), (long)(4 * CC), grd(c, 11), 4 * C,
-             4 * C, C, L, 1.0f);
-        // attproj: dY = residual gradient entering it (slots 2l + 1), X = attention output
-        item(it[3], dres_in(0, 1), C, 2 * sbtc, c->act<T>(p.atty), C, sbtc, grd(c, 6), (long)CC, grd(c, 7), C, C, C,
-             L, 1.0f);
-        // qkv: dY = qkv gradient, X = ln1
-        item(it[4], dqkv(0), 3 * C, sbt3c, c->act<T>(p.ln1), C, sbtc, grd(c, 4), (long)(3 * CC), grd(c, 5), 3 * C,
-             3 * C, C, L, 1.0f);
-        TRY(gemm_dw_group_launch(it, 5, s));
-    }
+    // every weight gradient of the step in one launch (running the classifier's
+    // or half of the layers' beside the chain on a second stream was slower)
+    if (grouped) TRY(dw_group(c, 0, L, true, s));
     // the encoder backward adds into wte's gradient after the classifier's
     TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, work, s));
     return GPT2_OK;
