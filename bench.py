@@ -1,19 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the GPT-2 training step on one MI355X.
 
-Workload: GPT-2 124M (L=12, NH=12, C=768, V=50257 padded to 50304), bf16
-activations and matrix products with fp32 master weights, gradients and AdamW
-state; micro-batch B=8, T=1024; one step = 2 micro-steps (forward + backward,
-gradients accumulated with dloss = 1/(2*B*T)) + one AdamW update (lr 6e-4,
-betas 0.9/0.999, eps 1e-8, weight decay 0.1).  Random GPT-2 initialisation and
-a Zipf(1.1) token stream (seeded, synthetic), all resident in HBM before the
-timed region.
+Workload (default): GPT-2 124M (L=12, NH=12, C=768, V=50257 padded to
+50304), bf16 activations and matrix products with fp32 master weights,
+gradients and AdamW state; micro-batch B=8, T=1024; one step = 2 micro-steps
+(forward + backward, gradients accumulated with dloss = 1/(2*B*T)) + one AdamW
+update (lr 6e-4, betas 0.9/0.999, eps 1e-8, weight decay 0.1).  Random GPT-2
+initialisation and a Zipf(1.1) token stream (seeded, synthetic), all resident
+in HBM before the timed region.
 
 Prints one JSON line: train tokens/s over the timed steps, MFU against the
 2.5 PFLOP/s dense bf16 peak, the roofline position of the dominant kernel
-(the classifier product, timed with HIP events that the library records around
-its launches inside the timed steps, on the step's stream), and the CPU oracle
-timed on a bounded sample of the same workload.
+(the one launch of every weight gradient, timed with HIP events that the
+library records around it inside the timed steps, on the step's stream), the
+position of every kernel family from two further instrumented steps, and the
+CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads: --model 1558m (GPT-2 1.5B, 10 steps of B=8 T=1024, lr 3e-4,
+wd 0, no accumulation, peak HBM reported), --workload c2 (GPT-2 124M fp32,
+B=4 T=64, 10 AdamW steps on one batch, lr 1e-4), --workload fused (the
+standalone fp32 Linear+GELU+softmax op), --workload generate (the page's
+generation loop).
 """
 
 from __future__ import annotations
@@ -43,22 +50,41 @@ def flops_per_token(L, C, V, T):
     return 3.0 * (24.0 * L * C * C + 2.0 * C * V + 2.0 * L * (T + 1) * C)
 
 
-def cpu_baseline(cfg, T=128, name="124M"):
+def host_cpu():
+    """The host's CPU model and logical core count."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def cpu_baseline(cfg, T=256, name="124M", bf16_init=True):
     """The CPU oracle (single-threaded C, fp64) on a bounded sample of the same
     workload: one micro-step (forward + backward) of the model on B=1 x T
-    tokens (124M at T = 128: about 15 s on the host cores)."""
+    tokens, about 30 s on the host cores for 124M at T = 256 (T = 1024 would
+    take about 2 minutes; per-token work at T = 256 is within 8% of it, the
+    causal attention's share being the difference)."""
     import oracle
     import synthetic as S
     params = S.init_params(cfg)
-    flat = oracle.pack_params(cfg, {k: S.round_to_bf16(v) for k, v in params.items()})
+    if bf16_init:
+        params = {k: S.round_to_bf16(v) for k, v in params.items()}
+    flat = oracle.pack_params(cfg, params)
     stream = S.token_stream(T + 1, cfg.vocab_size, dist="zipf")
     x, y = S.batch(stream, 0, 1, T)
     t0 = time.perf_counter()
     oracle.gpt2_step(cfg, flat, x, y)
     dt = time.perf_counter() - t0
-    return {"value": T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    model, ncpu = host_cpu()
+    return {"value": round(T / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"one forward+backward micro-step of GPT-2 {name}, B=1 T={T} (fp64, single thread), "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s",
+            "host_cpu": model, "host_nproc": ncpu}
 
 
 PEAK_FP32_TFLOPS = 157.3
@@ -251,7 +277,6 @@ class HipEvents:
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "classifier_fwd_8192x50304x768_traffic.md")
 GEMM_SRC = os.path.join(HERE, "transformer_lm_step_amd", "csrc", "gemm.hip")
 
 
@@ -261,28 +286,11 @@ def gemm_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the classifier forward product, as measured by
-    the FETCH_SIZE / WRITE_SIZE counter runs recorded in profiles/, if they were
-    taken on the current GEMM source; else None."""
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
-    vals = dict(l.split(":", 1) for l in text.splitlines() if l.startswith(("gemm_source_sha256:", "traffic_bytes_per_launch:")))
-    if vals.get("gemm_source_sha256", "").strip() != gemm_source_hash():
-        return None
-    try:
-        return float(vals["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
 def traffic_probe():
     """Kernels for the HBM-traffic counter runs: a 1 GiB device copy (the
-    reference of known size) and the classifier forward product, 3 launches each."""
+    reference of known size), 3 launches, then two steps of the benchmark
+    workload (one warm-up, one whose dispatches the summaries read)."""
     import torch
-    from transformer_lm_step_amd import binding as Bnd
     dev = torch.device("cuda:0")
     n = 1 << 28  # 2^28 floats = 1 GiB
     a = torch.ones(n, dtype=torch.float32, device=dev)
@@ -291,21 +299,17 @@ def traffic_probe():
         b.copy_(a)
     torch.cuda.synchronize()
     del a, b
-    M, N, K = 8192, 50304, 768
-    x = torch.randn(M, K, device=dev).to(torch.bfloat16)
-    w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
-    y = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-    sh = torch.cuda.current_stream().cuda_stream
-    for _ in range(3):
-        Bnd.gpt2_linear_forward(Bnd.GPT2_BF16, x.data_ptr(), w.data_ptr(), 0, y.data_ptr(), M, N, K, sh)
-    torch.cuda.synchronize()
+    args = argparse.Namespace(model="124m", batch=8, seq=1024, accum=2, steps=1, warmup=1, sr=False,
+                              no_cpu_baseline=True)
+    bench_gpt2(args)
     print(json.dumps({"traffic_probe": "done", "gemm_source_sha256": gemm_source_hash()}), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 10 for --model 1558m and --workload c2)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--seq", type=int, default=1024)
@@ -317,10 +321,12 @@ def main():
                     help="GPT-2 size of the training step (124M is the headline workload)")
     ap.add_argument("--sr", action="store_true",
                     help="train without fp32 master weights (bf16 parameters, stochastic rounding in AdamW)")
-    ap.add_argument("--workload", choices=("gpt2", "fused", "generate"), default="gpt2",
-                    help="gpt2: the GPT-2 124M training step (default); fused: the standalone "
-                         "Linear+GELU+softmax op; generate: the page's generation loop")
+    ap.add_argument("--workload", choices=("gpt2", "c2", "fused", "generate"), default="gpt2",
+                    help="gpt2: the GPT-2 training step (default); c2: GPT-2 124M fp32 at B=4 T=64; "
+                         "fused: the standalone Linear+GELU+softmax op; generate: the page's generation loop")
     args = ap.parse_args()
+    if args.steps is None and args.workload in ("fused", "generate"):
+        args.steps = 20
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the data-parallel multi-GPU path is not implemented.", file=sys.stderr)
@@ -334,24 +340,142 @@ def main():
     if args.workload == "generate":
         bench_generate(args)
         return
+    if args.workload == "c2":
+        bench_c2(args)
+        return
 
+    bench_gpt2(args)
+
+
+# ---------------------------------------------------------------------------
+# kernel families of the step: launch points of the library's timing hooks
+# and the algorithmic work of each launch, in launch order per call
+
+FAMILIES = [  # (name, timing point, bound)
+    ("weight gradients (all layers + classifier, one launch)", "WEIGHT_GRAD", "mfma"),
+    ("classifier forward", "CLASSIFIER_FWD", "mfma"),
+    ("classifier input gradient", "CLASSIFIER_DX", "mfma"),
+    ("layer forward products", "LAYER_FWD", "mfma"),
+    ("layer input-gradient products", "LAYER_DX", "mfma"),
+    ("attention forward", "ATTN_FWD", "mfma"),
+    ("attention backward", "ATTN_BWD", "mfma"),
+    ("LayerNorm forward", "LN_FWD", "hbm"),
+    ("LayerNorm backward", "LN_BWD", "hbm"),
+    ("softmax cross-entropy", "CE", "hbm"),
+    ("token/position embedding backward", "ENCODER_BWD", "hbm"),
+    ("AdamW", "ADAMW", "hbm"),
+]
+
+
+def launch_work(cfg, B, T, esz, grouped, sr, n_unique):
+    """Per timing point: the algorithmic work (FLOP or bytes) of each launch of
+    one micro-step (forward + backward), or of one update for ADAMW."""
+    L, C, Vp, P = cfg.num_layers, cfg.channels, cfg.padded_vocab_size, None
+    BT = B * T
+    att = 2.0 * B * T * (T + 1) * C  # causal: sum_t (t + 1) keys, two products
+    w = {
+        "CLASSIFIER_FWD": [2.0 * BT * Vp * C],
+        "CLASSIFIER_DX": [2.0 * BT * Vp * C],
+        "LAYER_FWD": [f for _ in range(L) for f in (2.0 * BT * C * 3 * C, 2.0 * BT * C * C,
+                                                    2.0 * BT * C * 4 * C, 2.0 * BT * 4 * C * C)],
+        "LAYER_DX": [f for _ in range(L) for f in (2.0 * BT * C * 4 * C, 2.0 * BT * 4 * C * C,
+                                                   2.0 * BT * C * C, 2.0 * BT * 3 * C * C)],
+        "ATTN_FWD": [att] * L,
+        "ATTN_BWD": [2.0 * att] * L,  # dP, dV, dQ, dK (the recomputed scores not counted)
+        # x read and y written, statistics written
+        "LN_FWD": [2.0 * BT * C * esz + 8.0 * BT] * (2 * L + 1),
+        # dy, x read; fp32 residual gradient read (not by the first) and
+        # written; its low-precision copy written (bf16; not after layer 0)
+        "LN_BWD": ([BT * C * (2 * esz + 4 + (esz if esz == 2 else 0)) + 8.0 * BT]
+                   + [f for l in range(L - 1, -1, -1)
+                      for f in (BT * C * (2 * esz + 8 + (esz if esz == 2 else 0)) + 8.0 * BT,
+                                BT * C * (2 * esz + 8 + (esz if esz == 2 and l > 0 else 0)) + 8.0 * BT)]),
+        "CE": [2.0 * BT * Vp * esz + 8.0 * BT],
+        # residual-gradient rows read, each present token's row read and
+        # written, position rows read and written (fp32)
+        "ENCODER_BWD": [4.0 * BT * C + 8.0 * n_unique * C + 8.0 * T * C],
+    }
+    if grouped:
+        w["WEIGHT_GRAD"] = [2.0 * BT * C * (Vp + 12 * L * C)]
+    else:
+        w["WEIGHT_GRAD"] = [2.0 * BT * Vp * C] + w["LAYER_DX"]
+    return w
+
+
+def family_report(cfg, B, T, esz, grouped, sr, n_unique, P, times, n_micro, n_updates, step_ms):
+    """times[point]: durations (ms) of every bracketed launch, in order."""
+    per_call = launch_work(cfg, B, T, esz, grouped, sr, n_unique)
+    per_call["ADAMW"] = [float(P) * (24 if sr else (30 if esz == 2 else 28))]
+    out = []
+    for name, point, bound in FAMILIES:
+        t = times.get(point)
+        if not t:
+            continue
+        wl = per_call[point]
+        calls = n_updates if point == "ADAMW" else n_micro
+        work = sum(wl) * calls
+        ms = float(np.sum(t))
+        if len(t) != len(wl) * calls:
+            raise RuntimeError(f"{point}: {len(t)} bracketed launches, expected {len(wl) * calls}")
+        steps = n_updates
+        rate = work / (ms / 1e3)
+        if bound == "mfma":
+            peak = PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS
+            ach, unit = rate / 1e12, "TFLOP/s"
+        else:
+            peak = PEAK_HBM_GBS
+            ach, unit = rate / 1e9, "GB/s"
+        out.append({"family": name, "bound": bound, "launches_per_step": len(t) // steps,
+                    "ms_per_step": round(ms / steps, 4), "share": round(ms / steps / step_ms, 4),
+                    "achieved": round(ach, 1), "unit": unit, "peak": peak, "frac": round(ach / peak, 4)})
+    return out
+
+
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gpt2_124m_bf16_step_traffic.md")
+
+
+def recorded_traffic(kernel_key):
+    """HBM bytes per launch of a kernel of the step (FETCH_SIZE + WRITE_SIZE
+    counter runs recorded in profiles/), if they were taken on the current
+    GEMM source; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith(("|", " ", "#")))
+    if vals.get("gemm_source_sha256", "").strip() != gemm_source_hash():
+        return None
+    try:
+        return float(vals[f"traffic_bytes_per_launch {kernel_key}"])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_gpt2(args):
     import torch
     import synthetic as S
     from transformer_lm_step_amd import binding as Bnd
     from transformer_lm_step_amd.model import GPT2
 
-    cfg = S.GPT2_124M if args.model == "124m" else S.GPT2_1558M
-    name = "124M" if args.model == "124m" else "1558M"
-    B, T, accum = args.batch, args.seq, args.accum
+    big = args.model == "1558m"
+    cfg = S.GPT2_1558M if big else S.GPT2_124M
+    name = "1558M" if big else "124M"
+    B, T = args.batch, args.seq
+    # the 1.5B workload: 10 steps, lr 3e-4, no weight decay, no accumulation
+    accum = 1 if big else args.accum
+    lr, wd = (3e-4, 0.0) if big else (6e-4, 0.1)
+    steps = args.steps if args.steps is not None else (10 if big else 20)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"bench: GPT-2 {name} bf16 B={B} T={T} accum={accum} steps={args.steps} warmup={args.warmup}"
+    log(f"bench: GPT-2 {name} bf16 B={B} T={T} accum={accum} steps={steps} warmup={args.warmup}"
         + (" (no master weights, stochastic rounding)" if args.sr else ""))
 
     model = GPT2(cfg, Bnd.GPT2_BF16_SR if args.sr else Bnd.GPT2_BF16, B, T)
     params = {k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}  # bf16-exact start
     model.init(model.pack(params))
-    n_micro = (args.warmup + args.steps) * accum
+    del params
+    n_instr = 2  # instrumented steps after the timed ones
+    n_micro = (args.warmup + steps + n_instr) * accum
     stream = S.token_stream(n_micro * B * T + 1, cfg.vocab_size, dist="zipf")
     toks = torch.from_numpy(stream).to(dev)
     BT = B * T
@@ -366,7 +490,7 @@ def main():
             i = s * accum + a
             model.forward(xs[i], ys[i], None, mean_loss[i:i + 1])
             model.backward(dloss)
-        model.update(6e-4, 0.9, 0.999, 1e-8, 0.1, s + 1)
+        model.update(lr, 0.9, 0.999, 1e-8, wd, s + 1)
 
     for s in range(args.warmup):
         step(s)
@@ -375,26 +499,26 @@ def main():
         raise RuntimeError("device-side error during warmup")
     log("bench: warmup done")
 
-    # HIP events around the classifier product of every forward in the timed
-    # steps (recorded by the library on the step's stream)
+    # HIP events around the weight-gradient launch of every backward in the
+    # timed steps (recorded by the library on the step's stream)
     hip = HipEvents()
-    n_ev = args.steps * accum
+    n_ev = steps * accum
     starts, ends = hip.create(n_ev), hip.create(n_ev)
-    hook = Bnd.gpt2_set_classifier_events(model.ctx, starts, ends)
+    hook = Bnd.gpt2_set_timing_events(model.ctx, Bnd.GPT2_TP_WEIGHT_GRAD, starts, ends)
     cur = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(cur)
-    for s in range(args.warmup, args.warmup + args.steps):
+    for s in range(args.warmup, args.warmup + steps):
         step(s)
     e1.record(cur)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    Bnd.gpt2_set_classifier_events(model.ctx, [], [])
+    Bnd.gpt2_set_timing_events(model.ctx, Bnd.GPT2_TP_WEIGHT_GRAD, [], [])
     del hook
-    ms = e0.elapsed_time(e1) / args.steps
-    losses = mean_loss.cpu().numpy()
+    ms = e0.elapsed_time(e1) / steps
+    losses = mean_loss[:(args.warmup + steps) * accum].cpu().numpy()
     if not np.all(np.isfinite(losses)):
         raise RuntimeError("non-finite loss")
     tok_s = accum * BT / (ms / 1e3)
@@ -403,34 +527,67 @@ def main():
     log(f"bench: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, MFU {mfu:.3f}, wall {wall:.2f}s, "
         f"loss first {losses[0]:.4f} last {losses[-1]:.4f}")
 
-    # ---- dominant kernel: the classifier product logits[BT,Vp] = lnf[BT,C] wte[Vp,C]^T,
-    # its launches inside the timed steps
+    # ---- dominant kernel: the one launch of every weight gradient of a
+    # micro-step, its launches inside the timed steps
     kms = float(np.mean([hip.elapsed_ms(a, b) for a, b in zip(starts, ends)]))
     hip.destroy(starts + ends)
-    M, N, K = BT, cfg.padded_vocab_size, cfg.channels
-    kflop = 2.0 * M * N * K
+    L, C, Vp = cfg.num_layers, cfg.channels, cfg.padded_vocab_size
+    kflop = 2.0 * BT * C * (Vp + 12 * L * C)
     achieved = kflop / (kms / 1e3) / 1e12
-    # the recorded counter figure is for the 124M product at B*T = 8192
-    traffic = recorded_traffic() if (M, N, K) == (8192, 50304, 768) else None
+    traffic = recorded_traffic("weight_grad") if (not big and (B, T) == (8, 1024)) else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": f"gemm_dtl_kernel (classifier forward, {M}x{N}x{K} bf16, in-step launches)",
+                "kernel": f"gemm_dtl_kernel, grouped weight gradients (classifier {Vp}x{C} + {L} layers x "
+                          f"4 products, K = B*T = {BT}, bf16, in-step launches)",
                 "avg_ms": round(kms, 4), "launches": n_ev}
-    log(f"bench: classifier GEMM in the step {kms:.3f} ms, {achieved:.1f} TFLOP/s")
+    log(f"bench: weight-gradient launch in the step {kms:.3f} ms, {achieved:.1f} TFLOP/s")
+
+    # ---- every kernel family, from n_instr further steps with all hooks set
+    points = {p: getattr(Bnd, "GPT2_TP_" + p) for _, p, _ in FAMILIES}
+    n_unique = int(np.mean([np.unique(stream[i * BT:(i + 1) * BT]).size for i in range(n_micro)]))
+    work = launch_work(cfg, B, T, 2, True, args.sr, n_unique)
+    evs = {}
+    for _, p, _ in FAMILIES:
+        per = 1 if p == "ADAMW" else len(work[p]) * accum
+        n = per * n_instr
+        evs[p] = (hip.create(n), hip.create(n))
+    hooks = [Bnd.gpt2_set_timing_events(model.ctx, points[p], a, b) for p, (a, b) in evs.items()]
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(cur)
+    for s in range(args.warmup + steps, args.warmup + steps + n_instr):
+        step(s)
+    e3.record(cur)
+    torch.cuda.synchronize()
+    for p in points:
+        Bnd.gpt2_set_timing_events(model.ctx, points[p], [], [])
+    del hooks
+    instr_ms = e2.elapsed_time(e3) / n_instr
+    times = {p: [hip.elapsed_ms(a, b) for a, b in zip(sa, ea)] for p, (sa, ea) in evs.items()}
+    for sa, ea in evs.values():
+        hip.destroy(sa + ea)
+    families = family_report(cfg, B, T, 2, True, args.sr, n_unique, model.num_params, times,
+                             n_instr * accum, n_instr, instr_ms)
+    for f in families:
+        log(f"bench:   {f['family']:55s} {f['ms_per_step']:8.3f} ms/step  {f['achieved']:8.1f} {f['unit']:8s} "
+            f"frac {f['frac']:.3f}")
+    peak_hbm = torch.cuda.max_memory_allocated(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle sample ...")
-        cpu = cpu_baseline(cfg, 128, name) if args.model == "124m" else cpu_baseline(cfg, 4, name)
-        log(f"bench: oracle {cpu['value']:.3f} tok/s ({cpu['sample']})")
+        cpu = cpu_baseline(cfg, 256, name) if not big else cpu_baseline(cfg, 16, name)
+        log(f"bench: oracle {cpu['value']:.3f} tok/s ({cpu['sample']}; host {cpu['host_cpu']}, "
+            f"{cpu['host_nproc']} logical cores)")
 
+    workload = (f"GPT-2 {name} training step: {accum} micro-step{'s' if accum > 1 else ''} of B={B} T={T} + "
+                f"AdamW (lr {lr:g}, wd {wd:g})")
     out = {
-        "metric": f"train tokens/sec + MFU, GPT-2 {name} bf16 B=8 T=1024 on 1x MI355X"
+        "metric": f"train tokens/sec + MFU, GPT-2 {name} bf16 B={B} T={T} on 1x MI355X"
                   + (" (bf16 parameters without master weights, stochastic rounding)" if args.sr else ""),
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
@@ -438,11 +595,88 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (Zipf(1.1) token stream, random GPT-2 init)",
-        "config": {"workload": f"GPT-2 {name} training step: {accum} micro-steps of B={B} T={T} + AdamW",
-                   "global_batch": accum * B, "seq_len": T, "grad_accum": accum, "parallelism": "single GPU"},
+        "config": {"workload": workload, "global_batch": accum * B, "seq_len": T, "grad_accum": accum,
+                   "parallelism": "single GPU"},
         "mfu": round(mfu, 4),
         "flops_per_token": fpt,
         "roofline": roofline,
+        "families": families,
+        "instrumented_ms_per_step": round(instr_ms, 4),
+        "peak_hbm_gb": round(peak_hbm / 1e9, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+
+
+def bench_c2(args):
+    """GPT-2 124M in fp32 (full fp32 products), B=4 T=64, 10 AdamW steps (lr
+    1e-4, wd 0) overfitting one batch: tokens/s and the fraction of the fp32
+    peak the step's algorithmic FLOPs reach; the oracle times one of the same
+    steps on the host."""
+    import torch
+    import synthetic as S
+    from transformer_lm_step_amd import binding as Bnd
+    from transformer_lm_step_amd.model import GPT2
+
+    cfg, B, T = S.GPT2_124M, 4, 64
+    steps = args.steps if args.steps is not None else 10
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    model = GPT2(cfg, Bnd.GPT2_FP32, B, T)
+    model.init(model.pack(S.init_params(cfg)))
+    stream = S.token_stream(B * T + 1, cfg.vocab_size, dist="zipf")
+    xb, yb = S.batch(stream, 0, B, T)
+    x = torch.from_numpy(xb.reshape(-1)).to(dev)
+    y = torch.from_numpy(yb.reshape(-1)).to(dev)
+    mean = torch.zeros(args.warmup + steps, dtype=torch.float32, device=dev)
+
+    def step(s):
+        model.zero_grad()
+        model.forward(x, y, None, mean[s:s + 1])
+        model.backward(1.0 / (B * T))
+        model.update(1e-4, 0.9, 0.999, 1e-8, 0.0, s + 1)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for s in range(args.warmup, args.warmup + steps):
+        step(s)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    if model.check() != 0:
+        raise RuntimeError("device-side error")
+    ms = e0.elapsed_time(e1) / steps
+    lo = mean.cpu().numpy()
+    tok_s = B * T / (ms / 1e3)
+    fpt = flops_per_token(cfg.num_layers, cfg.channels, cfg.vocab_size, T)
+    frac = tok_s * fpt / (PEAK_FP32_TFLOPS * 1e12)
+    log(f"bench: c2 fp32 {ms:.3f} ms/step, {tok_s:,.0f} tok/s, {frac:.4f} of the fp32 peak, "
+        f"loss {lo[0]:.4f} -> {lo[-1]:.4f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        flat = oracle.pack_params(cfg, S.init_params(cfg))
+        t0 = time.perf_counter()
+        oracle.gpt2_step(cfg, flat, xb, yb, dloss=1.0 / (B * T))
+        dt = time.perf_counter() - t0
+        model_name, ncpu = host_cpu()
+        cpu = {"value": round(B * T / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"one of the same steps (forward + backward, B=4 T=64, fp64, single thread), {dt:.1f} s",
+               "host_cpu": model_name, "host_nproc": ncpu}
+    out = {
+        "metric": "train tokens/sec, GPT-2 124M fp32 B=4 T=64 (10 steps on one batch) on 1x MI355X",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (Zipf(1.1) tokens, random GPT-2 init)",
+        "config": {"workload": "GPT-2 124M fp32 training step, B=4 T=64, AdamW lr 1e-4 wd 0, one batch"},
+        "fp32_peak_frac": round(frac, 5), "flops_per_token": fpt,
+        "roofline": {"bound": "mfma", "achieved": round(tok_s * fpt / 1e12, 2), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(frac, 5), "traffic": None,
+                     "kernel": "whole step (algorithmic FLOPs / step time)", "avg_ms": round(ms, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

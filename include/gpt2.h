@@ -199,6 +199,33 @@ int gpt2_act_tensor(gpt2_ctx* ctx, int which, void** d_ptr, size_t* count);
  * Errors: GPT2_E_ARG. */
 int gpt2_set_classifier_events(gpt2_ctx* ctx, void* const* d_start_events, void* const* d_end_events, int n);
 
+/* Timing hooks (diagnostics), one per launch point of the step: with n > 0
+ * every later launch at `point` is bracketed by d_start_events[i] and
+ * d_end_events[i] recorded on the call's hip_stream, i = number of earlier
+ * launches at that point since this call, modulo n.  Launch order within one
+ * call is fixed: GPT2_TP_LAYER_FWD brackets, for layers 0 .. L-1, the qkv,
+ * attention-projection, fc and fc-projection products (4 per layer);
+ * GPT2_TP_LAYER_DX the input-gradient products of layers L-1 .. 0 in the
+ * order fc-projection (with the GELU backward), fc, attention projection,
+ * qkv; GPT2_TP_LN_FWD the 2L + 1 forward LayerNorms (ln1, ln2 per layer,
+ * then the final one); GPT2_TP_LN_BWD the final one's backward and then
+ * ln2, ln1 of layers L-1 .. 0 (each with its parameter-gradient reduction);
+ * GPT2_TP_ATTN_FWD / GPT2_TP_ATTN_BWD one per layer; GPT2_TP_WEIGHT_GRAD
+ * the one launch of every weight gradient (bf16 contexts; fp32 contexts
+ * bracket each weight-gradient product, classifier first, then the layers in
+ * the order of GPT2_TP_LAYER_DX); GPT2_TP_CLASSIFIER_DX the classifier's
+ * input gradient (with its K-split reduction); GPT2_TP_CE the fused softmax
+ * cross-entropy; GPT2_TP_ENCODER_BWD the token/position embedding backward;
+ * GPT2_TP_ADAMW the optimizer update.  Arrays of n hipEvent_t handles each,
+ * owned by the caller and kept valid while the hook is set; n = 0 removes
+ * it.  gpt2_set_classifier_events(ctx, ...) is the GPT2_TP_CLASSIFIER_FWD
+ * hook.  Errors: GPT2_E_ARG (NULL context, point out of range, n < 0, n > 0
+ * with a NULL array). */
+enum { GPT2_TP_CLASSIFIER_FWD = 0, GPT2_TP_WEIGHT_GRAD = 1, GPT2_TP_CLASSIFIER_DX = 2, GPT2_TP_LAYER_FWD = 3,
+       GPT2_TP_LAYER_DX = 4, GPT2_TP_ATTN_FWD = 5, GPT2_TP_ATTN_BWD = 6, GPT2_TP_LN_FWD = 7, GPT2_TP_LN_BWD = 8,
+       GPT2_TP_CE = 9, GPT2_TP_ENCODER_BWD = 10, GPT2_TP_ADAMW = 11, GPT2_TP_COUNT = 12 };
+int gpt2_set_timing_events(gpt2_ctx* ctx, int point, void* const* d_start_events, void* const* d_end_events, int n);
+
 /* train_gpt2.cu, sample_softmax with the generation loop's indexing: for
  * every batch row b, sets d_tokens[b*T + t] to the token drawn from the
  * softmax over the first vocab_size logits of position t-1 of the last

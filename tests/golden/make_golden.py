@@ -13,8 +13,16 @@ own worker process (``--jobs``); gradients are summed in sequence order.
 
 Stored per case (numpy .npz, plain arrays): the mean losses, the per-position
 losses, per-tensor gradient L2 norms, the gradients and the AdamW-updated
-parameters at 1024 seeded sample indices per tensor (key-bias elements of qkvb
+parameters at seeded sample indices per tensor (key-bias elements of qkvb
 excluded: their exact gradient is zero and both sides carry only round-off).
+
+Samples: the 124M fp32 and 1558M cases take 1024 seeded indices per tensor.
+The 124M bf16 benchmark step takes tile-covering samples (tile_samples):
+every element of tensors up to 65536 elements; for larger ones one element
+in every 64 x 64 block of each layer's matrix (finer than any output tile of
+the weight-gradient products), for wte one element in every row whose token
+occurs in the step's batches, topped up with seeded random elements to at
+least 65536 per tensor.
 """
 
 from __future__ import annotations
@@ -56,6 +64,46 @@ def sample_indices(cfg):
     return out
 
 
+FULL_MAX = 65536  # tensors up to this size are stored whole
+BLOCK = 64        # one sample per BLOCK x BLOCK block of a layer's matrix
+
+
+def tile_samples(cfg, tokens):
+    """Per tensor (in parameter order) sorted flat int32 indices: see the
+    module docstring.  tokens: every token id of the step's batches."""
+    shapes = S.param_shapes(cfg)
+    rng = np.random.default_rng(SAMPLE_SEED + 1)
+    L, C = cfg.num_layers, cfg.channels
+    out = {}
+    for name in S.PARAM_NAMES:
+        shape = shapes[name]
+        n = int(np.prod(shape))
+        allowed = None
+        if name == "qkvb":
+            a = np.arange(n)
+            allowed = (a % (3 * C) < C) | (a % (3 * C) >= 2 * C)
+        if n <= FULL_MAX:
+            idx = np.arange(n) if allowed is None else np.nonzero(allowed)[0]
+            out[name] = idx.astype(np.int32)
+            continue
+        rows, cols = int(np.prod(shape[:-1])), shape[-1]
+        sel = set()
+        # one element per BLOCK x BLOCK block (layers are stacked along rows;
+        # every per-layer row count here is a multiple of BLOCK)
+        for r0 in range(0, rows, BLOCK):
+            nr = min(BLOCK, rows - r0)
+            for c0 in range(0, cols, BLOCK):
+                nc = min(BLOCK, cols - c0)
+                sel.add((r0 + int(rng.integers(nr))) * cols + c0 + int(rng.integers(nc)))
+        if name == "wte":
+            for t in np.unique(tokens):
+                sel.add(int(t) * cols + int(rng.integers(cols)))
+        while len(sel) < FULL_MAX:
+            sel.update(int(x) for x in rng.integers(0, n, FULL_MAX - len(sel)))
+        out[name] = np.array(sorted(sel), np.int32)
+    return out
+
+
 def _init_worker(cfg, flat):
     _W["cfg"], _W["flat"] = cfg, flat
 
@@ -82,13 +130,13 @@ def run_batch(pool, batch, dloss, want_grads, grads=None):
     return np.stack(losses), grads
 
 
-def norms_and_samples(cfg, flat, idx):
+def norms_and_samples(cfg, flat, idx, dtype=np.float64):
     off, cnt, _ = oracle.param_layout(cfg)
     norms, samp = [], []
     for i, name in enumerate(S.PARAM_NAMES):
         t = flat[off[i]:off[i] + cnt[i]]
         norms.append(np.linalg.norm(t))
-        samp.append(t[idx[name]])
+        samp.append(t[idx[name]].astype(dtype))
     return np.array(norms), np.concatenate(samp)
 
 
@@ -126,14 +174,17 @@ def case_c4(jobs):
     params = {k: S.round_to_bf16(v_) for k, v_ in S.init_params(cfg).items()}
     flat = oracle.pack_params(cfg, params)
     stream = S.token_stream(accum * B * T + 1, cfg.vocab_size, dist="zipf")
-    idx = sample_indices(cfg)
+    idx = tile_samples(cfg, stream[:accum * B * T])
+    print("c4 samples per tensor:", {k: int(v.size) for k, v in idx.items()}, flush=True)
     grads, means, losses = None, [], []
     with mp.get_context("fork").Pool(jobs, initializer=_init_worker, initargs=(cfg, flat)) as pool:
         for a in range(accum):
             lo, grads = run_batch(pool, S.batch(stream, a, B, T), 1.0 / (accum * B * T), True, grads)
             means.append(lo.mean()); losses.append(lo)
             print(f"c4 micro-step {a + 1}: loss {means[-1]:.6f}", flush=True)
-    gn, gs = norms_and_samples(cfg, grads, idx)
+    # gradients as float32 (far finer than the bf16 step's accuracy); updated
+    # and initial parameters as float64 (the update is a small difference)
+    gn, gs = norms_and_samples(cfg, grads, idx, np.float32)
     newp, _, _ = oracle.adamw(flat, grads, np.zeros_like(flat), np.zeros_like(flat), 6e-4, 0.9, 0.999, 1e-8, 0.1, 1)
     ps = norms_and_samples(cfg, newp, idx)[1]
     p0 = norms_and_samples(cfg, flat, idx)[1]

@@ -2,7 +2,7 @@
 gpt2_attention_backward, the launches the step makes) against the oracle's
 attention_forward / attention_backward in fp64 on the same bf16-exact inputs.
 
-Cases: head sizes 64 (the GPT-2 sizes), 32 and 128; T ragged against the
+Cases: head sizes 64 (the GPT-2 sizes), 32, 128 and 16; T ragged against the
 64-row blocks, T < 64, T = 1, T a multiple of 64 with many blocks, and the
 full GPT-2 124M layer shape (T = 1024, 12 heads) at B = 2; score scales 1
 and 3 (peakier softmax rows).
@@ -35,6 +35,9 @@ CASES = [
     (2, 100, 192, 6, 1.0),
     (1, 130, 256, 2, 1.0),
     (2, 1024, 768, 12, 1.0),
+    # head size 16 (its key dimension padded to 32 inside the kernels), ragged T
+    (2, 100, 64, 4, 1.0),
+    (1, 130, 64, 4, 3.0),
 ]
 
 

@@ -6,12 +6,15 @@ calls only the oracle), plus size-independent properties.
   wd 0): per-step mean loss rel <= 1e-5; step-1 gradients (norms and samples)
   rel <= 1e-4; step-2 gradients rel-L2 <= 1e-4 per full tensor against the
   oracle evaluated at the GPU's own parameters; trajectory gradients of steps
-  2..10 rel <= 1e-3 (AdamW's eps-region sensitivity, see the test); final
+  2..10 rel <= 3e-4 (AdamW's eps-region sensitivity, see the test); final
   sampled parameters rel-L2 <= 1e-4; the loss falls.
 * GPT-2 124M bf16, B=8 T=1024, step 1 of the benchmark workload (2
   micro-steps, AdamW lr 6e-4 wd 0.1): micro-step mean losses abs <= 2e-2;
-  sampled gradient cosine >= 0.995 per tensor; sampled update direction
-  cosine >= 0.9.
+  gradient cosine >= 0.995 per tensor on tile-covering samples (every element
+  of the small tensors, one per 64 x 64 block and per present token row of
+  the large ones, at least 65536 per tensor); gradient norms within 1e-2;
+  update cosine >= 0.95 and update signs agreeing on >= 99.8% of the
+  elements whose gradient exceeds 5% of the tensor's RMS.
 * GPT-2 1558M bf16, B=1 T=64 micro-step: loss abs <= 2e-2, sampled gradient
   cosine >= 0.995 per tensor; at B=8 T=1024 the loss at init is near
   ln V + C * 0.02^2 / 2 and falls over three small steps on one batch.
@@ -97,9 +100,10 @@ def test_gpt2_124m_fp32_ten_steps_one_batch():
         # step 1 starts from identical parameters: the kernels' own accuracy.
         # Later steps follow two trajectories (fp32 on the GPU, fp64 in the
         # oracle) whose AdamW updates differ wherever |g| is near eps;
-        # tests/golden/adam_eps_sensitivity.py measures 2-3e-5 of step-2
-        # gradient change from fp32-sized gradient noise alone.
-        tol = 1e-4 if s == 0 else 1e-3
+        # tests/test_adam_sensitivity.py bounds the step-2 gradient change
+        # from fp32-sized gradient noise alone by 1e-4 (measured 2-3e-5; the
+        # largest drift seen here over steps 3-10 is 7.6e-5).
+        tol = 1e-4 if s == 0 else 3e-4
         gn = _norms(model, grads)
         assert np.all(np.abs(gn - g["grad_norms"][s]) <= tol * g["grad_norms"][s] + 1e-30), s
         for name in S.PARAM_NAMES:
@@ -160,10 +164,20 @@ def test_gpt2_124m_bf16_benchmark_step1():
     gs = _samples(model, grads, g)
     ref = _split(cfg, g, g["grad_samples"])
     cos = {n: cosine(gs[n], ref[n]) for n in S.PARAM_NAMES}
-    say("124M bf16 sampled gradient cosines", {k: round(v, 5) for k, v in cos.items()})
-    assert min(cos.values()) >= 0.995
+    say("124M bf16 per-tensor gradient cosines (tile-covering samples)", {k: round(v, 5) for k, v in cos.items()})
+    for n, c in cos.items():
+        assert c >= 0.995, (n, c)
     gn = _norms(model, grads)
-    assert np.all(np.abs(gn / g["grad_norms"] - 1) < 0.05)
+    ratio = gn / g["grad_norms"]
+    say("124M bf16 gradient norm ratios", np.round(ratio, 5).tolist())
+    assert np.all(np.abs(ratio - 1) <= 1e-2), ratio
+    # The AdamW step-1 update is lr * (g / (|g| + eps) + wd * p): essentially
+    # lr * sign(g), so it can differ only where the bf16 gradient error flips
+    # a sign.  Where |g| > 5% of the tensor's RMS that takes an error of
+    # several times the error's own RMS (the 0.995 cosine bounds it at 10% of
+    # the gradient's RMS): at least 99.8% of those signs agree; over all
+    # elements the update directions keep a cosine of at least 0.95 (a few
+    # percent of sign flips among the smallest gradients).
     p1 = model.master().cpu().numpy()
     d_gpu = _samples(model, p1, g)
     d_p0 = _samples(model, p0, g)
@@ -171,8 +185,13 @@ def test_gpt2_124m_bf16_benchmark_step1():
     ref_p0 = _split(cfg, g, g["init_samples"])
     for n in S.PARAM_NAMES:
         assert np.array_equal(d_p0[n].astype(np.float64), ref_p0[n]), n  # same bf16-exact start
-        c = cosine(d_gpu[n] - d_p0[n], ref_p[n] - ref_p0[n])
-        assert c >= 0.9, (n, c)
+        du, dr = d_gpu[n] - d_p0[n], ref_p[n] - ref_p0[n]
+        c = cosine(du, dr)
+        r = ref[n].astype(np.float64)
+        big = np.abs(r) > 0.05 * np.sqrt(np.mean(r * r))
+        agree = float(np.mean(np.sign(du[big]) == np.sign(dr[big]))) if big.any() else 1.0
+        assert c >= 0.95, (n, c)
+        assert agree >= 0.998, (n, agree)
     model.close()
 
 

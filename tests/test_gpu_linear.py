@@ -61,8 +61,19 @@ def test_linear_forward_bias(M, K, N):
     assert excess <= 0.0
 
 
-# plus the qkv layer's exact shape (input gradient N = 768: fewer tiles than CUs)
-@pytest.mark.parametrize("M,K,N", SHAPES[:2] + [(8192, 768, 2304)])
+def _tile_rows(n, seed, tile=256):
+    """One seeded row in every `tile`-row block of n (and the last row): every
+    row tile of an output is checked."""
+    rng = np.random.default_rng(seed)
+    r = {min(n - 1, b + int(rng.integers(tile))) for b in range(0, n, tile)}
+    r.add(n - 1)
+    return np.array(sorted(r))
+
+
+# plus the qkv layer's exact shape (input gradient N = 768: fewer tiles than
+# CUs) and the tied classifier's (8192 x 768 from N = 50304: the K-split input
+# gradient, and a weight gradient of 197 x 3 tiles)
+@pytest.mark.parametrize("M,K,N", SHAPES[:2] + [(8192, 768, 2304), (8192, 768, 50304)])
 def test_linear_backward(M, K, N):
     import torch
     import oracle
@@ -91,12 +102,63 @@ def test_linear_backward(M, K, N):
     excess = _bf16_close(got, ref_dx)
     say(f"input gradient {M}x{K} from N={N}: worst excess over the bound {excess:.2e}")
     assert excess <= 0.0
-    # weight / bias gradient rows: full contractions over M, accumulated onto dw0 / db0
-    ocs = _rows(N, 12, 9)
+    # weight / bias gradient rows (one in every 256-row tile, all columns):
+    # full contractions over M, accumulated onto dw0 / db0
+    ocs = _tile_rows(N, 9)
     _, ref_dw, ref_db = oracle.matmul_backward(alpha * dy[:, ocs], x, w[ocs])
     got_dw = dw.cpu().numpy()[ocs].astype(np.float64)
     got_db = db.cpu().numpy()[ocs].astype(np.float64)
     e_w = rel_l2(got_dw - dw0[ocs], ref_dw)
     e_b = rel_l2(got_db - db0[ocs], ref_db)
+    say(f"weight gradient rows {ocs.size}: rel-L2 {e_w:.2e}, bias {e_b:.2e}")
+    assert e_w <= 1e-5 and e_b <= 1e-5
+
+
+def test_linear_backward_beyond_4gib():
+    """The classifier's backward products with B*T = 44000 rows: dlogits
+    [44000, 50304] bf16 is 4.4 GB, so tile ranges past 2 GiB from a tile's
+    origin are clamped.  Operands come from torch's seeded generator on the
+    device; the oracle checks one input-gradient row per 256-row tile range
+    sampled and one weight-gradient row in every 256-row tile (full
+    contractions over the 44000 rows)."""
+    import torch
+    import oracle
+    from transformer_lm_step_amd import binding as B
+
+    M, K, N = 44000, 768, 50304
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(S.DATA_SEED + 7)
+    bf = torch.bfloat16
+    x = torch.randn(M, K, generator=gen, device=dev).to(bf)
+    w = (0.02 * torch.randn(N, K, generator=gen, device=dev)).to(bf)
+    dy = (torch.randn(M, N, generator=gen, device=dev) * 1e-3).to(bf)
+    dx = torch.full((M, K), float("nan"), dtype=bf, device=dev)
+    dw = torch.zeros(N, K, dtype=torch.float32, device=dev)
+    db = torch.zeros(N, dtype=torch.float32, device=dev)
+    alpha = 0.25
+    wsz = B.gpt2_linear_backward_workspace(B.GPT2_BF16, M, N, K)
+    ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+    say(f"backward beyond 4 GiB: dy {M}x{N} bf16 = {M * N * 2 / 1e9:.1f} GB, workspace {wsz} bytes")
+    B.gpt2_linear_backward(B.GPT2_BF16, dy.data_ptr(), x.data_ptr(), w.data_ptr(), dx.data_ptr(), dw.data_ptr(),
+                           db.data_ptr(), M, N, K, alpha, ws.data_ptr(), wsz, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(dx).any()), "unwritten input-gradient elements"
+    w64 = w.float().cpu().numpy().astype(np.float64)
+    rows = np.array(sorted(set(_rows(M, 16, 10).tolist()) | {M - 1, M - 300, 43008}))
+    got = dx[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+    dyr = dy[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+    ref_dx = alpha * dyr @ w64
+    excess = _bf16_close(got, ref_dx)
+    say(f"input gradient rows {rows.size}: worst excess over the bound {excess:.2e}")
+    assert excess <= 0.0
+    ocs = _tile_rows(N, 11)
+    dyc = dy[:, torch.from_numpy(ocs).to(dev)].float().cpu().numpy().astype(np.float64)
+    x64 = x.float().cpu().numpy().astype(np.float64)
+    ref_dw = alpha * dyc.T @ x64
+    ref_db = alpha * dyc.sum(axis=0)
+    got_dw = dw.cpu().numpy()[ocs].astype(np.float64)
+    got_db = db.cpu().numpy()[ocs].astype(np.float64)
+    e_w, e_b = rel_l2(got_dw, ref_dw), rel_l2(got_db, ref_db)
     say(f"weight gradient rows {ocs.size}: rel-L2 {e_w:.2e}, bias {e_b:.2e}")
     assert e_w <= 1e-5 and e_b <= 1e-5

@@ -220,3 +220,20 @@ def test_caller_stream_without_host_syncs_matches_bitwise():
     for p in PARAM_NAMES:
         assert np.array_equal(g[p], ref["grads"][p]), p
         assert np.array_equal(p_[p], ref["params"][p]), p
+
+
+def test_fp32_token_embedding_gradient_two_position_blocks():
+    """B*T = 16448 positions: the token-embedding gradient runs over two
+    blocks of positions (16384, then 64), each block's sums added in block
+    order; Zipf tokens put the frequent ids in both blocks."""
+    cfg, B, T = S.TINY, 257, 64
+    say("case token blocks", B * T)
+    params, batches = make_inputs(cfg, B, T, perturb=True, dist="zipf")
+    o = oracle_step(cfg, params, batches, lr=1e-4)
+    g = gpu_step(cfg, 0, params, batches, lr=1e-4)
+    assert g["code"] == 0
+    assert abs(g["means"][0] - o["means"][0]) / abs(o["means"][0]) < 1e-5
+    for p in ("wte", "wpe"):
+        e = rel_l2(g["grads"][p], o["grads"][p])
+        say("two blocks", p, "gradient rel-L2", e)
+        assert e < 1e-4, (p, e)

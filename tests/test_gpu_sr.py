@@ -82,3 +82,40 @@ def test_sr_mode_gradients_equal_bf16_mode():
         grads.append(model.grads().cpu().numpy().copy())
         model.close()
     assert np.array_equal(grads[0].view(np.uint32), grads[1].view(np.uint32))
+
+
+def test_sr_update_matches_oracle_bitwise_124m():
+    """The same bit-for-bit check over all 124,475,904 parameters of GPT-2
+    124M (the size the benchmark's --sr mode updates), two steps from the
+    device's own gradients of a B=4, T=64 micro-step each."""
+    import torch
+    from transformer_lm_step_amd import binding as Bnd
+    from transformer_lm_step_amd.model import GPT2
+
+    cfg, B, T = S.GPT2_124M, 4, 64
+    params = {k: S.round_to_bf16(v) for k, v in S.init_params(cfg).items()}
+    stream = S.token_stream(2 * B * T + 1, cfg.vocab_size, dist="zipf", seed=12)
+    model = GPT2(cfg, Bnd.GPT2_BF16_SR, B, T)
+    model.init(model.pack(params))
+    p = _bits(model.params())
+    m = np.zeros(model.num_params, np.float32)
+    v = np.zeros(model.num_params, np.float32)
+    state = 13371337
+    lr, b1, b2, eps, wd = 6e-4, 0.9, 0.999, 1e-8, 0.1
+    for t in (1, 2):
+        x, y = S.batch(stream, t - 1, B, T)
+        model.zero_grad()
+        _micro(model, x, y)
+        torch.cuda.synchronize()
+        g = model.grads().cpu().numpy().copy()
+        model.update(lr, b1, b2, eps, wd, t)
+        torch.cuda.synchronize()
+        seed, state = oracle.xorshift_u32(state)
+        p, m, v = oracle.adamw_sr(p, g, m, v, lr, b1, b2, eps, wd, t, seed)
+        got = _bits(model.params())
+        say("124M SR step", t, "seed", seed, "elements", got.size, "mismatches", int((got != p).sum()))
+        assert got.size == 124475904
+        assert np.array_equal(got, p), t
+        assert np.array_equal(model.adam_m().cpu().numpy().view(np.uint32), m.view(np.uint32)), t
+        assert np.array_equal(model.adam_v().cpu().numpy().view(np.uint32), v.view(np.uint32)), t
+    model.close()

@@ -21,11 +21,14 @@ GPT2_BF16_SR = 2
 GPT2_OK, GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_STATE, GPT2_E_TOKEN, GPT2_E_ALIGN, GPT2_E_HIP = 0, -1, -2, -3, -4, -5, -6
 GPT2_E_FILE = -7
 GPT2_T_LOGITS, GPT2_T_LNF, GPT2_T_RESIDUAL, GPT2_T_DRESIDUAL, GPT2_T_ENCODED = 0, 1, 2, 3, 4
+(GPT2_TP_CLASSIFIER_FWD, GPT2_TP_WEIGHT_GRAD, GPT2_TP_CLASSIFIER_DX, GPT2_TP_LAYER_FWD, GPT2_TP_LAYER_DX,
+ GPT2_TP_ATTN_FWD, GPT2_TP_ATTN_BWD, GPT2_TP_LN_FWD, GPT2_TP_LN_BWD, GPT2_TP_CE, GPT2_TP_ENCODER_BWD,
+ GPT2_TP_ADAMW) = range(12)
 
 EXPORTED = (
     "gpt2_query_sizes", "gpt2_param_layout", "gpt2_init", "gpt2_forward", "gpt2_zero_grad",
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
-    "gpt2_set_classifier_events", "gpt2_set_rng_state", "gpt2_sample", "gpt2_generate", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
+    "gpt2_set_classifier_events", "gpt2_set_timing_events", "gpt2_set_rng_state", "gpt2_sample", "gpt2_generate", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
     "gpt2_linear_backward_workspace", "gpt2_attention_forward", "gpt2_attention_backward",
     "fused_linear_gelu_softmax_f32", "fused_linear_gelu_softmax_f32_workspace",
 )
@@ -70,6 +73,7 @@ def _load():
         "gpt2_check_device_error": (i, [vp, vp]),
         "gpt2_act_tensor": (i, [vp, i, ctypes.POINTER(vp), ctypes.POINTER(z)]),
         "gpt2_set_classifier_events": (i, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i]),
+        "gpt2_set_timing_events": (i, [vp, i, ctypes.POINTER(vp), ctypes.POINTER(vp), i]),
         "gpt2_set_rng_state": (i, [vp, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]),
         "gpt2_sample": (i, [vp, vp, vp, i, vp]),
         "gpt2_generate": (i, [vp, vp, vp, i, i, vp]),
@@ -186,6 +190,17 @@ def gpt2_set_classifier_events(ctx: int, starts, ends):
     a = (ctypes.c_void_p * max(n, 1))(*starts)
     b = (ctypes.c_void_p * max(n, 1))(*ends)
     _check(_lib.gpt2_set_classifier_events(ctx, a, b, n), "gpt2_set_classifier_events")
+    return a, b
+
+
+def gpt2_set_timing_events(ctx: int, point: int, starts, ends):
+    """As gpt2_set_classifier_events, for launch point `point` (GPT2_TP_*)."""
+    n = len(starts)
+    if len(ends) != n:
+        raise ValueError("starts and ends differ in length")
+    a = (ctypes.c_void_p * max(n, 1))(*starts)
+    b = (ctypes.c_void_p * max(n, 1))(*ends)
+    _check(_lib.gpt2_set_timing_events(ctx, point, a, b, n), "gpt2_set_timing_events")
     return a, b
 
 

@@ -39,16 +39,12 @@
 #include "device.h"
 #include "kernels.h"
 
-#ifndef ATTN_FWD_NS
-#define ATTN_FWD_NS 2
-#endif
-#ifndef ATTN_BWD_NS
-#define ATTN_BWD_NS 2
-#endif
 
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
+// stage buffers of the streamed key/value (or query/output-gradient) blocks
+constexpr int ATTN_FWD_NS = 2, ATTN_BWD_NS = 2;
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 // Row block `blk` (0 = the one with the most work) and (batch, head) of this

@@ -2,6 +2,8 @@
 // AdamW and small utilities (gfx950).
 #include <math.h>
 
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -37,62 +39,11 @@ __global__ void encoder_fwd_kernel(T* __restrict__ out, int* __restrict__ tok_co
 }
 
 // ------------------------------------------------------------ encoder bwd ---
-// train_gpt2.cu, encoder_backward_kernel, without atomics.  dwte: one wave per
-// position i; the wave scans the ids before i and stops if its id occurs
-// there.  The wave of the first occurrence of id v then sums, in increasing
-// position order, the residual-gradient rows of every position holding v and
-// adds the sum into dwte[v].  Each row of dwte is thus written by one wave
-// with a fixed order of summation.
-__global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict__ dwte, const float* __restrict__ dres,
-                                                              const int* __restrict__ tok, int BT, int C) {
-    const int lane = threadIdx.x & 63;
-    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= BT) return;
-    const int v = tok[i];
-    for (int j0 = 0; j0 < i; j0 += 64) {
-        const int j = j0 + lane;
-        const bool hit = (j < i) && tok[j] == v;
-        if (__any(hit)) return;
-    }
-    constexpr int NV = 8;  // C <= 2048 as float4 vectors over 64 lanes
-    const int nvec = C / 4;
-    float acc[NV][4];
-#pragma unroll
-    for (int k = 0; k < NV; k++) acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
-    for (int j0 = i; j0 < BT; j0 += 64) {
-        const int j = j0 + lane;
-        unsigned long long mask = __ballot(j < BT && tok[j] == v);
-        while (mask) {
-            const int jj = j0 + __ffsll((long long)mask) - 1;
-            mask &= mask - 1;
-            const float* r = dres + (long)jj * C;
-#pragma unroll
-            for (int k = 0; k < NV; k++) {
-                const int vv = lane + 64 * k;
-                if (vv < nvec) {
-                    float x[4];
-                    load4<float>(r + vv * 4, x);
-#pragma unroll
-                    for (int e = 0; e < 4; e++) acc[k][e] += x[e];
-                }
-            }
-        }
-    }
-    float* w = dwte + (long)v * C;
-#pragma unroll
-    for (int k = 0; k < NV; k++) {
-        const int vv = lane + 64 * k;
-        if (vv < nvec) {
-            float o[4];
-            load4<float>(w + vv * 4, o);
-#pragma unroll
-            for (int e = 0; e < 4; e++) o[e] += acc[k][e];
-            store4<float>(w + vv * 4, o);
-        }
-    }
-}
-
-// Sort-based variant (B*T <= 16384), all deterministic:
+// train_gpt2.cu, encoder_backward_kernel, without atomics: dwte[v] += the
+// residual-gradient rows of every position holding token v, summed in a
+// fixed order.  Positions are taken in blocks of up to 16384, one block
+// after the other (so every row of dwte receives its blocks' sums in block
+// order); within a block, all deterministic:
 //  1. the keys (id << shift | position) are sorted by rank (enc_rank_kernel):
 //     equal ids end up adjacent, in increasing position order;
 //  2. one wave per chunk of 16 sorted entries sums each run of equal ids in
@@ -628,33 +579,35 @@ int encoder_fwd_launch(T* out, int* tok_copy, const int* tok, const T* wte, cons
 }
 
 size_t encoder_bwd_workspace_bytes(int BT, int C) {
-    if (BT > ENC_SORT_MAX) return 0;
-    const size_t nch = (BT + ENC_CHUNK - 1) / ENC_CHUNK;
-    return (size_t)BT * 4 + nch * 3 * 4 + 2 * nch * C * 4 + 1024;
+    const int nb = BT < ENC_SORT_MAX ? BT : ENC_SORT_MAX;  // positions per block
+    const size_t nch = (nb + ENC_CHUNK - 1) / ENC_CHUNK;
+    return ((size_t)nb * 4 + 255) / 256 * 256 + (nch * 12 + 255) / 256 * 256 + 2 * nch * C * 4;
 }
 
 int encoder_bwd_launch(float* dwte, float* dwpe, const float* dres, const int* tok, int B, int T_, int C,
                        void* work, hipStream_t s) {
-    const int BT = B * T_;
+    const long BT = (long)B * T_;
     if (BT == 0) return 0;
-    if (BT <= ENC_SORT_MAX && work != nullptr) {
+    if (work == nullptr) return (int)hipErrorInvalidValue;
+    for (long p0 = 0; p0 < BT; p0 += ENC_SORT_MAX) {
+        const int nb = (int)std::min<long>(ENC_SORT_MAX, BT - p0);
         int shift = 0;
-        while ((1 << shift) < BT) shift++;
-        const int nch = (BT + ENC_CHUNK - 1) / ENC_CHUNK;
+        while ((1 << shift) < nb) shift++;
+        const int nch = (nb + ENC_CHUNK - 1) / ENC_CHUNK;
         char* w = (char*)work;
         unsigned* sorted = (unsigned*)w;
-        w += ((size_t)BT * 4 + 255) / 256 * 256;
+        w += ((size_t)nb * 4 + 255) / 256 * 256;
         int* meta = (int*)w;
         w += ((size_t)nch * 12 + 255) / 256 * 256;
         float* headws = (float*)w;
         float* tailws = headws + (size_t)nch * C;
-        hipLaunchKernelGGL(enc_rank_kernel, dim3((BT + 63) / 64), dim3(256), 0, s, sorted, tok, BT, shift);
-        hipLaunchKernelGGL(enc_chunk_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, dres,
-                           sorted, BT, C, shift, nch);
-        hipLaunchKernelGGL(enc_fix_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, sorted, BT,
+        const float* dr = dres + p0 * C;
+        const int* tk = tok + p0;
+        hipLaunchKernelGGL(enc_rank_kernel, dim3((nb + 63) / 64), dim3(256), 0, s, sorted, tk, nb, shift);
+        hipLaunchKernelGGL(enc_chunk_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, dr,
+                           sorted, nb, C, shift, nch);
+        hipLaunchKernelGGL(enc_fix_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, sorted, nb,
                            shift, C, nch);
-    } else {
-        hipLaunchKernelGGL(encoder_bwd_wte_kernel, dim3((BT + 3) / 4), dim3(256), 0, s, dwte, dres, tok, BT, C);
     }
     const long n4 = (long)T_ * C / 4;
     hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dwpe, dres, B, T_, C);

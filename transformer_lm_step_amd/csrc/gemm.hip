@@ -48,9 +48,6 @@
 namespace {
 
 constexpr int NTHREADS = 256;
-#ifndef GEMM_SCHED_GROUPS
-#define GEMM_SCHED_GROUPS 1
-#endif
 
 template <typename T, int BM_, int BN_, int WTM_ = 64, int WTN_ = 64>
 struct Tile {
@@ -608,7 +605,6 @@ __global__ __launch_bounds__((TileOf<T, BM, BN, WT>::NT), (TileOf<T, BM, BN, WT>
         }
         slab_store<T, BM, AK, NT>(sta_, sA[cur ^ 1], tid);
         slab_store<T, BN, BKM, NT>(stb_, sB[cur ^ 1], tid);
-#if GEMM_SCHED_GROUPS
         __builtin_amdgcn_sched_group_barrier(0x020, NRA + NRB, 0);  // global loads
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);         // step-0 fragments
 #pragma unroll
@@ -627,7 +623,6 @@ __global__ __launch_bounds__((TileOf<T, BM, BN, WT>::NT), (TileOf<T, BM, BN, WT>
                 }
             }
         }
-#endif
         __syncthreads();
     };
     if constexpr (DEPTH == 2) {
@@ -678,30 +673,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Stage depth BK (contraction elements per stage) and stage count NS per tile:
 // the 128x128 tiles (two workgroups per CU) keep four 32-deep stages so that
 // three are in flight while one is consumed; the larger tiles two 64-deep ones.
-#ifndef GEMM_DTL_BK128
-#define GEMM_DTL_BK128 64
-#endif
-#ifndef GEMM_DTL_NS128
-#define GEMM_DTL_NS128 2
-#endif
-#ifndef GEMM_DTL_NS_RECT
-#define GEMM_DTL_NS_RECT 3
-#endif
-#ifndef GEMM_HALF_LOADERS
-#define GEMM_HALF_LOADERS 1
-#endif
-#ifndef GEMM_DTL_BK256
-#define GEMM_DTL_BK256 64
-#endif
-#ifndef GEMM_DTL_NS256
-#define GEMM_DTL_NS256 2
-#endif
 template <int BM, int BN>
 struct DtlCfg {
-    static constexpr int BK = (BM == 128 && BN == 128) ? GEMM_DTL_BK128 : (BM == 256 && BN == 256) ? GEMM_DTL_BK256 : 64;
-    static constexpr int NS = (BM == 128 && BN == 128) ? GEMM_DTL_NS128
-                              : (BM == 256 && BN == 256) ? GEMM_DTL_NS256
-                              : (BM != BN ? GEMM_DTL_NS_RECT : 2);
+    static constexpr int BK = 64;
+    static constexpr int NS = BM != BN ? 3 : 2;
     static_assert(NS >= 2 && NS <= 4, "the stage loop unrolls 2 to 4 stage buffers");
     static_assert(BK == 32 || BK == 64, "stages are one or two 32-deep MFMA steps");
 };
@@ -995,7 +970,7 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
     // issues in order, so a loading wave stalls at the start of each stage;
     // its SIMD partner (wave w + 4) runs its MFMAs meanwhile instead of
     // stalling too (2-8% on the 8-wave tiles).
-    constexpr int NL = (NW == 8 && GEMM_HALF_LOADERS) ? 4 : NW;
+    constexpr int NL = NW == 8 ? 4 : NW;
     const bool loads = NL == NW || wave < NL;
     const int lw = NL == NW ? wave : wave % NL;
     DtlSlab<BM, AK, NL, BK> dA;
@@ -1312,24 +1287,14 @@ struct TileCfg {
     int bm, bn, wt, occ;
     double speed[3];  // forward, input gradient, weight gradient
 };
-#ifndef GEMM_SPEED_W128_DX
-#define GEMM_SPEED_W128_DX 1.01
-#endif
-#ifndef GEMM_SPEED_192
-#define GEMM_SPEED_192 0.92
-#endif
 const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}},
                             {256, 128, 64, 1, {0.92, 0.76, 0.66}},
                             {128, 256, 64, 1, {0.71, 0.92, 0.70}},
                             {128, 128, 64, 2, {0.81, 0.82, 0.70}},
-                            {256, 256, 128, 1, {1.00, GEMM_SPEED_W128_DX, 1.00}},
+                            {256, 256, 128, 1, {1.00, 1.01, 1.00}},
                             // forward products only: a k-strided slab needs
                             // a power-of-two row count
-                            {128, 192, 96, 1, {GEMM_SPEED_192, 0.0, 0.0}},
-#ifdef GEMM_ONLY_TILE_BM
-                            {256, 128, 128, 1, {1.0, 1.0, 1.0}},
-                            {128, 256, 128, 1, {1.0, 1.0, 1.0}},
-#endif
+                            {128, 192, 96, 1, {0.92, 0.0, 0.0}},
 };
 constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
 const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}}};
@@ -1353,9 +1318,6 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     double best_cost = 1e300;
     for (int c = 0; c < ncfg; c++) {
         const TileCfg& t = cfgs[c];
-#ifdef GEMM_ONLY_TILE_BM
-        if (bf16 && (t.bm != GEMM_ONLY_TILE_BM || t.bn != GEMM_ONLY_TILE_BN || t.wt != GEMM_ONLY_TILE_WT)) continue;
-#endif
         const long tiles = (long)((d.M + t.bm - 1) / t.bm) * ((d.N + t.bn - 1) / t.bn);
         const int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
         for (int s = 1; s <= max_split; s++) {
@@ -1380,14 +1342,10 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     return best;
 }
 
-#ifndef GEMM_DTL
-#define GEMM_DTL 1
-#endif
-
 template <typename T, int BM, int BN, int WT, bool AK, bool BKM, int EPI, typename OutT, bool BIAS = false>
 void launch_t(const Args& a, dim3 grid, int slots, hipStream_t s) {
     using TL = TileOf<T, BM, BN, WT>;
-    if constexpr (sizeof(T) == 2 && GEMM_DTL) {
+    if constexpr (sizeof(T) == 2) {
         if (dtl_persistent<BM, BN, WT, EPI, BIAS>() && grid.y == 1) grid.x = std::min((int)grid.x, slots);
         hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, WT, AK, BKM, EPI, OutT, BIAS>), grid, dim3(TL::NT), 0, s, a);
     } else
@@ -1447,10 +1405,6 @@ int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, i
     if constexpr (sizeof(T) == 2) {
         if (ch.wt == 128) {
             if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 128>(d, a, grid, slots, epi, s);
-#ifdef GEMM_ONLY_TILE_BM
-            if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 128>(d, a, grid, slots, epi, s);
-            if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 128>(d, a, grid, slots, epi, s);
-#endif
             return (int)hipErrorInvalidValue;
         }
         if (ch.wt == 96 && ch.bm == 128 && ch.bn == 192) return launch_epi<T, 128, 192, 96>(d, a, grid, slots, epi, s);

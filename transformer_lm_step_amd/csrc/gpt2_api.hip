@@ -175,10 +175,12 @@ struct gpt2_ctx {
     Plan plan;
     int last_fwd_targets;  // -1: no forward yet, 0: without targets, 1: with
     float dw_alpha = 1.0f;  // the classifier weight gradient's scale in the current backward
-    // timing hook around the classifier product (caller-owned events)
-    void* const* ev_start = nullptr;
-    void* const* ev_end = nullptr;
-    int ev_n = 0, ev_i = 0;
+    // timing hooks around the launches of each point (caller-owned events)
+    struct Hook {
+        void* const* start = nullptr;
+        void* const* end = nullptr;
+        int n = 0, i = 0;
+    } hooks[GPT2_TP_COUNT];
     char* acts() const { return (char*)buf.acts; }
     template <typename X> X* act(size_t ofs) const { return (X*)(acts() + ofs); }
     template <typename X> X* act_l(size_t ofs, size_t stride, int l) const { return (X*)(acts() + ofs + stride * l); }
@@ -189,6 +191,18 @@ struct gpt2_ctx {
 namespace {
 
 int hip_rc(int e) { return e == 0 ? GPT2_OK : GPT2_E_HIP; }
+
+// Runs launch(), bracketed by the timing hook of `point` if one is set.
+template <typename F>
+int timed(gpt2_ctx* c, int point, hipStream_t s, F&& launch) {
+    gpt2_ctx::Hook& h = c->hooks[point];
+    const int k = h.n > 0 ? h.i++ % h.n : -1;
+    if (k >= 0 && hipEventRecord((hipEvent_t)h.start[k], s) != hipSuccess) return GPT2_E_HIP;
+    const int e = launch();
+    if (e != 0) return e;
+    if (k >= 0 && hipEventRecord((hipEvent_t)h.end[k], s) != hipSuccess) return GPT2_E_HIP;
+    return 0;
+}
 
 // train_gpt2.cu, random_u32: Marsaglia's xorshift on 64 bits with the
 // xorshift* output multiplier, upper 32 bits of the product
@@ -263,32 +277,48 @@ int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, flo
         T* fch = c->act_l<T>(p.fch, p.s_bt4c, l);
         T* fchg = c->act_l<T>(p.fchg, p.s_bt4c, l);
         T* res3 = c->act_l<T>(p.res3, p.s_btc, l);
-        TRY(layernorm_fwd_launch<T>(ln1, c->act_l<float>(p.ln1m, p.s_bt, l), c->act_l<float>(p.ln1r, p.s_bt, l), res,
-                                    prm<T>(c, 2, l, C), prm<T>(c, 3, l, C), BT, C, s));
-        TRY(gemm(c, fwd_desc(BT, 3 * C, C, ln1, prm<T>(c, 4, l, 3 * CC), qkv, GEMM_BIAS, prm<T>(c, 5, l, 3 * C),
-                             nullptr, nullptr), s));
-        TRY(attention_fwd_launch<T>(atty, c->act_l<float>(p.lse, p.s_lse, l), qkv, B, Tn, C, NH, s));
-        TRY(gemm(c, fwd_desc(BT, C, C, atty, prm<T>(c, 6, l, CC), res2, GEMM_BIAS_RESID, prm<T>(c, 7, l, C), res,
-                             nullptr), s));
-        TRY(layernorm_fwd_launch<T>(ln2, c->act_l<float>(p.ln2m, p.s_bt, l), c->act_l<float>(p.ln2r, p.s_bt, l), res2,
-                                    prm<T>(c, 8, l, C), prm<T>(c, 9, l, C), BT, C, s));
-        TRY(gemm(c, fwd_desc(BT, 4 * C, C, ln2, prm<T>(c, 10, l, 4 * CC), fchg, GEMM_BIAS_GELU,
-                             prm<T>(c, 11, l, 4 * C), nullptr, fch), s));
-        TRY(gemm(c, fwd_desc(BT, C, 4 * C, fchg, prm<T>(c, 12, l, 4 * CC), res3, GEMM_BIAS_RESID,
-                             prm<T>(c, 13, l, C), res2, nullptr), s));
+        TRY(timed(c, GPT2_TP_LN_FWD, s, [&] {
+            return layernorm_fwd_launch<T>(ln1, c->act_l<float>(p.ln1m, p.s_bt, l), c->act_l<float>(p.ln1r, p.s_bt, l),
+                                           res, prm<T>(c, 2, l, C), prm<T>(c, 3, l, C), BT, C, s);
+        }));
+        TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
+            return gemm(c, fwd_desc(BT, 3 * C, C, ln1, prm<T>(c, 4, l, 3 * CC), qkv, GEMM_BIAS, prm<T>(c, 5, l, 3 * C),
+                                    nullptr, nullptr), s);
+        }));
+        TRY(timed(c, GPT2_TP_ATTN_FWD, s, [&] {
+            return attention_fwd_launch<T>(atty, c->act_l<float>(p.lse, p.s_lse, l), qkv, B, Tn, C, NH, s);
+        }));
+        TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
+            return gemm(c, fwd_desc(BT, C, C, atty, prm<T>(c, 6, l, CC), res2, GEMM_BIAS_RESID, prm<T>(c, 7, l, C), res,
+                                    nullptr), s);
+        }));
+        TRY(timed(c, GPT2_TP_LN_FWD, s, [&] {
+            return layernorm_fwd_launch<T>(ln2, c->act_l<float>(p.ln2m, p.s_bt, l), c->act_l<float>(p.ln2r, p.s_bt, l),
+                                           res2, prm<T>(c, 8, l, C), prm<T>(c, 9, l, C), BT, C, s);
+        }));
+        TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
+            return gemm(c, fwd_desc(BT, 4 * C, C, ln2, prm<T>(c, 10, l, 4 * CC), fchg, GEMM_BIAS_GELU,
+                                    prm<T>(c, 11, l, 4 * C), nullptr, fch), s);
+        }));
+        TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
+            return gemm(c, fwd_desc(BT, C, 4 * C, fchg, prm<T>(c, 12, l, 4 * CC), res3, GEMM_BIAS_RESID,
+                                    prm<T>(c, 13, l, C), res2, nullptr), s);
+        }));
     }
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
     T* lnf = c->act<T>(p.lnf);
-    TRY(layernorm_fwd_launch<T>(lnf, c->act<float>(p.lnfm), c->act<float>(p.lnfr), resL, prm<T>(c, 14), prm<T>(c, 15),
-                                BT, C, s));
+    TRY(timed(c, GPT2_TP_LN_FWD, s, [&] {
+        return layernorm_fwd_launch<T>(lnf, c->act<float>(p.lnfm), c->act<float>(p.lnfr), resL, prm<T>(c, 14),
+                                       prm<T>(c, 15), BT, C, s);
+    }));
     T* logits = c->act<T>(p.logits);
-    const int ev = c->ev_n > 0 ? c->ev_i++ % c->ev_n : -1;
-    if (ev >= 0) TRY((int)hipEventRecord((hipEvent_t)c->ev_start[ev], s));
-    TRY(gemm(c, fwd_desc(BT, Vp, C, lnf, prm<T>(c, 0), logits, GEMM_STORE, nullptr, nullptr, nullptr), s));
-    if (ev >= 0) TRY((int)hipEventRecord((hipEvent_t)c->ev_end[ev], s));
+    TRY(timed(c, GPT2_TP_CLASSIFIER_FWD, s, [&] {
+        return gemm(c, fwd_desc(BT, Vp, C, lnf, prm<T>(c, 0), logits, GEMM_STORE, nullptr, nullptr, nullptr), s);
+    }));
     if (targets) {
         float* losses = c->act<float>(p.losses);
-        TRY(classifier_ce_launch<T>(logits, losses, targets, BT, V, Vp, c->flag(), s));
+        TRY(timed(c, GPT2_TP_CE, s,
+                  [&] { return classifier_ce_launch<T>(logits, losses, targets, BT, V, Vp, c->flag(), s); }));
         if (d_losses) TRY((int)hipMemcpyAsync(d_losses, losses, (size_t)BT * 4, hipMemcpyDeviceToDevice, s));
         if (d_mean) TRY(mean_launch(d_mean, losses, BT, s));
     }
@@ -355,13 +385,19 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     auto dqkv = [&](int l) { return c->act<T>(p.dqkv + (grouped ? (size_t)l * p.s_bt3c : 0)); };
     auto lp_out = [&](int l, int which) { return grouped ? dres_in(l, which) : (T*)nullptr; };
     float* work = c->work();
-    auto dw_now = [&](const GemmDesc& d) { return grouped ? 0 : gemm(c, d, s); };
+    auto dw_now = [&](const GemmDesc& d) {
+        return grouped ? 0 : timed(c, GPT2_TP_WEIGHT_GRAD, s, [&] { return gemm(c, d, s); });
+    };
     // classifier (tied weights): dlnf = alpha * dlogits wte; dwte += alpha * dlogits^T lnf
-    TRY(gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s));
+    TRY(timed(c, GPT2_TP_CLASSIFIER_DX, s, [&] {
+        return gemm(c, dx_desc(BT, C, Vp, logits, prm<T>(c, 0), dbtc, GEMM_STORE, nullptr, alpha), s);
+    }));
     TRY(dw_now(dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr)));
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
-    TRY(layernorm_bwd_launch<T>(dres, lp_out(L - 1, 0), grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
-                                c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s));
+    TRY(timed(c, GPT2_TP_LN_BWD, s, [&] {
+        return layernorm_bwd_launch<T>(dres, lp_out(L - 1, 0), grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
+                                       c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s);
+    }));
     for (int l = L - 1; l >= 0; l--) {
         const T* res = l == 0 ? c->act<T>(p.enc) : c->act_l<T>(p.res3, p.s_btc, l - 1);
         const T* ln1 = c->act_l<T>(p.ln1, p.s_btc, l);
@@ -373,33 +409,49 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
         const T* fchg = c->act_l<T>(p.fchg, p.s_bt4c, l);
         // fcproj (+ GELU backward fused into its input-gradient product)
         TRY(dw_now(dw_desc(BT, 4 * C, C, dres_in(l, 0), fchg, grd(c, 12, l, 4 * CC), 1.0f, grd(c, 13, l, C))));
-        TRY(gemm(c, dx_desc(BT, 4 * C, C, dres_in(l, 0), prm<T>(c, 12, l, 4 * CC), dbt4c(l), GEMM_GELU_BWD, fch, 1.0f),
-                 s));
+        TRY(timed(c, GPT2_TP_LAYER_DX, s, [&] {
+            return gemm(c, dx_desc(BT, 4 * C, C, dres_in(l, 0), prm<T>(c, 12, l, 4 * CC), dbt4c(l), GEMM_GELU_BWD, fch,
+                                   1.0f), s);
+        }));
         // fc
         TRY(dw_now(dw_desc(BT, C, 4 * C, dbt4c(l), ln2, grd(c, 10, l, 4 * CC), 1.0f, grd(c, 11, l, 4 * C))));
-        TRY(gemm(c, dx_desc(BT, C, 4 * C, dbt4c(l), prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(layernorm_bwd_launch<T>(dres, lp_out(l, 1), grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
-                                    prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
-                                    c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s));
+        TRY(timed(c, GPT2_TP_LAYER_DX, s, [&] {
+            return gemm(c, dx_desc(BT, C, 4 * C, dbt4c(l), prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s);
+        }));
+        TRY(timed(c, GPT2_TP_LN_BWD, s, [&] {
+            return layernorm_bwd_launch<T>(dres, lp_out(l, 1), grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
+                                           prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
+                                           c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s);
+        }));
         // attproj
         TRY(dw_now(dw_desc(BT, C, C, dres_in(l, 1), atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C))));
-        TRY(gemm(c, dx_desc(BT, C, C, dres_in(l, 1), prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
+        TRY(timed(c, GPT2_TP_LAYER_DX, s, [&] {
+            return gemm(c, dx_desc(BT, C, C, dres_in(l, 1), prm<T>(c, 6, l, CC), dbtc, GEMM_STORE, nullptr, 1.0f), s);
+        }));
         // attention
-        TRY(attention_bwd_launch<T>(dqkv(l), c->act<float>(p.delta), dbtc, atty, qkv,
-                                    c->act_l<float>(p.lse, p.s_lse, l), B, Tn, C, NH, s));
+        TRY(timed(c, GPT2_TP_ATTN_BWD, s, [&] {
+            return attention_bwd_launch<T>(dqkv(l), c->act<float>(p.delta), dbtc, atty, qkv,
+                                           c->act_l<float>(p.lse, p.s_lse, l), B, Tn, C, NH, s);
+        }));
         // qkv
         TRY(dw_now(dw_desc(BT, C, 3 * C, dqkv(l), ln1, grd(c, 4, l, 3 * CC), 1.0f, grd(c, 5, l, 3 * C))));
-        TRY(gemm(c, dx_desc(BT, C, 3 * C, dqkv(l), prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s));
-        TRY(layernorm_bwd_launch<T>(dres, l > 0 ? lp_out(l - 1, 0) : (T*)nullptr, grd(c, 2, l, C), grd(c, 3, l, C),
-                                    dbtc, res, prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
-                                    c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, work, s));
+        TRY(timed(c, GPT2_TP_LAYER_DX, s, [&] {
+            return gemm(c, dx_desc(BT, C, 3 * C, dqkv(l), prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s);
+        }));
+        TRY(timed(c, GPT2_TP_LN_BWD, s, [&] {
+            return layernorm_bwd_launch<T>(dres, l > 0 ? lp_out(l - 1, 0) : (T*)nullptr, grd(c, 2, l, C),
+                                           grd(c, 3, l, C), dbtc, res, prm<T>(c, 2, l, C),
+                                           c->act_l<float>(p.ln1m, p.s_bt, l), c->act_l<float>(p.ln1r, p.s_bt, l), BT,
+                                           C, 1, work, s);
+        }));
 
     }
     // every weight gradient of the step in one launch (running the classifier's
     // or half of the layers' beside the chain on a second stream was slower)
-    if (grouped) TRY(dw_group(c, 0, L, true, s));
+    if (grouped) TRY(timed(c, GPT2_TP_WEIGHT_GRAD, s, [&] { return dw_group(c, 0, L, true, s); }));
     // the encoder backward adds into wte's gradient after the classifier's
-    TRY(encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, work, s));
+    TRY(timed(c, GPT2_TP_ENCODER_BWD, s,
+              [&] { return encoder_bwd_launch(grd(c, 0), grd(c, 1), dres, c->act<int>(p.tok), B, Tn, C, work, s); }));
     return GPT2_OK;
 }
 
@@ -525,21 +577,21 @@ int gpt2_adamw_update(gpt2_ctx* c, float lr, float beta1, float beta2, float eps
     if (c->sr) {
         const uint32_t seed = xorshift_u32(&c->rng);
         const float c1 = 1.0f - powf(beta1, (float)t), c2 = 1.0f - powf(beta2, (float)t);
-        return hip_rc(adamw_sr_launch((bf16_t*)c->buf.params, (const float*)c->buf.grads, (float*)c->buf.adam_m,
-                                      (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps, weight_decay, seed,
-                                      s));
+        return hip_rc(timed(c, GPT2_TP_ADAMW, s, [&] {
+            return adamw_sr_launch((bf16_t*)c->buf.params, (const float*)c->buf.grads, (float*)c->buf.adam_m,
+                                   (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps, weight_decay, seed, s);
+        }));
     }
     const float c1 = (float)(1.0 - pow((double)beta1, t));
     const float c2 = (float)(1.0 - pow((double)beta2, t));
-    int e;
-    if (c->prec == GPT2_BF16)
-        e = adamw_launch<bf16_t>((bf16_t*)c->buf.params, (float*)c->buf.master, (const float*)c->buf.grads,
-                                 (float*)c->buf.adam_m, (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps,
-                                 weight_decay, s);
-    else
-        e = adamw_launch<float>((float*)c->buf.params, nullptr, (const float*)c->buf.grads, (float*)c->buf.adam_m,
-                                (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps, weight_decay, s);
-    return hip_rc(e);
+    return hip_rc(timed(c, GPT2_TP_ADAMW, s, [&] {
+        if (c->prec == GPT2_BF16)
+            return adamw_launch<bf16_t>((bf16_t*)c->buf.params, (float*)c->buf.master, (const float*)c->buf.grads,
+                                        (float*)c->buf.adam_m, (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2,
+                                        eps, weight_decay, s);
+        return adamw_launch<float>((float*)c->buf.params, nullptr, (const float*)c->buf.grads, (float*)c->buf.adam_m,
+                                   (float*)c->buf.adam_v, c->P, lr, beta1, beta2, c1, c2, eps, weight_decay, s);
+    }));
 }
 
 int gpt2_set_rng_state(gpt2_ctx* c, uint64_t state, uint64_t* old) {
@@ -576,13 +628,19 @@ int gpt2_act_tensor(gpt2_ctx* c, int which, void** d_ptr, size_t* count) {
     }
 }
 
-int gpt2_set_classifier_events(gpt2_ctx* c, void* const* d_start_events, void* const* d_end_events, int n) {
-    if (!c || n < 0 || (n > 0 && (!d_start_events || !d_end_events))) return GPT2_E_ARG;
-    c->ev_start = n > 0 ? d_start_events : nullptr;
-    c->ev_end = n > 0 ? d_end_events : nullptr;
-    c->ev_n = n;
-    c->ev_i = 0;
+int gpt2_set_timing_events(gpt2_ctx* c, int point, void* const* d_start_events, void* const* d_end_events, int n) {
+    if (!c || point < 0 || point >= GPT2_TP_COUNT || n < 0 || (n > 0 && (!d_start_events || !d_end_events)))
+        return GPT2_E_ARG;
+    gpt2_ctx::Hook& h = c->hooks[point];
+    h.start = n > 0 ? d_start_events : nullptr;
+    h.end = n > 0 ? d_end_events : nullptr;
+    h.n = n;
+    h.i = 0;
     return GPT2_OK;
+}
+
+int gpt2_set_classifier_events(gpt2_ctx* c, void* const* d_start_events, void* const* d_end_events, int n) {
+    return gpt2_set_timing_events(c, GPT2_TP_CLASSIFIER_FWD, d_start_events, d_end_events, n);
 }
 
 int gpt2_free(gpt2_ctx* c) {

@@ -11,86 +11,145 @@
 // (the final one of the forward) stores instead, so the buffer needs no
 // separate zeroing.
 //
-// One wave64 per row; the row lives in registers as 16-byte vectors (lane l
-// owns vectors l, l+64, ...), so x is read once.  Statistics are fp32 in both
-// precisions.  The parameter gradients are reduced deterministically: each
-// workgroup sums its rows in registers, combines its 4 waves through LDS in
-// wave order, writes one partial row, and a second kernel sums the partials
-// in workgroup order.
+// A row is spread over LPR lanes of a wave (32 for rows of up to 96 16-byte
+// vectors, so a 768-wide bf16 row is exactly 3 vectors per lane; 64 for
+// wider ones) and lives in registers, so x is read once.  Statistics are
+// fp32 in both precisions.  The parameter gradients are reduced
+// deterministically: each workgroup sums its rows in registers, combines
+// the two row groups of a wave and then its 8 waves through LDS in a fixed
+// order, writes one partial row, and a second kernel sums the partials in
+// workgroup order.
 #include "device.h"
 #include "kernels.h"
 
 namespace {
 
-// Backward workgroups take 2 rows per wave: 8 waves (16 rows) when a row
-// fits in at most 2 vectors per lane, else 4 waves (8 rows, and the workspace
-// is sized for this smaller count).  Fewer, larger workgroups leave fewer
-// per-workgroup partial sums for the finishing reduction to read.
-constexpr int ROWS_PER_BLOCK_BWD = 8;
-#ifndef LN_BWD_WAVES
-#define LN_BWD_WAVES 8
-#endif
-template <int NV> constexpr int ln_bwd_waves() { return NV <= 2 ? LN_BWD_WAVES : 4; }
+// sum over the LPR lanes of this row
+template <int LPR>
+DEV float row_sum(float v) {
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
 
-// NV: 16-byte vectors per lane, ceil(C / (64 * VEC)), fixed at launch so the
-// row buffers take only the registers C needs.
-template <typename T, int NV>
-__global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out, float* __restrict__ mean,
-                                                     float* __restrict__ rstd, const T* __restrict__ x,
-                                                     const T* __restrict__ w, const T* __restrict__ b,
-                                                     int N, int C) {
+// Forward: LPR lanes per row (half a wave while a row is at most 3 vectors
+// per lane, else a whole wave), so a wave holds 64 / LPR rows per step; the
+// reads of all STEPS steps of a wave are issued before any row is reduced.
+// NV: 16-byte vectors per lane, ceil(C / VEC / LPR); two passes over the
+// registers give the exact two-pass variance.
+constexpr int LNF_WAVES = 4, LNF_ROWS = 16;  // rows per workgroup
+
+template <typename T, int NV, int LPR>
+__global__ __launch_bounds__(64 * LNF_WAVES) void ln_fwd_kernel(T* __restrict__ out, float* __restrict__ mean,
+                                                              float* __restrict__ rstd, const T* __restrict__ x,
+                                                              const T* __restrict__ w, const T* __restrict__ b,
+                                                              int N, int C) {
     constexpr int VEC = VecT<T>::N;
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= N) return;
+    constexpr int RPS = 64 / LPR, STEPS = LNF_ROWS / LNF_WAVES / RPS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hl = lane % LPR, grp = lane / LPR;
     const int nvec = C / VEC;
-    const T* xr = x + (size_t)row * C;
-    float xv[NV][VEC];
-    float s = 0.f;
+    auto row_of = [&](int p) { return blockIdx.x * LNF_ROWS + RPS * (wave + LNF_WAVES * p) + grp; };
+    uint4 raw[STEPS][NV];
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int v = lane + 64 * i;
-        if (v < nvec) {
-            unpack16<T>(ld16(xr + v * VEC), xv[i]);
+    for (int p = 0; p < STEPS; p++) {
+        const int row = row_of(p);
+        const size_t base = (size_t)(row < N ? row : 0) * C;
 #pragma unroll
-            for (int e = 0; e < VEC; e++) s += xv[i][e];
+        for (int i = 0; i < NV; i++) {
+            const int v = hl + LPR * i;
+            raw[p][i] = ld16(x + base + (size_t)(v < nvec ? v : 0) * VEC);
         }
     }
-    const float m = wave_sum(s) / (float)C;
-    float q = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int v = lane + 64 * i;
-        if (v < nvec) {
+    for (int p = 0; p < STEPS; p++) {
+        const int row = row_of(p);
+        float xv[NV][VEC];
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const bool in = hl + LPR * i < nvec;
+            unpack16<T>(raw[p][i], xv[i]);
 #pragma unroll
             for (int e = 0; e < VEC; e++) {
-                const float d = xv[i][e] - m;
+                if (!in) xv[i][e] = 0.f;
+                s += xv[i][e];
+            }
+        }
+        const float m = row_sum<LPR>(s) / (float)C;
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const bool in = hl + LPR * i < nvec;
+#pragma unroll
+            for (int e = 0; e < VEC; e++) {
+                const float d = in ? xv[i][e] - m : 0.f;
                 q += d * d;
             }
         }
-    }
-    const float rs = 1.0f / sqrtf(wave_sum(q) / (float)C + 1e-5f);
-    T* o = out + (size_t)row * C;
+        const float rs = 1.0f / sqrtf(row_sum<LPR>(q) / (float)C + 1e-5f);
+        if (row < N) {
+            T* o = out + (size_t)row * C;
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int v = lane + 64 * i;
-        if (v < nvec) {
-            float wv[VEC], bv[VEC], y[VEC];
-            unpack16<T>(ld16(w + v * VEC), wv);
-            unpack16<T>(ld16(b + v * VEC), bv);
+            for (int i = 0; i < NV; i++) {
+                const int v = hl + LPR * i;
+                if (v < nvec) {
+                    float wv[VEC], bv[VEC], y[VEC];
+                    unpack16<T>(ld16(w + v * VEC), wv);
+                    unpack16<T>(ld16(b + v * VEC), bv);
 #pragma unroll
-            for (int e = 0; e < VEC; e++) y[e] = (xv[i][e] - m) * rs * wv[e] + bv[e];
-            st16(o + v * VEC, pack16<T>(y));
+                    for (int e = 0; e < VEC; e++) y[e] = (xv[i][e] - m) * rs * wv[e] + bv[e];
+                    st16(o + v * VEC, pack16<T>(y));
+                }
+            }
+            if (hl == 0) {
+                mean[row] = m;
+                rstd[row] = rs;
+            }
         }
-    }
-    if (lane == 0) {
-        mean[row] = m;
-        rstd[row] = rs;
     }
 }
 
+// Backward: LPR lanes per row -- half a wave for rows of up to 96 vectors
+// (a 768-wide bf16 row is exactly 3 vectors per lane), a whole wave for
+// wider ones.  A wave takes 4 rows, in steps of 64 / LPR rows at a
+// time; all reads of a step (x, dy and, when accumulating, the fp32
+// residual gradient) are issued together, one step ahead of the one being
+// computed.  NV: vectors per lane, ceil(C / VEC / LPR).
+constexpr int LNB_WAVES = 8;
+constexpr int LNB_ROWS = 32;  // rows per workgroup (4 per wave)
+
 template <typename T, int NV>
-__global__ __launch_bounds__(64 * ln_bwd_waves<NV>()) void ln_bwd_kernel(float* __restrict__ dres, T* __restrict__ dres_lp,
+struct LnRow {
+    static constexpr int VEC = VecT<T>::N;
+    uint4 x[NV], g[NV];
+    float4 r[NV][VEC / 4];
+};
+
+template <typename T, int NV, int LPR, bool WITH_R>
+DEV void ln_row_load(LnRow<T, NV>& d, const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ dres,
+                     int row, int N, int C, int hl, bool acc) {
+    constexpr int VEC = VecT<T>::N;
+    const int nvec = C / VEC;
+    const bool ok = row < N;
+    const size_t base = (size_t)(ok ? row : 0) * C;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        const int v = hl + LPR * i;
+        const bool in = ok && v < nvec;
+        const size_t o = base + (size_t)(in ? v : 0) * VEC;
+        d.x[i] = ld16(x + o);
+        d.g[i] = ld16(dy + o);
+        if constexpr (WITH_R) {
+#pragma unroll
+            for (int q = 0; q < VEC / 4; q++)
+                d.r[i][q] = acc ? *reinterpret_cast<const float4*>(dres + o + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+template <typename T, int NV, int LPR>
+__global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(float* __restrict__ dres, T* __restrict__ dres_lp,
                                                      float* __restrict__ partial, const T* __restrict__ dy,
                                                      const T* __restrict__ x, const T* __restrict__ w,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -98,79 +157,110 @@ __global__ __launch_bounds__(64 * ln_bwd_waves<NV>()) void ln_bwd_kernel(float* 
     constexpr int VEC = VecT<T>::N;
     __shared__ float red[2 * 2048];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int RPS = 64 / LPR, STEPS = LNB_ROWS / LNB_WAVES / RPS;  // rows per step, steps per wave
+    const int hl = lane % LPR, half = lane / LPR;
     const int nvec = C / VEC;
+    const bool acc = accumulate != 0;
     float dw_acc[NV][VEC], db_acc[NV][VEC], wv[NV][VEC];
 #pragma unroll
     for (int i = 0; i < NV; i++) {
-        const int v = lane + 64 * i;
+        const int v = hl + LPR * i;
 #pragma unroll
         for (int e = 0; e < VEC; e++) { dw_acc[i][e] = 0.f; db_acc[i][e] = 0.f; wv[i][e] = 0.f; }
         if (v < nvec) unpack16<T>(ld16(w + v * VEC), wv[i]);
     }
-    constexpr int NWV = ln_bwd_waves<NV>();
-    const int r0 = blockIdx.x * 2 * NWV;
-    const int r1 = min(r0 + 2 * NWV, N);
-    for (int row = r0 + wave; row < r1; row += NWV) {
-        const float m = mean[row], rs = rstd[row];
-        const T* xr = x + (size_t)row * C;
-        const T* gr = dy + (size_t)row * C;
+    // row of step p of this wave and lane group
+    const int r0 = blockIdx.x * LNB_ROWS;
+    auto row_of = [&](int p) { return r0 + RPS * (wave + LNB_WAVES * p) + half; };
+    // Wide rows (a whole wave per row) have no room for a second set of row
+    // registers: each step loads its own, and the residual gradient is read
+    // after the row sums.
+    constexpr bool PREF = LPR == 32;
+    LnRow<T, NV> cur, nxt;
+    ln_row_load<T, NV, LPR, PREF>(cur, x, dy, dres, row_of(0), N, C, hl, acc);
+#pragma unroll(PREF ? STEPS : 1)
+    for (int p = 0; p < STEPS; p++) {
+        if (PREF && p + 1 < STEPS) ln_row_load<T, NV, LPR, PREF>(nxt, x, dy, dres, row_of(p + 1), N, C, hl, acc);
+        if (!PREF && p > 0) ln_row_load<T, NV, LPR, PREF>(cur, x, dy, dres, row_of(p), N, C, hl, acc);
+        const int row = row_of(p);
+        const bool ok = row < N;
+        const float m = ok ? mean[row] : 0.f, rs = ok ? rstd[row] : 0.f;
         float nv[NV][VEC], gv[NV][VEC];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int v = lane + 64 * i;
-            if (v < nvec) {
-                float xv[VEC];
-                unpack16<T>(ld16(xr + v * VEC), xv);
-                unpack16<T>(ld16(gr + v * VEC), gv[i]);
+            const bool in = ok && hl + LPR * i < nvec;
+            float xv[VEC];
+            unpack16<T>(cur.x[i], xv);
+            unpack16<T>(cur.g[i], gv[i]);
 #pragma unroll
-                for (int e = 0; e < VEC; e++) {
-                    nv[i][e] = (xv[e] - m) * rs;
-                    const float dn = wv[i][e] * gv[i][e];
-                    s1 += dn;
-                    s2 += dn * nv[i][e];
-                }
+            for (int e = 0; e < VEC; e++) {
+                if (!in) gv[i][e] = 0.f;
+                nv[i][e] = in ? (xv[e] - m) * rs : 0.f;
+                const float dn = wv[i][e] * gv[i][e];
+                s1 += dn;
+                s2 += dn * nv[i][e];
             }
         }
-        const float mdn = wave_sum(s1) / (float)C;
-        const float mdnn = wave_sum(s2) / (float)C;
-        float* dr = dres + (size_t)row * C;
+        const float mdn = row_sum<LPR>(s1) / (float)C;
+        const float mdnn = row_sum<LPR>(s2) / (float)C;
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int v = lane + 64 * i;
-            if (v < nvec) {
-                float o[VEC];
-                if (accumulate) {
-                    load4<float>(dr + v * VEC, o);
-                    if constexpr (VEC == 8) load4<float>(dr + v * VEC + 4, o + 4);
-                } else {
+            const int v = hl + LPR * i;
+            float o[VEC];
+            if constexpr (PREF) {
 #pragma unroll
-                    for (int e = 0; e < VEC; e++) o[e] = 0.f;
+                for (int q = 0; q < VEC / 4; q++) {
+                    o[4 * q] = cur.r[i][q].x; o[4 * q + 1] = cur.r[i][q].y;
+                    o[4 * q + 2] = cur.r[i][q].z; o[4 * q + 3] = cur.r[i][q].w;
                 }
+            } else {
+                const size_t ro = (size_t)(ok ? row : 0) * C + (size_t)(v < nvec ? v : 0) * VEC;
 #pragma unroll
-                for (int e = 0; e < VEC; e++) {
-                    const float dn = wv[i][e] * gv[i][e];
-                    o[e] += rs * (dn - mdn - nv[i][e] * mdnn);
-                    dw_acc[i][e] += nv[i][e] * gv[i][e];
-                    db_acc[i][e] += gv[i][e];
+                for (int e = 0; e < VEC; e++) o[e] = 0.f;
+                if (acc) {
+                    load4<float>(dres + ro, o);
+                    if constexpr (VEC == 8) load4<float>(dres + ro + 4, o + 4);
                 }
-                store4<float>(dr + v * VEC, o);
-                if constexpr (VEC == 8) store4<float>(dr + v * VEC + 4, o + 4);
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; e++) {
+                const float dn = wv[i][e] * gv[i][e];
+                o[e] += rs * (dn - mdn - nv[i][e] * mdnn);
+                dw_acc[i][e] += nv[i][e] * gv[i][e];
+                db_acc[i][e] += gv[i][e];
+            }
+            if (ok && v < nvec) {
+                float* dr = dres + (size_t)row * C + v * VEC;
+                store4<float>(dr, o);
+                if constexpr (VEC == 8) store4<float>(dr + 4, o + 4);
                 if (dres_lp != nullptr) st16(dres_lp + (size_t)row * C + v * VEC, pack16<T>(o));
             }
         }
+        if (PREF && p + 1 < STEPS) cur = nxt;
     }
-    // combine the waves in order 0, 1, 2, ...
-    for (int wv_turn = 0; wv_turn < NWV; wv_turn++) {
-        if (wave == wv_turn) {
+    // the two halves of the wave (same columns, different rows; half 0's sum
+    // first in both), then the waves in order 0, 1, 2, ... through LDS
+    if constexpr (LPR == 32) {
+#pragma unroll
+        for (int i = 0; i < NV; i++)
+#pragma unroll
+            for (int e = 0; e < VEC; e++) {
+                const float ow = __shfl_xor(dw_acc[i][e], 32, 64), ob = __shfl_xor(db_acc[i][e], 32, 64);
+                dw_acc[i][e] = half == 0 ? dw_acc[i][e] + ow : ow + dw_acc[i][e];
+                db_acc[i][e] = half == 0 ? db_acc[i][e] + ob : ob + db_acc[i][e];
+            }
+    }
+    for (int turn = 0; turn < LNB_WAVES; turn++) {
+        if (wave == turn && half == 0) {
 #pragma unroll
             for (int i = 0; i < NV; i++) {
-                const int v = lane + 64 * i;
+                const int v = hl + LPR * i;
                 if (v < nvec) {
 #pragma unroll
                     for (int e = 0; e < VEC; e++) {
                         const int c = v * VEC + e;
-                        if (wv_turn == 0) {
+                        if (turn == 0) {
                             red[c] = dw_acc[i][e];
                             red[2048 + c] = db_acc[i][e];
                         } else {
@@ -183,10 +273,10 @@ __global__ __launch_bounds__(64 * ln_bwd_waves<NV>()) void ln_bwd_kernel(float* 
         }
         __syncthreads();
     }
-    float* p = partial + (size_t)blockIdx.x * 2 * C;
-    for (int c = threadIdx.x; c < C; c += 64 * NWV) {
-        p[c] = red[c];
-        p[C + c] = red[2048 + c];
+    float* pp = partial + (size_t)blockIdx.x * 2 * C;
+    for (int c = threadIdx.x; c < C; c += 64 * LNB_WAVES) {
+        pp[c] = red[c];
+        pp[C + c] = red[2048 + c];
     }
 }
 
@@ -228,41 +318,49 @@ __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(float*
 
 }  // namespace
 
-template <typename T, int NV>
+template <typename T, int NV, int LPR = 32>
 void ln_fwd_nv(T* out, float* mean, float* rstd, const T* x, const T* w, const T* b, int N, int C, hipStream_t s) {
-    hipLaunchKernelGGL((ln_fwd_kernel<T, NV>), dim3((N + 3) / 4), dim3(256), 0, s, out, mean, rstd, x, w, b, N, C);
+    hipLaunchKernelGGL((ln_fwd_kernel<T, NV, LPR>), dim3((N + LNF_ROWS - 1) / LNF_ROWS), dim3(64 * LNF_WAVES), 0, s, out,
+                       mean, rstd, x, w, b, N, C);
 }
 
 template <typename T>
 int layernorm_fwd_launch(T* out, float* mean, float* rstd, const T* x, const T* w, const T* b,
                          int N, int C, hipStream_t s) {
     if (N <= 0) return 0;
-    const int nv = (C / VecT<T>::N + 63) / 64;
-    switch (nv) {
-        case 1: ln_fwd_nv<T, 1>(out, mean, rstd, x, w, b, N, C, s); break;
-        case 2: ln_fwd_nv<T, 2>(out, mean, rstd, x, w, b, N, C, s); break;
-        case 3: ln_fwd_nv<T, 3>(out, mean, rstd, x, w, b, N, C, s); break;
-        case 4: ln_fwd_nv<T, 4>(out, mean, rstd, x, w, b, N, C, s); break;
-        default:
-            if constexpr (sizeof(T) == 4) {
-                if (nv <= 8) { ln_fwd_nv<T, 8>(out, mean, rstd, x, w, b, N, C, s); break; }
-            }
-            return (int)hipErrorInvalidValue;
+    const int nvec = C / VecT<T>::N;
+    const int nv32 = (nvec + 31) / 32, nv64 = (nvec + 63) / 64;
+    if (nv32 <= 3) {
+        switch (nv32) {
+            case 1: ln_fwd_nv<T, 1>(out, mean, rstd, x, w, b, N, C, s); break;
+            case 2: ln_fwd_nv<T, 2>(out, mean, rstd, x, w, b, N, C, s); break;
+            default: ln_fwd_nv<T, 3>(out, mean, rstd, x, w, b, N, C, s); break;
+        }
+    } else {
+        switch (nv64) {
+            case 2: ln_fwd_nv<T, 2, 64>(out, mean, rstd, x, w, b, N, C, s); break;
+            case 3: ln_fwd_nv<T, 3, 64>(out, mean, rstd, x, w, b, N, C, s); break;
+            case 4: ln_fwd_nv<T, 4, 64>(out, mean, rstd, x, w, b, N, C, s); break;
+            default:
+                if constexpr (sizeof(T) == 4) {
+                    if (nv64 <= 8) { ln_fwd_nv<T, 8, 64>(out, mean, rstd, x, w, b, N, C, s); break; }
+                }
+                return (int)hipErrorInvalidValue;
+        }
     }
     return (int)hipGetLastError();
 }
 
 size_t layernorm_bwd_workspace_bytes(int N, int C) {
-    return (size_t)((N + ROWS_PER_BLOCK_BWD - 1) / ROWS_PER_BLOCK_BWD) * 2 * C * sizeof(float);
+    return (size_t)((N + LNB_ROWS - 1) / LNB_ROWS) * 2 * C * sizeof(float);
 }
 
-template <typename T, int NV>
+template <typename T, int NV, int LPR = 32>
 int ln_bwd_nv(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean, const float* rstd,
               int N, int C, int accumulate, float* partial, hipStream_t s) {
-    constexpr int NWV = ln_bwd_waves<NV>();
-    const int blocks = (N + 2 * NWV - 1) / (2 * NWV);
-    hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(blocks), dim3(64 * NWV), 0, s, dres, dres_lp, partial, dy, x, w,
-                       mean, rstd, N, C, accumulate);
+    const int blocks = (N + LNB_ROWS - 1) / LNB_ROWS;
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NV, LPR>), dim3(blocks), dim3(64 * LNB_WAVES), 0, s, dres, dres_lp, partial, dy, x,
+                       w, mean, rstd, N, C, accumulate);
     return blocks;
 }
 
@@ -271,21 +369,30 @@ int layernorm_bwd_launch(float* dres, T* dres_lp, float* dw, float* db, const T*
                          const T* w, const float* mean, const float* rstd, int N, int C,
                          int accumulate, float* partial, hipStream_t s) {
     if (N <= 0) return 0;
-    const int nv = (C / VecT<T>::N + 63) / 64;
+    // half a wave per row while that takes at most 3 vectors per lane, else a wave
+    const int nvec = C / VecT<T>::N;
+    const int nv32 = (nvec + 31) / 32, nv64 = (nvec + 63) / 64;
     int blocks = 0;
-    switch (nv) {
-        case 1: blocks = ln_bwd_nv<T, 1>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-        case 2: blocks = ln_bwd_nv<T, 2>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-        case 3: blocks = ln_bwd_nv<T, 3>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-        case 4: blocks = ln_bwd_nv<T, 4>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-        default:
-            if constexpr (sizeof(T) == 4) {
-                if (nv <= 8) {
-                    blocks = ln_bwd_nv<T, 8>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s);
-                    break;
+    if (nv32 <= 3) {
+        switch (nv32) {
+            case 1: blocks = ln_bwd_nv<T, 1>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 2: blocks = ln_bwd_nv<T, 2>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            default: blocks = ln_bwd_nv<T, 3>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+        }
+    } else {
+        switch (nv64) {
+            case 2: blocks = ln_bwd_nv<T, 2, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 3: blocks = ln_bwd_nv<T, 3, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 4: blocks = ln_bwd_nv<T, 4, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            default:
+                if constexpr (sizeof(T) == 4) {
+                    if (nv64 <= 8) {
+                        blocks = ln_bwd_nv<T, 8, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s);
+                        break;
+                    }
                 }
-            }
-            return (int)hipErrorInvalidValue;
+                return (int)hipErrorInvalidValue;
+        }
     }
     hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + FIN_COLS - 1) / FIN_COLS), dim3(FIN_COLS * FIN_PH), 0, s,
                        dw, db, partial, C, blocks);

@@ -47,10 +47,14 @@ GemmDesc bwd_dw_desc(const void* dy, const void* x, float* dw, float* db, int M,
 }
 }  // namespace
 
+// bf16 weight gradients run as the step runs them: the grouped weight-gradient
+// launch (one product, whole contraction per tile, no workspace); fp32 ones
+// through the K-split products
 extern "C" size_t gpt2_linear_backward_workspace(int precision, int M, int N, int K) {
     const int esz = precision == GPT2_BF16 ? 2 : 4;
     const size_t a = gemm_workspace_bytes(bwd_dx_desc(nullptr, nullptr, nullptr, M, N, K, 1.f), esz, 256);
-    const size_t b = gemm_workspace_bytes(bwd_dw_desc(nullptr, nullptr, nullptr, nullptr, M, N, K, 1.f), esz, 256);
+    const size_t b = esz == 2 ? 0 : gemm_workspace_bytes(bwd_dw_desc(nullptr, nullptr, nullptr, nullptr, M, N, K, 1.f),
+                                                         esz, 256);
     return a > b ? a : b;
 }
 
@@ -71,7 +75,12 @@ extern "C" int gpt2_linear_backward(int precision, const void* dy, const void* x
         if (need > 0 && (work == nullptr || work_bytes < need)) return GPT2_E_ARG;
         if (gemm_launch(d, esz, (float*)work, work_bytes, 256, s) != 0) return GPT2_E_HIP;
     }
-    if (dw) {
+    if (dw && esz == 2) {
+        GemmGroupItem it = {};
+        it.A = dy; it.lda = N; it.B = x; it.ldb = K; it.C = dw; it.ldc = K; it.dbias = db;
+        it.M = N; it.N = K; it.K = M; it.count = 1; it.alpha = alpha;
+        if (gemm_dw_group_launch(&it, 1, s) != 0) return GPT2_E_HIP;
+    } else if (dw) {
         const GemmDesc d = bwd_dw_desc(dy, x, dw, db, M, N, K, alpha);
         const size_t need = gemm_workspace_bytes(d, esz, 256);
         if (need > 0 && (work == nullptr || work_bytes < need)) return GPT2_E_ARG;

@@ -134,8 +134,8 @@ class GPT2:
         if dtype is None:
             if which == B.GPT2_T_DRESIDUAL:
                 dtype = torch.float32
-            else:
-                dtype = torch.bfloat16 if self.precision == B.GPT2_BF16 else torch.float32
+            else:  # bf16 activations in both bf16 modes (with and without master weights)
+                dtype = torch.float32 if self.precision == B.GPT2_FP32 else torch.bfloat16
         base = self.bufs["acts"]
         ofs = ptr - base.data_ptr()
         es = torch.tensor([], dtype=dtype).element_size()
