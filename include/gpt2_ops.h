@@ -62,6 +62,20 @@ int gpt2_attention_backward(int precision, const void* d_dout, const void* d_qkv
                             const float* d_lse, void* d_dqkv, float* d_delta, int B, int T, int C, int NH,
                             void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results as gpt2_attention_backward, with the delta array taken
+ * from a fixed device array inside the library (one per GPU, 4 MiB, held until
+ * the process ends) instead of a caller workspace.  No allocation of any kind.
+ * Runs on the current device (hip_stream must belong to it); the first call on
+ * a device looks the array's address up.  B*NH*T may be at most 1048576
+ * (GPT2_E_SHAPE otherwise).  Every call on one GPU shares that array: calls
+ * that overlap on one GPU (other streams, other threads) race and give wrong
+ * gradients.  Other arguments and errors as gpt2_attention_backward. */
+int gpt2_attention_backward_noalloc(int precision, const void* d_dout, const void* d_qkv, const void* d_out,
+                                    const float* d_lse, void* d_dqkv, int B, int T, int C, int NH,
+                                    void* hip_stream);
+
 /* POPCORNBENCH l12_default_gpt trajectory page, the problem statement (a
  * Linear layer followed by tanh-form GELU and a softmax over dim 1), in fp32:
  *   Y[m, :] = softmax_n( GELU_tanh( sum_k X[m,k] W[n,k] + b[n] ) )

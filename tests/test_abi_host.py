@@ -114,3 +114,13 @@ def test_null_context_calls_fail_cleanly():
     assert L.gpt2_zero_grad(None, None) == B.GPT2_E_ARG
     assert L.gpt2_adamw_update(None, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == B.GPT2_E_ARG
     assert B.strerror(B.GPT2_E_TOKEN).startswith("token")
+
+
+def test_noalloc_attention_backward_rejects_without_device_work():
+    from transformer_lm_step_amd import binding as B
+    L = B.lib()
+    # B*NH*T = 1048577 exceeds the library's 1048576-row delta array
+    assert L.gpt2_attention_backward_noalloc(1, 256, 256, 256, 256, 256, 1, 1048577, 64, 1, None) == B.GPT2_E_SHAPE
+    assert L.gpt2_attention_backward_noalloc(1, 256, 256, 256, 256, 256, 1, 16, 96, 2, None) == B.GPT2_E_SHAPE
+    assert L.gpt2_attention_backward_noalloc(1, None, 256, 256, 256, 256, 1, 16, 64, 1, None) == B.GPT2_E_ARG
+    assert L.gpt2_attention_backward_noalloc(1, 264, 256, 256, 256, 256, 1, 16, 64, 1, None) == B.GPT2_E_ALIGN

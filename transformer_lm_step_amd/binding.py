@@ -30,6 +30,7 @@ EXPORTED = (
     "gpt2_backward", "gpt2_adamw_update", "gpt2_check_device_error", "gpt2_act_tensor",
     "gpt2_set_classifier_events", "gpt2_set_timing_events", "gpt2_set_rng_state", "gpt2_sample", "gpt2_generate", "gpt2_checkpoint_header", "gpt2_checkpoint_read", "gpt2_free", "gpt2_strerror", "gpt2_linear_forward", "gpt2_linear_backward",
     "gpt2_linear_backward_workspace", "gpt2_attention_forward", "gpt2_attention_backward",
+    "gpt2_attention_backward_noalloc",
     "fused_linear_gelu_softmax_f32", "fused_linear_gelu_softmax_f32_workspace",
 )
 
@@ -86,6 +87,7 @@ def _load():
         "gpt2_linear_backward_workspace": (z, [i, i, i, i]),
         "gpt2_attention_forward": (i, [i, vp, vp, vp, i, i, i, i, vp]),
         "gpt2_attention_backward": (i, [i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]),
+        "gpt2_attention_backward_noalloc": (i, [i, vp, vp, vp, vp, vp, i, i, i, i, vp]),
         "fused_linear_gelu_softmax_f32": (i, [vp, vp, vp, vp, i, i, i, vp, z, vp]),
         "fused_linear_gelu_softmax_f32_workspace": (z, [i, i]),
     }
@@ -256,6 +258,12 @@ def gpt2_attention_backward(precision: int, d_dout: int, d_qkv: int, d_out: int,
                             d_delta: int, B: int, T: int, C: int, NH: int, stream: int):
     _check(_lib.gpt2_attention_backward(precision, d_dout, d_qkv, d_out, d_lse, d_dqkv, d_delta, B, T, C, NH,
                                         stream or None), "gpt2_attention_backward")
+
+
+def gpt2_attention_backward_noalloc(precision: int, d_dout: int, d_qkv: int, d_out: int, d_lse: int, d_dqkv: int,
+                                    B: int, T: int, C: int, NH: int, stream: int):
+    _check(_lib.gpt2_attention_backward_noalloc(precision, d_dout, d_qkv, d_out, d_lse, d_dqkv, B, T, C, NH,
+                                                stream or None), "gpt2_attention_backward_noalloc")
 
 
 def gpt2_linear_backward_workspace(precision: int, M: int, N: int, K: int) -> int:

@@ -2,6 +2,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gpt2.h"
 #include "gpt2_ops.h"
 #include "kernels.h"
@@ -120,6 +122,56 @@ extern "C" int gpt2_attention_backward(int precision, const void* dout, const vo
     if (e != GPT2_OK) return e;
     if (!dout || !qkv || !out || !lse || !dqkv || !delta) return GPT2_E_ARG;
     if (!al(dout) || !al(qkv) || !al(out) || !al(lse) || !al(dqkv) || !al(delta)) return GPT2_E_ALIGN;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    const int r = precision == GPT2_BF16
+                      ? attention_bwd_launch<bf16_t>((bf16_t*)dqkv, delta, (const bf16_t*)dout, (const bf16_t*)out,
+                                                     (const bf16_t*)qkv, lse, B, T, C, NH, s)
+                      : attention_bwd_launch<float>((float*)dqkv, delta, (const float*)dout, (const float*)out,
+                                                    (const float*)qkv, lse, B, T, C, NH, s);
+    return r == 0 ? GPT2_OK : GPT2_E_HIP;
+}
+
+// ------------------------------------------------ allocation-free variant ---
+// The attention backward's only scratch is the per-row delta array (B*NH*T
+// fp32).  gpt2_attention_backward_noalloc keeps it in this fixed device array
+// instead of a caller workspace: one copy per GPU, alive until the process
+// ends, shared by every call on that GPU.
+constexpr long kNoAllocDeltaMax = 1L << 20;  // fp32 elements: 4 MiB
+static __device__ __align__(256) float scratch[kNoAllocDeltaMax];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices];  // device address of scratch, per device
+
+// The device address of the current device's copy of scratch (looked up on
+// the first call on that device).  In host code the array's own name is not
+// a device address, so kernels get this pointer instead.
+int scratch_address(float** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GPT2_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GPT2_E_HIP;
+        g_scratch_dev[dev] = (float*)p;
+    }
+    *out = g_scratch_dev[dev];
+    return GPT2_OK;
+}
+}  // namespace
+
+extern "C" int gpt2_attention_backward_noalloc(int precision, const void* dout, const void* qkv, const void* out,
+                                               const float* lse, void* dqkv, int B, int T, int C, int NH,
+                                               void* hip_stream) {
+    const int e = attn_args(precision, B, T, C, NH);
+    if (e != GPT2_OK) return e;
+    if ((long)B * NH * T > kNoAllocDeltaMax) return GPT2_E_SHAPE;
+    if (!dout || !qkv || !out || !lse || !dqkv) return GPT2_E_ARG;
+    if (!al(dout) || !al(qkv) || !al(out) || !al(lse) || !al(dqkv)) return GPT2_E_ALIGN;
+    float* delta = nullptr;
+    const int a = scratch_address(&delta);
+    if (a != GPT2_OK) return a;
     const hipStream_t s = (hipStream_t)hip_stream;
     const int r = precision == GPT2_BF16
                       ? attention_bwd_launch<bf16_t>((bf16_t*)dqkv, delta, (const bf16_t*)dout, (const bf16_t*)out,
