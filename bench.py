@@ -321,6 +321,9 @@ def main():
                     help="GPT-2 size of the training step (124M is the headline workload)")
     ap.add_argument("--sr", action="store_true",
                     help="train without fp32 master weights (bf16 parameters, stochastic rounding in AdamW)")
+    ap.add_argument("--profile-summary", nargs="+", metavar="DIR",
+                    help="print markdown tables from rocprofv3 output folders of this bench (kernel stats of a "
+                         "--kernel-trace --stats run; per-kernel means of --pmc runs) instead of running")
     ap.add_argument("--workload", choices=("gpt2", "c2", "fused", "generate"), default="gpt2",
                     help="gpt2: the GPT-2 training step (default); c2: GPT-2 124M fp32 at B=4 T=64; "
                          "fused: the standalone Linear+GELU+softmax op; generate: the page's generation loop")
@@ -331,6 +334,9 @@ def main():
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the data-parallel multi-GPU path is not implemented.", file=sys.stderr)
         sys.exit(2)
+    if args.profile_summary:
+        profile_summary(args.profile_summary)
+        return
     if args.traffic_probe:
         traffic_probe()
         return
@@ -365,6 +371,117 @@ FAMILIES = [  # (name, timing point, bound)
     ("token/position embedding backward", "ENCODER_BWD", "hbm"),
     ("AdamW", "ADAMW", "hbm"),
 ]
+
+
+def _short_kernel_name(name):
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "").strip()
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):  # cut the argument list: the first "(" outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    return n[:cut]
+
+
+def _find(folder, suffix):
+    hits = []
+    for root, _, files in os.walk(folder):
+        hits += [os.path.join(root, f) for f in files if f.endswith(suffix)]
+    return sorted(hits)
+
+
+def profile_summary(folders):
+    """Markdown tables from rocprofv3 output folders of this bench.
+
+    Kernel statistics (--kernel-trace --stats): per kernel, per optimizer step
+    (the step count is the number of AdamW launches in the run).  Counter runs
+    (--pmc over --traffic-probe): the per-dispatch mean of each counter per
+    kernel, plus derived columns: HBM MB per dispatch from FETCH_SIZE and
+    WRITE_SIZE (KiB, each scaled by what it reads for the probe's 1 GiB device
+    copies) and, with a kernel-statistics folder among the arguments, GB/s
+    over that kernel's average duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
+    / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); dependency wait =
+    SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; LDS conflict = SQ_LDS_BANK_CONFLICT /
+    SQ_LDS_IDX_ACTIVE."""
+    import csv
+    avg_us = {}
+    counters = {}  # kernel -> {counter: (sum, n)}
+    scale = {}
+    for folder in folders:
+        for path in _find(folder, "kernel_stats.csv"):
+            rows = list(csv.DictReader(open(path)))
+            steps = sum(int(r["Calls"]) for r in rows if "adamw" in r["Name"])
+            tot = sum(float(r["TotalDurationNs"]) for r in rows)
+            print(f"### {os.path.relpath(path)}: {steps} optimizer steps, {tot / max(steps, 1) / 1e6:.3f} ms of "
+                  "kernel time per step\n")
+            print("| kernel | calls | avg us | per step ms | share |\n|---|---|---|---|---|")
+            for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+                t = float(r["TotalDurationNs"])
+                name = _short_kernel_name(r["Name"])
+                avg_us[name] = float(r["AverageNs"]) / 1e3
+                print(f"| `{name}` | {r['Calls']} | {avg_us[name]:.1f} | "
+                      f"{t / max(steps, 1) / 1e6:.3f} | {100 * t / tot:.2f}% |")
+            print()
+        for path in _find(folder, "counter_collection.csv"):
+            per = {}  # (dispatch, kernel) -> {counter: value}
+            for r in csv.DictReader(open(path)):
+                d = per.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            # the traffic probe's first three device copies move 1 GiB each
+            copies = [d for (i, k), d in sorted(per.items()) if "copyBuffer" in k][:3]
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                vals = [d[c] for d in copies if c in d]
+                if len(vals) == 3:
+                    scale[c] = (1 << 20) / float(np.mean(vals))
+            for (i, k), d in per.items():
+                a = counters.setdefault(_short_kernel_name(k), {})
+                for c, v in d.items():
+                    s, n = a.get(c, (0.0, 0))
+                    a[c] = (s + v, n + 1)
+    if not counters:
+        return
+    mean = {k: {c: s / n for c, (s, n) in a.items()} for k, a in counters.items()}
+    names = sorted(k for k in mean if "copyBuffer" not in k and "at::native" not in k)
+    if scale:
+        print("### HBM traffic per dispatch" + "".join(f"; {c} x {s:.3f}" for c, s in scale.items())
+              + " (1 GiB copy)\n")
+        print("| kernel | fetched MB | written MB | total MB | avg us | GB/s | of 8 TB/s |\n|---|---|---|---|---|---|---|")
+        for k in names:
+            m = mean[k]
+            if "FETCH_SIZE" not in m and "WRITE_SIZE" not in m:
+                continue
+            f = m.get("FETCH_SIZE", 0.0) * scale.get("FETCH_SIZE", 1.0) * 1024 / 1e6
+            w = m.get("WRITE_SIZE", 0.0) * scale.get("WRITE_SIZE", 1.0) * 1024 / 1e6
+            us = avg_us.get(k)
+            rate = (f + w) / us * 1e3 if us else None  # MB per us is TB/s
+            print(f"| `{k}` | {f:,.1f} | {w:,.1f} | {f + w:,.1f} | " + (f"{us:.1f} | {rate:,.0f} | {rate / PEAK_HBM_GBS:.3f} |"
+                                                                        if us else "- | - | - |"))
+        print()
+    busy_cols = [c for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT")
+                 if any(c in mean[k] for k in names)]
+    if busy_cols:
+        print("### Issue counters per dispatch\n")
+        raw = sorted({c for k in names for c in mean[k] if c not in ("FETCH_SIZE", "WRITE_SIZE")})
+        head = ["kernel"] + raw + ["MFMA busy", "dependency wait", "LDS conflict"]
+        print("| " + " | ".join(head) + " |\n|" + "---|" * len(head))
+        for k in names:
+            m = mean[k]
+            if not any(c in m for c in raw):
+                continue
+            cells = [f"`{k}`"] + [f"{m[c]:,.0f}" if c in m else "-" for c in raw]
+            g_act = m.get("GRBM_GUI_ACTIVE", 0.0)
+            mb = m.get("SQ_VALU_MFMA_BUSY_CYCLES")
+            cells.append(f"{mb / (g_act / 8 * 1024):.3f}" if mb is not None and g_act else "-")
+            cells.append(f"{m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.3f}"
+                         if m.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in m else "-")
+            cells.append(f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.3f}"
+                         if m.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in m else "-")
+            print("| " + " | ".join(cells) + " |")
+        print()
 
 
 def launch_work(cfg, B, T, esz, grouped, sr, n_unique):
