@@ -46,35 +46,58 @@ __global__ void encoder_fwd_kernel(T* __restrict__ out, int* __restrict__ tok_co
 // order); within a block, all deterministic:
 //  1. the keys (id << shift | position) are sorted by rank (enc_rank_kernel):
 //     equal ids end up adjacent, in increasing position order;
-//  2. one wave per chunk of 16 sorted entries sums each run of equal ids in
-//     order.  A run that neither continues from the previous chunk nor into the
-//     next one is complete and is added into dwte by that wave; otherwise the
-//     piece goes to workspace (a run continuing from the previous chunk is a
-//     "head" piece, one that starts here and continues is a "tail" piece);
-//  3. for every tail piece, one wave adds the head pieces of the following
-//     chunks that continue the run, in chunk order, and adds the total into
-//     dwte.
+//  2. one workgroup per chunk of 16 sorted entries sums each run of equal ids
+//     in order.  A run that neither continues from the previous chunk nor into
+//     the next one is complete and is added into dwte by that workgroup;
+//     otherwise the piece goes to workspace (a run continuing from the
+//     previous chunk is a "head" piece, one that starts here and continues is
+//     a "tail" piece);
+//  3. for every tail piece, one workgroup adds the head pieces of the
+//     following chunks that continue the run, in chunk order, and adds the
+//     total into dwte.
+// Rows are split over the threads by float4 column, and each thread requests
+// every row it needs (up to 16) before adding any: a chunk costs one round
+// trip to memory, not one per entry.  The loads are unconditional (a skipped
+// entry reads a row that another load of the same thread reads anyway), since
+// a load under a branch is waited for before the branch closes.
 constexpr int ENC_CHUNK = 16;
 constexpr int ENC_SORT_MAX = 16384;
 
 // Keys (id << shift | position) are distinct, so a key's place in sorted
 // order is the number of keys below it.  Each workgroup stages all keys in LDS
 // and ranks 64 of them: lane l of wave w counts the keys below key
-// 64 * blockIdx.x + l among the w-th quarter of the keys (every lane of a wave
-// reads the same LDS words), and the four partial counts are added.
-__global__ __launch_bounds__(256) void enc_rank_kernel(unsigned* __restrict__ sorted, const int* __restrict__ tok,
-                                                       int BT, int shift) {
+// 64 * blockIdx.x + l among the w-th sixteenth of the keys (every lane of a
+// wave reads the same LDS words), and the 16 partial counts are added.
+constexpr int ENC_RANK_WAVES = 16;
+__global__ __launch_bounds__(64 * ENC_RANK_WAVES) void enc_rank_kernel(unsigned* __restrict__ sorted,
+                                                                       const int* __restrict__ tok, int BT, int shift) {
+    constexpr int NT = 64 * ENC_RANK_WAVES, NWV = ENC_RANK_WAVES;
     __shared__ __attribute__((aligned(16))) unsigned keys[ENC_SORT_MAX];
-    __shared__ int part[4][64];
+    __shared__ int part[NWV][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n4 = (BT + 3) & ~3;
-    for (int j = threadIdx.x; j < n4; j += 256)
-        keys[j] = j < BT ? (((unsigned)tok[j] << shift) | (unsigned)j) : 0xffffffffu;
+    // staged 16 ids per thread at a time: all loads issued before the stores
+    for (int j0 = 0; j0 < n4; j0 += NT * 16) {
+        unsigned k[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) {
+            const int j = j0 + NT * u + threadIdx.x;
+            // the load is used unconditionally (masked, not selected), so
+            // the 16 loads overlap instead of each waiting under a branch
+            const unsigned t = (unsigned)tok[min(j, BT - 1)];
+            k[u] = (t << shift) | (unsigned)j | (j < BT ? 0u : 0xffffffffu);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; u++) {
+            const int j = j0 + NT * u + threadIdx.x;
+            if (j < n4) keys[j] = k[u];
+        }
+    }
     __syncthreads();
     const int i = blockIdx.x * 64 + lane;
     const unsigned ki = i < BT ? keys[i] : 0u;
-    const int W = n4 / 4;  // 16-byte words of keys, split into quarters
-    const int j0 = 4 * (wave * W / 4), j1 = 4 * ((wave + 1) * W / 4);
+    const int W = n4 / 4;  // 16-byte words of keys, split into NWV parts
+    const int j0 = 4 * (wave * W / NWV), j1 = 4 * ((wave + 1) * W / NWV);
     int cnt = 0;
 #pragma unroll 8
     for (int j = j0; j < j1; j += 4) {
@@ -83,110 +106,101 @@ __global__ __launch_bounds__(256) void enc_rank_kernel(unsigned* __restrict__ so
     }
     part[wave][lane] = cnt;
     __syncthreads();
-    if (wave == 0 && i < BT) sorted[part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = ki;
+    if (wave == 0 && i < BT) {
+        int r = 0;
+#pragma unroll
+        for (int w = 0; w < NWV; w++) r += part[w][lane];
+        sorted[r] = ki;
+    }
 }
 
-// One wave per chunk.  The chunk's keys sit one per lane; the dres row (and
-// the dwte row) of entry i + 1 are requested before entry i is added, so the
-// row reads overlap instead of forming a chain of round trips.
+// One workgroup per chunk c of sorted entries e0 .. e0 + n - 1.
 __global__ __launch_bounds__(256) void enc_chunk_kernel(float* __restrict__ dwte, float* __restrict__ headws,
                                                         float* __restrict__ tailws, int* __restrict__ meta,
                                                         const float* __restrict__ dres,
                                                         const unsigned* __restrict__ sorted, int BT, int C,
-                                                        int shift, int nch) {
-    constexpr int NV = 8;
-    static_assert(ENC_CHUNK <= 64, "one key per lane");
-    const int lane = threadIdx.x & 63;
-    const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (c >= nch) return;
+                                                        int shift) {
+    const int c = blockIdx.x;
     const int e0 = c * ENC_CHUNK, n = min(ENC_CHUNK, BT - e0);
     const unsigned pmask = (1u << shift) - 1u;
     const int prev = e0 > 0 ? (int)(sorted[e0 - 1] >> shift) : -1;
     const int next = e0 + n < BT ? (int)(sorted[e0 + n] >> shift) : -1;
-    const unsigned kl = lane < n ? sorted[e0 + lane] : 0u;
+    unsigned key[ENC_CHUNK];
+    int tk[ENC_CHUNK];
+#pragma unroll
+    for (int i = 0; i < ENC_CHUNK; i++) {
+        key[i] = i < n ? sorted[e0 + i] : 0u;
+        tk[i] = i < n ? (int)(key[i] >> shift) : -2;
+    }
+    // entry i closes a run when the next entry holds another id; the run's
+    // piece is a head (continues from the previous chunk), a tail (continues
+    // into the next chunk) or complete
     const int nvec = C / 4;
-    auto key_at = [&](int i) { return (unsigned)__shfl((int)kl, i, 64); };
-    float acc[NV][4], x[NV][4], w[NV][4];
+    for (int vv = threadIdx.x; vv < nvec; vv += blockDim.x) {
+        float x[ENC_CHUNK][4], w[ENC_CHUNK][4];
+        int run_start = 0;
 #pragma unroll
-    for (int k = 0; k < NV; k++) acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
-    auto load_rows = [&](unsigned key, float (&xr)[NV][4], float (&wr)[NV][4]) {
-        const float* r = dres + (long)(key & pmask) * C;
-        const float* q = dwte + (long)(key >> shift) * C;
-#pragma unroll
-        for (int k = 0; k < NV; k++) {
-            const int vv = lane + 64 * k;
-            if (vv < nvec) {
-                load4<float>(r + vv * 4, xr[k]);
-                load4<float>(q + vv * 4, wr[k]);
-            }
+        for (int i = 0; i < ENC_CHUNK; i++) {
+            // entries past n re-read entry n - 1's rows; w[i] is the id's
+            // current gradient row, used where entry i closes a complete run
+            const int ii = min(i, n - 1);
+            load4<float>(dres + (long)(key[ii] & pmask) * C + vv * 4, x[i]);
+            load4<float>(dwte + (long)tk[ii] * C + vv * 4, w[i]);
         }
-    };
-    load_rows(key_at(0), x, w);
-    int head_tok = -1, head_cont = 0, tail_tok = -1, run_start = 0;
-    for (int i = 0; i < n; i++) {
-        const unsigned key = key_at(i);
-        const int v = (int)(key >> shift);
-        const bool last = i == n - 1;
-        const unsigned knext = key_at(last ? i : i + 1);
-        float xn[NV][4], wn[NV][4];
-        if (!last) load_rows(knext, xn, wn);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < NV; k++)
+        for (int i = 0; i < ENC_CHUNK; i++) {
+            if (i < n) {
 #pragma unroll
-            for (int q = 0; q < 4; q++) acc[k][q] += x[k][q];
-        const bool end = last || (int)(knext >> shift) != v;
-        if (end) {
-            const bool head = run_start == 0 && prev == v;
-            const bool tail = last && next == v;
-            float* dst = (!head && !tail) ? dwte + (long)v * C : (head ? headws : tailws) + (long)c * C;
-#pragma unroll
-            for (int k = 0; k < NV; k++) {
-                const int vv = lane + 64 * k;
-                if (vv < nvec) {
+                for (int q = 0; q < 4; q++) acc[q] += x[i][q];
+                const bool last = i == n - 1;
+                const bool end = last || tk[i + (i + 1 < ENC_CHUNK ? 1 : 0)] != tk[i];
+                if (end) {
+                    const bool head = run_start == 0 && prev == tk[i];
+                    const bool tail = last && next == tk[i];
                     float o[4];
+                    float* dst;
+                    if (!head && !tail) {
 #pragma unroll
-                    for (int q = 0; q < 4; q++) o[q] = ((!head && !tail) ? w[k][q] : 0.f) + acc[k][q];
+                        for (int q = 0; q < 4; q++) o[q] = w[i][q] + acc[q];
+                        dst = dwte + (long)tk[i] * C;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) o[q] = 0.f + acc[q];
+                        dst = (head ? headws : tailws) + (long)c * C;
+                    }
                     store4<float>(dst + vv * 4, o);
-                }
-                acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
-            }
-            if (head) {
-                head_tok = v;
-                head_cont = tail ? 1 : 0;
-            } else if (tail) {
-                tail_tok = v;
-            }
-            run_start = i + 1;
-        }
-        if (!last) {
 #pragma unroll
-            for (int k = 0; k < NV; k++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    x[k][q] = xn[k][q];
-                    w[k][q] = wn[k][q];
+                    for (int q = 0; q < 4; q++) acc[q] = 0.f;
+                    run_start = i + 1;
                 }
+            }
         }
     }
-    if (lane == 0) {
+    if (threadIdx.x == 0) {
+        // the chunk's head piece (and whether it also runs into the next
+        // chunk), and the id of its tail piece
+        int head_tok = -1, head_cont = 0, tail_tok = -1;
+        if (prev == tk[0]) {
+            head_tok = tk[0];
+            head_cont = (tk[n - 1] == tk[0] && next == tk[0]) ? 1 : 0;
+        }
+        if (next == tk[n - 1] && !(head_cont && tk[n - 1] == head_tok)) tail_tok = tk[n - 1];
         meta[3 * c + 0] = head_tok;
         meta[3 * c + 1] = head_cont;
         meta[3 * c + 2] = tail_tok;
     }
 }
 
-// One wave per chunk with a tail piece of token v: the run continues as the
-// head pieces of chunks c+1 .. cl, where cl holds v's last entry (found by a
-// binary search over the sorted keys); those pieces are added in chunk order,
-// four reads in flight.
+// One workgroup per chunk c with a tail piece of id v: the run continues as
+// the head pieces of chunks c+1 .. cl, where cl holds v's last entry (found by
+// a binary search over the sorted keys); those pieces are added in chunk
+// order, each thread requesting 16 of them before adding.
 __global__ __launch_bounds__(256) void enc_fix_kernel(float* __restrict__ dwte, const float* __restrict__ headws,
                                                       const float* __restrict__ tailws, const int* __restrict__ meta,
-                                                      const unsigned* __restrict__ sorted, int BT, int shift, int C,
-                                                      int nch) {
-    constexpr int NV = 8;
-    const int lane = threadIdx.x & 63;
-    const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (c >= nch) return;
+                                                      const unsigned* __restrict__ sorted, int BT, int shift, int C) {
+    constexpr int NB = 16;
+    const int c = blockIdx.x;
     const int v = meta[3 * c + 2];
     if (v < 0) return;
     // first index with a key above every key of v
@@ -199,54 +213,24 @@ __global__ __launch_bounds__(256) void enc_fix_kernel(float* __restrict__ dwte, 
     }
     const int cl = (lo - 1) / ENC_CHUNK;
     const int nvec = C / 4;
-    float acc[NV][4];
+    for (int vv = threadIdx.x; vv < nvec; vv += blockDim.x) {
+        float acc[4], o[4];
+        load4<float>(tailws + (long)c * C + vv * 4, acc);
+        load4<float>(dwte + (long)v * C + vv * 4, o);
+        for (int c2 = c + 1; c2 <= cl; c2 += NB) {
+            float h[NB][4];
 #pragma unroll
-    for (int k = 0; k < NV; k++) {
-        const int vv = lane + 64 * k;
-        acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
-        if (vv < nvec) load4<float>(tailws + (long)c * C + vv * 4, acc[k]);
-    }
-    int c2 = c + 1;
-    for (; c2 + 3 <= cl; c2 += 4) {
-        float h[4][NV][4];
+            for (int u = 0; u < NB; u++)  // past cl: re-read piece cl (unused)
+                load4<float>(headws + (long)min(c2 + u, cl) * C + vv * 4, h[u]);
 #pragma unroll
-        for (int u = 0; u < 4; u++)
+            for (int u = 0; u < NB; u++)
+                if (c2 + u <= cl)
 #pragma unroll
-            for (int k = 0; k < NV; k++) {
-                const int vv = lane + 64 * k;
-                if (vv < nvec) load4<float>(headws + (long)(c2 + u) * C + vv * 4, h[u][k]);
-            }
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-#pragma unroll
-            for (int k = 0; k < NV; k++)
-                if (lane + 64 * k < nvec)
-#pragma unroll
-                    for (int q = 0; q < 4; q++) acc[k][q] += h[u][k][q];
-    }
-    for (; c2 <= cl; c2++) {
-#pragma unroll
-        for (int k = 0; k < NV; k++) {
-            const int vv = lane + 64 * k;
-            if (vv < nvec) {
-                float x[4];
-                load4<float>(headws + (long)c2 * C + vv * 4, x);
-#pragma unroll
-                for (int q = 0; q < 4; q++) acc[k][q] += x[q];
-            }
+                    for (int q = 0; q < 4; q++) acc[q] += h[u][q];
         }
-    }
-    float* w = dwte + (long)v * C;
 #pragma unroll
-    for (int k = 0; k < NV; k++) {
-        const int vv = lane + 64 * k;
-        if (vv < nvec) {
-            float o[4];
-            load4<float>(w + vv * 4, o);
-#pragma unroll
-            for (int q = 0; q < 4; q++) o[q] += acc[k][q];
-            store4<float>(w + vv * 4, o);
-        }
+        for (int q = 0; q < 4; q++) o[q] += acc[q];
+        store4<float>(dwte + (long)v * C + vv * 4, o);
     }
 }
 
@@ -603,11 +587,13 @@ int encoder_bwd_launch(float* dwte, float* dwpe, const float* dres, const int* t
         float* tailws = headws + (size_t)nch * C;
         const float* dr = dres + p0 * C;
         const int* tk = tok + p0;
-        hipLaunchKernelGGL(enc_rank_kernel, dim3((nb + 63) / 64), dim3(256), 0, s, sorted, tk, nb, shift);
-        hipLaunchKernelGGL(enc_chunk_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, dr,
-                           sorted, nb, C, shift, nch);
-        hipLaunchKernelGGL(enc_fix_kernel, dim3((nch + 3) / 4), dim3(256), 0, s, dwte, headws, tailws, meta, sorted, nb,
-                           shift, C, nch);
+        hipLaunchKernelGGL(enc_rank_kernel, dim3((nb + 63) / 64), dim3(64 * ENC_RANK_WAVES), 0, s, sorted, tk, nb,
+                           shift);
+        const int thr = std::min(256, (C / 4 + 63) / 64 * 64);
+        hipLaunchKernelGGL(enc_chunk_kernel, dim3(nch), dim3(thr), 0, s, dwte, headws, tailws, meta, dr, sorted, nb, C,
+                           shift);
+        hipLaunchKernelGGL(enc_fix_kernel, dim3(nch), dim3(thr), 0, s, dwte, headws, tailws, meta, sorted, nb, shift,
+                           C);
     }
     const long n4 = (long)T_ * C / 4;
     hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dwpe, dres, B, T_, C);
