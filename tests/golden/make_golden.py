@@ -16,13 +16,14 @@ losses, per-tensor gradient L2 norms, the gradients and the AdamW-updated
 parameters at seeded sample indices per tensor (key-bias elements of qkvb
 excluded: their exact gradient is zero and both sides carry only round-off).
 
-Samples: the 124M fp32 and 1558M cases take 1024 seeded indices per tensor.
-The 124M bf16 benchmark step takes tile-covering samples (tile_samples):
+Samples: the 124M fp32 case takes 1024 seeded indices per tensor.  The
+124M bf16 benchmark step and the 1558M micro-step take tile-covering samples
+(tile_samples):
 every element of tensors up to 65536 elements; for larger ones one element
 in every 64 x 64 block of each layer's matrix (finer than any output tile of
 the weight-gradient products), for wte one element in every row whose token
 occurs in the step's batches, topped up with seeded random elements to at
-least 65536 per tensor.
+least 65536 per tensor.  Their gradients are stored as float32.
 """
 
 from __future__ import annotations
@@ -202,9 +203,10 @@ def case_c5(jobs):
     del params
     stream = S.token_stream(B * T + 1, cfg.vocab_size, dist="zipf")
     x, y = S.batch(stream, 0, B, T)
-    idx = sample_indices(cfg)
+    idx = tile_samples(cfg, x.ravel())
+    print("c5 samples per tensor:", {k: int(v.size) for k, v in idx.items()}, flush=True)
     r = oracle.gpt2_step(cfg, flat, x, y, dloss=1.0 / (B * T))
-    gn, gs = norms_and_samples(cfg, r["grads"], idx)
+    gn, gs = norms_and_samples(cfg, r["grads"], idx, np.float32)
     print(f"c5 loss {r['mean_loss']:.6f}", flush=True)
     np.savez_compressed(os.path.join(HERE, "gpt2_1558m_bf16_b1t64.npz"),
                         mean_loss=np.array([r["mean_loss"]]), losses=r["losses"], grad_norms=gn, grad_samples=gs,

@@ -15,8 +15,9 @@ calls only the oracle), plus size-independent properties.
   the large ones, at least 65536 per tensor); gradient norms within 1e-2;
   update cosine >= 0.95 and update signs agreeing on >= 99.8% of the
   elements whose gradient exceeds 5% of the tensor's RMS.
-* GPT-2 1558M bf16, B=1 T=64 micro-step: loss abs <= 2e-2, sampled gradient
-  cosine >= 0.995 per tensor; at B=8 T=1024 the loss at init is near
+* GPT-2 1558M bf16, B=1 T=64 micro-step: loss abs <= 2e-2; gradient cosine
+  >= 0.995 per tensor on tile-covering samples and gradient norms within
+  1e-2; at B=8 T=1024 the loss at init is near
   ln V + C * 0.02^2 / 2 and falls over three small steps on one batch.
 """
 
@@ -220,10 +221,12 @@ def test_gpt2_1558m_bf16_micro_step_b1t64():
     gs = _samples(model, grads, g)
     ref = _split(cfg, g, g["grad_samples"])
     cos = {n: cosine(gs[n], ref[n]) for n in S.PARAM_NAMES}
-    say("1558M bf16 sampled gradient cosines", {k: round(v, 5) for k, v in cos.items()})
-    assert min(cos.values()) >= 0.995
-    gn = _norms(model, grads)
-    assert np.all(np.abs(gn / g["grad_norms"] - 1) < 0.05)
+    say("1558M bf16 per-tensor gradient cosines (tile-covering samples)", {k: round(v, 5) for k, v in cos.items()})
+    for n, c in cos.items():
+        assert c >= 0.995, (n, c)
+    ratio = _norms(model, grads) / g["grad_norms"]
+    say("1558M bf16 gradient norm ratios", np.round(ratio, 5).tolist())
+    assert np.all(np.abs(ratio - 1) <= 1e-2), ratio
     model.close()
 
 
