@@ -208,8 +208,9 @@ int gpt2_set_classifier_events(gpt2_ctx* ctx, void* const* d_start_events, void*
  * GPT2_TP_LAYER_DX the input-gradient products of layers L-1 .. 0 in the
  * order fc-projection (with the GELU backward), fc, attention projection,
  * qkv; GPT2_TP_LN_FWD the 2L + 1 forward LayerNorms (ln1, ln2 per layer,
- * then the final one); GPT2_TP_LN_BWD the final one's backward and then
- * ln2, ln1 of layers L-1 .. 0 (each with its parameter-gradient reduction);
+ * then the final one); GPT2_TP_LN_BWD the final one's backward, then ln2,
+ * ln1 of layers L-1 .. 0, then one launch that reduces the parameter
+ * gradients of all of them (one per 128 LayerNorms);
  * GPT2_TP_ATTN_FWD / GPT2_TP_ATTN_BWD one per layer; GPT2_TP_WEIGHT_GRAD
  * the one launch of every weight gradient (bf16 contexts; fp32 contexts
  * bracket each weight-gradient product, classifier first, then the layers in

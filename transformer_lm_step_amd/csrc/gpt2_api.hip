@@ -44,7 +44,7 @@ struct Plan {
     // per-layer strides (bytes)
     size_t s_btc, s_bt3c, s_bt4c, s_bt, s_lse;
     // scratch
-    size_t flag, work, work_bytes, scratch_bytes;
+    size_t flag, work, work_bytes, lnpart, scratch_bytes;
 };
 
 void param_layout(const gpt2_config& c, size_t off[16], size_t cnt[16], size_t* total) {
@@ -136,16 +136,16 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     p.dqkv = take((keep ? L : 1) * p.s_bt3c);
     p.delta = take(p.s_lse);
     p.acts_bytes = o;
-    // scratch: device flag + a workspace shared (in stream order) by the
-    // split-K partials, LayerNorm-backward partials and the encoder-backward
-    // sort
+    // scratch: device flag, a workspace shared (in stream order) by the
+    // split-K partials and the encoder-backward sort, and the partial column
+    // sums of all 2L + 1 LayerNorm backwards of a pass (summed by one launch
+    // after the last of them)
     size_t w = 0;
     w = std::max(w, dx_workspace(BT, C, p.Vp, p.esz, GEMM_STORE));
     w = std::max(w, dx_workspace(BT, 4 * C, C, p.esz, GEMM_GELU_BWD));
     w = std::max(w, dx_workspace(BT, C, 4 * C, p.esz, GEMM_STORE));
     w = std::max(w, dx_workspace(BT, C, C, p.esz, GEMM_STORE));
     w = std::max(w, dx_workspace(BT, C, 3 * C, p.esz, GEMM_STORE));
-    w = std::max(w, layernorm_bwd_workspace_bytes((int)BT, (int)C));
     w = std::max(w, encoder_bwd_workspace_bytes((int)BT, (int)C));
     if (!keep) {
         w = std::max(w, dw_workspace(p.Vp, C, BT, p.esz));
@@ -157,7 +157,8 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     p.flag = 0;
     p.work = kAlign;
     p.work_bytes = align_up(w);
-    p.scratch_bytes = p.work + p.work_bytes;
+    p.lnpart = p.work + p.work_bytes;
+    p.scratch_bytes = p.lnpart + align_up((2 * L + 1) * (size_t)layernorm_bwd_partial_rows((int)BT) * 2 * C * 4);
     return p;
 }
 
@@ -186,6 +187,10 @@ struct gpt2_ctx {
     template <typename X> X* act_l(size_t ofs, size_t stride, int l) const { return (X*)(acts() + ofs + stride * l); }
     int* flag() const { return (int*)((char*)buf.scratch + plan.flag); }
     float* work() const { return (float*)((char*)buf.scratch + plan.work); }
+    float* lnpart(int slot) const {
+        return (float*)((char*)buf.scratch + plan.lnpart) +
+               (size_t)slot * layernorm_bwd_partial_rows((int)plan.BT) * 2 * plan.C;
+    }
 };
 
 namespace {
@@ -384,6 +389,10 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     auto dbt4c = [&](int l) { return c->act<T>(p.dbt4c + (grouped ? (size_t)l * p.s_bt4c : 0)); };
     auto dqkv = [&](int l) { return c->act<T>(p.dqkv + (grouped ? (size_t)l * p.s_bt3c : 0)); };
     auto lp_out = [&](int l, int which) { return grouped ? dres_in(l, which) : (T*)nullptr; };
+    // slots of the LayerNorm backwards' partial column sums, in the order the
+    // backward runs them: the final LayerNorm, then ln2 and ln1 of layers
+    // L-1 .. 0 (parameter tensors 14, 8 and 2)
+    auto ln_slot = [&](int tensor, int l) { return tensor == 14 ? 0 : 1 + 2 * (L - 1 - l) + (tensor == 2 ? 1 : 0); };
     float* work = c->work();
     auto dw_now = [&](const GemmDesc& d) {
         return grouped ? 0 : timed(c, GPT2_TP_WEIGHT_GRAD, s, [&] { return gemm(c, d, s); });
@@ -395,8 +404,8 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
     TRY(dw_now(dw_desc(BT, C, Vp, logits, lnf, grd(c, 0), alpha, nullptr)));
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
     TRY(timed(c, GPT2_TP_LN_BWD, s, [&] {
-        return layernorm_bwd_launch<T>(dres, lp_out(L - 1, 0), grd(c, 14), grd(c, 15), dbtc, resL, prm<T>(c, 14),
-                                       c->act<float>(p.lnfm), c->act<float>(p.lnfr), BT, C, 0, work, s);
+        return layernorm_bwd_launch<T>(dres, lp_out(L - 1, 0), dbtc, resL, prm<T>(c, 14), c->act<float>(p.lnfm),
+                                       c->act<float>(p.lnfr), BT, C, 0, c->lnpart(ln_slot(14, 0)), s);
     }));
     for (int l = L - 1; l >= 0; l--) {
         const T* res = l == 0 ? c->act<T>(p.enc) : c->act_l<T>(p.res3, p.s_btc, l - 1);
@@ -419,9 +428,9 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
             return gemm(c, dx_desc(BT, C, 4 * C, dbt4c(l), prm<T>(c, 10, l, 4 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s);
         }));
         TRY(timed(c, GPT2_TP_LN_BWD, s, [&] {
-            return layernorm_bwd_launch<T>(dres, lp_out(l, 1), grd(c, 8, l, C), grd(c, 9, l, C), dbtc, res2,
-                                           prm<T>(c, 8, l, C), c->act_l<float>(p.ln2m, p.s_bt, l),
-                                           c->act_l<float>(p.ln2r, p.s_bt, l), BT, C, 1, work, s);
+            return layernorm_bwd_launch<T>(dres, lp_out(l, 1), dbtc, res2, prm<T>(c, 8, l, C),
+                                           c->act_l<float>(p.ln2m, p.s_bt, l), c->act_l<float>(p.ln2r, p.s_bt, l), BT,
+                                           C, 1, c->lnpart(ln_slot(8, l)), s);
         }));
         // attproj
         TRY(dw_now(dw_desc(BT, C, C, dres_in(l, 1), atty, grd(c, 6, l, CC), 1.0f, grd(c, 7, l, C))));
@@ -439,13 +448,37 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
             return gemm(c, dx_desc(BT, C, 3 * C, dqkv(l), prm<T>(c, 4, l, 3 * CC), dbtc, GEMM_STORE, nullptr, 1.0f), s);
         }));
         TRY(timed(c, GPT2_TP_LN_BWD, s, [&] {
-            return layernorm_bwd_launch<T>(dres, l > 0 ? lp_out(l - 1, 0) : (T*)nullptr, grd(c, 2, l, C),
-                                           grd(c, 3, l, C), dbtc, res, prm<T>(c, 2, l, C),
-                                           c->act_l<float>(p.ln1m, p.s_bt, l), c->act_l<float>(p.ln1r, p.s_bt, l), BT,
-                                           C, 1, work, s);
+            return layernorm_bwd_launch<T>(dres, l > 0 ? lp_out(l - 1, 0) : (T*)nullptr, dbtc, res,
+                                           prm<T>(c, 2, l, C), c->act_l<float>(p.ln1m, p.s_bt, l),
+                                           c->act_l<float>(p.ln1r, p.s_bt, l), BT, C, 1, c->lnpart(ln_slot(2, l)), s);
         }));
 
     }
+    // the LayerNorm parameters' gradients: every slot's partial sums in one
+    // launch (up to kMaxLnSlots slots per launch)
+    TRY(timed(c, GPT2_TP_LN_BWD, s, [&] {
+        const int slots = 2 * L + 1;
+        for (int s0 = 0; s0 < slots; s0 += kMaxLnSlots) {
+            LnFinishArgs fa = {};
+            for (int j = 0; j < slots; j++) {
+                if (j < s0 || j >= s0 + kMaxLnSlots) continue;
+                float*& w = fa.dw[j - s0];
+                float*& b = fa.db[j - s0];
+                if (j == 0) {
+                    w = grd(c, 14);
+                    b = grd(c, 15);
+                } else {
+                    const int l = L - 1 - (j - 1) / 2;
+                    const bool ln1 = (j - 1) % 2 == 1;
+                    w = grd(c, ln1 ? 2 : 8, l, C);
+                    b = grd(c, ln1 ? 3 : 9, l, C);
+                }
+            }
+            const int r = layernorm_bwd_finish_launch(fa, std::min(kMaxLnSlots, slots - s0), c->lnpart(s0), BT, C, s);
+            if (r != 0) return r;
+        }
+        return 0;
+    }));
     // every weight gradient of the step in one launch (running the classifier's
     // or half of the layers' beside the chain on a second stream was slower)
     if (grouped) TRY(timed(c, GPT2_TP_WEIGHT_GRAD, s, [&] { return dw_group(c, 0, L, true, s); }));

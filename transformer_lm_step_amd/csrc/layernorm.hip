@@ -280,17 +280,20 @@ __global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(float* __restric
     }
 }
 
-// dw[c] += sum_blocks partial[blk][c]; db[c] += sum_blocks partial[blk][C + c].
-// 16 columns per workgroup (so 2C/16 workgroups share the reads) and 64
-// phases of blocks per column (block k goes to phase k % 64); each thread
-// issues all of its reads before adding (one round trip instead of a chain),
-// and the phases are combined in order 0..63 through LDS.
+// For every LayerNorm backward (slot) of a pass: dw[c] += sum_blocks
+// partial[blk][c], db[c] += sum_blocks partial[blk][C + c], over that slot's
+// partial rows.  One launch for all slots (blockIdx.y); 16 columns per
+// workgroup (so 2C/16 workgroups share the reads) and 64 phases of blocks per
+// column (block k goes to phase k % 64); each thread issues all of its reads
+// before adding (one round trip instead of a chain), and the phases are
+// combined in order 0..63 through LDS.
 constexpr int FIN_PH = 64, FIN_COLS = 16, FIN_MAXR = 16;  // up to FIN_PH * FIN_MAXR partial rows at once
-__global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(float* __restrict__ dw,
-                                                                         float* __restrict__ db,
+__global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(const LnFinishArgs a,
                                                                          const float* __restrict__ partial, int C,
                                                                          int blocks) {
     __shared__ float red[FIN_PH][FIN_COLS];
+    const int slot = blockIdx.y;
+    const float* part = partial + (size_t)slot * blocks * 2 * C;
     const int col = threadIdx.x % FIN_COLS, ph = threadIdx.x / FIN_COLS;
     const int j = blockIdx.x * FIN_COLS + col;
     float s = 0.f;
@@ -299,11 +302,14 @@ __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(float*
             float v[FIN_MAXR];
 #pragma unroll
             for (int i = 0; i < FIN_MAXR; i++) {
+                // unconditional load (a row past the end re-reads row k0), so
+                // the 16 loads overlap
                 const int k = k0 + i * FIN_PH;
-                v[i] = k < blocks ? partial[(size_t)k * 2 * C + j] : 0.f;
+                v[i] = part[(size_t)(k < blocks ? k : k0) * 2 * C + j];
             }
 #pragma unroll
-            for (int i = 0; i < FIN_MAXR; i++) s += v[i];
+            for (int i = 0; i < FIN_MAXR; i++)
+                if (k0 + i * FIN_PH < blocks) s += v[i];
         }
     }
     red[ph][col] = s;
@@ -311,8 +317,8 @@ __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(float*
     if (ph == 0 && j < 2 * C) {
         float t = red[0][col];
         for (int q = 1; q < FIN_PH; q++) t += red[q][col];
-        if (j < C) dw[j] += t;
-        else db[j - C] += t;
+        if (j < C) a.dw[slot][j] += t;
+        else a.db[slot][j - C] += t;
     }
 }
 
@@ -351,57 +357,57 @@ int layernorm_fwd_launch(T* out, float* mean, float* rstd, const T* x, const T* 
     return (int)hipGetLastError();
 }
 
-size_t layernorm_bwd_workspace_bytes(int N, int C) {
-    return (size_t)((N + LNB_ROWS - 1) / LNB_ROWS) * 2 * C * sizeof(float);
-}
+int layernorm_bwd_partial_rows(int N) { return (N + LNB_ROWS - 1) / LNB_ROWS; }
 
 template <typename T, int NV, int LPR = 32>
-int ln_bwd_nv(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean, const float* rstd,
-              int N, int C, int accumulate, float* partial, hipStream_t s) {
-    const int blocks = (N + LNB_ROWS - 1) / LNB_ROWS;
-    hipLaunchKernelGGL((ln_bwd_kernel<T, NV, LPR>), dim3(blocks), dim3(64 * LNB_WAVES), 0, s, dres, dres_lp, partial, dy, x,
-                       w, mean, rstd, N, C, accumulate);
-    return blocks;
+void ln_bwd_nv(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean, const float* rstd,
+               int N, int C, int accumulate, float* partial, hipStream_t s) {
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NV, LPR>), dim3(layernorm_bwd_partial_rows(N)), dim3(64 * LNB_WAVES), 0, s, dres,
+                       dres_lp, partial, dy, x, w, mean, rstd, N, C, accumulate);
 }
 
 template <typename T>
-int layernorm_bwd_launch(float* dres, T* dres_lp, float* dw, float* db, const T* dy, const T* x,
-                         const T* w, const float* mean, const float* rstd, int N, int C,
-                         int accumulate, float* partial, hipStream_t s) {
+int layernorm_bwd_launch(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean,
+                         const float* rstd, int N, int C, int accumulate, float* partial, hipStream_t s) {
     if (N <= 0) return 0;
     // half a wave per row while that takes at most 3 vectors per lane, else a wave
     const int nvec = C / VecT<T>::N;
     const int nv32 = (nvec + 31) / 32, nv64 = (nvec + 63) / 64;
-    int blocks = 0;
     if (nv32 <= 3) {
         switch (nv32) {
-            case 1: blocks = ln_bwd_nv<T, 1>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-            case 2: blocks = ln_bwd_nv<T, 2>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-            default: blocks = ln_bwd_nv<T, 3>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 1: ln_bwd_nv<T, 1>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 2: ln_bwd_nv<T, 2>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            default: ln_bwd_nv<T, 3>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
         }
     } else {
         switch (nv64) {
-            case 2: blocks = ln_bwd_nv<T, 2, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-            case 3: blocks = ln_bwd_nv<T, 3, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
-            case 4: blocks = ln_bwd_nv<T, 4, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 2: ln_bwd_nv<T, 2, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 3: ln_bwd_nv<T, 3, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
+            case 4: ln_bwd_nv<T, 4, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s); break;
             default:
                 if constexpr (sizeof(T) == 4) {
                     if (nv64 <= 8) {
-                        blocks = ln_bwd_nv<T, 8, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s);
+                        ln_bwd_nv<T, 8, 64>(dres, dres_lp, dy, x, w, mean, rstd, N, C, accumulate, partial, s);
                         break;
                     }
                 }
                 return (int)hipErrorInvalidValue;
         }
     }
-    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + FIN_COLS - 1) / FIN_COLS), dim3(FIN_COLS * FIN_PH), 0, s,
-                       dw, db, partial, C, blocks);
+    return (int)hipGetLastError();
+}
+
+int layernorm_bwd_finish_launch(const LnFinishArgs& a, int slots, const float* partial, int N, int C, hipStream_t s) {
+    if (N <= 0 || slots <= 0) return 0;
+    if (slots > kMaxLnSlots) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + FIN_COLS - 1) / FIN_COLS, slots), dim3(FIN_COLS * FIN_PH), 0,
+                       s, a, partial, C, layernorm_bwd_partial_rows(N));
     return (int)hipGetLastError();
 }
 
 template int layernorm_fwd_launch<float>(float*, float*, float*, const float*, const float*, const float*, int, int, hipStream_t);
 template int layernorm_fwd_launch<bf16_t>(bf16_t*, float*, float*, const bf16_t*, const bf16_t*, const bf16_t*, int, int, hipStream_t);
-template int layernorm_bwd_launch<float>(float*, float*, float*, float*, const float*, const float*, const float*,
-                                         const float*, const float*, int, int, int, float*, hipStream_t);
-template int layernorm_bwd_launch<bf16_t>(float*, bf16_t*, float*, float*, const bf16_t*, const bf16_t*, const bf16_t*,
-                                          const float*, const float*, int, int, int, float*, hipStream_t);
+template int layernorm_bwd_launch<float>(float*, float*, const float*, const float*, const float*, const float*,
+                                         const float*, int, int, int, float*, hipStream_t);
+template int layernorm_bwd_launch<bf16_t>(float*, bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float*,
+                                          const float*, int, int, int, float*, hipStream_t);
