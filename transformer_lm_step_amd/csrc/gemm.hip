@@ -1229,12 +1229,21 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
 #undef GEMM_DTL_STAGE
 }
 
-// C[i] (+)= sum_z ws[z*MN + i], z in increasing order (float4 groups; MN % 4 == 0).
-// Blocks past the first cblocks (when db is given) do the bias partials:
+// v = sum_z ws[z*MN + i], z in increasing order (float4 groups of a row-major
+// M x N output, N % 4 == 0), then the product's epilogue on v, in the order the
+// tile epilogue applies it (alpha is already in the partials):
+//   GEMM_ACCUM  C (fp32) += v          GEMM_STORE  C = v
+//   GEMM_BIAS   C = v + bias[n]        GEMM_BIAS_RESID  C = v + bias[n] + aux_in
+//   GEMM_BIAS_GELU  aux_out = v + bias[n]; C = gelu(aux_out as stored)
+//   GEMM_GELU_BWD   C = v * gelu'(aux_in)
+// aux_in / aux_out have the output's row pitch N.  Blocks past the first
+// cblocks (when db is given) do the bias-gradient partials:
 // db[m] += sum_z wsb[z*M + m], z in increasing order.
-template <typename OutT, bool ACCUM>
+template <typename OutT, int EPI>
 __global__ void splitk_reduce_kernel(OutT* __restrict__ C, const float* __restrict__ ws, size_t MN, int splits,
-                                     int cblocks, float* __restrict__ db, const float* __restrict__ wsb, int M) {
+                                     int cblocks, float* __restrict__ db, const float* __restrict__ wsb, int M, int N,
+                                     const OutT* __restrict__ bias, const OutT* __restrict__ aux_in,
+                                     OutT* __restrict__ aux_out) {
     if ((int)blockIdx.x >= cblocks) {
         const int m = ((int)blockIdx.x - cblocks) * blockDim.x + threadIdx.x;
         if (m >= M) return;
@@ -1253,11 +1262,29 @@ __global__ void splitk_reduce_kernel(OutT* __restrict__ C, const float* __restri
 #pragma unroll
         for (int r = 0; r < 4; r++) s[r] += w[r];
     }
-    if constexpr (ACCUM) {
+    if constexpr (EPI == GEMM_ACCUM) {
         float c[4];
         load4<float>((const float*)C + i, c);
 #pragma unroll
         for (int r = 0; r < 4; r++) s[r] += c[r];
+    }
+    const int n = (int)(i % (size_t)N);
+    if constexpr (EPI == GEMM_BIAS || EPI == GEMM_BIAS_GELU || EPI == GEMM_BIAS_RESID) {
+        float bb[4];
+        load4<OutT>(bias + n, bb);
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[r] += bb[r];
+    }
+    if constexpr (EPI == GEMM_BIAS_GELU) {
+        store4<OutT>(aux_out + i, s);
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[r] = gelu_f<OutT>(to_f<OutT>(from_f<OutT>(s[r])));
+    }
+    if constexpr (EPI == GEMM_BIAS_RESID || EPI == GEMM_GELU_BWD) {
+        float a[4];
+        load4<OutT>(aux_in + i, a);
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[r] = EPI == GEMM_BIAS_RESID ? s[r] + a[r] : s[r] * gelu_grad_f<OutT>(a[r]);
     }
     store4<OutT>(C + i, s);
 }
@@ -1302,16 +1329,24 @@ const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}}};
 
 // Pick the tile and the K split minimising a simple cost: waves of
 // workgroups over the CUs times the work per workgroup, plus the split
-// partials' extra HBM traffic.  Split-K only for plain-store and accumulate
-// epilogues (their epilogue moves into the reduction).
+// partials' extra HBM traffic.  Split-K where the caller allows it
+// (split_ok) for plain-store and accumulate epilogues, and in fp32 for the
+// bias / GELU / residual / GELU-backward epilogues too (every epilogue moves
+// into the reduction).
 Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     const bool bf16 = elem_bytes == 2;
     const TileCfg* cfgs = bf16 ? kCfgBf16 : kCfgF32;
     const int ncfg = bf16 ? kNumCfgBf16 : 1;
     const int bk = 128 / elem_bytes;
     const int ktiles = (d.K + bk - 1) / bk;
-    const bool can_split = d.split_ok && (d.epi == GEMM_ACCUM || d.epi == GEMM_STORE) && (d.N % 4 == 0) &&
-                           d.ldc == d.N;
+    // fp32 products also split with a bias, GELU, residual or GELU-backward
+    // epilogue (it moves into the reduction): their tiles are 4x as costly
+    // per element, so a small row count leaves most CUs idle otherwise
+    const bool epi_ok = d.epi == GEMM_ACCUM || d.epi == GEMM_STORE ||
+                        (!bf16 && (d.epi == GEMM_BIAS || d.epi == GEMM_BIAS_GELU || d.epi == GEMM_BIAS_RESID ||
+                                   d.epi == GEMM_GELU_BWD) &&
+                         d.ldaux == d.N);
+    const bool can_split = d.split_ok && epi_ok && (d.N % 4 == 0) && d.ldc == d.N;
     const int lay = d.a_kmajor && d.b_kmajor ? 0 : (d.a_kmajor ? 1 : 2);
     const double flop_rate = 2.5e15 / 256.0;  // per CU, dense bf16
     const double hbm = 5.0e12;                // bytes/s usable
@@ -1371,6 +1406,12 @@ int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int slots, int epi, 
             case GEMM_BIAS_GELU_SMX:
                 if constexpr (sizeof(T) == 4) {
                     launch_t<T, BM, BN, WT, true, true, GEMM_BIAS_GELU_SMX, T>(a, grid, slots, s);
+                    return 0;
+                }
+                break;
+            case EPI_SPLIT:  // fp32 forward products split over K (bf16 ones never do)
+                if constexpr (sizeof(T) == 4) {
+                    launch_t<T, BM, BN, WT, true, true, EPI_SPLIT, float>(a, grid, slots, s);
                     return 0;
                 }
                 break;
@@ -1445,12 +1486,29 @@ int gemm_launch_t(const GemmDesc& d, float* ws, size_t ws_bytes, int num_cus, hi
         if (e) return e;
         const int cblocks = (int)((MN / 4 + 255) / 256);
         const int bblocks = a.dbias ? (d.M + 255) / 256 : 0;
-        if (d.epi == GEMM_ACCUM)
-            hipLaunchKernelGGL((splitk_reduce_kernel<float, true>), dim3(cblocks + bblocks), dim3(256), 0, s,
-                               (float*)d.C, ws, MN, ch.splits, cblocks, d.dbias, a.wsb, d.M);
-        else
-            hipLaunchKernelGGL((splitk_reduce_kernel<T, false>), dim3(cblocks), dim3(256), 0, s, (T*)d.C, ws, MN,
-                               ch.splits, cblocks, (float*)nullptr, (const float*)nullptr, 0);
+        const T* bias = (const T*)d.bias;
+        const T* aux_in = (const T*)d.aux_in;
+        T* aux_out = (T*)d.aux_out;
+        switch (d.epi) {
+            case GEMM_ACCUM:
+                hipLaunchKernelGGL((splitk_reduce_kernel<float, GEMM_ACCUM>), dim3(cblocks + bblocks), dim3(256), 0, s,
+                                   (float*)d.C, ws, MN, ch.splits, cblocks, d.dbias, a.wsb, d.M, d.N, nullptr, nullptr,
+                                   nullptr);
+                break;
+#define GEMM_SPLIT_REDUCE(E)                                                                                      \
+    case E:                                                                                                       \
+        hipLaunchKernelGGL((splitk_reduce_kernel<T, E>), dim3(cblocks), dim3(256), 0, s, (T*)d.C, ws, MN, ch.splits, \
+                           cblocks, (float*)nullptr, (const float*)nullptr, d.M, d.N, bias, aux_in, aux_out);       \
+        break;
+            GEMM_SPLIT_REDUCE(GEMM_STORE)
+            GEMM_SPLIT_REDUCE(GEMM_BIAS)
+            GEMM_SPLIT_REDUCE(GEMM_BIAS_GELU)
+            GEMM_SPLIT_REDUCE(GEMM_BIAS_RESID)
+            GEMM_SPLIT_REDUCE(GEMM_GELU_BWD)
+#undef GEMM_SPLIT_REDUCE
+            default:
+                return (int)hipErrorInvalidValue;
+        }
         return (int)hipGetLastError();
     }
     a.kps = ktiles;

@@ -84,9 +84,17 @@ size_t dw_workspace(size_t OC, size_t IC, size_t BT, int esz) {
     d.M = (int)OC; d.N = (int)IC; d.K = (int)BT; d.ldc = (long)IC; d.epi = GEMM_ACCUM; d.split_ok = 1;
     return gemm_workspace_bytes(d, esz, kPlanCUs);
 }
+size_t fwd_workspace(size_t BT, size_t OC, size_t IC, int esz, int epi) {
+    GemmDesc d = {};
+    d.M = (int)BT; d.N = (int)OC; d.K = (int)IC; d.ldc = (long)OC; d.ldaux = (long)OC; d.epi = epi;
+    d.a_kmajor = 1; d.b_kmajor = 1;
+    d.split_ok = esz == 4;
+    return gemm_workspace_bytes(d, esz, kPlanCUs);
+}
 size_t dx_workspace(size_t BT, size_t IC, size_t OC, int esz, int epi) {
     GemmDesc d = {};
-    d.M = (int)BT; d.N = (int)IC; d.K = (int)OC; d.ldc = (long)IC; d.epi = epi; d.split_ok = 1;
+    d.M = (int)BT; d.N = (int)IC; d.K = (int)OC; d.ldc = (long)IC; d.ldaux = (long)IC; d.epi = epi; d.split_ok = 1;
+    d.a_kmajor = 1; d.b_kmajor = 0;  // the layout of dx_desc: the chooser's speeds depend on it
     return gemm_workspace_bytes(d, esz, kPlanCUs);
 }
 
@@ -137,10 +145,16 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     p.delta = take(p.s_lse);
     p.acts_bytes = o;
     // scratch: device flag, a workspace shared (in stream order) by the
-    // split-K partials and the encoder-backward sort, and the partial column
+    // split-K partials (of every product that may split) and the
+    // encoder-backward sort, and the partial column
     // sums of all 2L + 1 LayerNorm backwards of a pass (summed by one launch
     // after the last of them)
     size_t w = 0;
+    w = std::max(w, fwd_workspace(BT, 3 * C, C, p.esz, GEMM_BIAS));
+    w = std::max(w, fwd_workspace(BT, C, C, p.esz, GEMM_BIAS_RESID));
+    w = std::max(w, fwd_workspace(BT, 4 * C, C, p.esz, GEMM_BIAS_GELU));
+    w = std::max(w, fwd_workspace(BT, C, 4 * C, p.esz, GEMM_BIAS_RESID));
+    w = std::max(w, fwd_workspace(BT, p.Vp, C, p.esz, GEMM_STORE));
     w = std::max(w, dx_workspace(BT, C, p.Vp, p.esz, GEMM_STORE));
     w = std::max(w, dx_workspace(BT, 4 * C, C, p.esz, GEMM_GELU_BWD));
     w = std::max(w, dx_workspace(BT, C, 4 * C, p.esz, GEMM_STORE));
@@ -225,14 +239,17 @@ template <typename T>
 T* prm(gpt2_ctx* c, int i, size_t l = 0, size_t per = 0) { return (T*)c->buf.params + c->off[i] + l * per; }
 float* grd(gpt2_ctx* c, int i, size_t l = 0, size_t per = 0) { return (float*)c->buf.grads + c->off[i] + l * per; }
 
+// Y[M, N] = X[M, K] W[N, K]^T with the epilogue; fp32 products may split K
+// (their epilogue then runs in the reduction), bf16 ones do not
 GemmDesc fwd_desc(int M, int N, int K, const void* X, const void* W, void* Y, int epi, const void* bias,
-                  const void* aux_in, void* aux_out) {
+                  const void* aux_in, void* aux_out, int esz) {
     GemmDesc d = {};
     d.M = M; d.N = N; d.K = K;
     d.A = X; d.lda = K; d.a_kmajor = 1;
     d.B = W; d.ldb = K; d.b_kmajor = 1;
     d.C = Y; d.ldc = N; d.epi = epi; d.alpha = 1.0f;
     d.bias = bias; d.aux_in = aux_in; d.aux_out = aux_out; d.ldaux = N;
+    d.split_ok = esz == 4;
     return d;
 }
 // dX[BT, IC] = alpha * dY[BT, OC] W[OC, IC]
@@ -288,14 +305,14 @@ int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, flo
         }));
         TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
             return gemm(c, fwd_desc(BT, 3 * C, C, ln1, prm<T>(c, 4, l, 3 * CC), qkv, GEMM_BIAS, prm<T>(c, 5, l, 3 * C),
-                                    nullptr, nullptr), s);
+                                    nullptr, nullptr, (int)sizeof(T)), s);
         }));
         TRY(timed(c, GPT2_TP_ATTN_FWD, s, [&] {
             return attention_fwd_launch<T>(atty, c->act_l<float>(p.lse, p.s_lse, l), qkv, B, Tn, C, NH, s);
         }));
         TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
             return gemm(c, fwd_desc(BT, C, C, atty, prm<T>(c, 6, l, CC), res2, GEMM_BIAS_RESID, prm<T>(c, 7, l, C), res,
-                                    nullptr), s);
+                                    nullptr, (int)sizeof(T)), s);
         }));
         TRY(timed(c, GPT2_TP_LN_FWD, s, [&] {
             return layernorm_fwd_launch<T>(ln2, c->act_l<float>(p.ln2m, p.s_bt, l), c->act_l<float>(p.ln2r, p.s_bt, l),
@@ -303,11 +320,11 @@ int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, flo
         }));
         TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
             return gemm(c, fwd_desc(BT, 4 * C, C, ln2, prm<T>(c, 10, l, 4 * CC), fchg, GEMM_BIAS_GELU,
-                                    prm<T>(c, 11, l, 4 * C), nullptr, fch), s);
+                                    prm<T>(c, 11, l, 4 * C), nullptr, fch, (int)sizeof(T)), s);
         }));
         TRY(timed(c, GPT2_TP_LAYER_FWD, s, [&] {
             return gemm(c, fwd_desc(BT, C, 4 * C, fchg, prm<T>(c, 12, l, 4 * CC), res3, GEMM_BIAS_RESID,
-                                    prm<T>(c, 13, l, C), res2, nullptr), s);
+                                    prm<T>(c, 13, l, C), res2, nullptr, (int)sizeof(T)), s);
         }));
     }
     const T* resL = c->act_l<T>(p.res3, p.s_btc, L - 1);
@@ -318,7 +335,8 @@ int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, flo
     }));
     T* logits = c->act<T>(p.logits);
     TRY(timed(c, GPT2_TP_CLASSIFIER_FWD, s, [&] {
-        return gemm(c, fwd_desc(BT, Vp, C, lnf, prm<T>(c, 0), logits, GEMM_STORE, nullptr, nullptr, nullptr), s);
+        return gemm(c, fwd_desc(BT, Vp, C, lnf, prm<T>(c, 0), logits, GEMM_STORE, nullptr, nullptr, nullptr,
+                                (int)sizeof(T)), s);
     }));
     if (targets) {
         float* losses = c->act<float>(p.losses);
