@@ -83,8 +83,9 @@ typedef struct {
  *  grads, adam_m, adam_v : fp32, flat, same layout.
  *  acts   : forward activations and backward scratch (opaque except for the
  *           tensors gpt2_act_tensor exposes).
- *  scratch: split-K and reduction workspaces (opaque; one for the
- *           input-gradient chain, one for the weight-gradient stream). */
+ *  scratch: workspaces (opaque): the split-K partials of the products that
+ *           split, the LayerNorm backwards' partial column sums and the
+ *           embedding backward's sort. */
 typedef struct {
     void *params, *master, *grads, *adam_m, *adam_v, *acts, *scratch;
 } gpt2_buffers;
@@ -137,11 +138,9 @@ int gpt2_zero_grad(gpt2_ctx* ctx, void* hip_stream);
  * consecutive backwards accumulate (gradient accumulation).  dloss scales the
  * loss gradient: dloss <= 0 means 1/(B*T), the page's fixed choice; with
  * accumulation over n micro-steps pass 1/(n*B*T).  The residual-stream
- * gradient is kept in fp32 and re-initialised by every backward.
- * The weight-gradient products run on a second stream that the context owns,
- * forked from hip_stream with events and joined back into it (a wait on
- * hip_stream for that stream's last event) as the call's last enqueued
- * operation: to the caller the whole pass is still ordered on hip_stream.
+ * gradient is kept in fp32 and re-initialised by every backward.  Every
+ * kernel is enqueued on hip_stream; in bf16 mode all weight and bias
+ * gradients of the pass run in one launch after the input-gradient chain.
  * Errors: GPT2_E_ARG, GPT2_E_STATE (the last forward had no targets),
  * GPT2_E_HIP. */
 int gpt2_backward(gpt2_ctx* ctx, float dloss, void* hip_stream);

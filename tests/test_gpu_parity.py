@@ -24,12 +24,17 @@ RAGGED32 = S.Config(max_seq_len=160, vocab_size=997, padded_vocab_size=1000, num
 # T a multiple of 64 with several full key blocks before the diagonal one
 BLOCKS64 = S.Config(max_seq_len=256, vocab_size=500, padded_vocab_size=512, num_layers=1, num_heads=2, channels=128)
 
+# 64 layers: 129 LayerNorm backwards, more than one launch of their
+# parameter-gradient reduction takes (128)
+DEEP = S.Config(max_seq_len=16, vocab_size=128, padded_vocab_size=128, num_layers=64, num_heads=2, channels=64)
+
 FP32_CASES = [
     ("tiny", S.TINY, 4, 64, False),
     ("tiny-perturbed", S.TINY, 4, 64, True),
     ("ragged-hs64", RAGGED64, 2, 150, True),
     ("ragged-hs32", RAGGED32, 3, 100, True),
     ("blocks-hs64", BLOCKS64, 2, 256, True),
+    ("deep-l64", DEEP, 2, 16, True),
 ]
 
 
