@@ -508,9 +508,11 @@ def launch_work(cfg, B, T, esz, grouped, sr, n_unique):
                       for f in (BT * C * (2 * esz + 8 + (esz if esz == 2 else 0)) + 8.0 * BT,
                                 BT * C * (2 * esz + 8 + (esz if esz == 2 and l > 0 else 0)) + 8.0 * BT)]
                    # then the parameter gradients of all 2L + 1: their partial
-                   # column sums (one row of 2C per 32 rows) read, dw and db
+                   # column sums (one row of 2C per workgroup of 16 rows, 32
+                   # for rows of more than 96 16-byte vectors) read, dw and db
                    # read and written
-                   + [(2 * L + 1) * (math.ceil(BT / 32) * 2 * C * 4 + 2 * 2 * C * 4)]),
+                   + [(2 * L + 1) * (math.ceil(BT / (16 if math.ceil(C * esz / 16 / 32) <= 3 else 32)) * 2 * C * 4
+                                     + 2 * 2 * C * 4)]),
         "CE": [2.0 * BT * Vp * esz + 8.0 * BT],
         # residual-gradient rows read, each present token's row read and
         # written, position rows read and written (fp32)

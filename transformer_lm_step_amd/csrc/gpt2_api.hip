@@ -172,7 +172,7 @@ Plan make_plan(const gpt2_config& c, int precision, int B, int T) {
     p.work = kAlign;
     p.work_bytes = align_up(w);
     p.lnpart = p.work + p.work_bytes;
-    p.scratch_bytes = p.lnpart + align_up((2 * L + 1) * (size_t)layernorm_bwd_partial_rows((int)BT) * 2 * C * 4);
+    p.scratch_bytes = p.lnpart + align_up((2 * L + 1) * (size_t)layernorm_bwd_partial_rows((int)BT, (int)C, (int)e) * 2 * C * 4);
     return p;
 }
 
@@ -203,7 +203,7 @@ struct gpt2_ctx {
     float* work() const { return (float*)((char*)buf.scratch + plan.work); }
     float* lnpart(int slot) const {
         return (float*)((char*)buf.scratch + plan.lnpart) +
-               (size_t)slot * layernorm_bwd_partial_rows((int)plan.BT) * 2 * plan.C;
+               (size_t)slot * layernorm_bwd_partial_rows((int)plan.BT, (int)plan.C, plan.esz) * 2 * plan.C;
     }
 };
 
@@ -492,7 +492,8 @@ int backward_impl(gpt2_ctx* c, float dloss, hipStream_t s) {
                     b = grd(c, ln1 ? 3 : 9, l, C);
                 }
             }
-            const int r = layernorm_bwd_finish_launch(fa, std::min(kMaxLnSlots, slots - s0), c->lnpart(s0), BT, C, s);
+            const int r =
+                layernorm_bwd_finish_launch(fa, std::min(kMaxLnSlots, slots - s0), c->lnpart(s0), BT, C, p.esz, s);
             if (r != 0) return r;
         }
         return 0;

@@ -68,11 +68,12 @@ int layernorm_fwd_launch(T* out, float* mean, float* rstd, const T* x, const T* 
                          int N, int C, hipStream_t s);
 // dres (fp32) = (accumulate ? dres : 0) + dx; dres_lp (may be NULL) = T(dres).
 // The weight and bias column sums of each workgroup's rows go to `partial`:
-// layernorm_bwd_partial_rows(N) rows of 2C floats (weight sums, then bias).
+// layernorm_bwd_partial_rows(N, C, sizeof(T)) rows of 2C floats (weight sums,
+// then bias).
 template <typename T>
 int layernorm_bwd_launch(float* dres, T* dres_lp, const T* dy, const T* x, const T* w, const float* mean,
                          const float* rstd, int N, int C, int accumulate, float* partial, hipStream_t s);
-int layernorm_bwd_partial_rows(int N);
+int layernorm_bwd_partial_rows(int N, int C, int esz);
 // For slots j = 0 .. slots-1 (LayerNorm backwards of N rows whose partial
 // rows lie one after another, slot j at partial + j * rows * 2C):
 // dw[j][c] += sum of the slot's weight sums, db[j][c] += of its bias sums
@@ -82,7 +83,8 @@ struct LnFinishArgs {
     float* dw[kMaxLnSlots];
     float* db[kMaxLnSlots];
 };
-int layernorm_bwd_finish_launch(const LnFinishArgs& a, int slots, const float* partial, int N, int C, hipStream_t s);
+int layernorm_bwd_finish_launch(const LnFinishArgs& a, int slots, const float* partial, int N, int C, int esz,
+                                hipStream_t s);
 
 // ---------------------------------------------------------- attention -------
 // qkv [B,T,3C] -> out [B,T,C], lse [B,NH,T] (base-2 log-sum-exp of the scaled scores)
