@@ -406,7 +406,8 @@ def profile_summary(folders):
     over that kernel's average duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
     / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); dependency wait =
     SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; LDS conflict = SQ_LDS_BANK_CONFLICT /
-    SQ_LDS_IDX_ACTIVE."""
+    SQ_LDS_IDX_ACTIVE; L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS) and the
+    L2 request rate per XCD over the kernel's average duration."""
     import csv
     avg_us = {}
     counters = {}  # kernel -> {counter: (sum, n)}
@@ -461,16 +462,29 @@ def profile_summary(folders):
             print(f"| `{k}` | {f:,.1f} | {w:,.1f} | {f + w:,.1f} | " + (f"{us:.1f} | {rate:,.0f} | {rate / PEAK_HBM_GBS:.3f} |"
                                                                         if us else "- | - | - |"))
         print()
+    if any("TCC_REQ_sum" in mean[k] for k in names):
+        print("### L2 (TCC) requests per dispatch\n")
+        print("| kernel | requests | hit rate | avg us | requests per us per XCD | x 128 B (TB/s) |\n|---|---|---|---|---|---|")
+        for k in names:
+            m = mean[k]
+            if "TCC_REQ_sum" not in m:
+                continue
+            h, ms, q = m.get("TCC_HIT_sum", 0.0), m.get("TCC_MISS_sum", 0.0), m["TCC_REQ_sum"]
+            us = avg_us.get(k)
+            rate = f"{q / us / 8:,.0f} | {q * 128 / us / 1e6:.1f}" if us else "- | -"
+            print(f"| `{k}` | {q:,.0f} | {h / (h + ms) if h + ms else 0.0:.3f} | " + (f"{us:.1f}" if us else "-")
+                  + f" | {rate} |")
+        print()
     busy_cols = [c for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT")
                  if any(c in mean[k] for k in names)]
     if busy_cols:
         print("### Issue counters per dispatch\n")
-        raw = sorted({c for k in names for c in mean[k] if c not in ("FETCH_SIZE", "WRITE_SIZE")})
+        raw = sorted({c for k in names for c in mean[k] if c not in ("FETCH_SIZE", "WRITE_SIZE") and not c.startswith("TCC_")})
         head = ["kernel"] + raw + ["MFMA busy", "dependency wait", "LDS conflict"]
         print("| " + " | ".join(head) + " |\n|" + "---|" * len(head))
         for k in names:
             m = mean[k]
-            if not any(c in m for c in raw):
+            if not any(c in m for c in raw if c != "GRBM_GUI_ACTIVE"):
                 continue
             cells = [f"`{k}`"] + [f"{m[c]:,.0f}" if c in m else "-" for c in raw]
             g_act = m.get("GRBM_GUI_ACTIVE", 0.0)

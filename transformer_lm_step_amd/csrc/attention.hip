@@ -45,6 +45,9 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 // stage buffers of the streamed key/value (or query/output-gradient) blocks
 constexpr int ATTN_FWD_NS = 2, ATTN_BWD_NS = 2;
+// waves (16 query rows each) per forward workgroup: 128 rows per workgroup
+// halve the K/V traffic of 64 (28.7 against 29.5 us per 124M layer)
+constexpr int ATTN_FWD_WAVES = 8;
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 // Row block `blk` (0 = the one with the most work) and (batch, head) of this
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
 // NS - 1 blocks ahead into NS stage buffers: no registers hold staged data, no
 // LDS store instructions are issued, and a wave waits for a block's loads only
 // when that block is about to be used.  One barrier per block makes the
-// block's loads (issued by all four waves) visible and frees the stage buffer
+// block's loads (issued by all the waves) visible and frees the stage buffer
 // the next loads overwrite.  Each wave's 16-byte lane loads fill 1 KB (8 rows
 // of 128 bytes) contiguously, so the layout is set by which element a lane
 // fetches:
@@ -334,16 +337,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
 //            covers every bank once per 32 lanes.
 // Rows past T_ read as zeros (buffer range); the row sums come from an
 // all-ones operand held in registers instead of extra V columns.
-template <int NS>
-__global__ __launch_bounds__(256, 2) void attn_fwd_dtl_kernel(bf16_t* __restrict__ out, float* __restrict__ lse,
-                                                           const bf16_t* __restrict__ qkv, int T_, int C, int NH,
-                                                           float sl2) {
-    constexpr int HS = 64, BLK = 64 * HS;
+//
+// A workgroup of NWV waves owns QR = 16 NWV query rows (one 16-row group per
+// wave) and streams the 64-key blocks 0 .. (its last row) / 64.  Every K/V
+// block a workgroup loads feeds all its rows: with 128 rows per workgroup the
+// K/V traffic from L2 is half that of 64, and the step's kernels all run at
+// about the same L2 request rate, so that traffic sets the time.  A wave skips
+// the blocks past its own rows (it still takes part in the loads and
+// barriers) and masks only the blocks that reach past its first row.
+template <int NS, int NWV>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t* __restrict__ out,
+                                                                      float* __restrict__ lse,
+                                                                      const bf16_t* __restrict__ qkv, int T_, int C,
+                                                                      int NH, float sl2) {
+    constexpr int HS = 64, BLK = 64 * HS, QR = 16 * NWV, NLD = 8 / NWV;  // NLD: 1 KB loads per wave per operand
+    static_assert(NWV == 4 || NWV == 8, "64 or 128 query rows per workgroup");
     __shared__ __attribute__((aligned(1024))) bf16_t sKV[NS][2][BLK];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int nb = (T_ + 63) / 64;
+    const int nb = (T_ + QR - 1) / QR;
     int blk, h, b;
     attn_block(nb, NH, blk, h, b);
     const int qb = nb - 1 - blk;
@@ -351,17 +364,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dtl_kernel(bf16_t* __restrict
     const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
     const bf16_t* Kh = Qh + C;
     const bf16_t* Vh = Qh + 2 * C;
-    const int q = qb * 64 + wave * 16 + l16;
+    const int qw = qb * QR + wave * 16;  // this wave's first row
+    const int q = qw + l16;
+    // the last key block any row of the workgroup sees
+    const int kb_last = min((qb * QR + QR - 1) / 64, (T_ - 1) / 64);
 
     Frag<bf16_t> fq[2];
     row_frags<bf16_t, HS>(fq, Qh, rs, q, T_, g4);
 
-    // byte offsets (from the block's first row) of this lane's two K and two
-    // V loads: load i of wave w fills rows 8 (w + 4 i) .. + 7 of the block
-    uint32_t koff[2], voff[2];
+    // byte offsets (from the block's first row) of this lane's K and V loads:
+    // load i of wave w fills rows 8 (w + NWV i) .. + 7 of the block
+    uint32_t koff[NLD], voff[NLD];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int r = 8 * (wave + 4 * i) + (lane >> 3);
+    for (int i = 0; i < NLD; i++) {
+        const int r = 8 * (wave + NWV * i) + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
         const int u = ((lane & 7) >> 1) ^ ((r >> 1) & 3);
         koff[i] = (uint32_t)(((long)r * rs + 8 * c) * 2);
@@ -375,9 +391,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dtl_kernel(bf16_t* __restrict
         const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(Vh + org, bytes);
         bf16_t* st = sKV[kb % NS][0];
 #pragma unroll
-        for (int i = 0; i < 2; i++) lds_dma16(rk, koff[i], st + (wave + 4 * i) * 512);
+        for (int i = 0; i < NLD; i++) lds_dma16(rk, koff[i], st + (wave + NWV * i) * 512);
 #pragma unroll
-        for (int i = 0; i < 2; i++) lds_dma16(rv, voff[i], st + BLK + (wave + 4 * i) * 512);
+        for (int i = 0; i < NLD; i++) lds_dma16(rv, voff[i], st + BLK + (wave + NWV * i) * 512);
     };
     // fragment read offsets (elements): S^T operand K rows 16 kt + l16, chunk
     // 4 ks + g4; V^T operand rows 32 c + 4 g4 + l16 / 4 (+ 16), d tile dt
@@ -397,14 +413,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dtl_kernel(bf16_t* __restrict
 
 #pragma unroll
     for (int p = 0; p < NS - 1; p++)
-        if (p <= qb) issue(p);
+        if (p <= kb_last) issue(p);
     auto block = [&](int kb, auto diag) {
         // this wave's loads of block kb are done once at most those of the
         // blocks issued after it (up to NS - 2) are outstanding
-        if (NS > 2 && kb + NS - 2 <= qb) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 4));
+        if (NS > 2 && kb + NS - 2 <= kb_last) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NLD));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         asm volatile("s_barrier" ::: "memory");
-        if (kb + NS - 1 <= qb) issue(kb + NS - 1);
+        if (kb + NS - 1 <= kb_last) issue(kb + NS - 1);
         const bf16_t* sK = sKV[kb % NS][0];
         const bf16_t* sV = sK + BLK;
         f32x4_t s[4];
@@ -462,8 +478,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dtl_kernel(bf16_t* __restrict
             mma(o[4], fones, fp);
         }
     };
-    for (int kb = 0; kb < qb; kb++) block(kb, std::false_type{});
-    block(qb, std::true_type{});
+    // a block past this wave's rows: the wave still waits for its own loads,
+    // passes the barrier and issues its share of the next block
+    auto skip_block = [&](int kb) {
+        if (NS > 2 && kb + NS - 2 <= kb_last) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NLD));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + NS - 1 <= kb_last) issue(kb + NS - 1);
+    };
+    // (a wave's 16 rows lie in one 64-key block, kd: blocks before it are
+    // whole, kd is masked, later ones are the other waves')
+    const int kd = qw / 64;
+    for (int kb = 0; kb < kd; kb++) block(kb, std::false_type{});
+    block(kd, std::true_type{});
+    for (int kb = kd + 1; kb <= kb_last; kb++) skip_block(kb);
 
     if (q < T_) {
         const float l_run = o[4][0];
@@ -1078,8 +1106,10 @@ int fwd_hs(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipSt
     if constexpr (std::is_same_v<T, bf16_t> && HS == 64) {
         // direct-to-LDS loads address a batch's rows with 32-bit byte offsets
         if ((long)T_ * 3 * C * 2 < (1L << 31)) {
-            hipLaunchKernelGGL((attn_fwd_dtl_kernel<ATTN_FWD_NS>), dim3(nb * NH * B), dim3(256), 0, s, out, lse, qkv, T_,
-                               C, NH, sl2);
+            constexpr int NWV = ATTN_FWD_WAVES;
+            const int nq = (T_ + 16 * NWV - 1) / (16 * NWV);
+            hipLaunchKernelGGL((attn_fwd_dtl_kernel<ATTN_FWD_NS, NWV>), dim3(nq * NH * B), dim3(64 * NWV), 0, s, out,
+                               lse, qkv, T_, C, NH, sl2);
             return (int)hipGetLastError();
         }
     }
