@@ -646,22 +646,33 @@ def bench_gpt2(args):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # one event between consecutive steps: per-step times for the median
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)]
     e0.record(cur)
-    for s in range(args.warmup, args.warmup + steps):
+    for i, s in enumerate(range(args.warmup, args.warmup + steps)):
         step(s)
+        if i < steps - 1:
+            marks[i].record(cur)
     e1.record(cur)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     Bnd.gpt2_set_timing_events(model.ctx, Bnd.GPT2_TP_WEIGHT_GRAD, [], [])
     del hook
     ms = e0.elapsed_time(e1) / steps
+    bounds = [e0] + marks + [e1]
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps)]
+    ms_median = float(np.median(step_ms))
     losses = mean_loss[:(args.warmup + steps) * accum].cpu().numpy()
     if not np.all(np.isfinite(losses)):
         raise RuntimeError("non-finite loss")
     tok_s = accum * BT / (ms / 1e3)
     fpt = flops_per_token(cfg.num_layers, cfg.channels, cfg.vocab_size, T)
     mfu = tok_s * fpt / (PEAK_BF16_TFLOPS * 1e12)
-    log(f"bench: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, MFU {mfu:.3f}, wall {wall:.2f}s, "
+    # the common 6N + 12 L C T convention (N = every parameter, embeddings included)
+    fpt_6n = 6.0 * model.num_params + 12.0 * cfg.num_layers * cfg.channels * T
+    mfu_6n = tok_s * fpt_6n / (PEAK_BF16_TFLOPS * 1e12)
+    log(f"bench: {ms:.3f} ms/step (median {ms_median:.3f}), {tok_s:,.0f} tok/s, MFU {mfu:.3f} "
+        f"(6N+12LCT: {mfu_6n:.3f}), wall {wall:.2f}s, "
         f"loss first {losses[0]:.4f} last {losses[-1]:.4f}")
 
     # ---- dominant kernel: the one launch of every weight gradient of a
@@ -734,8 +745,11 @@ def bench_gpt2(args):
         "data": "synthetic (Zipf(1.1) token stream, random GPT-2 init)",
         "config": {"workload": workload, "global_batch": accum * B, "seq_len": T, "grad_accum": accum,
                    "parallelism": "single GPU"},
+        "ms_per_step_median": round(ms_median, 4),
         "mfu": round(mfu, 4),
         "flops_per_token": fpt,
+        "mfu_6n": round(mfu_6n, 4),
+        "flops_per_token_6n": fpt_6n,
         "roofline": roofline,
         "families": families,
         "instrumented_ms_per_step": round(instr_ms, 4),

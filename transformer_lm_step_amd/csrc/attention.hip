@@ -67,6 +67,10 @@ DEV void attn_block(int nb, int NH, int& blk, int& h, int& b) {
     b = hb / NH;
 }
 
+// Maximum over the four 16-lane groups of a wave that hold one query's scores
+// (lanes l, l ^ 16, l ^ 32, l ^ 48): two lane swaps, no LDS round trip.
+DEV float max_over_groups(float x) { return xor32_combine(xor16_combine(x, MaxOp()), MaxOp()); }
+
 template <typename T, int HS>
 struct ACfg {
     static constexpr int KD = HS < 32 ? 32 : HS;         // d extent padded to one MFMA step
@@ -270,8 +274,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
 #pragma unroll
         for (int kt = 0; kt < 4; kt++)
             mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        mloc = max_over_groups(mloc);
         const float m_new = fmaxf(m_run, mloc);
         if (__any(m_new > m_run)) {
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
@@ -445,8 +448,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t*
 #pragma unroll
         for (int kt = 0; kt < 4; kt++)
             mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        mloc = max_over_groups(mloc);
         const float m_new = fmaxf(m_run, mloc);
         if (__any(m_new > m_run)) {
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
@@ -1023,8 +1025,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dtl_kernel(bf16_t* __restr
     for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int j = 0; j < 8; j++) Dq += (float)fo[ks].v[j] * (float)fy[ks].v[j];
-    Dq += __shfl_xor(Dq, 16, 64);
-    Dq += __shfl_xor(Dq, 32, 64);
+    Dq = xor32_combine(xor16_combine(Dq, AddOp()), AddOp());
     if (q < T_ && g4 == 0) delta[((long)b * NH + h) * T_ + q] = Dq;
     f32x4_t dq[4];
 #pragma unroll

@@ -153,17 +153,57 @@ template <> DEV void load4<bf16_t>(const bf16_t* p, float* f) {
 }
 
 // ------------------------------------------------------------- reductions ---
+// Cross-lane sums and maxima without a round trip through the LDS crossbar
+// (where a shuffle goes): DPP row permutations -- mirror within 16 lanes,
+// mirror within 8, then the two exchanges inside each group of 4 -- combine
+// the lanes of a 16-lane row, and the gfx950 lane-swap instructions pair lane
+// l with l ^ 16 and with l ^ 32.  In every step a lane and its partner combine
+// the same two values (the swaps always put the lower lane's value first), so
+// all lanes of a group end with the same bits.  Every lane of the wave must be
+// active.
 
-DEV float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+struct AddOp {
+    DEV float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+    DEV float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+template <int CTRL>
+DEV float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141, kDppQuadXor1 = 0xb1, kDppQuadXor2 = 0x4e;
+
+// op(v(l), v(l ^ 16)) and op(v(l), v(l ^ 32)), the lower lane's value first
+template <typename Op>
+DEV float xor16_combine(float v, Op op) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+DEV float xor32_combine(float v, Op op) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// op over each aligned group of LANES (16, 32 or 64) lanes
+template <int LANES, typename Op>
+DEV float lane_reduce(float v, Op op) {
+    static_assert(LANES == 16 || LANES == 32 || LANES == 64, "groups of 16, 32 or 64 lanes");
+    v = op(v, dpp_mov<kDppRowMirror>(v));
+    v = op(v, dpp_mov<kDppRowHalfMirror>(v));
+    v = op(v, dpp_mov<kDppQuadXor1>(v));
+    v = op(v, dpp_mov<kDppQuadXor2>(v));
+    if constexpr (LANES >= 32) v = xor16_combine(v, op);
+    if constexpr (LANES == 64) v = xor32_combine(v, op);
     return v;
 }
-DEV float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
+
+DEV float wave_sum(float v) { return lane_reduce<64>(v, AddOp()); }
+DEV float wave_max(float v) { return lane_reduce<64>(v, MaxOp()); }
 
 // -------------------------------------------------------------- fragments ---
 

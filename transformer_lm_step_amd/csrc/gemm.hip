@@ -213,16 +213,14 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
                 }
                 if (ok && m < g.M) store4<OutT>((OutT*)g.C + (size_t)m * g.ldc + n, v[j]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mx = xor32_combine(xor16_combine(mx, MaxOp()), MaxOp());
             float sm = 0.f;
 #pragma unroll
             for (int j = 0; j < TN; j++)
                 if (nw + 16 * j + 4 * g4 < g.N)
 #pragma unroll
                     for (int r = 0; r < 4; r++) sm += expf(v[j][r] - mx);
-            sm += __shfl_xor(sm, 16, 64);
-            sm += __shfl_xor(sm, 32, 64);
+            sm = xor32_combine(xor16_combine(sm, AddOp()), AddOp());
             if (g4 == 0 && m < g.M && nw < g.N) part[(size_t)m * g.ldaux + nw / 64] = make_float2(mx, sm);
         }
         return;
@@ -635,8 +633,8 @@ __global__ __launch_bounds__((TileOf<T, BM, BN, WT>::NT), (TileOf<T, BM, BN, WT>
     }
 
     if (do_bias) {
-        if constexpr (TPR >= 2) bsum += __shfl_xor(bsum, 1, 64);
-        if constexpr (TPR >= 4) bsum += __shfl_xor(bsum, 2, 64);
+        if constexpr (TPR >= 2) bsum += dpp_mov<kDppQuadXor1>(bsum);
+        if constexpr (TPR >= 4) bsum += dpp_mov<kDppQuadXor2>(bsum);
         const int m = m0 + tid / TPR;
         if ((tid % TPR) == 0 && m < g.M) {
             if constexpr (EPI == EPI_SPLIT) g.wsb[(size_t)blockIdx.y * g.M + m] = g.alpha * bsum;

@@ -24,12 +24,10 @@
 
 namespace {
 
-// sum over the LPR lanes of this row
+// sum over the LPR lanes of this row (the same bits in all of them)
 template <int LPR>
 DEV float row_sum(float v) {
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return lane_reduce<LPR>(v, AddOp());
 }
 
 // Forward: LPR lanes per row (half a wave while a row is at most 3 vectors
@@ -252,9 +250,8 @@ __global__ __launch_bounds__(64 * LnbShape<LPR>::WAVES) void ln_bwd_kernel(float
         for (int i = 0; i < NV; i++)
 #pragma unroll
             for (int e = 0; e < VEC; e++) {
-                const float ow = __shfl_xor(dw_acc[i][e], 32, 64), ob = __shfl_xor(db_acc[i][e], 32, 64);
-                dw_acc[i][e] = half == 0 ? dw_acc[i][e] + ow : ow + dw_acc[i][e];
-                db_acc[i][e] = half == 0 ? db_acc[i][e] + ob : ob + db_acc[i][e];
+                dw_acc[i][e] = xor32_combine(dw_acc[i][e], AddOp());
+                db_acc[i][e] = xor32_combine(db_acc[i][e], AddOp());
             }
     }
     for (int turn = 0; turn < LNB_WAVES; turn++) {
