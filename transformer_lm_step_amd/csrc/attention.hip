@@ -338,8 +338,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(T* __restrict__ out, f
 //   V block: 32-byte unit u (16 d values) of key row r at unit u ^ ((r >> 1) & 3),
 //            so each transposing read of V^T (rows 4g..4g+3 for lane group g)
 //            covers every bank once per 32 lanes.
-// Rows past T_ read as zeros (buffer range); the row sums come from an
-// all-ones operand held in registers instead of extra V columns.
+// Rows past T_ read as zeros (buffer range).  Each lane sums the fp32
+// weights of its 16 keys per block, and the four lane groups of a query are
+// added once at the end.
 //
 // A workgroup of NWV waves owns QR = 16 NWV query rows (one 16-row group per
 // wave) and streams the 64-key blocks 0 .. (its last row) / 64.  Every K/V
@@ -407,12 +408,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t*
 #pragma unroll
     for (int dt = 0; dt < 4; dt++) vofs[dt] = (4 * g4 + (l16 >> 2)) * 64 + ((dt ^ vf) << 4) + 4 * (l16 & 3);
 
-    Frag<bf16_t> fones;
-    fones.v = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
-    float m_run = -INFINITY;
-    f32x4_t o[5];
+    float m_run = -INFINITY, l_part = 0.f;
+    f32x4_t o[4];
 #pragma unroll
-    for (int dt = 0; dt < 5; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 4; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
     for (int p = 0; p < NS - 1; p++)
@@ -449,18 +448,29 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t*
         for (int kt = 0; kt < 4; kt++)
             mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
         mloc = max_over_groups(mloc);
-        const float m_new = fmaxf(m_run, mloc);
-        if (__any(m_new > m_run)) {
+        // A row's running maximum moves only when its block maximum lies more
+        // than 8 (in exp2 units) above it; until then the weights
+        // exp2((s - m_run) sl2) stay below 2^8 and the accumulators need no
+        // rescaling.  The row sums and the log-sum-exp use the same m_run, so
+        // the result is the same softmax.  The decision is per row (rows that
+        // do not move scale by exp2(0) = 1 exactly), so no row's result
+        // depends on another row's scores.
+        const bool up = (mloc - m_run) * sl2 > 8.0f;
+        if (__any(up)) {
+            const float m_new = up ? fmaxf(m_run, mloc) : m_run;
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
 #pragma unroll
-            for (int dt = 0; dt < 5; dt++) o[dt] *= alpha;
+            for (int dt = 0; dt < 4; dt++) o[dt] *= alpha;
+            l_part *= alpha;
+            m_run = m_new;
         }
-        m_run = m_new;
-        const float mc = -m_new * sl2;
+        const float mc = -m_run * sl2;
 #pragma unroll
         for (int kt = 0; kt < 4; kt++)
 #pragma unroll
             for (int r = 0; r < 4; r++) s[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][r], sl2, mc));
+        l_part += ((s[0][0] + s[0][1]) + (s[0][2] + s[0][3])) + ((s[1][0] + s[1][1]) + (s[1][2] + s[1][3])) +
+                  (((s[2][0] + s[2][1]) + (s[2][2] + s[2][3])) + ((s[3][0] + s[3][1]) + (s[3][2] + s[3][3])));
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             float pv[8] = {s[2 * c][0], s[2 * c][1], s[2 * c][2], s[2 * c][3],
@@ -477,7 +487,6 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t*
                 fv.v = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, bb, 0, 1, 2, 3, 4, 5, 6, 7));
                 mma(o[dt], fv, fp);
             }
-            mma(o[4], fones, fp);
         }
     };
     // a block past this wave's rows: the wave still waits for its own loads,
@@ -495,8 +504,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t*
     block(kd, std::true_type{});
     for (int kb = kd + 1; kb <= kb_last; kb++) skip_block(kb);
 
+    const float l_run = xor32_combine(xor16_combine(l_part, AddOp()), AddOp());
     if (q < T_) {
-        const float l_run = o[4][0];
         const float inv = 1.0f / l_run;
         bf16_t* orow = out + ((long)b * T_ + q) * C + h * HS;
 #pragma unroll
