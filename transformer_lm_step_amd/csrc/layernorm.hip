@@ -48,6 +48,15 @@ __global__ __launch_bounds__(64 * LNF_WAVES) void ln_fwd_kernel(T* __restrict__ 
     const int hl = lane % LPR, grp = lane / LPR;
     const int nvec = C / VEC;
     auto row_of = [&](int p) { return blockIdx.x * LNF_ROWS + RPS * (wave + LNF_WAVES * p) + grp; };
+    // the lane's weight and bias vectors, requested with the rows (not after
+    // the row sums, which would add a dependent round trip per step)
+    uint4 wraw[NV], braw[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        const int v = hl + LPR * i;
+        wraw[i] = ld16(w + (size_t)(v < nvec ? v : 0) * VEC);
+        braw[i] = ld16(b + (size_t)(v < nvec ? v : 0) * VEC);
+    }
     uint4 raw[STEPS][NV];
 #pragma unroll
     for (int p = 0; p < STEPS; p++) {
@@ -93,8 +102,8 @@ __global__ __launch_bounds__(64 * LNF_WAVES) void ln_fwd_kernel(T* __restrict__ 
                 const int v = hl + LPR * i;
                 if (v < nvec) {
                     float wv[VEC], bv[VEC], y[VEC];
-                    unpack16<T>(ld16(w + v * VEC), wv);
-                    unpack16<T>(ld16(b + v * VEC), bv);
+                    unpack16<T>(wraw[i], wv);
+                    unpack16<T>(braw[i], bv);
 #pragma unroll
                     for (int e = 0; e < VEC; e++) y[e] = (xv[i][e] - m) * rs * wv[e] + bv[e];
                     st16(o + v * VEC, pack16<T>(y));
@@ -127,15 +136,19 @@ struct LnRow {
     static constexpr int VEC = VecT<T>::N;
     uint4 x[NV], g[NV];
     float4 r[NV][VEC / 4];
+    float m, rs;  // the row's mean and 1/std (0 past the last row)
 };
 
 template <typename T, int NV, int LPR, bool WITH_R>
 DEV void ln_row_load(LnRow<T, NV>& d, const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ dres,
-                     int row, int N, int C, int hl, bool acc) {
+                     const float* __restrict__ mean, const float* __restrict__ rstd, int row, int N, int C, int hl,
+                     bool acc) {
     constexpr int VEC = VecT<T>::N;
     const int nvec = C / VEC;
     const bool ok = row < N;
     const size_t base = (size_t)(ok ? row : 0) * C;
+    d.m = mean[ok ? row : 0];
+    d.rs = rstd[ok ? row : 0];
 #pragma unroll
     for (int i = 0; i < NV; i++) {
         const int v = hl + LPR * i;
@@ -181,14 +194,14 @@ __global__ __launch_bounds__(64 * LnbShape<LPR>::WAVES) void ln_bwd_kernel(float
     // after the row sums.
     constexpr bool PREF = LPR == 32;
     LnRow<T, NV> cur, nxt;
-    ln_row_load<T, NV, LPR, PREF>(cur, x, dy, dres, row_of(0), N, C, hl, acc);
+    ln_row_load<T, NV, LPR, PREF>(cur, x, dy, dres, mean, rstd, row_of(0), N, C, hl, acc);
 #pragma unroll(PREF ? STEPS : 1)
     for (int p = 0; p < STEPS; p++) {
-        if (PREF && p + 1 < STEPS) ln_row_load<T, NV, LPR, PREF>(nxt, x, dy, dres, row_of(p + 1), N, C, hl, acc);
-        if (!PREF && p > 0) ln_row_load<T, NV, LPR, PREF>(cur, x, dy, dres, row_of(p), N, C, hl, acc);
+        if (PREF && p + 1 < STEPS) ln_row_load<T, NV, LPR, PREF>(nxt, x, dy, dres, mean, rstd, row_of(p + 1), N, C, hl, acc);
+        if (!PREF && p > 0) ln_row_load<T, NV, LPR, PREF>(cur, x, dy, dres, mean, rstd, row_of(p), N, C, hl, acc);
         const int row = row_of(p);
         const bool ok = row < N;
-        const float m = ok ? mean[row] : 0.f, rs = ok ? rstd[row] : 0.f;
+        const float m = cur.m, rs = cur.rs;
         float nv[NV][VEC], gv[NV][VEC];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
