@@ -930,12 +930,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dtl_kernel(bf16_t* __res
         if (wave == 0 && qb + 1 < nqb) load_ld(qb + 1);
         const bf16_t* sQ = sQO[qb % NS][0];
         const bf16_t* sdO = sQ + BLK;
-        // S[q][key] and dP[q][key]: lane holds q = 16qt + 4g4 + r, key = l16 (+ block offsets)
+        // S[q][key] and dP[q][key] - delta[q] (the dP accumulators start at
+        // -delta): lane holds q = 16qt + 4g4 + r, key = l16 (+ block offsets)
         f32x4_t p[4], ds[4];
 #pragma unroll
         for (int qt = 0; qt < 4; qt++) {
             p[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            ds[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const float4 D4 = *reinterpret_cast<const float4*>(sD + 16 * qt + 4 * g4);
+            ds[qt] = f32x4_t{-D4.x, -D4.y, -D4.z, -D4.w};
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
                 Frag<bf16_t> fa;
@@ -948,16 +950,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dtl_kernel(bf16_t* __res
 #pragma unroll
         for (int qt = 0; qt < 4; qt++) {
             const float4 L4 = *reinterpret_cast<const float4*>(sL + 16 * qt + 4 * g4);
-            const float4 D4 = *reinterpret_cast<const float4*>(sD + 16 * qt + 4 * g4);
             const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
-            const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 float pr = __builtin_amdgcn_exp2f(fmaf(p[qt][r], sl2, -Lr[r]));
                 if constexpr (decltype(diag)::value)
                     if (key > qb * 64 + 16 * qt + 4 * g4 + r) pr = 0.f;
                 p[qt][r] = pr;
-                ds[qt][r] = pr * (ds[qt][r] - Dr[r]);
+                ds[qt][r] = pr * ds[qt][r];
             }
         }
         // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
@@ -1058,12 +1058,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dtl_kernel(bf16_t* __restr
         if (kb + NS - 1 <= qb) issue(kb + NS - 1);
         const bf16_t* sK = sKV[kb % NS][0];
         const bf16_t* sV = sK + BLK;
-        // S^T[key][q], dP^T[key][q]: lane holds key = 16kt + 4g4 + r, q = l16
+        // S^T[key][q], dP^T[key][q] - delta[q] (the dP accumulators start at
+        // -delta): lane holds key = 16kt + 4g4 + r, q = l16
         f32x4_t s[4], dp[4];
 #pragma unroll
         for (int kt = 0; kt < 4; kt++) {
             s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dp[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dp[kt] = f32x4_t{-Dq, -Dq, -Dq, -Dq};
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
                 Frag<bf16_t> fa;
@@ -1080,7 +1081,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dtl_kernel(bf16_t* __restr
                 float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], sl2, -Lq));
                 if constexpr (decltype(diag)::value)
                     if (kb * 64 + 16 * kt + 4 * g4 + r > q) pr = 0.f;
-                s[kt][r] = pr * (dp[kt][r] - Dq);  // dS^T / scale
+                s[kt][r] = pr * dp[kt][r];  // dS^T / scale
             }
         // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
 #pragma unroll
