@@ -670,12 +670,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Stage depth BK (contraction elements per stage) and stage count NS per tile:
 // 64-deep stages; two for the square tiles (a 256x256 stage is 64 KB), three
-// for the rectangular ones (a 128x192 stage is 40 KB), which run their
-// short-K products 10-20% faster than with two.
+// for the rectangular ones whose three stages fit in LDS beside the epilogue's
+// bias row (a 128x192 stage is 40 KB), which run their short-K products 10-20%
+// faster than with two; two for 256x192 (56 KB a stage).
 template <int BM, int BN>
 struct DtlCfg {
     static constexpr int BK = 64;
-    static constexpr int NS = BM != BN ? 3 : 2;
+    static constexpr int NS = BM != BN && 3 * (BM + BN) * BK * 2 <= 150 * 1024 ? 3 : 2;
     static_assert(NS >= 2 && NS <= 4, "the stage loop unrolls 2 to 4 stage buffers");
     static_assert(BK == 32 || BK == 64, "stages are one or two 32-deep MFMA steps");
 };
@@ -1308,22 +1309,30 @@ struct Choice {
 // with 128-row waves 3.9 TFLOP/s per CU.  The 128-row-wave tile's
 // input-gradient figure is set from the step as well: on the classifier's
 // input gradient (K = Vp, split) it beats the 16-wave 256x256 tile, whose
-// epilogue cannot stage its stores through LDS.
+// epilogue cannot stage its stores through LDS.  The 256x192 tile (8 waves of
+// 64x96, two stages) is set from the qkv and fc forward products (8192 x 2304
+// and 8192 x 3072, K = 768, with their bias and GELU epilogues), where it runs
+// 11-14% faster than 128x192 and 256x128 (1.5 and 2 rounds of tiles against 3);
+// on the classifier (N = 50304, the weights streaming from HBM rather than
+// staying in L2) it is 5% slower than 256x256, so it is offered only up to
+// N = 8192 (max_n).
 struct TileCfg {
     int bm, bn, wt, occ;
     double speed[3];  // forward, input gradient, weight gradient
+    int max_n;        // largest N the tile is offered for (0: any)
 };
-const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}},
-                            {256, 128, 64, 1, {0.92, 0.76, 0.66}},
-                            {128, 256, 64, 1, {0.71, 0.92, 0.70}},
-                            {128, 128, 64, 2, {0.81, 0.82, 0.70}},
-                            {256, 256, 128, 1, {1.00, 1.01, 1.00}},
+const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
+                            {256, 128, 64, 1, {0.92, 0.76, 0.66}, 0},
+                            {128, 256, 64, 1, {0.71, 0.92, 0.70}, 0},
+                            {128, 128, 64, 2, {0.81, 0.82, 0.70}, 0},
+                            {256, 256, 128, 1, {1.00, 1.01, 1.00}, 0},
                             // forward products only: a k-strided slab needs
                             // a power-of-two row count
-                            {128, 192, 96, 1, {0.92, 0.0, 0.0}},
+                            {128, 192, 96, 1, {0.92, 0.0, 0.0}, 0},
+                            {256, 192, 96, 1, {1.42, 0.0, 0.0}, 8192},
 };
 constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
-const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}}};
+const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}, 0}};
 
 // Pick the tile and the K split minimising a simple cost: waves of
 // workgroups over the CUs times the work per workgroup, plus the split
@@ -1352,6 +1361,7 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     double best_cost = 1e300;
     for (int c = 0; c < ncfg; c++) {
         const TileCfg& t = cfgs[c];
+        if (t.max_n > 0 && d.N > t.max_n) continue;
         const long tiles = (long)((d.M + t.bm - 1) / t.bm) * ((d.N + t.bn - 1) / t.bn);
         const int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
         for (int s = 1; s <= max_split; s++) {
@@ -1448,6 +1458,7 @@ int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, i
             return (int)hipErrorInvalidValue;
         }
         if (ch.wt == 96 && ch.bm == 128 && ch.bn == 192) return launch_epi<T, 128, 192, 96>(d, a, grid, slots, epi, s);
+        if (ch.wt == 96 && ch.bm == 256 && ch.bn == 192) return launch_epi<T, 256, 192, 96>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 64>(d, a, grid, slots, epi, s);
