@@ -302,8 +302,11 @@ __global__ __launch_bounds__(64 * LnbShape<LPR>::WAVES) void ln_bwd_kernel(float
 // workgroup (so 2C/16 workgroups share the reads) and 64 phases of blocks per
 // column (block k goes to phase k % 64); each thread issues all of its reads
 // before adding (one round trip instead of a chain), and the phases are
-// combined in order 0..63 through LDS.
-constexpr int FIN_PH = 64, FIN_COLS = 16, FIN_MAXR = 16;  // up to FIN_PH * FIN_MAXR partial rows at once
+// combined in order 0..63 through LDS.  MAXR (partial rows per thread and
+// pass) is the smallest of 4, 8, 16 that covers the rows in one pass where
+// it can, so few of the unconditional reads are repeats.
+constexpr int FIN_PH = 64, FIN_COLS = 16;
+template <int FIN_MAXR>
 __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(const LnFinishArgs a,
                                                                          const float* __restrict__ partial, int C,
                                                                          int blocks) {
@@ -424,8 +427,11 @@ int layernorm_bwd_finish_launch(const LnFinishArgs& a, int slots, const float* p
                                 hipStream_t s) {
     if (N <= 0 || slots <= 0) return 0;
     if (slots > kMaxLnSlots) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + FIN_COLS - 1) / FIN_COLS, slots), dim3(FIN_COLS * FIN_PH), 0,
-                       s, a, partial, C, layernorm_bwd_partial_rows(N, C, esz));
+    const int blocks = layernorm_bwd_partial_rows(N, C, esz);
+    const dim3 grid((2 * C + FIN_COLS - 1) / FIN_COLS, slots);
+    if (blocks <= FIN_PH * 4) hipLaunchKernelGGL(ln_bwd_finish_kernel<4>, grid, dim3(FIN_COLS * FIN_PH), 0, s, a, partial, C, blocks);
+    else if (blocks <= FIN_PH * 8) hipLaunchKernelGGL(ln_bwd_finish_kernel<8>, grid, dim3(FIN_COLS * FIN_PH), 0, s, a, partial, C, blocks);
+    else hipLaunchKernelGGL(ln_bwd_finish_kernel<16>, grid, dim3(FIN_COLS * FIN_PH), 0, s, a, partial, C, blocks);
     return (int)hipGetLastError();
 }
 
