@@ -11,9 +11,10 @@ Bars.  fp32: rel-L2 <= 1e-5 for out and each third of dqkv.  bf16 (P and dS
 enter their products rounded to bf16, outputs are bf16): rel-L2 <= 1e-2 and
 max |error| <= 2^-5 max(max|ref|, 1e-3) per output tensor.  lse, against log2 of the
 softmax denominator summed in fp64 from the same q and k: |error| <= 1e-5
-(fp32); bf16 <= 2^-8, since the denominator is summed from the bf16-rounded
-probabilities that also weight V (each within 2^-9 relative, so the sum is
-too and its log2 within log2(1 + 2^-9) = 0.0028).  Every output element is written (NaN-filled
+(fp32); bf16 <= 2^-8: the head-size-64 kernel sums the fp32 weights, the
+others sum the bf16-rounded probabilities that also weight V (each within
+2^-9 relative, so the sum is too and its log2 within log2(1 + 2^-9) =
+0.0028).  Every output element is written (NaN-filled
 beforehand).
 """
 
