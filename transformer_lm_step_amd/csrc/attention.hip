@@ -67,6 +67,26 @@ DEV void attn_block(int nb, int NH, int& blk, int& h, int& b) {
     b = hb / NH;
 }
 
+// The forward's launch is a single round (every workgroup resident at once,
+// three per CU at the GPT-2 sizes), and the dispatcher hands out workgroup
+// ids in passes of one per CU, so a CU's blocks come from the same position
+// of consecutive passes.  Issued longest-first, a CU would take the longest
+// block of every pass (up to 1.3 times the mean work); reversing every
+// other full pass, in groups of 8 ids so that every id keeps its XCD, pairs
+// a long block with short ones (within 4% of the mean).  P: CUs per pass (a
+// multiple of 8).
+constexpr int kAttnCUs = 256;
+DEV void attn_block_snake(int nb, int NH, int P, int& blk, int& h, int& b) {
+    int o = blockIdx.x;
+    const int pass = o / P, j = o - pass * P;
+    if ((pass & 1) && (pass + 1) * P <= (int)gridDim.x) o = pass * P + (P - 8 - (j & ~7)) + (j & 7);
+    const int nhb = gridDim.x / nb;
+    blk = o / nhb;
+    const int hb = o - blk * nhb;
+    h = hb % NH;
+    b = hb / NH;
+}
+
 // Maximum over the four 16-lane groups of a wave that hold one query's scores
 // (lanes l, l ^ 16, l ^ 32, l ^ 48): two lane swaps, no LDS round trip.
 DEV float max_over_groups(float x) { return xor32_combine(xor16_combine(x, MaxOp()), MaxOp()); }
@@ -362,7 +382,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t*
     const int l16 = lane & 15, g4 = lane >> 4;
     const int nb = (T_ + QR - 1) / QR;
     int blk, h, b;
-    attn_block(nb, NH, blk, h, b);
+    attn_block_snake(nb, NH, kAttnCUs, blk, h, b);
     const int qb = nb - 1 - blk;
     const long rs = 3L * C;
     const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
