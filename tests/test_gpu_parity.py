@@ -24,6 +24,11 @@ RAGGED32 = S.Config(max_seq_len=160, vocab_size=997, padded_vocab_size=1000, num
 # T a multiple of 64 with several full key blocks before the diagonal one
 BLOCKS64 = S.Config(max_seq_len=256, vocab_size=500, padded_vocab_size=512, num_layers=1, num_heads=2, channels=128)
 
+# B*T = 8192 rows with C = 800: the qkv (N = 2400) and fc (N = 3200) forward
+# products and the N = 800 projections run on 256x192 tiles whose last column
+# tile is ragged (bias, bias + GELU and bias + residual epilogues)
+WIDE = S.Config(max_seq_len=1024, vocab_size=997, padded_vocab_size=1000, num_layers=1, num_heads=25, channels=800)
+
 # 64 layers: 129 LayerNorm backwards, more than one launch of their
 # parameter-gradient reduction takes (128)
 DEEP = S.Config(max_seq_len=16, vocab_size=128, padded_vocab_size=128, num_layers=64, num_heads=2, channels=64)
@@ -242,3 +247,34 @@ def test_fp32_token_embedding_gradient_two_position_blocks():
         e = rel_l2(g["grads"][p], o["grads"][p])
         say("two blocks", p, "gradient rel-L2", e)
         assert e < 1e-4, (p, e)
+
+
+def test_bf16_wide_forward_ragged_tiles():
+    """The logits of the last sequence of a B=8, T=1024, C=800 forward against
+    the oracle's forward of that sequence (fp64 from the same bf16-exact
+    parameters): rel-L2 <= 2e-2 over the real vocabulary columns.  The MLP and
+    attention branches dominate the one-layer residual stream at this init,
+    so wrong values in one ragged column tile of a product move the logits
+    far past the bar."""
+    import oracle
+    import torch
+    from transformer_lm_step_amd import binding as Bnd
+    from transformer_lm_step_amd.model import GPT2
+    cfg, B, T = WIDE, 8, 1024
+    say("case wide forward", B, T, cfg.channels)
+    params, [(x, y)] = make_inputs(cfg, B, T, perturb=True, bf16=True)
+    m = GPT2(cfg, 1, B, T)
+    m.init(m.pack(params))
+    m.forward(torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).cuda())
+    torch.cuda.synchronize()
+    assert m.check() == 0
+    got = m.act(Bnd.GPT2_T_LOGITS).float().cpu().numpy().reshape(B, T, -1)
+    m.close()
+    b = B - 1
+    ref = oracle.gpt2_step(cfg, oracle.pack_params(cfg, params), x[b:b + 1], want_grads=False,
+                           want_logits=True)["logits"][0]
+    V = cfg.vocab_size
+    e = rel_l2(got[b, :, :V], ref[:, :V])
+    say("wide forward logits rel-L2", e)
+    assert e <= 2e-2, e
+

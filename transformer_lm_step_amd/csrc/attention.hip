@@ -67,19 +67,21 @@ DEV void attn_block(int nb, int NH, int& blk, int& h, int& b) {
     b = hb / NH;
 }
 
-// The forward's launch is a single round (every workgroup resident at once,
-// three per CU at the GPT-2 sizes), and the dispatcher hands out workgroup
-// ids in passes of one per CU, so a CU's blocks come from the same position
-// of consecutive passes.  Issued longest-first, a CU would take the longest
-// block of every pass (up to 1.3 times the mean work); reversing every
-// other full pass, in groups of 8 ids so that every id keeps its XCD, pairs
-// a long block with short ones (within 4% of the mean).  P: CUs per pass (a
-// multiple of 8).
-constexpr int kAttnCUs = 256;
+// The forward holds three workgroups per CU (66 registers, 32 KB of LDS), so
+// at the GPT-2 124M shape its launch is a single round, and the dispatcher
+// hands out workgroup ids in passes of one per CU: a CU's resident blocks
+// come from the same position of consecutive passes.  Issued longest-first,
+// a CU would take the longest block of every pass (up to 1.3 times the mean
+// work); reversing the second of the resident passes, in groups of 8 ids so
+// that every id keeps its XCD, pairs a long block with short ones (within 4%
+// of the mean).  Later passes (larger launches) start as slots free up and
+// keep the longest-first order.  P: CUs per pass (a multiple of 8).
+constexpr int kAttnCUs = 256, kAttnFwdResident = 3;
 DEV void attn_block_snake(int nb, int NH, int P, int& blk, int& h, int& b) {
     int o = blockIdx.x;
     const int pass = o / P, j = o - pass * P;
-    if ((pass & 1) && (pass + 1) * P <= (int)gridDim.x) o = pass * P + (P - 8 - (j & ~7)) + (j & 7);
+    if ((pass & 1) && pass < kAttnFwdResident && (pass + 1) * P <= (int)gridDim.x)
+        o = pass * P + (P - 8 - (j & ~7)) + (j & 7);
     const int nhb = gridDim.x / nb;
     blk = o / nhb;
     const int hb = o - blk * nhb;
