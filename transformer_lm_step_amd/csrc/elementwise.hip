@@ -274,8 +274,10 @@ DEV void st16_stream(void* p, const uint4& v) {
 // columns.  The loss-gradient scale is applied later, by the classifier's
 // backward products.  Columns >= V are set to -inf in registers right after
 // the load, so every pass treats all elements alike (exp2(-inf) = 0 both in
-// the sum and in the written gradient); exponentials are exp2(z log2(e) - c),
-// one FMA and the hardware exp2 per element.
+// the sum and in the written gradient).  Each element's exponential is taken
+// once, exp2(z log2(e) - max log2(e)) (one FMA and the hardware exp2), summed,
+// and kept in the row's registers (in the row's precision) for the write,
+// which scales it by 1/sum.
 template <typename T, int NT, int NV>
 __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T* __restrict__ logits, float* __restrict__ losses,
                                                            const int* __restrict__ targets, int V, int Vp,
@@ -329,7 +331,11 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T*
             float f[VEC];
             unpack16<T>(reg[k], f);
 #pragma unroll
-            for (int e = 0; e < VEC; e++) sm += __builtin_amdgcn_exp2f(fmaf(f[e], L2E, mc));
+            for (int e = 0; e < VEC; e++) {
+                f[e] = __builtin_amdgcn_exp2f(fmaf(f[e], L2E, mc));
+                sm += f[e];
+            }
+            reg[k] = pack16<T>(f);  // the row now holds exp(z - max)
         }
     }
     sm = wave_sum(sm);
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T*
     for (int w = 0; w < NW; w++) tot += red[w];
     const float lse = mx + __logf(tot);
     if (tid == 0) losses[row] = lse - zt_s;
-    const float lc = -lse * L2E;
+    const float inv = 1.0f / tot;
     const int vt = tgt / VEC;
 #pragma unroll
     for (int k = 0; k < NV; k++) {
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T*
             float f[VEC];
             unpack16<T>(reg[k], f);
 #pragma unroll
-            for (int e = 0; e < VEC; e++) f[e] = __builtin_amdgcn_exp2f(fmaf(f[e], L2E, lc));
+            for (int e = 0; e < VEC; e++) f[e] *= inv;
             if (v == vt) {
 #pragma unroll
                 for (int e = 0; e < VEC; e++)
