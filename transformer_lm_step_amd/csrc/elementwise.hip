@@ -348,7 +348,6 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T*
     const float lse = mx + __logf(tot);
     if (tid == 0) losses[row] = lse - zt_s;
     const float inv = 1.0f / tot;
-    const int vt = tgt / VEC;
 #pragma unroll
     for (int k = 0; k < NV; k++) {
         const int v = tid + NT * k;
@@ -357,13 +356,15 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 2) void classifier_ce_kernel(T*
             unpack16<T>(reg[k], f);
 #pragma unroll
             for (int e = 0; e < VEC; e++) f[e] *= inv;
-            if (v == vt) {
-#pragma unroll
-                for (int e = 0; e < VEC; e++)
-                    if (v * VEC + e == tgt) f[e] -= 1.0f;
-            }
             st16_stream(z + (long)v * VEC, pack16<T>(f));
         }
+    }
+    // the target column: softmax - 1, from the same exponential (recomputed
+    // from the target logit exactly as the sum pass took it), stored by the
+    // thread that stored its vector, after it
+    if (tid == (tgt / VEC) % NT) {
+        const float et = to_f<T>(from_f<T>(__builtin_amdgcn_exp2f(fmaf(zt_s, L2E, mc))));
+        __builtin_nontemporal_store(from_f<T>(et * inv - 1.0f), z + tgt);
     }
 }
 
