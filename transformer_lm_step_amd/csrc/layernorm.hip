@@ -298,14 +298,15 @@ __global__ __launch_bounds__(64 * LnbShape<LPR>::WAVES) void ln_bwd_kernel(float
 
 // For every LayerNorm backward (slot) of a pass: dw[c] += sum_blocks
 // partial[blk][c], db[c] += sum_blocks partial[blk][C + c], over that slot's
-// partial rows.  One launch for all slots (blockIdx.y); 16 columns per
-// workgroup (so 2C/16 workgroups share the reads) and 64 phases of blocks per
-// column (block k goes to phase k % 64); each thread issues all of its reads
-// before adding (one round trip instead of a chain), and the phases are
-// combined in order 0..63 through LDS.  MAXR (partial rows per thread and
-// pass) is the smallest of 4, 8, 16 that covers the rows in one pass where
-// it can, so few of the unconditional reads are repeats.
-constexpr int FIN_PH = 64, FIN_COLS = 16;
+// partial rows.  One launch for all slots (blockIdx.y); 32 columns per
+// workgroup, so each workgroup reads whole 128-byte lines (with 16, two
+// workgroups on different XCDs fetched every line), and 32 phases of blocks
+// per column (block k goes to phase k % 32); each thread issues all of its
+// reads before adding (one round trip instead of a chain), and the phases
+// are combined in order 0..31 through LDS.  MAXR (partial rows per thread
+// and pass) is the smallest of 4, 8, 16 that covers the rows in one pass
+// where it can, so few of the unconditional reads are repeats.
+constexpr int FIN_PH = 32, FIN_COLS = 32;
 template <int FIN_MAXR>
 __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(const LnFinishArgs a,
                                                                          const float* __restrict__ partial, int C,
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(FIN_COLS * FIN_PH) void ln_bwd_finish_kernel(const 
 #pragma unroll
             for (int i = 0; i < FIN_MAXR; i++) {
                 // unconditional load (a row past the end re-reads row k0), so
-                // the 16 loads overlap
+                // the loads overlap
                 const int k = k0 + i * FIN_PH;
                 v[i] = part[(size_t)(k < blocks ? k : k0) * 2 * C + j];
             }
