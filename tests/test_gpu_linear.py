@@ -22,6 +22,11 @@ pytestmark = pytest.mark.gpu
 
 # (M, K, N): ragged layer-sized products, and a classifier-shaped one
 SHAPES = [(8232, 776, 3120), (8200, 3080, 776), (4104, 768, 50304), (8232, 776, 1000)]
+# products taken by the 256 x 288 tile: the qkv layer's exact shape (one
+# tile per CU), ragged in M, N and K within one round, and ragged with three
+# tiles per workgroup (the persistent loop, next tile's stages issued before
+# the epilogue)
+SHAPES_288 = [(8192, 768, 2304), (8100, 776, 2296), (8200, 1608, 6392)]
 
 
 def _rows(M, n, seed):
@@ -36,7 +41,7 @@ def _bf16_close(got, ref):
     return float(np.max(np.abs(got - ref) - tol))
 
 
-@pytest.mark.parametrize("M,K,N", SHAPES)
+@pytest.mark.parametrize("M,K,N", SHAPES + SHAPES_288)
 def test_linear_forward_bias(M, K, N):
     import torch
     import oracle

@@ -28,6 +28,9 @@ BLOCKS64 = S.Config(max_seq_len=256, vocab_size=500, padded_vocab_size=512, num_
 # products and the N = 800 projections run on 256x192 tiles whose last column
 # tile is ragged (bias, bias + GELU and bias + residual epilogues)
 WIDE = S.Config(max_seq_len=1024, vocab_size=997, padded_vocab_size=1000, num_layers=1, num_heads=25, channels=800)
+# C = 576 at B*T = 8192: the fc product (8192 x 2304, with its GELU
+# epilogue) runs on the 256 x 288 tile
+WIDE576 = S.Config(max_seq_len=1024, vocab_size=997, padded_vocab_size=1000, num_layers=1, num_heads=9, channels=576)
 
 # 64 layers: 129 LayerNorm backwards, more than one launch of their
 # parameter-gradient reduction takes (128)
@@ -249,8 +252,9 @@ def test_fp32_token_embedding_gradient_two_position_blocks():
         assert e < 1e-4, (p, e)
 
 
-def test_bf16_wide_forward_ragged_tiles():
-    """The logits of the last sequence of a B=8, T=1024, C=800 forward against
+@pytest.mark.parametrize("cfg", [WIDE, WIDE576], ids=["c800", "c576"])
+def test_bf16_wide_forward_ragged_tiles(cfg):
+    """The logits of the last sequence of a B=8, T=1024, C=800 (or 576) forward against
     the oracle's forward of that sequence (fp64 from the same bf16-exact
     parameters): rel-L2 <= 2e-2 over the real vocabulary columns.  The MLP and
     attention branches dominate the one-layer residual stream at this init,
@@ -260,7 +264,7 @@ def test_bf16_wide_forward_ragged_tiles():
     import torch
     from transformer_lm_step_amd import binding as Bnd
     from transformer_lm_step_amd.model import GPT2
-    cfg, B, T = WIDE, 8, 1024
+    B, T = 8, 1024
     say("case wide forward", B, T, cfg.channels)
     params, [(x, y)] = make_inputs(cfg, B, T, perturb=True, bf16=True)
     m = GPT2(cfg, 1, B, T)

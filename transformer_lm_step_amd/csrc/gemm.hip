@@ -70,10 +70,11 @@ struct Tile {
 };
 
 // Wave tile selector used by the kernels' template argument WT: 64 -> 64x64,
-// 96 -> 64x96, 128 -> 128x64 outputs per wave (128x128 waves need 256
-// accumulators per lane, which the compiler only fits by spilling).
+// 96 -> 64x96, 128 -> 128x64, 144 -> 64x144 outputs per wave (128x128 waves
+// need 256 accumulators per lane, which the compiler only fits by spilling).
 template <typename T, int BM, int BN, int WT>
-using TileOf = Tile<T, BM, BN, (WT >= 128 ? 128 : 64), (WT == 256 ? 128 : WT == 96 ? 96 : 64)>;
+using TileOf = Tile<T, BM, BN, (WT == 128 || WT == 256 ? 128 : 64),
+                    (WT == 256 ? 128 : WT == 96 ? 96 : WT == 144 ? 144 : 64)>;
 
 // Per-thread register count for staging an R x BK slab (both layouts).
 template <int R, int NT> struct StageRegs {
@@ -887,10 +888,13 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
     // requested before the epilogue of the current one.
     constexpr bool PERSIST = !GRP && dtl_persistent<BM, BN, WT, EPI, BIAS>();
     constexpr bool RP = dtl_rp<BM, BN, WT, AK, BKM, EPI>();
-    // bf16 outputs are staged through the LDS buffer of stage NS - 1 (the
-    // larger of its two slabs), which no load targets until the next tile's
-    // first stage
-    constexpr bool CAN_STAGE = NW * 16 * (TL::WTN + 8) <= (BM > BN ? BM : BN) * BK;
+    // bf16 outputs are staged through the LDS buffers of stage NS - 1, which
+    // no load targets until the next tile's first stage: the larger of its two
+    // slabs, or (64x144 waves) the first half of the waves in the A slab and
+    // the second half in the B slab
+    constexpr bool STAGE_ONE = NW * 16 * (TL::WTN + 8) <= (BM > BN ? BM : BN) * BK;
+    constexpr bool STAGE_TWO = !STAGE_ONE && (NW / 2) * 16 * (TL::WTN + 8) <= (BM < BN ? BM : BN) * BK;
+    constexpr bool CAN_STAGE = STAGE_ONE || STAGE_TWO;
     // Persistent bf16-output tiles (XS): the bias is the accumulators' initial
     // value, and the epilogue's stores stay in flight while the next tile
     // starts -- each wave issues exactly XS_STORES of them, so the waits of
@@ -1213,7 +1217,8 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
         // the staging buffer: every wave must be done reading it first
         T* const lastA = NS == 2 ? sA1 : NS == 3 ? sA2 : sA3;
         T* const lastB = NS == 2 ? sB1 : NS == 3 ? sB2 : sB3;
-        T* const stage = (BN >= BM ? lastB : lastA) + wave * 16 * (TL::WTN + 8);
+        T* const stage = STAGE_TWO ? (wave < NW / 2 ? lastA : lastB) + (wave % (NW / 2)) * 16 * (TL::WTN + 8)
+                                   : (BN >= BM ? lastB : lastA) + wave * 16 * (TL::WTN + 8);
         if (CAN_STAGE && !more) {
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
             asm volatile("s_barrier" ::: "memory");
@@ -1315,11 +1320,18 @@ struct Choice {
 // 11-14% faster than 128x192 and 256x128 (1.5 and 2 rounds of tiles against 3);
 // on the classifier (N = 50304, the weights streaming from HBM rather than
 // staying in L2) it is 5% slower than 256x256, so it is offered only up to
-// N = 8192 (max_n).
+// N = 8192 (max_n).  The 256x288 tile (8 waves of 64x144, two stages; the
+// most MFMA work per fragment read of the tiles here) covers the 124M qkv
+// forward product (8192 x 2304) in exactly one round of 256 tiles, 19%
+// faster than 1.5 rounds of 256x192, and the 1558M fc forward (8192 x 6400,
+// 2.9 rounds) 10-15% faster than 256x192.  Where it leaves CUs idle (the
+// 1558M attproj, 192 tiles) it was 4% slower than 224 tiles of 256x256, so
+// it is offered only when its tiles fill every CU at least once (fill).
 struct TileCfg {
     int bm, bn, wt, occ;
     double speed[3];  // forward, input gradient, weight gradient
     int max_n;        // largest N the tile is offered for (0: any)
+    bool fill;        // offered only with at least one tile per CU
 };
 const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
                             {256, 128, 64, 1, {0.92, 0.76, 0.66}, 0},
@@ -1330,6 +1342,7 @@ const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
                             // a power-of-two row count
                             {128, 192, 96, 1, {0.92, 0.0, 0.0}, 0},
                             {256, 192, 96, 1, {1.42, 0.0, 0.0}, 8192},
+                            {256, 288, 144, 1, {1.32, 0.0, 0.0}, 8192, true},
 };
 constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
 const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}, 0}};
@@ -1363,6 +1376,7 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
         const TileCfg& t = cfgs[c];
         if (t.max_n > 0 && d.N > t.max_n) continue;
         const long tiles = (long)((d.M + t.bm - 1) / t.bm) * ((d.N + t.bn - 1) / t.bn);
+        if (t.fill && tiles < num_cus) continue;
         const int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
         for (int s = 1; s <= max_split; s++) {
             const int kps = (ktiles + s - 1) / s;
@@ -1459,6 +1473,7 @@ int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, i
         }
         if (ch.wt == 96 && ch.bm == 128 && ch.bn == 192) return launch_epi<T, 128, 192, 96>(d, a, grid, slots, epi, s);
         if (ch.wt == 96 && ch.bm == 256 && ch.bn == 192) return launch_epi<T, 256, 192, 96>(d, a, grid, slots, epi, s);
+        if (ch.wt == 144 && ch.bm == 256 && ch.bn == 288) return launch_epi<T, 256, 288, 144>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 64>(d, a, grid, slots, epi, s);
