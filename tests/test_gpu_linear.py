@@ -77,8 +77,9 @@ def _tile_rows(n, seed, tile=256):
 
 # plus the qkv layer's exact shape (input gradient N = 768: fewer tiles than
 # CUs) and the tied classifier's (8192 x 768 from N = 50304: the K-split input
-# gradient, and a weight gradient of 197 x 3 tiles)
-@pytest.mark.parametrize("M,K,N", SHAPES[:2] + [(8192, 768, 2304), (8192, 768, 50304)])
+# gradient, and a weight gradient of 197 x 3 tiles), and an input gradient
+# ragged in M, N and K on 256 x 192 tiles (the 12-unit k-strided slab)
+@pytest.mark.parametrize("M,K,N", SHAPES[:2] + [(8192, 768, 2304), (8192, 768, 50304), (8100, 3064, 776)])
 def test_linear_backward(M, K, N):
     import torch
     import oracle

@@ -688,9 +688,38 @@ template <int BK>
 DEV int dtl_swz(int r) {
     return BK == 64 ? (r & 7) : ((r >> 1) & 3);
 }
+// Unit swizzle of a k-strided slab: contraction row k holds its R / 16 units
+// of 16 rows permuted by the key dtl_fk(k) -- an XOR for power-of-two unit
+// counts, a rotation otherwise.  The 16 contraction rows one transposing read
+// takes (k = 8 g + q, q < 4, g < 4) get keys 0..15 (mod the unit count), so
+// with a unit count that is a multiple of four, and so a row pitch that is a
+// multiple of 128 bytes, their units fall evenly on the four 32-byte bank
+// groups.
 template <int R>
-DEV int dtl_fk(int k) {  // unit swizzle of contraction row k in a k-strided slab
-    return ((k & 3) | (((k >> 3) & 3) << 2)) & (R / 16 - 1);
+DEV int dtl_fk(int k) {
+    constexpr int U = R / 16;
+    const int f = (k & 3) | (((k >> 3) & 3) << 2);
+    return (U & (U - 1)) == 0 ? (f & (U - 1)) : f % U;
+}
+template <int R>
+DEV int dtl_lds_unit(int g, int k) {  // LDS unit holding unit g of row k
+    constexpr int U = R / 16;
+    if constexpr ((U & (U - 1)) == 0) {
+        return g ^ dtl_fk<R>(k);
+    } else {
+        const int u = g - dtl_fk<R>(k);
+        return u < 0 ? u + U : u;
+    }
+}
+template <int R>
+DEV int dtl_glob_unit(int u, int k) {  // unit of row k held in LDS unit u
+    constexpr int U = R / 16;
+    if constexpr ((U & (U - 1)) == 0) {
+        return u ^ dtl_fk<R>(k);
+    } else {
+        const int g = u + dtl_fk<R>(k);
+        return g >= U ? g - U : g;
+    }
 }
 
 template <int R_, bool KMAJ_, int NW_, int BK_>
@@ -713,12 +742,9 @@ struct DtlSlab {
                 kc[q] = 8 * c;
                 off[q] = (uint32_t)(((long)r * ld + 8 * c) * 2);
             } else {
-                constexpr int KPI = 512 / R;  // contraction rows per 1 KB
-                const int p = 16 * lane;
-                const int k = j * KPI + p / (2 * R);
-                const int b = p % (2 * R);
-                const int u = (b >> 5) ^ dtl_fk<R>(k);
-                const int r = 16 * u + 8 * ((b >> 4) & 1);
+                const int e = 512 * j + 8 * lane;  // element of the slab, in LDS order
+                const int k = e / R, c = e % R;
+                const int r = 16 * dtl_glob_unit<R>(c >> 4, k) + (c & 8);
                 off[q] = (uint32_t)(((long)k * ld + r) * 2);
             }
         }
@@ -767,9 +793,9 @@ struct DtlFrag {
                 if constexpr (KMAJ) {
                     ofs[t][ks] = (rb + l16) * BK + (((4 * ks + g4) ^ dtl_swz<BK>(rb + l16)) << 3);
                 } else {
-                    const int fk = ((l16 >> 2) | (g4 << 2)) & (R / 16 - 1);  // dtl_fk of every row read here
+                    // (rows k and k + 4, the two transposing reads, share their unit key)
                     const int k = 32 * ks + 8 * g4 + (l16 >> 2);
-                    ofs[t][ks] = k * R + ((((rb >> 4) ^ fk)) << 4) + 4 * (l16 & 3);
+                    ofs[t][ks] = k * R + (dtl_lds_unit<R>(rb >> 4, k) << 4) + 4 * (l16 & 3);
                 }
             }
         }
@@ -1013,7 +1039,7 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
                 const int k = bkg * KPG + i;
                 const int m = 4 * bq;
                 const uint2 v = *reinterpret_cast<const uint2*>(
-                    a_s + k * BM + ((((m >> 4) ^ dtl_fk<BM>(k))) << 4) + (m & 15));
+                    a_s + k * BM + (dtl_lds_unit<BM>(m >> 4, k) << 4) + (m & 15));
                 bs[0] += __uint_as_float(v.x << 16);
                 bs[1] += __uint_as_float(v.x & 0xffff0000u);
                 bs[2] += __uint_as_float(v.y << 16);
@@ -1320,7 +1346,11 @@ struct Choice {
 // 11-14% faster than 128x192 and 256x128 (1.5 and 2 rounds of tiles against 3);
 // on the classifier (N = 50304, the weights streaming from HBM rather than
 // staying in L2) it is 5% slower than 256x256, so it is offered only up to
-// N = 8192 (max_n).  The 256x288 tile (8 waves of 64x144, two stages; the
+// N = 8192 (max_n).  On the input-gradient layout (B k-strided, a rotation
+// swizzle for its 12-unit slab) it takes the fcproj input gradient with the
+// GELU backward (8192 x 3072, K = 768) in 2 rounds instead of 3 of 128x256,
+// 6.5% faster, and the classifier input gradient in 2 K splits instead of 8
+// of 256x256 (4% faster).  The 256x288 tile (8 waves of 64x144, two stages; the
 // most MFMA work per fragment read of the tiles here) covers the 124M qkv
 // forward product (8192 x 2304) in exactly one round of 256 tiles, 19%
 // faster than 1.5 rounds of 256x192, and the 1558M fc forward (8192 x 6400,
@@ -1338,10 +1368,11 @@ const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
                             {128, 256, 64, 1, {0.71, 0.92, 0.70}, 0},
                             {128, 128, 64, 2, {0.81, 0.82, 0.70}, 0},
                             {256, 256, 128, 1, {1.00, 1.01, 1.00}, 0},
-                            // forward products only: a k-strided slab needs
-                            // a power-of-two row count
+                            // forward products only (128x192: equal to
+                            // 128x256 on the input gradients; 256x288: a
+                            // k-strided slab needs a multiple of 64 rows)
                             {128, 192, 96, 1, {0.92, 0.0, 0.0}, 0},
-                            {256, 192, 96, 1, {1.42, 0.0, 0.0}, 8192},
+                            {256, 192, 96, 1, {1.42, 0.98, 0.0}, 8192},
                             {256, 288, 144, 1, {1.32, 0.0, 0.0}, 8192, true},
 };
 constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
@@ -1416,8 +1447,9 @@ void launch_t(const Args& a, dim3 grid, int slots, hipStream_t s) {
 template <typename T, int BM, int BN, int WT>
 int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int slots, int epi, hipStream_t s) {
     const int lay = (d.a_kmajor ? 2 : 0) | (d.b_kmajor ? 1 : 0);
-    // k-strided slabs (input- and weight-gradient layouts) need power-of-two rows
-    constexpr bool KSTRIDED = (BM & (BM - 1)) == 0 && (BN & (BN - 1)) == 0;
+    // k-strided slabs (input- and weight-gradient layouts) need a multiple of
+    // four 16-row units (the swizzle's bank spread)
+    constexpr bool KSTRIDED = BM % 64 == 0 && BN % 64 == 0;
     if (lay != 3 && !KSTRIDED) return (int)hipErrorInvalidValue;
     if (lay == 3) {
         switch (epi) {
