@@ -1349,8 +1349,9 @@ struct Choice {
 // N = 8192 (max_n).  On the input-gradient layout (B k-strided, a rotation
 // swizzle for its 12-unit slab) it takes the fcproj input gradient with the
 // GELU backward (8192 x 3072, K = 768) in 2 rounds instead of 3 of 128x256,
-// 6.5% faster, and the classifier input gradient in 2 K splits instead of 8
-// of 256x256 (4% faster).  The 256x288 tile (8 waves of 64x144, two stages; the
+// 6.5% faster; on the classifier input gradient (2 K splits of 25k instead of
+// 8 of 256x256) it was 1.6% slower in the step, so it takes no K split
+// (max_split).  The 256x288 tile (8 waves of 64x144, two stages; the
 // most MFMA work per fragment read of the tiles here) covers the 124M qkv
 // forward product (8192 x 2304) in exactly one round of 256 tiles, 19%
 // faster than 1.5 rounds of 256x192, and the 1558M fc forward (8192 x 6400,
@@ -1362,6 +1363,7 @@ struct TileCfg {
     double speed[3];  // forward, input gradient, weight gradient
     int max_n;        // largest N the tile is offered for (0: any)
     bool fill;        // offered only with at least one tile per CU
+    int max_split;    // most K splits the tile is offered with (0: any)
 };
 const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
                             {256, 128, 64, 1, {0.92, 0.76, 0.66}, 0},
@@ -1372,7 +1374,7 @@ const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
                             // 128x256 on the input gradients; 256x288: a
                             // k-strided slab needs a multiple of 64 rows)
                             {128, 192, 96, 1, {0.92, 0.0, 0.0}, 0},
-                            {256, 192, 96, 1, {1.42, 0.98, 0.0}, 8192},
+                            {256, 192, 96, 1, {1.42, 0.98, 0.0}, 8192, false, 1},
                             {256, 288, 144, 1, {1.32, 0.0, 0.0}, 8192, true},
 };
 constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
@@ -1408,7 +1410,8 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
         if (t.max_n > 0 && d.N > t.max_n) continue;
         const long tiles = (long)((d.M + t.bm - 1) / t.bm) * ((d.N + t.bn - 1) / t.bn);
         if (t.fill && tiles < num_cus) continue;
-        const int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
+        int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
+        if (t.max_split > 0) max_split = std::min(max_split, t.max_split);
         for (int s = 1; s <= max_split; s++) {
             const int kps = (ktiles + s - 1) / s;
             const int sp = (ktiles + kps - 1) / kps;
