@@ -27,6 +27,9 @@ SHAPES = [(8232, 776, 3120), (8200, 3080, 776), (4104, 768, 50304), (8232, 776, 
 # tiles per workgroup (the persistent loop, next tile's stages issued before
 # the epilogue)
 SHAPES_288 = [(8192, 768, 2304), (8100, 776, 2296), (8200, 1608, 6392)]
+# products taken by the depth-sliced 128 x 192 tile (N <= 768, K >= 1536):
+# the MLP projection's shape, and ragged in M, N and K
+SHAPES_SLICED = [(8192, 3072, 768), (8100, 3080, 760)]
 
 
 def _rows(M, n, seed):
@@ -41,7 +44,7 @@ def _bf16_close(got, ref):
     return float(np.max(np.abs(got - ref) - tol))
 
 
-@pytest.mark.parametrize("M,K,N", SHAPES + SHAPES_288)
+@pytest.mark.parametrize("M,K,N", SHAPES + SHAPES_288 + SHAPES_SLICED)
 def test_linear_forward_bias(M, K, N):
     import torch
     import oracle
@@ -78,8 +81,11 @@ def _tile_rows(n, seed, tile=256):
 # plus the qkv layer's exact shape (input gradient N = 768: fewer tiles than
 # CUs) and the tied classifier's (8192 x 768 from N = 50304: the K-split input
 # gradient, and a weight gradient of 197 x 3 tiles), and an input gradient
-# ragged in M, N and K on 256 x 192 tiles (the 12-unit k-strided slab)
-@pytest.mark.parametrize("M,K,N", SHAPES[:2] + [(8192, 768, 2304), (8192, 768, 50304), (8100, 3064, 776)])
+# ragged in M, N and K on 256 x 192 tiles (the 12-unit k-strided slab), and
+# input gradients on the depth-sliced 128 x 192 tile (the fc layer's shape,
+# and ragged)
+@pytest.mark.parametrize("M,K,N", SHAPES[:2] + [(8192, 768, 2304), (8192, 768, 50304), (8100, 3064, 776),
+                                               (8192, 768, 3072), (8100, 760, 3080)])
 def test_linear_backward(M, K, N):
     import torch
     import oracle

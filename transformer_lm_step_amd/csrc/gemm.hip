@@ -49,9 +49,10 @@ namespace {
 
 constexpr int NTHREADS = 256;
 
-template <typename T, int BM_, int BN_, int WTM_ = 64, int WTN_ = 64>
+template <typename T, int BM_, int BN_, int WTM_ = 64, int WTN_ = 64, int SK_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
+    static constexpr int SK = SK_;  // waves sharing one output tile, each a slice of every stage's depth
     static constexpr int BK = 128 / (int)sizeof(T);  // contraction depth per stage
     static constexpr int PAD = 16 / (int)sizeof(T);
     static constexpr int LDSK = BK + PAD;            // LDS row pitch (elements)
@@ -59,7 +60,7 @@ struct Tile {
     static constexpr int KSTEPS = BK / 32;           // MFMA steps per stage
     static constexpr int WTM = WTM_, WTN = WTN_;     // output tile of one wave
     static constexpr int WM = BM / WTM, WN = BN / WTN;
-    static constexpr int NT = 64 * WM * WN;          // threads per workgroup
+    static constexpr int NT = 64 * WM * WN * SK;     // threads per workgroup
     static constexpr int TM = WTM / 16, TN = WTN / 16;  // 16x16 MFMA tiles per wave
     static constexpr int OCC = NT == 256 && WTM == 64 && WTN == 64 ? 2 : 1;  // workgroups per CU
     // slab prefetch distance and fragment buffers, within the register budget
@@ -71,10 +72,12 @@ struct Tile {
 
 // Wave tile selector used by the kernels' template argument WT: 64 -> 64x64,
 // 96 -> 64x96, 128 -> 128x64, 144 -> 64x144 outputs per wave (128x128 waves
-// need 256 accumulators per lane, which the compiler only fits by spilling).
+// need 256 accumulators per lane, which the compiler only fits by spilling);
+// 97 -> 64x96 with the depth sliced: two waves per output tile, each taking
+// one 32-deep half of every stage, their sums added at the end.
 template <typename T, int BM, int BN, int WT>
 using TileOf = Tile<T, BM, BN, (WT == 128 || WT == 256 ? 128 : 64),
-                    (WT == 256 ? 128 : WT == 96 ? 96 : WT == 144 ? 144 : 64)>;
+                    (WT == 256 ? 128 : WT == 96 || WT == 97 ? 96 : WT == 144 ? 144 : 64), (WT == 97 ? 2 : 1)>;
 
 // Per-thread register count for staging an R x BK slab (both layouts).
 template <int R, int NT> struct StageRegs {
@@ -264,7 +267,7 @@ DEV void gemm_epilogue(const Args& g, const f32x4_t (&acc)[TL::TM][TL::TN], int 
     // auxiliary reads in groups of G tile rows (at most 32 registers per
     // group); group gi + 1 is requested before group gi is stored.  With 16
     // waves per workgroup (128 registers per lane) one tile row at a time.
-    constexpr bool TIGHT = TL::NT >= 1024;
+    constexpr bool TIGHT = TL::NT >= 1024 || TL::SK > 1;
     constexpr int RPR = (int)sizeof(Raw) / 4;
     constexpr int G = !HAS_AUX ? TM : TIGHT ? 1 : (TM * TN * RPR <= 32 ? TM : std::max(1, 32 / (TN * RPR)));
     constexpr int NBUF = HAS_AUX && !TIGHT ? 2 : 1;
@@ -780,22 +783,23 @@ DEV void dtl_issue(const uint32_t* off, const int* kc, bf16_t* dst, const bf16_t
 
 // Per-lane element offsets of the fragment reads of one operand: KT tiles of 16
 // rows starting at wave row wb, for each 32-deep MFMA step of a stage.
-template <int R, bool KMAJ, int KT, int BK>
+template <int R, bool KMAJ, int KT, int BK, int NKS = BK / 32>
 struct DtlFrag {
-    static constexpr int KS = BK / 32;
+    static constexpr int KS = NKS;
     int ofs[KT][KS];  // [tile][step] (k-strided: the first of the two transpose reads)
-    DEV void init(int wb, int l16, int g4) {
+    DEV void init(int wb, int l16, int g4, int ks0 = 0) {
 #pragma unroll
         for (int t = 0; t < KT; t++) {
             const int rb = wb + 16 * t;
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
+            for (int kk = 0; kk < KS; kk++) {
+                const int ks = ks0 + kk;
                 if constexpr (KMAJ) {
-                    ofs[t][ks] = (rb + l16) * BK + (((4 * ks + g4) ^ dtl_swz<BK>(rb + l16)) << 3);
+                    ofs[t][kk] = (rb + l16) * BK + (((4 * ks + g4) ^ dtl_swz<BK>(rb + l16)) << 3);
                 } else {
                     // (rows k and k + 4, the two transposing reads, share their unit key)
                     const int k = 32 * ks + 8 * g4 + (l16 >> 2);
-                    ofs[t][ks] = k * R + (dtl_lds_unit<R>(rb >> 4, k) << 4) + 4 * (l16 & 3);
+                    ofs[t][kk] = k * R + (dtl_lds_unit<R>(rb >> 4, k) << 4) + 4 * (l16 & 3);
                 }
             }
         }
@@ -835,7 +839,7 @@ constexpr bool dtl_rp() {
     using TL = TileOf<bf16_t, BM, BN, WT>;
     constexpr int per_simd = (TL::NT / 64) * TL::OCC / 4;
     constexpr int regs = 512 / (per_simd < 1 ? 1 : per_simd);
-    constexpr int KS = DtlCfg<BM, BN>::BK / 32;
+    constexpr int KS = DtlCfg<BM, BN>::BK / 32 / TL::SK;
     constexpr bool fits = 2 * (TL::TM + TL::TN) * KS * 4 + TL::TM * TL::TN * 4 + 48 <= regs;
     return per_simd <= 1 ? fits : fits && AK && !BKM && (EPI == GEMM_STORE || EPI == GEMM_GELU_BWD);
 }
@@ -843,7 +847,7 @@ constexpr bool dtl_rp() {
 template <int BM, int BN, int WT, int EPI, bool BIAS>
 constexpr bool dtl_persistent() {
     constexpr int NT = TileOf<bf16_t, BM, BN, WT>::NT;
-    if (BIAS) return false;
+    if (BIAS || TileOf<bf16_t, BM, BN, WT>::SK > 1) return false;
     return EPI == GEMM_STORE || EPI == GEMM_BIAS || (EPI == GEMM_BIAS_GELU && NT <= 512);
 }
 
@@ -884,7 +888,8 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
     static_assert(!GRP || (EPI == GEMM_ACCUM && !AK && !BKM), "grouped launches are weight-gradient products");
     using TL = TileOf<T, BM, BN, WT>;
     constexpr int TM = TL::TM, TN = TL::TN, NT = TL::NT, NW = NT / 64;
-    constexpr int BK = DtlCfg<BM, BN>::BK, NS = DtlCfg<BM, BN>::NS, KS = BK / 32;
+    constexpr int BK = DtlCfg<BM, BN>::BK, NS = DtlCfg<BM, BN>::NS, SK = TL::SK, KS = BK / 32 / SK;
+    static_assert(SK == 1 || (SK == 2 && BK / 32 == 2 && !BIAS && !GRP), "two depth slices of a 64-deep stage");
     static_assert(!BIAS || !AK, "the fused bias sum reads a k-strided A slab");
     // one LDS array per stage and operand, so the compiler can tell which
     // buffer an LDS-destination load writes and which one a fragment read uses
@@ -902,7 +907,10 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
     // (the wave index is the same in all lanes; readfirstlane lets the
     // compiler see that, so branches on it are scalar)
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % TL::WM, wn = wave / TL::WM;
+    // SK = 2: waves w and w + WM * WN hold the same outputs over the two
+    // 32-deep halves of every stage
+    const int kslice = wave / (TL::WM * TL::WN), wsub = wave % (TL::WM * TL::WN);
+    const int wm = wsub % TL::WM, wn = wsub / TL::WM;
     const int l16 = lane & 15, g4 = lane >> 4;
 
     // Tiles are numbered u = 0 .. ntiles-1 and mapped so that the tiles of
@@ -1007,10 +1015,10 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
     DtlSlab<BN, BKM, NL, BK> dB;
     dA.init(g.lda, lane, lw);
     dB.init(g.ldb, lane, lw);
-    DtlFrag<BM, AK, TM, BK> fA;
-    DtlFrag<BN, BKM, TN, BK> fB;
-    fA.init(wm * TL::WTM, l16, g4);
-    fB.init(wn * TL::WTN, l16, g4);
+    DtlFrag<BM, AK, TM, BK, KS> fA;
+    DtlFrag<BN, BKM, TN, BK, KS> fB;
+    fA.init(wm * TL::WTM, l16, g4, kslice * KS);
+    fB.init(wn * TL::WTN, l16, g4, kslice * KS);
     constexpr int NQS = DtlSlab<BM, AK, NL, BK>::NQ + DtlSlab<BN, BKM, NL, BK>::NQ;
     static_assert((NS - 1) * NQS <= 63, "vmcnt range");
 
@@ -1207,6 +1215,30 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
                 if constexpr (NS > 3) GEMM_DTL_STAGE(3)
             }
         }
+        if constexpr (SK == 2) {
+            // the two slices swap their partial sums one accumulator row at a
+            // time (each slice's row in a slab of its own) and both add: fp32
+            // addition commutes, so both hold the same sum; slice 1 then ends
+            float* const mine = reinterpret_cast<float*>(kslice == 0 ? sB0 : sB1);
+            const float* const other = reinterpret_cast<const float*>(kslice == 0 ? sB1 : sB0);
+            static_assert((NT / 2) * TN * 16 <= BN * BK * 2, "a slice's accumulator row fits one B slab");
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the last fragment reads are done
+            asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    *reinterpret_cast<f32x4_t*>(mine + ((wsub * TN + j) * 64 + lane) * 4) = acc[i][j];
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = acc[i][j] + *reinterpret_cast<const f32x4_t*>(other + ((wsub * TN + j) * 64 + lane) * 4);
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                asm volatile("s_barrier" ::: "memory");
+            }
+            if (kslice != 0) return;
+        }
         // the bias (its load landed before the first stage's), added after the
         // sum as the epilogue would: the same rounding
         add_bias();
@@ -1245,7 +1277,7 @@ gemm_dtl_kernel(const KernArgs<GRP> ka) {
         T* const lastB = NS == 2 ? sB1 : NS == 3 ? sB2 : sB3;
         T* const stage = STAGE_TWO ? (wave < NW / 2 ? lastA : lastB) + (wave % (NW / 2)) * 16 * (TL::WTN + 8)
                                    : (BN >= BM ? lastB : lastA) + wave * 16 * (TL::WTN + 8);
-        if (CAN_STAGE && !more) {
+        if (CAN_STAGE && !more && SK == 1) {
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
             asm volatile("s_barrier" ::: "memory");
         }
@@ -1358,12 +1390,20 @@ struct Choice {
 // 2.9 rounds) 10-15% faster than 256x192.  Where it leaves CUs idle (the
 // 1558M attproj, 192 tiles) it was 4% slower than 224 tiles of 256x256, so
 // it is offered only when its tiles fill every CU at least once (fill).
+// The depth-sliced 128x192 tile (8 waves: two per 64x96 output tile, one per
+// 32-deep half of each stage, partial sums swapped through LDS at the end)
+// keeps the 256 tiles of the N = 768 products with two waves per SIMD
+// instead of one: fc and qkv input gradients 11-17% faster than 128x256,
+// fcproj forward 9-12% faster than the 4-wave 128x192.  With K = 768 the
+// final exchange is not paid back (attproj forward 4% slower), so it is
+// offered from K = 1536 (min_k), and without K splits.
 struct TileCfg {
     int bm, bn, wt, occ;
     double speed[3];  // forward, input gradient, weight gradient
     int max_n;        // largest N the tile is offered for (0: any)
     bool fill;        // offered only with at least one tile per CU
     int max_split;    // most K splits the tile is offered with (0: any)
+    int min_k;        // shortest contraction the tile is offered for (0: any)
 };
 const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
                             {256, 128, 64, 1, {0.92, 0.76, 0.66}, 0},
@@ -1376,6 +1416,7 @@ const TileCfg kCfgBf16[] = {{256, 256, 64, 1, {0.99, 1.00, 0.75}, 0},
                             {128, 192, 96, 1, {0.92, 0.0, 0.0}, 0},
                             {256, 192, 96, 1, {1.42, 0.98, 0.0}, 8192, false, 1},
                             {256, 288, 144, 1, {1.32, 0.0, 0.0}, 8192, true},
+                            {128, 192, 97, 1, {1.045, 0.80, 0.0}, 8192, false, 1, 1536},
 };
 constexpr int kNumCfgBf16 = sizeof(kCfgBf16) / sizeof(kCfgBf16[0]);
 const TileCfg kCfgF32[] = {{128, 128, 64, 2, {1.0, 1.0, 1.0}, 0}};
@@ -1408,6 +1449,7 @@ Choice choose(const GemmDesc& d, int elem_bytes, int num_cus) {
     for (int c = 0; c < ncfg; c++) {
         const TileCfg& t = cfgs[c];
         if (t.max_n > 0 && d.N > t.max_n) continue;
+        if (t.min_k > 0 && d.K < t.min_k) continue;
         const long tiles = (long)((d.M + t.bm - 1) / t.bm) * ((d.N + t.bn - 1) / t.bn);
         if (t.fill && tiles < num_cus) continue;
         int max_split = can_split ? std::min(32, std::max(1, ktiles / 4)) : 1;
@@ -1481,6 +1523,8 @@ int launch_epi(const GemmDesc& d, const Args& a, dim3 grid, int slots, int epi, 
             case GEMM_GELU_BWD: launch_t<T, BM, BN, WT, true, false, GEMM_GELU_BWD, T>(a, grid, slots, s); return 0;
             case EPI_SPLIT: launch_t<T, BM, BN, WT, true, false, EPI_SPLIT, float>(a, grid, slots, s); return 0;
         }
+    } else if constexpr (TileOf<T, BM, BN, WT>::SK > 1) {
+        return (int)hipErrorInvalidValue;  // depth-sliced tiles: forward and input-gradient layouts
     } else if (lay == 0) {
         const bool bias = a.dbias != nullptr;
         switch (epi) {
@@ -1509,6 +1553,7 @@ int launch_tile(const GemmDesc& d, const Args& a, const Choice& ch, dim3 grid, i
         if (ch.wt == 96 && ch.bm == 128 && ch.bn == 192) return launch_epi<T, 128, 192, 96>(d, a, grid, slots, epi, s);
         if (ch.wt == 96 && ch.bm == 256 && ch.bn == 192) return launch_epi<T, 256, 192, 96>(d, a, grid, slots, epi, s);
         if (ch.wt == 144 && ch.bm == 256 && ch.bn == 288) return launch_epi<T, 256, 288, 144>(d, a, grid, slots, epi, s);
+        if (ch.wt == 97 && ch.bm == 128 && ch.bn == 192) return launch_epi<T, 128, 192, 97>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 256) return launch_epi<T, 256, 256, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 256 && ch.bn == 128) return launch_epi<T, 256, 128, 64>(d, a, grid, slots, epi, s);
         if (ch.bm == 128 && ch.bn == 256) return launch_epi<T, 128, 256, 64>(d, a, grid, slots, epi, s);
