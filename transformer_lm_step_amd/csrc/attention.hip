@@ -72,15 +72,20 @@ DEV void attn_block(int nb, int NH, int& blk, int& h, int& b) {
 // hands out workgroup ids in passes of one per CU: a CU's resident blocks
 // come from the same position of consecutive passes.  Issued longest-first,
 // a CU would take the longest block of every pass (up to 1.3 times the mean
-// work); reversing the second of the resident passes, in groups of 8 ids so
+// work); reversing every second one of the resident passes, in groups of 8 ids so
 // that every id keeps its XCD, pairs a long block with short ones (within 4%
 // of the mean).  Later passes (larger launches) start as slots free up and
-// keep the longest-first order.  P: CUs per pass (a multiple of 8).
-constexpr int kAttnCUs = 256, kAttnFwdResident = 3;
-DEV void attn_block_snake(int nb, int NH, int P, int& blk, int& h, int& b) {
+// keep the longest-first order.  P: CUs per pass (a multiple of 8).  The
+// backward kernels use the same order with their own resident counts: dQ
+// holds five 4-wave workgroups per CU (94 registers, 32 KB of LDS), dK/dV
+// four (121 registers, 33 KB); there the reversal took the pair from 82 to
+// 80 µs at the GPT-2 124M layer shape (1.5 rounds of 1536 workgroups, the
+// later ones filling slots as they free up).
+constexpr int kAttnCUs = 256, kAttnFwdResident = 3, kAttnDqResident = 5, kAttnDkdvResident = 4;
+DEV void attn_block_snake(int nb, int NH, int P, int resident, int& blk, int& h, int& b) {
     int o = blockIdx.x;
     const int pass = o / P, j = o - pass * P;
-    if ((pass & 1) && pass < kAttnFwdResident && (pass + 1) * P <= (int)gridDim.x)
+    if ((pass & 1) && pass < resident && (pass + 1) * P <= (int)gridDim.x)
         o = pass * P + (P - 8 - (j & ~7)) + (j & 7);
     const int nhb = gridDim.x / nb;
     blk = o / nhb;
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_fwd_dtl_kernel(bf16_t*
     const int l16 = lane & 15, g4 = lane >> 4;
     const int nb = (T_ + QR - 1) / QR;
     int blk, h, b;
-    attn_block_snake(nb, NH, kAttnCUs, blk, h, b);
+    attn_block_snake(nb, NH, kAttnCUs, kAttnFwdResident, blk, h, b);
     const int qb = nb - 1 - blk;
     const long rs = 3L * C;
     const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
@@ -897,7 +902,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dtl_kernel(bf16_t* __res
     const int l16 = lane & 15, g4 = lane >> 4;
     const int nqb = (T_ + 63) / 64;
     int kb, h, b;
-    attn_block(nqb, NH, kb, h, b);
+    attn_block_snake(nqb, NH, kAttnCUs, kAttnDkdvResident, kb, h, b);
     const long rs = 3L * C;
     const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
     const bf16_t* Kh = Qh + C;
@@ -1035,7 +1040,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dtl_kernel(bf16_t* __restr
     const int l16 = lane & 15, g4 = lane >> 4;
     const int nb = (T_ + 63) / 64;
     int blk, h, b;
-    attn_block(nb, NH, blk, h, b);
+    attn_block_snake(nb, NH, kAttnCUs, kAttnDqResident, blk, h, b);
     const int qb = nb - 1 - blk;
     const long rs = 3L * C;
     const bf16_t* Qh = qkv + (long)b * T_ * rs + h * HS;
