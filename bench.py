@@ -675,8 +675,9 @@ def bench_gpt2(args):
         f"(6N+12LCT: {mfu_6n:.3f}), wall {wall:.2f}s, "
         f"loss first {losses[0]:.4f} last {losses[-1]:.4f}")
 
-    # ---- dominant kernel: the one launch of every weight gradient of a
-    # micro-step, its launches inside the timed steps
+    # ---- dominant kernel: the weight-gradient launches of a micro-step (one
+    # grouped launch, followed by the attention projections' own launch on
+    # 128x256 tiles where that saves a round of tiles), inside the timed steps
     kms = float(np.mean([hip.elapsed_ms(a, b) for a, b in zip(starts, ends)]))
     hip.destroy(starts + ends)
     L, C, Vp = cfg.num_layers, cfg.channels, cfg.padded_vocab_size
@@ -686,7 +687,8 @@ def bench_gpt2(args):
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": f"gemm_dtl_kernel, grouped weight gradients (classifier {Vp}x{C} + {L} layers x "
-                          f"4 products, K = B*T = {BT}, bf16, in-step launches)",
+                          f"4 products, K = B*T = {BT}, bf16, in-step launches; the attention projections "
+                          f"in a second launch on 128x256 tiles where that saves a round)",
                 "avg_ms": round(kms, 4), "launches": n_ev}
     log(f"bench: weight-gradient launch in the step {kms:.3f} ms, {achieved:.1f} TFLOP/s")
 

@@ -1623,8 +1623,9 @@ int gemm_launch_t(const GemmDesc& d, float* ws, size_t ws_bytes, int num_cus, hi
 
 }  // namespace
 
-int gemm_dw_group_launch(const GemmGroupItem* items, int n, hipStream_t s) {
-    constexpr int BM = 256, BN = 256, WT = 128;
+namespace {
+template <int BM, int BN, int WT>
+int dw_group_t(const GemmGroupItem* items, int n, hipStream_t s) {
     if (n < 1 || n > kMaxGroup || !items) return (int)hipErrorInvalidValue;
     GroupArgs ga = {};
     long total = 0;
@@ -1650,6 +1651,21 @@ int gemm_dw_group_launch(const GemmGroupItem* items, int n, hipStream_t s) {
     hipLaunchKernelGGL((gemm_dtl_kernel<BM, BN, WT, false, false, GEMM_ACCUM, float, true, true>), dim3((unsigned)total),
                        dim3(TL::NT), 0, s, ga);
     return (int)hipGetLastError();
+}
+}  // namespace
+
+int gemm_dw_group_launch(const GemmGroupItem* items, int n, hipStream_t s, int tile) {
+    if (tile == 0) return dw_group_t<256, 256, 128>(items, n, s);
+    if (tile == 1) return dw_group_t<128, 256, 64>(items, n, s);
+    return (int)hipErrorInvalidValue;
+}
+
+long gemm_dw_group_tiles(const GemmGroupItem* items, int n, int tile) {
+    const int bm = tile == 0 ? 256 : 128, bn = 256;
+    long t = 0;
+    for (int i = 0; i < n; i++)
+        t += (long)((items[i].M + bm - 1) / bm) * ((items[i].N + bn - 1) / bn) * items[i].count;
+    return t;
 }
 
 size_t gemm_workspace_bytes(const GemmDesc& d, int elem_bytes, int num_cus) {

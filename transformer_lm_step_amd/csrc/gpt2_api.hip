@@ -351,7 +351,12 @@ int forward_impl(gpt2_ctx* c, const int32_t* inputs, const int32_t* targets, flo
 // dW += dY^T X (M = OC, N = IC, K = BT) and db += column sums of dY for
 // layers l0 .. l1 - 1 in one launch (and the classifier's tied-weight
 // gradient first in the tile order when cls: its 197 x 3 tiles are the
-// largest product)
+// largest product).  Every tile of that launch runs the whole contraction,
+// so it takes ceil(tiles / CUs) rounds of about equal length; when leaving
+// the attention projections (C x C products) out saves a round and their own
+// launch on 128x256 tiles (half the work per tile, about 0.71 of a round
+// each) costs less, they follow in a second launch (124M at B*T = 8192:
+// 1887 tiles, 8 rounds, become 1779 + 216 half tiles).
 int dw_group(gpt2_ctx* c, int l0, int l1, bool cls, hipStream_t s) {
     const Plan& p = c->plan;
     const int BT = (int)p.BT, C = (int)p.C, Vp = (int)p.Vp;
@@ -359,7 +364,7 @@ int dw_group(gpt2_ctx* c, int l0, int l1, bool cls, hipStream_t s) {
     const long sbtc = (long)(p.s_btc / e), sbt4c = (long)(p.s_bt4c / e), sbt3c = (long)(p.s_bt3c / e);
     const float alpha = c->dw_alpha;
     GemmGroupItem it[5];
-    int n = 0;
+    int n = 0, ia = -1;
     auto item = [&](const void* A, long lda, long sA, const void* Bm, long ldb, long sB, float* Cm, long sC, float* db,
                     long sdb, int M, int N, int cnt, float a) {
         GemmGroupItem& g = it[n++];
@@ -379,11 +384,27 @@ int dw_group(gpt2_ctx* c, int l0, int l1, bool cls, hipStream_t s) {
         // attproj: dY = residual gradient entering it (slots 2l + 1), X = attention output
         item(act(p.dres_lp + p.s_btc, 2 * p.s_btc, l0), C, 2 * sbtc, act(p.atty, p.s_btc, l0), C, sbtc,
              grd(c, 6, l0, CC), (long)CC, grd(c, 7, l0, C), C, C, C, cnt, 1.0f);
+        ia = n - 1;
         // qkv: dY = qkv gradient, X = ln1
         item(act(p.dqkv, p.s_bt3c, l0), 3 * C, sbt3c, act(p.ln1, p.s_btc, l0), C, sbtc, grd(c, 4, l0, 3 * CC),
              (long)(3 * CC), grd(c, 5, l0, 3 * C), 3 * C, 3 * C, C, cnt, 1.0f);
     }
-    return n ? gemm_dw_group_launch(it, n, s) : 0;
+    if (n == 0) return 0;
+    if (ia >= 0 && n > 1) {
+        GemmGroupItem rest[5];
+        int nr = 0;
+        for (int i = 0; i < n; i++)
+            if (i != ia) rest[nr++] = it[i];
+        auto rounds = [](long tiles) { return (tiles + kPlanCUs - 1) / kPlanCUs; };
+        const long r_all = rounds(gemm_dw_group_tiles(it, n, 0));
+        const long r_rest = rounds(gemm_dw_group_tiles(rest, nr, 0));
+        const long r_att = rounds(gemm_dw_group_tiles(&it[ia], 1, 1));
+        if ((double)r_rest + 0.71 * (double)r_att < (double)r_all - 0.1) {
+            const int e = gemm_dw_group_launch(rest, nr, s, 0);
+            return e ? e : gemm_dw_group_launch(&it[ia], 1, s, 1);
+        }
+    }
+    return gemm_dw_group_launch(it, n, s, 0);
 }
 
 template <typename T>

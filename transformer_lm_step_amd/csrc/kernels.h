@@ -41,8 +41,9 @@ struct GemmDesc {
 //   C_l[m,n] += alpha * sum_k A_l[k*lda + m] * B_l[k*ldb + n]
 //   dbias_l[m] += alpha * sum_k A_l[k*lda + m]          (when dbias != NULL)
 // for product l = 0 .. count-1 of each item, with X_l = X + l * sX (elements).
-// Up to 8 items; no K split and no workspace (one 256x256 tile per workgroup
-// over the whole contraction).  Returns 0 or a hipError_t.
+// Up to 8 items; no K split and no workspace (one tile per workgroup over the
+// whole contraction; tile 0: 256x256 with 128x64 outputs per wave, tile 1:
+// 128x256 with 64x64 per wave).  Returns 0 or a hipError_t.
 struct GemmGroupItem {
     const void* A; long lda; long sA;
     const void* B; long ldb; long sB;
@@ -51,7 +52,9 @@ struct GemmGroupItem {
     int M, N, K, count;
     float alpha;
 };
-int gemm_dw_group_launch(const GemmGroupItem* items, int n, hipStream_t s);
+int gemm_dw_group_launch(const GemmGroupItem* items, int n, hipStream_t s, int tile = 0);
+// Workgroups (tiles) such a launch takes.
+long gemm_dw_group_tiles(const GemmGroupItem* items, int n, int tile);
 // Row softmax from the per-64-column partials of GEMM_BIAS_GELU_SMX:
 // Y[m, :] = exp(Y[m, :] - M_m) / S_m, in place (fp32, N % 4 == 0).
 int softmax_finish_launch(float* Y, const float2* part, int M, int N, int np, hipStream_t s);

@@ -81,7 +81,11 @@ extern "C" int gpt2_linear_backward(int precision, const void* dy, const void* x
         GemmGroupItem it = {};
         it.A = dy; it.lda = N; it.B = x; it.ldb = K; it.C = dw; it.ldc = K; it.dbias = db;
         it.M = N; it.N = K; it.K = M; it.count = 1; it.alpha = alpha;
-        if (gemm_dw_group_launch(&it, 1, s) != 0) return GPT2_E_HIP;
+        // 128x256 tiles (half the work each, about 0.71 of a 256x256 tile's
+        // time) where they take fewer rounds of the 256 CUs' worth
+        const long r0 = (gemm_dw_group_tiles(&it, 1, 0) + 255) / 256, r1 = (gemm_dw_group_tiles(&it, 1, 1) + 255) / 256;
+        const int tile = 0.71 * (double)r1 < (double)r0 - 0.1 ? 1 : 0;
+        if (gemm_dw_group_launch(&it, 1, s, tile) != 0) return GPT2_E_HIP;
     } else if (dw) {
         const GemmDesc d = bwd_dw_desc(dy, x, dw, db, M, N, K, alpha);
         const size_t need = gemm_workspace_bytes(d, esz, 256);
