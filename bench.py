@@ -11,8 +11,9 @@ in HBM before the timed region.
 
 Prints one JSON line: train tokens/s over the timed steps, MFU against the
 2.5 PFLOP/s dense bf16 peak, the roofline position of the dominant kernel
-(the one launch of every weight gradient, timed with HIP events that the
-library records around it inside the timed steps, on the step's stream), the
+(the grouped launches of every weight gradient of a micro-step, timed with
+HIP events that the library records around them inside the timed steps, on
+the step's stream), the
 position of every kernel family from two further instrumented steps, and the
 CPU oracle timed on a bounded sample of the same workload.
 
@@ -358,7 +359,7 @@ def main():
 # and the algorithmic work of each launch, in launch order per call
 
 FAMILIES = [  # (name, timing point, bound)
-    ("weight gradients (all layers + classifier, one launch)", "WEIGHT_GRAD", "mfma"),
+    ("weight gradients (all layers + classifier, grouped launches)", "WEIGHT_GRAD", "mfma"),
     ("classifier forward", "CLASSIFIER_FWD", "mfma"),
     ("classifier input gradient", "CLASSIFIER_DX", "mfma"),
     ("layer forward products", "LAYER_FWD", "mfma"),
